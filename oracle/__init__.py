@@ -1,0 +1,136 @@
+"""Python handle on the CPU oracle (``oracle/moe_oracle.c``).
+
+TEST INFRASTRUCTURE ONLY: the tests, the smoke check and the benchmark's
+CPU-baseline leg are the only callers.  The product library never imports,
+loads or runs anything in this directory.
+
+All floating-point results come back as float64 numpy arrays.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "moe_oracle.c")
+LIB_PATH = os.path.join(_HERE, "liboracle.so")
+
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (plain C, OpenMP, no fast-math)."""
+    if force or not os.path.exists(LIB_PATH):
+        tmp = LIB_PATH + ".tmp"
+        cmd = ["gcc", "-std=c11", "-D_DEFAULT_SOURCE", "-O2", "-fno-fast-math",
+               "-ffp-contract=off", "-fopenmp", "-fPIC", "-shared", "-Wall",
+               "-Wextra", "-o", tmp, _SRC, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, LIB_PATH)
+    return LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            build(force=False)
+        lib = ctypes.CDLL(LIB_PATH)
+        P = ctypes.c_void_p
+        i32, i64, dbl = ctypes.c_int32, ctypes.c_int64, ctypes.c_double
+        lib.oracle_num_threads.restype = ctypes.c_int
+        lib.oracle_route.argtypes = [P, i64, i32, P, P, P, P, P]
+        lib.oracle_route.restype = ctypes.c_int
+        lib.oracle_tiles.argtypes = [P, P, i32, i32, i32, P, i64, P]
+        lib.oracle_tiles.restype = ctypes.c_int
+        lib.oracle_weight.argtypes = [P, P, P, i64, i64, i32, i64, i64, i64]
+        lib.oracle_weight.restype = dbl
+        lib.oracle_gelu_tanh.argtypes = [dbl]
+        lib.oracle_gelu_tanh.restype = dbl
+        lib.oracle_ffn_tokens.argtypes = [i32] * 6 + [P] * 9 + [P, i32, P, P, P]
+        lib.oracle_ffn_tokens.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def _ptr(a: Optional[np.ndarray]):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def num_threads() -> int:
+    return int(_load().oracle_num_threads())
+
+
+def route(ids: np.ndarray, E: int):
+    """Stable counting sort of the flat assignments by expert id.
+
+    Returns (counts[E], offsets[E+1], perm[A], inv_perm[A], n_invalid).
+    """
+    ids = np.ascontiguousarray(ids, dtype=np.int32).ravel()
+    A = ids.size
+    counts = np.zeros(E, np.int32)
+    offsets = np.zeros(E + 1, np.int32)
+    perm = np.zeros(max(A, 1), np.int32)
+    inv = np.zeros(max(A, 1), np.int32)
+    bad = np.zeros(1, np.int32)
+    rc = _load().oracle_route(_ptr(ids), A, E, _ptr(counts), _ptr(offsets),
+                              _ptr(perm), _ptr(inv), _ptr(bad))
+    if rc != 0:
+        raise ValueError(f"oracle_route failed ({rc})")
+    return counts, offsets, perm[:A], inv[:A], int(bad[0])
+
+
+def tiles(counts: np.ndarray, offsets: np.ndarray, bm_big: int = 32, bm_small: int = 16):
+    """Tile descriptors [n, 4] = {expert, row_begin, row_count, bm}."""
+    counts = np.ascontiguousarray(counts, dtype=np.int32)
+    offsets = np.ascontiguousarray(offsets, dtype=np.int32)
+    E = counts.size
+    nt = np.zeros(1, np.int32)
+    lib = _load()
+    rc = lib.oracle_tiles(_ptr(counts), _ptr(offsets), E, bm_big, bm_small, None, 0, _ptr(nt))
+    n = int(nt[0])
+    out = np.zeros((max(n, 1), 4), np.int32)
+    rc = lib.oracle_tiles(_ptr(counts), _ptr(offsets), E, bm_big, bm_small, _ptr(out), n, _ptr(nt))
+    if rc != 0:
+        raise ValueError(f"oracle_tiles failed ({rc})")
+    return out[:n]
+
+
+def weight(P: np.ndarray, S: np.ndarray, B: np.ndarray, gs: int, e: int, n: int, c: int) -> float:
+    """One dequantised weight W[e, n, c] of a packed [E, rows, K/8] matrix."""
+    E, rows, kw = P.shape
+    return float(_load().oracle_weight(_ptr(P), _ptr(S), _ptr(B), rows, kw * 8, gs, e, n, c))
+
+
+def gelu_tanh(v: float) -> float:
+    return float(_load().oracle_gelu_tanh(float(v)))
+
+
+def ffn_tokens(p, tokens=None, want_h: bool = True, want_y: bool = True,
+               want_out: bool = True):
+    """Expert FFN for a list of tokens of problem ``p`` (a moe_synth.Problem).
+
+    Returns dict with h [n*k, I], y [n*k, H] (unweighted), out [n, H]; row
+    i*k + j belongs to assignment tokens[i]*k + j.
+    """
+    if tokens is None:
+        tokens = np.arange(p.T, dtype=np.int32)
+    tokens = np.ascontiguousarray(tokens, dtype=np.int32)
+    n = tokens.size
+    h = np.zeros((n * p.k, p.I)) if want_h else None
+    y = np.zeros((n * p.k, p.H)) if want_y else None
+    out = np.zeros((n, p.H)) if want_out else None
+    arrs = [np.ascontiguousarray(a) for a in (p.x, p.topk_ids, p.topk_weights, p.w_gateup,
+                                              p.s_gateup, p.b_gateup, p.w_down, p.s_down,
+                                              p.b_down)]
+    assert arrs[1].dtype == np.int32 and arrs[2].dtype == np.float32
+    rc = _load().oracle_ffn_tokens(p.T, p.k, p.E, p.H, p.I, p.gs, *[_ptr(a) for a in arrs],
+                                   _ptr(tokens), n, _ptr(h), _ptr(y), _ptr(out))
+    if rc != 0:
+        raise ValueError(f"oracle_ffn_tokens failed ({rc})")
+    return dict(h=h, y=y, out=out, tokens=tokens)

@@ -1,0 +1,243 @@
+/*
+ * CPU oracle for the routed 4-bit MoE expert FFN (switch-GLU with a tanh-GELU
+ * product, "GeGLU").
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the
+ * benchmark's CPU-baseline leg may load this library.  It shares no code,
+ * header, table or helper with the HIP library, and the HIP library never
+ * calls it.
+ *
+ * Everything is the plain definition, written out in IEEE double:
+ *
+ *   route   counts, exclusive offsets, and a stable counting sort of the flat
+ *           assignment index a = t*k + j by expert id: the "sorted indices"
+ *           that the Layr-Labs/mlx PR #4 page ("What") feeds its expert-tile
+ *           kernel.
+ *   tiles   per expert, runs of at most bm_big sorted rows; a run of at most
+ *           bm_small rows is marked bm_small: the page's "BM32 expert tiles,
+ *           BM16 fallback rows" ("What"), emitted in expert order as its
+ *           scan-plus-upper-bound builder produces them.
+ *   weight  W[e,n,c] = S[e,n,c/gs] * q + B[e,n,c/gs], q the 4-bit code of
+ *           element c (low nibble first in each uint32 word): the affine
+ *           4-bit, group-size-64 format of the PR #4 page ("What"), with the
+ *           scale and bias widened before use (mlx-node PR #168 page: the
+ *           sidecars are promoted to f32 "either way").
+ *   gate|up g = x . W_gu[e, n, :], u = x . W_gu[e, I+n, :]  (PR #168 page:
+ *           one packed "MLP gate|up" projection split in two halves).
+ *   GeGLU   h = gelu_tanh(g) * u, with
+ *           gelu_tanh(v) = 0.5 v (1 + tanh(sqrt(2/pi) (v + 0.044715 v^3)))
+ *           (SwiftLM issue #236, "Still missing": activation(xGate) * xUp with
+ *           activation = geluApproximate).
+ *   down    y[a, m] = W_d[e, m, :] . h
+ *   combine out[t, m] = sum_j w[t, j] * y[t*k + j, m]  (SwiftLM issue #236
+ *           "Already on main": weightedExpertSum; PR #4 "Measured standing":
+ *           the direct weighted unsort back to token order).
+ *
+ * Expert ids outside [0, E) are not routed: they are counted, placed after all
+ * valid rows in the sorted order (ascending a), get no tile, and contribute
+ * zero to the combine.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define ORACLE_OK 0
+#define ORACLE_ERR_ARG (-1)
+#define ORACLE_ERR_ALLOC (-2)
+
+/* bf16 is the upper half of an IEEE binary32; widening is exact. */
+static double bf16_value(uint16_t bits) {
+    uint32_t u = (uint32_t)bits << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+int oracle_num_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+/* ---------------------------------------------------------------- route */
+
+int oracle_route(const int32_t* ids, int64_t A, int32_t E,
+                 int32_t* counts, int32_t* offsets, int32_t* perm,
+                 int32_t* inv_perm, int32_t* n_invalid) {
+    if (A < 0 || E <= 0 || (A > 0 && (!ids || !perm || !inv_perm)) || !counts ||
+        !offsets || !n_invalid)
+        return ORACLE_ERR_ARG;
+    int32_t* fill = (int32_t*)calloc((size_t)E, sizeof(int32_t));
+    if (!fill) return ORACLE_ERR_ALLOC;
+    for (int32_t e = 0; e < E; ++e) counts[e] = 0;
+    int32_t bad = 0;
+    for (int64_t a = 0; a < A; ++a) {
+        int32_t e = ids[a];
+        if (e >= 0 && e < E)
+            counts[e] += 1;
+        else
+            bad += 1;
+    }
+    offsets[0] = 0;
+    for (int32_t e = 0; e < E; ++e) offsets[e + 1] = offsets[e] + counts[e];
+    int32_t bad_fill = 0;
+    for (int64_t a = 0; a < A; ++a) {
+        int32_t e = ids[a];
+        int32_t s;
+        if (e >= 0 && e < E)
+            s = offsets[e] + fill[e]++;
+        else
+            s = offsets[E] + bad_fill++;
+        perm[s] = (int32_t)a;
+        inv_perm[a] = s;
+    }
+    *n_invalid = bad;
+    free(fill);
+    return ORACLE_OK;
+}
+
+/* tiles: 4 int32 per tile {expert, row_begin, row_count, bm}. */
+int oracle_tiles(const int32_t* counts, const int32_t* offsets, int32_t E,
+                 int32_t bm_big, int32_t bm_small, int32_t* tiles,
+                 int64_t max_tiles, int32_t* num_tiles) {
+    if (!counts || !offsets || E <= 0 || bm_big <= 0 || bm_small <= 0 ||
+        bm_small > bm_big || !num_tiles)
+        return ORACLE_ERR_ARG;
+    int64_t nt = 0;
+    for (int32_t e = 0; e < E; ++e) {
+        for (int32_t done = 0; done < counts[e]; done += bm_big) {
+            int32_t rows = counts[e] - done;
+            if (rows > bm_big) rows = bm_big;
+            if (nt < max_tiles && tiles) {
+                tiles[4 * nt + 0] = e;
+                tiles[4 * nt + 1] = offsets[e] + done;
+                tiles[4 * nt + 2] = rows;
+                tiles[4 * nt + 3] = (rows <= bm_small) ? bm_small : bm_big;
+            }
+            ++nt;
+        }
+    }
+    *num_tiles = (int32_t)nt;
+    return nt <= max_tiles ? ORACLE_OK : ORACLE_ERR_ARG;
+}
+
+/* ------------------------------------------------------------- weights */
+
+/* The 4-bit code of column c in one packed row (8 codes per word, low nibble
+ * first). */
+static int32_t code_at(const uint32_t* packed_row, int64_t c) {
+    uint32_t word = packed_row[c / 8];
+    return (int32_t)((word >> (4 * (c % 8))) & 15u);
+}
+
+/* Dequantised weight W[e, n, c] of a [E, rows, K] matrix. */
+double oracle_weight(const uint32_t* P, const uint16_t* S, const uint16_t* B,
+                     int64_t rows, int64_t K, int32_t gs, int64_t e, int64_t n,
+                     int64_t c) {
+    const int64_t row = e * rows + n;
+    const int64_t groups = K / gs;
+    double s = bf16_value(S[row * groups + c / gs]);
+    double b = bf16_value(B[row * groups + c / gs]);
+    return s * (double)code_at(P + row * (K / 8), c) + b;
+}
+
+double oracle_gelu_tanh(double v) {
+    const double k0 = sqrt(2.0 / M_PI);
+    return 0.5 * v * (1.0 + tanh(k0 * (v + 0.044715 * v * v * v)));
+}
+
+/* dot(W[e, n, :], v) over K columns, v in double. */
+static double row_dot(const uint32_t* P, const uint16_t* S, const uint16_t* B,
+                      int64_t rows, int64_t K, int32_t gs, int64_t e, int64_t n,
+                      const double* v) {
+    double acc = 0.0;
+    for (int64_t c = 0; c < K; ++c)
+        acc += oracle_weight(P, S, B, rows, K, gs, e, n, c) * v[c];
+    return acc;
+}
+
+/* ------------------------------------------------------------- forward */
+
+/*
+ * Expert FFN for the listed tokens.  For list entry i (token t = tokens[i])
+ * and slot j, assignment a = t*k + j is stored at row r = i*k + j of
+ *   h   [ntok*k, I]  gelu_tanh(g) * u        (NULL to skip)
+ *   y   [ntok*k, H]  unweighted expert output (NULL to skip)
+ *   out [ntok, H]    sum_j w[t, j] * y[t*k+j] (NULL to skip)
+ * Rows of an assignment with an out-of-range expert id are zero.
+ */
+int oracle_ffn_tokens(int32_t T, int32_t k, int32_t E, int32_t H, int32_t I,
+                      int32_t gs, const uint16_t* x, const int32_t* ids,
+                      const float* w, const uint32_t* w_gu, const uint16_t* s_gu,
+                      const uint16_t* b_gu, const uint32_t* w_d,
+                      const uint16_t* s_d, const uint16_t* b_d,
+                      const int32_t* tokens, int32_t ntok, double* h, double* y,
+                      double* out) {
+    if (T < 0 || k <= 0 || E <= 0 || H <= 0 || I <= 0 || gs <= 0 || H % gs ||
+        I % gs || H % 8 || I % 8 || ntok < 0 || (ntok > 0 && !tokens))
+        return ORACLE_ERR_ARG;
+    for (int32_t i = 0; i < ntok; ++i)
+        if (tokens[i] < 0 || tokens[i] >= T) return ORACLE_ERR_ARG;
+    const int64_t n_rows = (int64_t)ntok * k;
+    double* yy = (double*)calloc((size_t)(n_rows > 0 ? n_rows : 1) * (size_t)H,
+                                 sizeof(double));
+    if (!yy) return ORACLE_ERR_ALLOC;
+    int failed = 0;
+
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t r = 0; r < n_rows; ++r) {
+        const int64_t t = tokens[r / k];
+        const int64_t a = t * k + (r % k);
+        const int32_t e = ids[a];
+        double* xv = (double*)malloc(sizeof(double) * (size_t)H);
+        double* hv = (double*)malloc(sizeof(double) * (size_t)I);
+        if (!xv || !hv) {
+            failed = 1;
+            free(xv);
+            free(hv);
+            continue;
+        }
+        for (int64_t c = 0; c < H; ++c) xv[c] = bf16_value(x[t * H + c]);
+        if (e >= 0 && e < E) {
+            for (int64_t n = 0; n < I; ++n) {
+                double g = row_dot(w_gu, s_gu, b_gu, 2 * (int64_t)I, H, gs, e, n, xv);
+                double u = row_dot(w_gu, s_gu, b_gu, 2 * (int64_t)I, H, gs, e, I + n, xv);
+                hv[n] = oracle_gelu_tanh(g) * u;
+            }
+            for (int64_t m = 0; m < H; ++m)
+                yy[r * H + m] = row_dot(w_d, s_d, b_d, H, I, gs, e, m, hv);
+        } else {
+            for (int64_t n = 0; n < I; ++n) hv[n] = 0.0;
+        }
+        if (h) memcpy(h + r * I, hv, sizeof(double) * (size_t)I);
+        free(xv);
+        free(hv);
+    }
+    if (failed) {
+        free(yy);
+        return ORACLE_ERR_ALLOC;
+    }
+    if (y) memcpy(y, yy, sizeof(double) * (size_t)n_rows * (size_t)H);
+    if (out) {
+        for (int64_t i = 0; i < ntok; ++i) {
+            const int64_t t = tokens[i];
+            for (int64_t m = 0; m < H; ++m) {
+                double acc = 0.0;
+                for (int64_t j = 0; j < k; ++j) {
+                    const int32_t e = ids[t * k + j];
+                    if (e < 0 || e >= E) continue;
+                    acc += (double)w[t * k + j] * yy[(i * k + j) * H + m];
+                }
+                out[i * H + m] = acc;
+            }
+        }
+    }
+    free(yy);
+    return ORACLE_OK;
+}

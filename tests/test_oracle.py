@@ -1,0 +1,302 @@
+"""Pins for the CPU oracle, checked against things other than the oracle itself.
+
+Runs on the CPU only.  Each test names what fixes the expected value: a
+hand-worked example, a library routine (numpy's stable argsort, torch's
+tanh-GELU, numpy matmul), a closed form, an invariant, or a brute-force dense
+recomputation that routes nothing.
+"""
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import moe_synth as ms
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# --------------------------------------------------------------- helpers
+def unpack_codes(P: np.ndarray) -> np.ndarray:
+    """Independent nibble unpack: view the little-endian words as bytes; byte i
+    of a word holds codes 2i (low nibble) and 2i+1 (high nibble)."""
+    b = np.ascontiguousarray(P).view(np.uint8)
+    lo = b & 0x0F
+    hi = b >> 4
+    q = np.stack([lo, hi], axis=-1).reshape(*P.shape[:-1], P.shape[-1] * 8)
+    return q.astype(np.float64)
+
+
+def dense_weights(P, S, B, gs):
+    q = unpack_codes(P)
+    s = np.repeat(ms.bf16_bits_to_f32(S).astype(np.float64), gs, axis=-1)
+    b = np.repeat(ms.bf16_bits_to_f32(B).astype(np.float64), gs, axis=-1)
+    return s * q + b
+
+
+def torch_gelu_tanh(v: np.ndarray) -> np.ndarray:
+    return torch.nn.functional.gelu(torch.from_numpy(v), approximate="tanh").numpy()
+
+
+def brute_force_out(p) -> np.ndarray:
+    """Dense, unrouted recomputation: every token through every expert, then
+    out[t] = sum_e C[t, e] * FFN_e(x_t) with C[t, e] = sum_j [ids[t,j] == e] w[t,j]."""
+    x = ms.bf16_bits_to_f32(p.x).astype(np.float64)
+    Wgu = dense_weights(p.w_gateup, p.s_gateup, p.b_gateup, p.gs)
+    Wd = dense_weights(p.w_down, p.s_down, p.b_down, p.gs)
+    C = np.zeros((p.T, p.E))
+    for j in range(p.k):
+        valid = (p.topk_ids[:, j] >= 0) & (p.topk_ids[:, j] < p.E)
+        t = np.nonzero(valid)[0]
+        np.add.at(C, (t, p.topk_ids[t, j]), p.topk_weights[t, j].astype(np.float64))
+    out = np.zeros((p.T, p.H))
+    for e in range(p.E):
+        gu = x @ Wgu[e].T
+        hid = torch_gelu_tanh(gu[:, : p.I]) * gu[:, p.I:]
+        out += C[:, e: e + 1] * (hid @ Wd[e].T)
+    return out
+
+
+def rel_err(a, b):
+    return np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300)
+
+
+def read_worked_example():
+    d = {"tile": []}
+    with open(os.path.join(GOLDEN, "route_worked_example.txt")) as f:
+        for line in f:
+            line = line.split("#")[0].strip()
+            if not line:
+                continue
+            key, val = [s.strip() for s in line.split("=")]
+            vals = [int(v) for v in val.split()]
+            if key == "tile":
+                d["tile"].append(vals)
+            else:
+                d[key] = np.array(vals, np.int32)
+    d["tile"] = np.array(d["tile"], np.int32)
+    return d
+
+
+# ----------------------------------------------------------------- route
+def test_route_worked_example(oracle_lib):
+    ex = read_worked_example()
+    counts, offsets, perm, inv, bad = oracle_lib.route(ex["ids"], 4)
+    assert bad == 0
+    np.testing.assert_array_equal(counts, ex["counts"])
+    np.testing.assert_array_equal(offsets, ex["offsets"])
+    np.testing.assert_array_equal(perm, ex["perm"])
+    np.testing.assert_array_equal(inv, ex["inv_perm"])
+    tiles = oracle_lib.tiles(counts, offsets, bm_big=2, bm_small=1)
+    np.testing.assert_array_equal(tiles, ex["tile"])
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_route_matches_stable_argsort(oracle_lib, seed):
+    rng = np.random.default_rng(100 + seed)
+    E = int(rng.choice([1, 3, 8, 128]))
+    A = int(rng.integers(0, 3000))
+    ids = rng.integers(-2, E + 2, size=A).astype(np.int32)
+    if seed % 2 == 0:
+        ids = np.clip(ids, 0, E - 1).astype(np.int32)
+    counts, offsets, perm, inv, bad = oracle_lib.route(ids, E)
+    valid = (ids >= 0) & (ids < E)
+    key = np.where(valid, ids, E)
+    np.testing.assert_array_equal(perm, np.argsort(key, kind="stable"))
+    np.testing.assert_array_equal(counts, np.bincount(ids[valid], minlength=E))
+    assert bad == int((~valid).sum())
+    assert offsets[0] == 0 and offsets[E] == A - bad
+    np.testing.assert_array_equal(np.diff(offsets), counts)
+    # bijection and inverse
+    np.testing.assert_array_equal(np.sort(perm), np.arange(A))
+    np.testing.assert_array_equal(inv[perm], np.arange(A))
+    # sortedness as the PR #4 review defines it: adjacent pairs non-decreasing
+    sorted_ids = key[perm]
+    assert np.all(sorted_ids[1:] >= sorted_ids[:-1])
+    # stable: within one expert, ascending flat index
+    same = sorted_ids[1:] == sorted_ids[:-1]
+    assert np.all(perm[1:][same] > perm[:-1][same])
+
+
+@pytest.mark.parametrize("bm_big,bm_small", [(32, 16), (64, 16), (16, 16), (128, 32)])
+@pytest.mark.parametrize("name", ["tiny", "decode", "prefill8k", "prefill16k"])
+def test_tiles_invariants(oracle_lib, name, bm_big, bm_small):
+    c = ms.CONFIGS[name]
+    rng = np.random.default_rng(0)
+    p_logits = ms._router_logits(rng, c["router"], c["T"], c["E"])
+    ids, _ = ms.route_topk(p_logits, c["k"])
+    counts, offsets, perm, inv, bad = oracle_lib.route(ids, c["E"])
+    tiles = oracle_lib.tiles(counts, offsets, bm_big, bm_small)
+    A = ids.size
+    assert len(tiles) == int(np.sum((counts + bm_big - 1) // bm_big))
+    assert len(tiles) <= A // bm_big + min(c["E"], A)
+    # disjoint, in-order cover of [0, A)
+    assert tiles[0, 1] == 0
+    np.testing.assert_array_equal(tiles[1:, 1], tiles[:-1, 1] + tiles[:-1, 2])
+    assert tiles[-1, 1] + tiles[-1, 2] == A
+    assert np.all(tiles[:, 2] >= 1) and np.all(tiles[:, 2] <= bm_big)
+    np.testing.assert_array_equal(tiles[:, 3] == bm_small, tiles[:, 2] <= bm_small)
+    assert set(np.unique(tiles[:, 3])) <= {bm_small, bm_big}
+    # expert-major; every row of a tile belongs to its expert; only the last
+    # tile of an expert may be short
+    assert np.all(np.diff(tiles[:, 0]) >= 0)
+    for e, rb, rc, _ in tiles:
+        assert np.all(ids.ravel()[perm[rb: rb + rc]] == e)
+    last_of_expert = np.r_[tiles[1:, 0] != tiles[:-1, 0], True]
+    assert np.all(tiles[~last_of_expert, 2] == bm_big)
+
+
+def test_route_empty_and_all_invalid(oracle_lib):
+    counts, offsets, perm, inv, bad = oracle_lib.route(np.zeros(0, np.int32), 5)
+    assert perm.size == 0 and bad == 0 and np.all(offsets == 0)
+    assert oracle_lib.tiles(counts, offsets).shape == (0, 4)
+    ids = np.array([7, -1, 5, 9], np.int32)
+    counts, offsets, perm, inv, bad = oracle_lib.route(ids, 5)
+    assert bad == 4 and offsets[-1] == 0
+    np.testing.assert_array_equal(perm, [0, 1, 2, 3])
+
+
+# --------------------------------------------------------------- dequant
+def test_unit_scale_gives_codes(oracle_lib):
+    rng = np.random.default_rng(1)
+    E, R, K, gs = 2, 3, 128, 64
+    P = rng.integers(0, 2**32, size=(E, R, K // 8), dtype=np.uint32)
+    S = np.full((E, R, K // gs), 0x3F80, np.uint16)   # bf16 1.0
+    B = np.zeros((E, R, K // gs), np.uint16)
+    q = unpack_codes(P)
+    for e in range(E):
+        for n in range(R):
+            for c in range(0, K, 5):
+                assert oracle_lib.weight(P, S, B, gs, e, n, c) == q[e, n, c]
+
+
+def test_group_indexing(oracle_lib):
+    """Scale g+1 and bias -(g+1)/2 on group g: fixes which group a column uses."""
+    rng = np.random.default_rng(2)
+    E, R, K, gs = 1, 2, 256, 64
+    P = rng.integers(0, 2**32, size=(E, R, K // 8), dtype=np.uint32)
+    g = np.arange(K // gs, dtype=np.float32)
+    S = np.broadcast_to(ms.f32_to_bf16_bits(g + 1), (E, R, K // gs)).copy()
+    B = np.broadcast_to(ms.f32_to_bf16_bits(-(g + 1) / 2), (E, R, K // gs)).copy()
+    q = unpack_codes(P)
+    for n in range(R):
+        for c in range(K):
+            want = (c // gs + 1) * q[0, n, c] - (c // gs + 1) / 2
+            assert oracle_lib.weight(P, S, B, gs, 0, n, c) == want
+
+
+def test_dequant_matches_independent_unpack(oracle_lib):
+    p = ms.make_problem(E=3, H=128, I=64, T=1, k=1, seed=3)
+    W = dense_weights(p.w_gateup, p.s_gateup, p.b_gateup, p.gs)
+    rng = np.random.default_rng(4)
+    for _ in range(200):
+        e, n, c = rng.integers(0, 3), rng.integers(0, 128), rng.integers(0, 128)
+        assert oracle_lib.weight(p.w_gateup, p.s_gateup, p.b_gateup, p.gs, e, n, c) == W[e, n, c]
+
+
+def test_symmetric_code_gives_zero_output(oracle_lib):
+    """q = 8 everywhere with B = -8 S dequantises to exactly zero."""
+    p = ms.make_problem(E=4, H=128, I=64, T=6, k=2, seed=5)
+    p.w_gateup[:] = 0x88888888
+    r = oracle_lib.ffn_tokens(p)
+    assert np.all(r["h"] == 0) and np.all(r["out"] == 0)
+
+
+# ------------------------------------------------------------------ GELU
+def test_gelu_closed_forms(oracle_lib):
+    assert oracle_lib.gelu_tanh(0.0) == 0.0
+    for v in np.linspace(-6, 6, 97):
+        # odd identity of x * Phi-like gates: gelu(x) - gelu(-x) = x
+        assert abs(oracle_lib.gelu_tanh(v) - oracle_lib.gelu_tanh(-v) - v) <= 4e-15 * max(1, abs(v))
+    assert oracle_lib.gelu_tanh(30.0) == 30.0
+    assert oracle_lib.gelu_tanh(-30.0) == 0.0
+
+
+def test_gelu_matches_torch_tanh_approximation(oracle_lib):
+    v = np.linspace(-8, 8, 1001)
+    ref = torch_gelu_tanh(v)
+    got = np.array([oracle_lib.gelu_tanh(t) for t in v])
+    np.testing.assert_allclose(got, ref, rtol=1e-14, atol=1e-15)
+    # and it is the tanh form, not erf: the two differ by at most ~4.7e-4
+    erf = np.array([0.5 * t * (1 + math.erf(t / math.sqrt(2))) for t in v])
+    d = np.abs(got - erf).max()
+    assert 3e-4 < d < 5e-4
+
+
+# ------------------------------------------------------------------- FFN
+def test_single_expert_is_dense_ffn(oracle_lib):
+    """E = 1, k = 1: the routed FFN reduces to a dense quantised FFN."""
+    p = ms.make_problem(E=1, H=192, I=128, T=5, k=1, seed=6)
+    x = ms.bf16_bits_to_f32(p.x).astype(np.float64)
+    Wgu = dense_weights(p.w_gateup, p.s_gateup, p.b_gateup, p.gs)[0]
+    Wd = dense_weights(p.w_down, p.s_down, p.b_down, p.gs)[0]
+    gate = x @ Wgu[: p.I].T
+    up = x @ Wgu[p.I:].T
+    h = torch_gelu_tanh(gate) * up
+    y = h @ Wd.T
+    r = oracle_lib.ffn_tokens(p)
+    assert rel_err(r["h"], h) < 1e-12
+    assert rel_err(r["y"], y) < 1e-12
+    np.testing.assert_allclose(r["out"], y * p.topk_weights[:, :1], rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_tiny_config_matches_brute_force(oracle_lib, seed):
+    p = ms.make_config("tiny", seed=seed)
+    r = oracle_lib.ffn_tokens(p)
+    ref = brute_force_out(p)
+    assert rel_err(r["out"], ref) < 1e-12
+    assert np.abs(r["out"] - ref).max() < 1e-10 * np.sqrt((ref ** 2).mean())
+
+
+@pytest.mark.parametrize("shape", [(3, 64, 64, 7, 2), (5, 128, 192, 3, 5), (2, 64, 128, 1, 2)])
+def test_fuzz_shapes_match_brute_force(oracle_lib, shape):
+    E, H, I, T, k = shape
+    p = ms.make_problem(E, H, I, T, k, seed=E * 7 + T)
+    r = oracle_lib.ffn_tokens(p)
+    assert rel_err(r["out"], brute_force_out(p)) < 1e-12
+
+
+def test_invalid_ids_contribute_zero(oracle_lib):
+    p = ms.make_problem(E=4, H=64, I=64, T=4, k=2, seed=8)
+    ref = brute_force_out(p)
+    p.topk_ids[1, 0] = 4
+    p.topk_ids[2, 1] = -3
+    r = oracle_lib.ffn_tokens(p)
+    bf = brute_force_out(p)       # brute force drops the same copies
+    assert rel_err(r["out"], bf) < 1e-12
+    assert np.all(r["h"][2] == 0) and np.all(r["y"][2] == 0)
+    assert rel_err(r["out"][[0, 3]], ref[[0, 3]]) < 1e-12
+
+
+def test_combine_linear_in_weights(oracle_lib):
+    p = ms.make_problem(E=4, H=64, I=64, T=5, k=3, seed=9)
+    r1 = oracle_lib.ffn_tokens(p)
+    p.topk_weights = (p.topk_weights * np.float32(2)).astype(np.float32)
+    r2 = oracle_lib.ffn_tokens(p)
+    np.testing.assert_array_equal(r2["out"], 2 * r1["out"])
+    np.testing.assert_array_equal(r2["y"], r1["y"])
+
+
+def test_identical_experts_give_plain_ffn(oracle_lib):
+    """All experts equal and weights summing to one: out = FFN(x)."""
+    p = ms.make_problem(E=4, H=64, I=64, T=6, k=3, seed=10)
+    for arr in (p.w_gateup, p.s_gateup, p.b_gateup, p.w_down, p.s_down, p.b_down):
+        arr[:] = arr[0:1]
+    r = oracle_lib.ffn_tokens(p)
+    ffn = r["y"].reshape(p.T, p.k, p.H)[:, 0]
+    wsum = p.topk_weights.astype(np.float64).sum(1, keepdims=True)
+    assert np.abs(wsum - 1).max() < 1e-6
+    np.testing.assert_allclose(r["out"], ffn * wsum, rtol=1e-12, atol=1e-12)
+
+
+def test_token_subset_is_consistent(oracle_lib):
+    p = ms.make_config("tiny")
+    full = oracle_lib.ffn_tokens(p)
+    toks = np.array([63, 0, 17, 17], np.int32)
+    sub = oracle_lib.ffn_tokens(p, toks)
+    np.testing.assert_array_equal(sub["out"], full["out"][toks])
+    rows = (toks[:, None] * p.k + np.arange(p.k)[None, :]).ravel()
+    np.testing.assert_array_equal(sub["h"], full["h"][rows])
+    np.testing.assert_array_equal(sub["y"], full["y"][rows])

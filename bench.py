@@ -1,0 +1,290 @@
+#!/usr/bin/env python3
+"""Benchmark of the routed 4-bit MoE expert FFN forward on one MI355X.
+
+One step = one full forward (route/sort/tile, gate|up + GeGLU, down +
+weighted unsort, combine) over one batch of synthetic inputs that are already
+resident in HBM.  Several full copies of every input are rotated step by step
+so that the 256 MB Infinity Cache cannot serve a step from the previous one.
+
+Prints ONE JSON line:
+  value         whole-forward assignments/s over the timed steps (host clock,
+                synchronised on both sides), no per-stage events in that loop;
+  roofline      the dominant kernel's algorithmic bytes (or flops) per launch
+                divided by its mean duration, from HIP events recorded on the
+                library's stream in a second, instrumented loop;
+  cpu_baseline  the CPU oracle on this host's cores, on a bounded sample of the
+                same workload, with a parity check of the GPU output against it.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "expert-FFN assignments/s and TFLOP/s (or HBM GB/s) vs roofline, 1 MI355X"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+STAGES = ("moe_route_sort_tiles", "moe_gateup_geglu", "moe_down", "moe_combine")
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def algorithmic_work(p, touched: int):
+    """Per-launch algorithmic bytes and flops of each kernel (what the method
+    must move and compute, not what a kernel happens to re-read)."""
+    E, H, I, T, k = p.E, p.H, p.I, p.T, p.k
+    A = T * k
+    G_h, G_i = H // 64, I // 64
+    gu_expert = 2 * I * H // 2 + 2 * (2 * I * G_h * 2)      # packed codes + scales + biases
+    d_expert = H * I // 2 + 2 * (H * G_i * 2)
+    work = {
+        "moe_route_sort_tiles": dict(bytes=A * 4 + A * 8 + (2 * E + 1) * 4, flops=0),
+        "moe_gateup_geglu": dict(bytes=touched * gu_expert + T * H * 2 + A * I * 2,
+                                 flops=A * 4 * H * I),
+        "moe_down": dict(bytes=touched * d_expert + A * I * 2 + A * H * 4 + A * 4,
+                         flops=A * 2 * H * I),
+        "moe_combine": dict(bytes=A * H * 4 + T * H * 2 + A * 4, flops=A * H),
+    }
+    fwd = dict(bytes=touched * (gu_expert + d_expert) + T * H * 2 + A * 8 + T * H * 2,
+               flops=A * 6 * H * I)
+    return work, fwd
+
+
+def bound_of(w):
+    t_hbm = w["bytes"] / (HBM_PEAK_GBS * 1e9)
+    t_mfma = w["flops"] / (BF16_PEAK_TFLOPS * 1e12)
+    return "hbm" if t_hbm >= t_mfma else "mfma"
+
+
+def roofline_entry(w, seconds):
+    b = bound_of(w)
+    if b == "hbm":
+        ach = w["bytes"] / seconds / 1e9
+        return dict(bound="hbm", achieved=round(ach, 2), peak=HBM_PEAK_GBS, unit="GB/s",
+                    frac=round(ach / HBM_PEAK_GBS, 4))
+    ach = w["flops"] / seconds / 1e12
+    return dict(bound="mfma", achieved=round(ach, 2), peak=BF16_PEAK_TFLOPS, unit="TFLOP/s",
+                frac=round(ach / BF16_PEAK_TFLOPS, 4))
+
+
+def load_traffic(kernel: str, workload: str):
+    """HBM bytes per launch measured with rocprofv3 counters, if a summary for
+    this kernel, workload and kernel source is committed under profiles/."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+        from bit_gathered_quantized_amd.build import source_digest
+        if rec.get("source_digest") != source_digest():
+            return None
+        return rec.get("bytes_per_launch")
+    except Exception:
+        return None
+
+
+def cpu_baseline_leg(p, gpu_out, seconds_budget: float):
+    """The oracle (as it stands) on this host's cores, on a bounded sample of
+    the same workload; the same run checks the GPU output."""
+    import numpy as np
+
+    import oracle
+    import moe_synth as ms
+
+    if p.T <= 16:
+        tokens = np.arange(p.T, dtype=np.int32)
+        sample = f"full batch: {p.T} tokens x top-{p.k} = {p.T * p.k} assignments"
+    else:
+        rng = np.random.default_rng(123)
+        n = 48
+        tokens = np.sort(rng.choice(p.T, size=n, replace=False)).astype(np.int32)
+        sample = f"{n} random tokens of {p.T} (x top-{p.k} = {n * p.k} assignments)"
+    times = []
+    ref = None
+    t_start = time.perf_counter()
+    while True:
+        t0 = time.perf_counter()
+        r = oracle.ffn_tokens(p, tokens, want_h=False, want_y=False)
+        times.append(time.perf_counter() - t0)
+        if ref is None:
+            ref = r["out"]
+        if len(times) >= 2 and time.perf_counter() - t_start >= seconds_budget:
+            break
+        if len(times) >= 50:
+            break
+    med = statistics.median(times)
+    n_asg = tokens.size * p.k
+    got = gpu_out[tokens]
+    rms = float(np.sqrt(np.mean(ref ** 2)))
+    allow = np.exp2(np.floor(np.log2(np.maximum(np.maximum(np.abs(got), np.abs(ref)), 1e-38))) - 8)
+    excess = float(np.max(np.abs(got - ref) - allow)) / rms
+    base = dict(value=round(n_asg / med, 3), unit="assignments/s", cores=oracle.num_threads(),
+                kind="oracle", sample=f"{sample}; median of {len(times)} runs",
+                seconds_per_run=round(med, 4))
+    parity = dict(tokens=int(tokens.size), bf16_excess_over_rms=round(excess, 6), bar=2e-2,
+                  ok=bool(excess <= 2e-2))
+    return base, parity
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="decode",
+                    choices=["tiny", "decode", "prefill4k", "prefill8k", "prefill16k"])
+    ap.add_argument("--copies", type=int, default=4, help="input copies rotated across steps")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} (WORLD_SIZE={world}) is not "
+              "supported: the expert FFN here runs on a single MI355X.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import bit_gathered_quantized_amd as bgq
+    import moe_synth as ms
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    bgq.lib()  # fail loudly if the HIP library is missing
+
+    p = ms.make_config(args.workload, seed=0)
+    A = p.T * p.k
+    counts = np.bincount(p.topk_ids.ravel(), minlength=p.E)
+    touched = int(np.count_nonzero(counts))
+    n_tiles = int(np.sum((counts + 31) // 32))
+    log(f"workload {args.workload}: E={p.E} H={p.H} I={p.I} T={p.T} k={p.k} A={A} "
+        f"touched={touched} tiles={n_tiles}")
+
+    dev = torch.device("cuda", 0)
+
+    def upload():
+        def t(a, dt):
+            return torch.from_numpy(np.ascontiguousarray(a).view(dt)).to(dev)
+        return [t(p.x, np.int16).view(torch.bfloat16), t(p.topk_ids, np.int32),
+                t(p.topk_weights, np.float32), t(p.w_gateup, np.int32), t(p.s_gateup, np.int16),
+                t(p.b_gateup, np.int16), t(p.w_down, np.int32), t(p.s_down, np.int16),
+                t(p.b_down, np.int16)]
+
+    sets = [upload() for _ in range(max(1, args.copies))]
+    prob = bgq.problem(p.T, p.k, p.E, p.H, p.I, 0)
+    ws = torch.empty(bgq.workspace_bytes(prob), dtype=torch.uint8, device=dev)
+    out = torch.empty((p.T, p.H), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(i, events=None):
+        bgq.expert_ffn_forward(*sets[i % len(sets)], out=out, workspace=ws, stream=stream,
+                               events=events)
+
+    # warm-up
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # timed loop: whole forward, host clock
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = elapsed / args.steps * 1e3
+
+    # instrumented loop: per-kernel durations from events on the same stream
+    n_ev = min(args.steps, 100)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(n_ev)]
+    for row in evs:
+        for e in row:
+            e.record(stream)
+    torch.cuda.synchronize()
+    for i in range(n_ev):
+        step(i, events=[e.cuda_event for e in evs[i]])
+    torch.cuda.synchronize()
+    stage_us = {s: [] for s in STAGES}
+    fwd_us = []
+    for row in evs:
+        for j, s in enumerate(STAGES):
+            stage_us[s].append(row[j].elapsed_time(row[j + 1]) * 1e3)
+        fwd_us.append(row[0].elapsed_time(row[4]) * 1e3)
+    mean_us = {s: statistics.fmean(v) for s, v in stage_us.items()}
+
+    work, fwd_work = algorithmic_work(p, touched)
+    dominant = max(STAGES, key=lambda s: mean_us[s])
+    roof = roofline_entry(work[dominant], mean_us[dominant] * 1e-6)
+    roof["kernel"] = dominant
+    traffic = load_traffic(dominant, args.workload)
+    roof["traffic"] = traffic
+
+    fwd_s = statistics.median(fwd_us) * 1e-6
+    forward = dict(
+        event_us_median=round(statistics.median(fwd_us), 2),
+        event_us_p10=round(float(np.percentile(fwd_us, 10)), 2),
+        event_us_p90=round(float(np.percentile(fwd_us, 90)), 2),
+        tflops=round(fwd_work["flops"] / fwd_s / 1e12, 2),
+        hbm_gbs=round(fwd_work["bytes"] / fwd_s / 1e9, 1),
+        algorithmic_bytes=int(fwd_work["bytes"]),
+        algorithmic_flops=int(fwd_work["flops"]),
+        bound=bound_of(fwd_work),
+        frac=roofline_entry(fwd_work, fwd_s)["frac"],
+        wall_frac=roofline_entry(fwd_work, ms_per_step * 1e-3)["frac"],
+    )
+    kernels = {}
+    for s in STAGES:
+        e = roofline_entry(work[s], mean_us[s] * 1e-6)
+        kernels[s] = dict(mean_us=round(mean_us[s], 2), bound=e["bound"], achieved=e["achieved"],
+                          unit=e["unit"], frac=e["frac"])
+
+    result = {
+        "metric": METRIC,
+        "value": round(A / (ms_per_step * 1e-3), 1),
+        "unit": "assignments/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "E": p.E, "H": p.H, "I": p.I, "T": p.T,
+                   "k": p.k, "assignments": A, "group_size": 64, "bits": 4,
+                   "router": ms.CONFIGS[args.workload]["router"], "seed": 0,
+                   "touched_experts": touched, "tiles_bm32": n_tiles,
+                   "input_copies": len(sets)},
+        "roofline": roof,
+        "forward": forward,
+        "kernels": kernels,
+    }
+
+    if not args.no_cpu_baseline:
+        gpu_out = out.float().cpu().numpy().astype(np.float64)
+        # the last forward ran on copy (n_ev - 1) % copies: all copies hold the same data
+        base, parity = cpu_baseline_leg(p, gpu_out, args.cpu_seconds)
+        result["cpu_baseline"] = base
+        result["parity"] = parity
+    else:
+        result["cpu_baseline"] = None
+
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,223 @@
+// C ABI of libmoeffn: argument checks, workspace layout and the launch
+// sequence of the forward.  Nothing here allocates, frees or waits on the
+// device; everything is enqueued on the caller's stream.
+#include <limits.h>
+#include <stddef.h>
+
+#include "moe_internal.h"
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Shape checks shared by the forward's size queries and the forward itself.
+moe_status check_problem(const moe_problem* p) {
+    if (!p) return MOE_ERR_NULL;
+    if (p->bits != 4 || p->group_size != moe::kGroup) return MOE_ERR_UNSUPPORTED;
+    if (p->flags & ~(MOE_F_FP32_OUT | MOE_F_FP32_INTERMEDIATE)) return MOE_ERR_UNSUPPORTED;
+    if (p->T < 0 || p->k < 1 || p->E < 1 || p->H < 1 || p->I < 1) return MOE_ERR_SHAPE;
+    if (p->E > MOE_MAX_EXPERTS) return MOE_ERR_UNSUPPORTED;
+    if (p->k > p->E) return MOE_ERR_SHAPE;
+    if (p->H % moe::kGroup || p->I % moe::kGroup) return MOE_ERR_SHAPE;
+    const int64_t A = static_cast<int64_t>(p->T) * p->k;
+    if (A > INT32_MAX / 2) return MOE_ERR_SHAPE;
+    return MOE_OK;
+}
+
+moe_ws_layout make_layout(const moe_problem* p) {
+    moe_ws_layout l = {};
+    const int64_t A = static_cast<int64_t>(p->T) * p->k;
+    l.bm_big = moe::kBmBig;
+    l.bm_small = moe::kBmSmall;
+    l.max_tiles = moe_max_tiles(A, p->E, moe::kBmBig);
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t at = off;
+        off = align_up(off + bytes);
+        return at;
+    };
+    const size_t hbytes = (p->flags & MOE_F_FP32_INTERMEDIATE) ? 4 : 2;
+    l.counts = take(sizeof(int32_t) * p->E);
+    l.offsets = take(sizeof(int32_t) * (p->E + 1));
+    l.perm = take(sizeof(int32_t) * A);
+    l.inv_perm = take(sizeof(int32_t) * A);
+    l.tiles = take(sizeof(moe_tile) * l.max_tiles);
+    l.num_tiles = take(sizeof(int32_t) * 2);
+    l.h = take(hbytes * A * p->I);
+    l.y = take(sizeof(float) * A * p->H);
+    l.total = off;
+    return l;
+}
+
+moe_status forward_impl(const moe_problem* p, const void* x, const int32_t* ids,
+                        const float* topk_w, const uint32_t* w_gu, const void* s_gu,
+                        const void* b_gu, const uint32_t* w_d, const void* s_d,
+                        const void* b_d, void* out, void* ws, size_t ws_bytes, void* stream,
+                        void* const* events) {
+    const moe_status st = check_problem(p);
+    if (st != MOE_OK) return st;
+    if (p->T == 0) return MOE_OK;
+    if (!x || !ids || !topk_w || !w_gu || !s_gu || !b_gu || !w_d || !s_d || !b_d || !out)
+        return MOE_ERR_NULL;
+    if (!ws) return MOE_ERR_WORKSPACE;
+    const moe_ws_layout l = make_layout(p);
+    if (ws_bytes < l.total) return MOE_ERR_WORKSPACE;
+    const bool f32out = p->flags & MOE_F_FP32_OUT;
+    if (!aligned(x, 16) || !aligned(w_gu, 16) || !aligned(w_d, 16) || !aligned(ids, 4) ||
+        !aligned(topk_w, 4) || !aligned(s_gu, 2) || !aligned(b_gu, 2) || !aligned(s_d, 2) ||
+        !aligned(b_d, 2) || !aligned(out, f32out ? 16 : 8) || !aligned(ws, kAlign))
+        return MOE_ERR_ALIGN;
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    char* base = static_cast<char*>(ws);
+    auto ev = [&](int i) -> hipError_t {
+        if (!events || !events[i]) return hipSuccess;
+        return hipEventRecord(static_cast<hipEvent_t>(events[i]), s);
+    };
+
+    moe::RouteArgs r;
+    r.ids = ids;
+    r.A = p->T * p->k;
+    r.E = p->E;
+    r.bm_big = l.bm_big;
+    r.bm_small = l.bm_small;
+    r.max_tiles = l.max_tiles;
+    r.counts = reinterpret_cast<int32_t*>(base + l.counts);
+    r.offsets = reinterpret_cast<int32_t*>(base + l.offsets);
+    r.perm = reinterpret_cast<int32_t*>(base + l.perm);
+    r.inv_perm = reinterpret_cast<int32_t*>(base + l.inv_perm);
+    r.tiles = reinterpret_cast<int32_t*>(base + l.tiles);
+    r.num_tiles = reinterpret_cast<int32_t*>(base + l.num_tiles);
+
+    moe::FfnArgs f;
+    f.T = p->T;
+    f.k = p->k;
+    f.E = p->E;
+    f.H = p->H;
+    f.I = p->I;
+    f.max_tiles = l.max_tiles;
+    f.flags = p->flags;
+    f.x = static_cast<const uint16_t*>(x);
+    f.ids = ids;
+    f.topk_w = topk_w;
+    f.w_gu = w_gu;
+    f.s_gu = static_cast<const uint16_t*>(s_gu);
+    f.b_gu = static_cast<const uint16_t*>(b_gu);
+    f.w_d = w_d;
+    f.s_d = static_cast<const uint16_t*>(s_d);
+    f.b_d = static_cast<const uint16_t*>(b_d);
+    f.perm = r.perm;
+    f.tiles = r.tiles;
+    f.num_tiles = r.num_tiles;
+    f.h = base + l.h;
+    f.y = reinterpret_cast<float*>(base + l.y);
+    f.out = out;
+
+    if (ev(0) != hipSuccess) return MOE_ERR_HIP;
+    if (moe::launch_route(r, s) != hipSuccess) return MOE_ERR_HIP;
+    if (ev(1) != hipSuccess) return MOE_ERR_HIP;
+    if (moe::launch_gateup(f, s) != hipSuccess) return MOE_ERR_HIP;
+    if (ev(2) != hipSuccess) return MOE_ERR_HIP;
+    if (moe::launch_down(f, s) != hipSuccess) return MOE_ERR_HIP;
+    if (ev(3) != hipSuccess) return MOE_ERR_HIP;
+    if (moe::launch_combine(f, s) != hipSuccess) return MOE_ERR_HIP;
+    if (ev(4) != hipSuccess) return MOE_ERR_HIP;
+    return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t moe_max_tiles(int64_t A, int32_t E, int32_t bm_big) {
+    if (A < 0 || E < 1 || bm_big < 1) return -1;
+    const int64_t v = A / bm_big + (A < E ? A : E);
+    return v > INT32_MAX ? -1 : static_cast<int32_t>(v);
+}
+
+moe_status moe_sort_build_tiles(const int32_t* topk_ids, int32_t T, int32_t k, int32_t E,
+                                int32_t bm_big, int32_t bm_small, int32_t* counts,
+                                int32_t* offsets, int32_t* perm, int32_t* inv_perm,
+                                moe_tile* tiles, int32_t max_tiles, int32_t* num_tiles,
+                                void* stream) {
+    if (T < 0 || k < 1 || E < 1) return MOE_ERR_SHAPE;
+    if (E > MOE_MAX_EXPERTS) return MOE_ERR_UNSUPPORTED;
+    if (bm_small < 1 || bm_big < bm_small) return MOE_ERR_SHAPE;
+    const int64_t A = static_cast<int64_t>(T) * k;
+    if (A > INT32_MAX / 2) return MOE_ERR_SHAPE;
+    if (!counts || !offsets || !num_tiles || !tiles) return MOE_ERR_NULL;
+    if (A > 0 && (!topk_ids || !perm || !inv_perm)) return MOE_ERR_NULL;
+    const int32_t need = moe_max_tiles(A, E, bm_big);
+    if (need < 0 || max_tiles < need) return MOE_ERR_WORKSPACE;
+    if (!aligned(tiles, 16) || !aligned(counts, 4) || !aligned(offsets, 4) ||
+        !aligned(num_tiles, 4) || (A > 0 && (!aligned(topk_ids, 4) || !aligned(perm, 4) ||
+                                             !aligned(inv_perm, 4))))
+        return MOE_ERR_ALIGN;
+    moe::RouteArgs r;
+    r.ids = topk_ids;
+    r.A = static_cast<int32_t>(A);
+    r.E = E;
+    r.bm_big = bm_big;
+    r.bm_small = bm_small;
+    r.max_tiles = max_tiles;
+    r.counts = counts;
+    r.offsets = offsets;
+    r.perm = perm;
+    r.inv_perm = inv_perm;
+    r.tiles = reinterpret_cast<int32_t*>(tiles);
+    r.num_tiles = num_tiles;
+    return moe::launch_route(r, static_cast<hipStream_t>(stream)) == hipSuccess ? MOE_OK
+                                                                               : MOE_ERR_HIP;
+}
+
+size_t moe_ffn_workspace_bytes(const moe_problem* p) {
+    if (check_problem(p) != MOE_OK) return 0;
+    return make_layout(p).total;
+}
+
+moe_status moe_ffn_workspace_layout(const moe_problem* p, moe_ws_layout* layout) {
+    if (!layout) return MOE_ERR_NULL;
+    const moe_status st = check_problem(p);
+    if (st != MOE_OK) return st;
+    *layout = make_layout(p);
+    return MOE_OK;
+}
+
+moe_status moe_expert_ffn_forward(const moe_problem* p, const void* x, const int32_t* topk_ids,
+                                  const float* topk_weights, const uint32_t* w_gateup,
+                                  const void* s_gateup, const void* b_gateup,
+                                  const uint32_t* w_down, const void* s_down, const void* b_down,
+                                  void* out, void* ws, size_t ws_bytes, void* stream) {
+    return forward_impl(p, x, topk_ids, topk_weights, w_gateup, s_gateup, b_gateup, w_down,
+                        s_down, b_down, out, ws, ws_bytes, stream, nullptr);
+}
+
+moe_status moe_expert_ffn_forward_timed(const moe_problem* p, const void* x,
+                                        const int32_t* topk_ids, const float* topk_weights,
+                                        const uint32_t* w_gateup, const void* s_gateup,
+                                        const void* b_gateup, const uint32_t* w_down,
+                                        const void* s_down, const void* b_down, void* out,
+                                        void* ws, size_t ws_bytes, void* stream,
+                                        void* const* events) {
+    return forward_impl(p, x, topk_ids, topk_weights, w_gateup, s_gateup, b_gateup, w_down,
+                        s_down, b_down, out, ws, ws_bytes, stream, events);
+}
+
+const char* moe_status_string(moe_status s) {
+    switch (s) {
+        case MOE_OK: return "ok";
+        case MOE_ERR_NULL: return "a required pointer is NULL";
+        case MOE_ERR_SHAPE: return "invalid or inconsistent sizes";
+        case MOE_ERR_UNSUPPORTED: return "unsupported configuration (bits, group size, flags or expert count)";
+        case MOE_ERR_ALIGN: return "a pointer is misaligned";
+        case MOE_ERR_WORKSPACE: return "workspace or tile buffer missing or too small";
+        case MOE_ERR_HIP: return "HIP runtime error while enqueueing work";
+        default: return "unknown status";
+    }
+}
+
+}  // extern "C"

@@ -1,0 +1,191 @@
+// Route / sort / tile kernel: one workgroup of 1024 threads (16 waves).
+//
+// Prior art: the descriptor builder of the Layr-Labs/mlx PR #4 page ("What"),
+// which runs on one 128-thread threadgroup over *pre-sorted* expert indices:
+// a binary search of each expert's range, a Hillis-Steele exclusive scan of
+// per-expert tile counts and a strided upper-bound emission of the tiles.
+// Here the input is the raw top-k id array, so the kernel also sorts:
+//
+//   1. each wave owns a contiguous segment of the assignments and counts the
+//      keys in it, 64 at a time, grouping equal keys with a wave match-any
+//      (one ballot per key bit) -- no atomics, so counts are exact and the
+//      work is deterministic;
+//   2. per-key totals and an exclusive scan give counts and offsets, and a
+//      scan over waves gives each (wave, key) its first sorted slot;
+//   3. each wave walks its segment again in order and scatters every
+//      assignment to base + (rank among equal keys in lower lanes): a stable
+//      counting sort;
+//   4. tiles per expert = ceil(count / bm_big), scanned; thread i emits tile i
+//      after an upper-bound search of the scanned tile offsets.
+//
+// Keys are expert ids; ids outside [0, E) get key E, which sorts after all
+// experts and gets no tiles.
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+constexpr int kMaxKeys = MOE_MAX_EXPERTS + 1;
+
+// Lanes of the wave whose key equals this lane's key, among `active` lanes.
+__device__ __forceinline__ uint64_t match_any(uint32_t key, int nbits, uint64_t active) {
+    uint64_t m = active;
+    for (int b = 0; b < nbits; ++b) {
+        const bool bit = (key >> b) & 1u;
+        const uint64_t bal = __ballot(bit);
+        m &= bit ? bal : ~bal;
+    }
+    return m;
+}
+
+// Exclusive scan of in[0, n) into out[0, n], out[n] = total.  n <= 2 * 1024.
+// Every thread of the block must call it.
+__device__ void block_exclusive_scan(const int32_t* in, int32_t* out, int n, int32_t* wsum) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int i0 = 2 * tid, i1 = 2 * tid + 1;
+    const int32_t v0 = i0 < n ? in[i0] : 0;
+    const int32_t v1 = i1 < n ? in[i1] : 0;
+    const int32_t s = v0 + v1;
+    int32_t inc = s;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int32_t t = __shfl_up(inc, d);
+        if (lane >= d) inc += t;
+    }
+    if (lane == 63) wsum[wave] = inc;
+    __syncthreads();
+    if (wave == 0) {
+        const int32_t w = lane < kRouteWaves ? wsum[lane] : 0;
+        int32_t winc = w;
+#pragma unroll
+        for (int d = 1; d < kRouteWaves; d <<= 1) {
+            const int32_t t = __shfl_up(winc, d);
+            if (lane >= d) winc += t;
+        }
+        if (lane < kRouteWaves) wsum[lane] = winc - w;
+        if (lane == kRouteWaves - 1) wsum[kRouteWaves] = winc;
+    }
+    __syncthreads();
+    const int32_t excl = inc - s + wsum[wave];
+    if (i0 < n) out[i0] = excl;
+    if (i1 < n) out[i1] = excl + v0;
+    if (tid == 0) out[n] = wsum[kRouteWaves];
+    __syncthreads();
+}
+
+__global__ __launch_bounds__(kRouteThreads) void moe_route_sort_tiles(RouteArgs a) {
+    __shared__ int32_t s_tab[kRouteWaves * kMaxKeys];  // per-wave key counts, then bases
+    __shared__ int32_t s_cnt[kMaxKeys];
+    __shared__ int32_t s_off[kMaxKeys + 1];
+    __shared__ int32_t s_toff[kMaxKeys + 1];
+    __shared__ int32_t s_wsum[kRouteWaves + 1];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int E = a.E, A = a.A;
+    const int nkeys = E + 1;
+    const int nbits = 32 - __clz(E);  // bits of the largest key, E
+    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+
+    for (int i = tid; i < kRouteWaves * nkeys; i += kRouteThreads) s_tab[i] = 0;
+    __syncthreads();
+
+    // Contiguous, 64-aligned segment of the assignments per wave.
+    const int per = ((A + kRouteWaves - 1) / kRouteWaves + 63) & ~63;
+    const int beg = wave * per;
+    const int end = min(A, beg + per);
+    int32_t* tab = s_tab + wave * nkeys;
+
+    // 1. per-wave histogram
+    for (int base = beg; base < end; base += 64) {
+        const int ai = base + lane;
+        const bool act = ai < end;
+        uint32_t key = 0;
+        if (act) {
+            const int32_t id = a.ids[ai];
+            key = (id >= 0 && id < E) ? static_cast<uint32_t>(id) : static_cast<uint32_t>(E);
+        }
+        const uint64_t m = match_any(key, nbits, __ballot(act));
+        if (act && (m & below) == 0) tab[key] += __popcll(m);
+    }
+    __syncthreads();
+
+    // 2. totals, offsets, per-(wave, key) bases
+    for (int key = tid; key < nkeys; key += kRouteThreads) {
+        int32_t s = 0;
+        for (int w = 0; w < kRouteWaves; ++w) s += s_tab[w * nkeys + key];
+        s_cnt[key] = s;
+    }
+    __syncthreads();
+    block_exclusive_scan(s_cnt, s_off, nkeys, s_wsum);
+    for (int key = tid; key < nkeys; key += kRouteThreads) {
+        int32_t run = s_off[key];
+        for (int w = 0; w < kRouteWaves; ++w) {
+            const int32_t c = s_tab[w * nkeys + key];
+            s_tab[w * nkeys + key] = run;
+            run += c;
+        }
+    }
+    __syncthreads();
+
+    // 3. stable scatter
+    for (int base = beg; base < end; base += 64) {
+        const int ai = base + lane;
+        const bool act = ai < end;
+        uint32_t key = 0;
+        if (act) {
+            const int32_t id = a.ids[ai];
+            key = (id >= 0 && id < E) ? static_cast<uint32_t>(id) : static_cast<uint32_t>(E);
+        }
+        const uint64_t m = match_any(key, nbits, __ballot(act));
+        int32_t slot = 0;
+        if (act) slot = tab[key] + __popcll(m & below);
+        if (act) {
+            a.perm[slot] = ai;
+            a.inv_perm[ai] = slot;
+        }
+        if (act && (m & below) == 0) tab[key] += __popcll(m);
+    }
+
+    // 4. counts, offsets, tiles
+    for (int e = tid; e < E; e += kRouteThreads) {
+        a.counts[e] = s_cnt[e];
+        a.offsets[e] = s_off[e];
+    }
+    if (tid == 0) {
+        a.offsets[E] = s_off[E];
+        a.num_tiles[1] = s_cnt[E];
+    }
+    // tiles per expert into s_tab's first row (no longer needed)
+    __syncthreads();
+    for (int e = tid; e < E; e += kRouteThreads) s_tab[e] = (s_cnt[e] + a.bm_big - 1) / a.bm_big;
+    __syncthreads();
+    block_exclusive_scan(s_tab, s_toff, E, s_wsum);
+    const int total = s_toff[E];
+    for (int i = tid; i < total && i < a.max_tiles; i += kRouteThreads) {
+        // upper bound: first e with s_toff[e] > i, over s_toff[0..E]
+        int lo = 0, hi = E + 1;
+        while (lo < hi) {
+            const int mid = (lo + hi) >> 1;
+            if (s_toff[mid] <= i) lo = mid + 1; else hi = mid;
+        }
+        const int e = lo - 1;
+        const int local = i - s_toff[e];
+        const int row0 = local * a.bm_big;
+        const int rows = min(a.bm_big, s_cnt[e] - row0);
+        int32_t* t = a.tiles + 4 * i;
+        t[0] = e;
+        t[1] = s_off[e] + row0;
+        t[2] = rows;
+        t[3] = rows <= a.bm_small ? a.bm_small : a.bm_big;
+    }
+    if (tid == 0) a.num_tiles[0] = total;
+}
+
+}  // namespace
+
+hipError_t launch_route(const RouteArgs& a, hipStream_t stream) {
+    hipLaunchKernelGGL(moe_route_sort_tiles, dim3(1), dim3(kRouteThreads), 0, stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,194 @@
+/*
+ * moe_ffn.h -- C ABI of libmoeffn, the routed 4-bit MoE expert FFN for AMD
+ * MI355X (gfx950).
+ *
+ * The operation (switch-GLU expert FFN with a tanh-GELU product):
+ *
+ *   for every token t and slot j < k, with e = topk_ids[t, j]:
+ *     g = x[t] . Wg[e]^T,  u = x[t] . Wu[e]^T          (one packed gate|up
+ *         projection; mlx-node PR #168 page: the "MLP gate|up" split)
+ *     h = gelu_tanh(g) * u                              (SwiftLM issue #236,
+ *         "Still missing": activation(xGate) * xUp, activation =
+ *         geluApproximate)
+ *     y = h . Wd[e]^T
+ *   out[t] = sum_j topk_weights[t, j] * y(t, j)         (SwiftLM issue #236,
+ *         "Already on main": weightedExpertSum; Layr-Labs/mlx PR #4,
+ *         "Measured standing": direct weighted unsort)
+ *
+ * with gelu_tanh(v) = 0.5 v (1 + tanh(sqrt(2/pi) (v + 0.044715 v^3))).
+ *
+ * Weights are affine 4-bit, group size 64, in the layout of the Layr-Labs/mlx
+ * PR #4 page ("What": packed gate/up [128, 1408, 352] and down [128, 2816, 88]
+ * uint32 for 128 experts, hidden 2816, intermediate 704):
+ *
+ *   w_gateup uint32 [E, 2I, H/8]  rows [0, I) gate, [I, 2I) up; K contiguous
+ *   s_gateup bf16   [E, 2I, H/64] b_gateup bf16 [E, 2I, H/64]
+ *   w_down   uint32 [E, H, I/8]   s_down bf16 [E, H, I/64]  b_down bf16 [E, H, I/64]
+ *
+ * Element c of a row is the 4-bit code q at bits 4*(c%8) of word c/8 (low
+ * nibble first) and dequantises to  W = S[c/64] * q + B[c/64]  in fp32.
+ *
+ * Conventions for every entry point:
+ *  - All array pointers are DEVICE pointers owned by the caller; the library
+ *    never allocates, frees or synchronises.  Work is enqueued on `stream`
+ *    (a hipStream_t; NULL is the default stream) and is stream-ordered.
+ *  - Entry points never throw and never abort.  Host-checkable errors are
+ *    returned before anything is enqueued.
+ *  - The library keeps no mutable global state; concurrent calls on distinct
+ *    buffers are safe.
+ */
+#ifndef MOE_FFN_H
+#define MOE_FFN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t moe_status;
+enum {
+    MOE_OK = 0,
+    MOE_ERR_NULL = -1,        /* a required pointer is NULL                    */
+    MOE_ERR_SHAPE = -2,       /* a size is negative, inconsistent or overflows */
+    MOE_ERR_UNSUPPORTED = -3, /* bits != 4, group_size != 64, E too large, ... */
+    MOE_ERR_ALIGN = -4,       /* a pointer is not aligned as required          */
+    MOE_ERR_WORKSPACE = -5,   /* workspace missing or too small                */
+    MOE_ERR_HIP = -6          /* the HIP runtime rejected a launch             */
+};
+
+/* One tile of sorted rows of a single expert: rows
+ * [row_begin, row_begin + row_count) of the sorted order.  bm is the tile
+ * height class: bm_small when row_count <= bm_small, else bm_big
+ * (Layr-Labs/mlx PR #4, "What": BM32 expert tiles with BM16 fallback rows). */
+typedef struct {
+    int32_t expert;
+    int32_t row_begin;
+    int32_t row_count;
+    int32_t bm;
+} moe_tile;
+
+/* Problem description.  Append-only: new fields go at the end. */
+typedef struct {
+    int32_t T;          /* tokens, >= 0                                  */
+    int32_t k;          /* experts per token, 1 <= k <= E                */
+    int32_t E;          /* experts, 1 <= E <= MOE_MAX_EXPERTS            */
+    int32_t H;          /* hidden size, multiple of 64                   */
+    int32_t I;          /* intermediate size, multiple of 64             */
+    int32_t group_size; /* must be 64                                    */
+    int32_t bits;       /* must be 4                                     */
+    uint32_t flags;     /* MOE_F_* below                                 */
+} moe_problem;
+
+#define MOE_MAX_EXPERTS 1024
+/* out is fp32 [T, H] instead of bf16 */
+#define MOE_F_FP32_OUT 1u
+/* the GeGLU intermediate h is kept in fp32 instead of bf16 (the
+ * fp32-accumulator path); combine with MOE_F_FP32_OUT for a full-fp32 result */
+#define MOE_F_FP32_INTERMEDIATE 2u
+
+/* Upper bound on the number of tiles for A assignments over E experts with
+ * tile height bm_big: floor(A / bm_big) + min(E, A).  Returns -1 on bad input. */
+int32_t moe_max_tiles(int64_t A, int32_t E, int32_t bm_big);
+
+/*
+ * Route the T*k assignments by expert and cut them into tiles
+ * (Layr-Labs/mlx PR #4, "What": sorted expert indices and the parallel tile
+ * descriptor builder -- binary search, exclusive scan, upper-bound emission).
+ *
+ *   topk_ids  int32 [T*k]  expert of flat assignment a = t*k + j
+ *   counts    int32 [E]    rows per expert (valid ids only)
+ *   offsets   int32 [E+1]  exclusive scan of counts; offsets[E] = valid rows
+ *   perm      int32 [T*k]  sorted slot -> flat assignment.  Stable: within an
+ *                          expert, ascending a.  Assignments whose id is
+ *                          outside [0, E) follow all valid rows, ascending a.
+ *   inv_perm  int32 [T*k]  flat assignment -> sorted slot
+ *   tiles     moe_tile [max_tiles]  in expert order; per expert, tiles of
+ *                          bm_big rows, the last one possibly short
+ *   num_tiles int32 [2]    [0] = number of tiles written, [1] = number of
+ *                          assignments with an out-of-range expert id
+ *
+ * Requires 1 <= bm_small <= bm_big, E <= MOE_MAX_EXPERTS and
+ * max_tiles >= moe_max_tiles(T*k, E, bm_big).  T = 0 is valid (counts and
+ * offsets are zeroed).  All outputs are bit-exact and deterministic.
+ */
+moe_status moe_sort_build_tiles(const int32_t* topk_ids, int32_t T, int32_t k,
+                                int32_t E, int32_t bm_big, int32_t bm_small,
+                                int32_t* counts, int32_t* offsets, int32_t* perm,
+                                int32_t* inv_perm, moe_tile* tiles,
+                                int32_t max_tiles, int32_t* num_tiles,
+                                void* stream);
+
+/* Bytes of device workspace moe_expert_ffn_forward needs for problem p
+ * (0 on invalid p). */
+size_t moe_ffn_workspace_bytes(const moe_problem* p);
+
+/* Byte offsets of the forward's intermediates inside its workspace, so that
+ * callers and tests can inspect them after a forward on the same stream. */
+typedef struct {
+    size_t counts;    /* int32 [E]                                        */
+    size_t offsets;   /* int32 [E+1]                                      */
+    size_t perm;      /* int32 [A]                                        */
+    size_t inv_perm;  /* int32 [A]                                        */
+    size_t tiles;     /* moe_tile [max_tiles]                             */
+    size_t num_tiles; /* int32 [2]                                        */
+    size_t h;         /* [A, I] sorted order; bf16, or fp32 with
+                         MOE_F_FP32_INTERMEDIATE                          */
+    size_t y;         /* fp32 [A, H] flat order a = t*k + j, already
+                         multiplied by topk_weights; rows of assignments
+                         with an out-of-range id are not written          */
+    size_t total;     /* == moe_ffn_workspace_bytes(p)                    */
+    int32_t max_tiles;
+    int32_t bm_big;
+    int32_t bm_small;
+    int32_t reserved;
+} moe_ws_layout;
+
+moe_status moe_ffn_workspace_layout(const moe_problem* p, moe_ws_layout* layout);
+
+/*
+ * Full expert FFN forward: route/sort/tile, gathered 4-bit gate|up matmul with
+ * the fused GeGLU product, gathered 4-bit down matmul with the weighted
+ * unsort, and the combine back to tokens.
+ *
+ *   x            bf16 [T, H]        16-byte aligned
+ *   topk_ids     int32 [T, k]
+ *   topk_weights fp32 [T, k]        used as given (no renormalisation)
+ *   w_gateup ... b_down             see the layout above; w_* 16-byte aligned
+ *   out          [T, H] bf16, or fp32 with MOE_F_FP32_OUT
+ *   ws           device workspace of at least moe_ffn_workspace_bytes(p)
+ *                bytes, 256-byte aligned
+ *
+ * Assignments with an expert id outside [0, E) contribute zero (they are
+ * counted in the workspace's num_tiles[1]).  The host never waits on the
+ * device: the tile count stays in device memory.  Results are deterministic
+ * and independent of the order of tokens.
+ */
+moe_status moe_expert_ffn_forward(const moe_problem* p, const void* x,
+                                  const int32_t* topk_ids, const float* topk_weights,
+                                  const uint32_t* w_gateup, const void* s_gateup,
+                                  const void* b_gateup, const uint32_t* w_down,
+                                  const void* s_down, const void* b_down, void* out,
+                                  void* ws, size_t ws_bytes, void* stream);
+
+/* Same as moe_expert_ffn_forward, and records events[0..4] (hipEvent_t,
+ * created by the caller) on `stream` before the route kernel, after it, after
+ * the gate|up kernel, after the down kernel and after the combine kernel, so
+ * that each stage can be timed on the stream it runs on.  events may be NULL. */
+moe_status moe_expert_ffn_forward_timed(const moe_problem* p, const void* x,
+                                        const int32_t* topk_ids,
+                                        const float* topk_weights,
+                                        const uint32_t* w_gateup, const void* s_gateup,
+                                        const void* b_gateup, const uint32_t* w_down,
+                                        const void* s_down, const void* b_down,
+                                        void* out, void* ws, size_t ws_bytes,
+                                        void* stream, void* const* events);
+
+/* Static description of a status code. */
+const char* moe_status_string(moe_status s);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_FFN_H */

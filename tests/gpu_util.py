@@ -1,0 +1,143 @@
+"""Helpers for the GPU parity tests: upload a problem, run the library, read
+its workspace, and the tolerance rules.
+
+Tolerances (from the target statement of this path):
+  * integer outputs (sort, tiles): bit-exact;
+  * bf16 outputs: max_i(|gpu_i - ref_i| - half_ulp_bf16(max(|gpu_i|, |ref_i|)))
+    <= 2e-2 * rms(ref) -- the half-ulp allowance is the rounding of the
+    output itself, which even an exact result pays;
+  * the fp32-intermediate, fp32-output path: ||gpu - ref||_2 / ||ref||_2 <= 1e-3.
+"""
+from __future__ import annotations
+
+import ctypes
+import sys
+
+import numpy as np
+import torch
+
+import bit_gathered_quantized_amd as bgq
+import moe_synth as ms
+
+BF16_MAX_REL_RMS = 2e-2
+FP32_L2_REL = 1e-3
+
+
+def log(msg: str):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def dev_arrays(p, dev="cuda"):
+    def t(a, dt):
+        return torch.from_numpy(np.ascontiguousarray(a).view(dt)).to(dev)
+    return dict(
+        x=t(p.x, np.int16).view(torch.bfloat16),
+        ids=t(p.topk_ids, np.int32),
+        w=t(p.topk_weights, np.float32),
+        w_gu=t(p.w_gateup, np.int32),
+        s_gu=t(p.s_gateup, np.int16),
+        b_gu=t(p.b_gateup, np.int16),
+        w_d=t(p.w_down, np.int32),
+        s_d=t(p.s_down, np.int16),
+        b_d=t(p.b_down, np.int16),
+    )
+
+
+def run_forward(p, fp32=False, d=None, workspace=None):
+    """Run the forward; return (out as float64 numpy, workspace tensor, layout)."""
+    if d is None:
+        d = dev_arrays(p)
+    flags = (bgq.MOE_F_FP32_OUT | bgq.MOE_F_FP32_INTERMEDIATE) if fp32 else 0
+    prob = bgq.problem(p.T, p.k, p.E, p.H, p.I, flags)
+    lay = bgq.workspace_layout(prob)
+    if workspace is None:
+        workspace = torch.zeros(max(lay.total, 256), dtype=torch.uint8, device="cuda")
+    out = bgq.expert_ffn_forward(d["x"], d["ids"], d["w"], d["w_gu"], d["s_gu"], d["b_gu"],
+                                 d["w_d"], d["s_d"], d["b_d"], fp32_out=fp32,
+                                 fp32_intermediate=fp32, workspace=workspace)
+    torch.cuda.synchronize()
+    o = out.float().cpu().numpy().astype(np.float64)
+    return o, workspace, lay
+
+
+def ws_view(ws, offset, count, dtype):
+    itemsize = np.dtype(dtype).itemsize
+    raw = ws[offset: offset + count * itemsize].cpu().numpy()
+    return raw.view(dtype)
+
+
+def ws_h(ws, lay, p, fp32):
+    A = p.T * p.k
+    if fp32:
+        return ws_view(ws, lay.h, A * p.I, np.float32).reshape(A, p.I).astype(np.float64)
+    bits = ws_view(ws, lay.h, A * p.I, np.uint16).reshape(A, p.I)
+    return ms.bf16_bits_to_f32(bits).astype(np.float64)
+
+
+def ws_y_rows(ws, lay, p, rows):
+    """Rows (flat assignment indices) of the weighted y buffer."""
+    out = np.zeros((len(rows), p.H))
+    for i, a in enumerate(rows):
+        out[i] = ws_view(ws, lay.y + int(a) * p.H * 4, p.H, np.float32)
+    return out
+
+
+def half_ulp_bf16(v: np.ndarray) -> np.ndarray:
+    v = np.abs(v)
+    e = np.floor(np.log2(np.maximum(v, 1e-38)))
+    return np.where(v > 0, np.exp2(e - 8), 0.0)
+
+
+def bf16_excess(gpu: np.ndarray, ref: np.ndarray) -> float:
+    """max(|gpu - ref| - half_ulp(max(|gpu|, |ref|))) / rms(ref)."""
+    rms = float(np.sqrt(np.mean(ref ** 2)))
+    allow = half_ulp_bf16(np.maximum(np.abs(gpu), np.abs(ref)))
+    return float(np.max(np.abs(gpu - ref) - allow)) / max(rms, 1e-300)
+
+
+def max_rel_rms(gpu, ref) -> float:
+    rms = float(np.sqrt(np.mean(ref ** 2)))
+    return float(np.max(np.abs(gpu - ref))) / max(rms, 1e-300)
+
+
+def l2_rel(gpu, ref) -> float:
+    return float(np.linalg.norm(gpu - ref) / max(np.linalg.norm(ref), 1e-300))
+
+
+def assert_bf16_close(gpu, ref, what=""):
+    ex = bf16_excess(gpu, ref)
+    log(f"  {what}: bf16 excess/rms={ex:.4g} (literal max/rms={max_rel_rms(gpu, ref):.4g}, "
+        f"l2rel={l2_rel(gpu, ref):.3g})")
+    assert ex <= BF16_MAX_REL_RMS, f"{what}: {ex} > {BF16_MAX_REL_RMS}"
+
+
+def assert_fp32_close(gpu, ref, what="", tol=FP32_L2_REL):
+    e = l2_rel(gpu, ref)
+    log(f"  {what}: fp32 l2rel={e:.3g} max/rms={max_rel_rms(gpu, ref):.3g}")
+    assert e <= tol, f"{what}: {e} > {tol}"
+
+
+def sample_tokens(p, n=24, seed=1):
+    """A spread of tokens: first, last, random, and ones routed to the most
+    and least loaded experts (tile tails)."""
+    rng = np.random.default_rng(seed)
+    counts = np.bincount(p.topk_ids[(p.topk_ids >= 0) & (p.topk_ids < p.E)], minlength=p.E)
+    hot = int(np.argmax(counts))
+    nz = np.nonzero(counts)[0]
+    cold = int(nz[np.argmin(counts[nz])])
+    pick = {0, p.T - 1}
+    for e in (hot, cold):
+        rows = np.nonzero((p.topk_ids == e).any(axis=1))[0]
+        pick.update(rows[:2].tolist())
+        pick.update(rows[-2:].tolist())
+    extra = rng.choice(p.T, size=min(p.T, n), replace=False)
+    for t in extra:
+        if len(pick) >= n:
+            break
+        pick.add(int(t))
+    return np.array(sorted(pick), np.int32)
+
+
+def ctypes_ptr(t):
+    return ctypes.c_void_p(t.data_ptr())

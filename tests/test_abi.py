@@ -1,0 +1,119 @@
+"""The C ABI on the CPU: the library loads, exports every declared entry
+point, and rejects bad arguments before enqueueing anything (no GPU needed:
+every call here fails a host-side check first)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import bit_gathered_quantized_amd as bgq
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                      "include", "moe_ffn.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    names = declared_functions()
+    assert len(names) >= 7
+    L = bgq.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    assert sorted(bgq.EXPORTED_SYMBOLS) == names
+
+
+def test_max_tiles():
+    assert bgq.max_tiles(16384, 128, 32) == 512 + 128
+    assert bgq.max_tiles(64, 128, 32) == 2 + 64
+    assert bgq.max_tiles(0, 8, 32) == 0
+    assert bgq.max_tiles(-1, 8, 32) == -1
+    assert bgq.max_tiles(10, 0, 32) == -1
+
+
+def test_workspace_layout_and_sizes():
+    p = bgq.problem(2048, 8, 128, 2816, 704)
+    lay = bgq.workspace_layout(p)
+    A = 2048 * 8
+    assert lay.total == bgq.workspace_bytes(p)
+    offs = [lay.counts, lay.offsets, lay.perm, lay.inv_perm, lay.tiles, lay.num_tiles, lay.h, lay.y]
+    assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
+    assert lay.y - lay.h >= A * 704 * 2 and lay.total - lay.y >= A * 2816 * 4
+    assert lay.max_tiles == 640 and lay.bm_big == 32 and lay.bm_small == 16
+    p32 = bgq.problem(2048, 8, 128, 2816, 704, bgq.MOE_F_FP32_INTERMEDIATE)
+    assert bgq.workspace_layout(p32).total - bgq.workspace_layout(p32).y == lay.total - lay.y
+    assert bgq.workspace_layout(p32).y - bgq.workspace_layout(p32).h >= A * 704 * 4
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(bits=8), -3), (dict(group_size=32), -3), (dict(E=2000), -3), (dict(flags=8), -3),
+    (dict(H=100), -2), (dict(I=96), -2), (dict(k=0), -2), (dict(k=9, E=8), -2), (dict(T=-1), -2),
+])
+def test_bad_problem(kw, status):
+    base = dict(T=4, k=2, E=8, H=256, I=128, flags=0, group_size=64, bits=4)
+    base.update(kw)
+    p = bgq.problem(**base)
+    assert bgq.workspace_bytes(p) == 0
+    with pytest.raises(bgq.MoeError) as e:
+        bgq.workspace_layout(p)
+    assert e.value.status == status
+
+
+def _forward(p, ptrs, out, ws, ws_bytes):
+    L = bgq.lib()
+    return L.moe_expert_ffn_forward(ctypes.byref(p), *ptrs, out, ws, ws_bytes, None)
+
+
+def test_forward_host_checks():
+    p = bgq.problem(4, 2, 8, 256, 128)
+    need = bgq.workspace_bytes(p)
+    good = [ctypes.c_void_p(0x10000)] * 9
+    out = ctypes.c_void_p(0x20000)
+    ws = ctypes.c_void_p(0x40000)
+    # null pointer
+    assert _forward(p, [None] + good[1:], out, ws, need) == -1
+    assert _forward(p, good, None, ws, need) == -1
+    # workspace missing / too small
+    assert _forward(p, good, out, None, need) == -5
+    assert _forward(p, good, out, ws, need - 1) == -5
+    # misaligned x, weights, out, workspace
+    assert _forward(p, [ctypes.c_void_p(0x10002)] + good[1:], out, ws, need) == -4
+    bad_w = list(good)
+    bad_w[3] = ctypes.c_void_p(0x10008)
+    assert _forward(p, bad_w, out, ws, need) == -4
+    assert _forward(p, good, ctypes.c_void_p(0x20002), ws, need) == -4
+    assert _forward(p, good, out, ctypes.c_void_p(0x40080), need) == -4
+    # zero tokens: nothing to do, nothing touched
+    p0 = bgq.problem(0, 2, 8, 256, 128)
+    assert _forward(p0, [None] * 9, None, None, 0) == 0
+    # bad problem wins over pointers
+    assert _forward(bgq.problem(4, 2, 8, 256, 128, 0, 64, 3), good, out, ws, need) == -3
+
+
+def test_sort_host_checks():
+    L = bgq.lib()
+    P = ctypes.c_void_p
+    d = P(0x10000)
+    mt = bgq.max_tiles(40, 8, 32)
+    # bm_small > bm_big
+    assert L.moe_sort_build_tiles(d, 10, 4, 8, 16, 32, d, d, d, d, d, mt, d, None) == -2
+    # too few tiles
+    assert L.moe_sort_build_tiles(d, 10, 4, 8, 32, 16, d, d, d, d, d, mt - 1, d, None) == -5
+    # null outputs
+    assert L.moe_sort_build_tiles(d, 10, 4, 8, 32, 16, None, d, d, d, d, mt, d, None) == -1
+    assert L.moe_sort_build_tiles(None, 10, 4, 8, 32, 16, d, d, d, d, d, mt, d, None) == -1
+    # too many experts
+    assert L.moe_sort_build_tiles(d, 10, 4, 5000, 32, 16, d, d, d, d, d, mt, d, None) == -3
+    # misaligned tile buffer
+    assert L.moe_sort_build_tiles(d, 10, 4, 8, 32, 16, d, d, d, d, P(0x10004), mt, d, None) == -4
+
+
+def test_status_strings():
+    for s in range(-6, 1):
+        assert bgq.status_string(s) and "unknown" not in bgq.status_string(s)
+    assert "unknown" in bgq.status_string(-99)

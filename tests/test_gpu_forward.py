@@ -1,0 +1,129 @@
+"""Expert FFN forward against the oracle (GPU).
+
+Small problems are compared in full; the 128-expert workloads on sampled
+tokens (all k assignments of each), in the same launch configuration the
+benchmark times.  Intermediates (h in sorted order, weighted y in flat
+order) are read from the documented workspace layout and compared too.
+"""
+import numpy as np
+import pytest
+import torch
+
+import bit_gathered_quantized_amd as bgq
+import moe_synth as ms
+from gpu_util import (assert_bf16_close, assert_fp32_close, bf16_excess, dev_arrays, log,
+                      run_forward, sample_tokens, ws_h, ws_view, ws_y_rows)
+
+pytestmark = pytest.mark.gpu
+
+
+def compare(oracle_lib, p, fp32, tokens=None):
+    log(f"forward: {p.name} E={p.E} H={p.H} I={p.I} T={p.T} k={p.k} fp32={fp32} "
+        f"tokens={'all' if tokens is None else len(tokens)}")
+    out, ws, lay = run_forward(p, fp32=fp32)
+    toks = np.arange(p.T, dtype=np.int32) if tokens is None else tokens
+    ref = oracle_lib.ffn_tokens(p, toks)
+    rows = (toks[:, None] * p.k + np.arange(p.k)[None, :]).ravel()
+    valid = ((p.topk_ids.ravel()[rows] >= 0) & (p.topk_ids.ravel()[rows] < p.E))
+    # h: sorted order -> flat order through inv_perm
+    A = p.T * p.k
+    inv = ws_view(ws, lay.inv_perm, A, np.int32)
+    h = ws_h(ws, lay, p, fp32)[inv[rows]]
+    # y: weighted, flat order
+    y = ws_y_rows(ws, lay, p, rows[valid])
+    yref = (ref["y"] * p.topk_weights.ravel()[rows][:, None])[valid]
+    o = out[toks]
+    if fp32:
+        assert_fp32_close(h[valid], ref["h"][valid], "h")
+        assert_fp32_close(y, yref, "y")
+        assert_fp32_close(o, ref["out"], "out")
+    else:
+        # h is the bf16 rounding of an fp32 value: only the half-ulp remains
+        assert bf16_excess(h[valid], ref["h"][valid]) <= 1e-3
+        # y is fp32 but built from the bf16 h, whose rounding (2^-9 relative
+        # per element) gives ~1.6e-3 L2-relative; the bar is 2.5x that
+        assert_fp32_close(y, yref, "y (from bf16 h)", tol=4e-3)
+        assert_bf16_close(o, ref["out"], "out")
+    return out
+
+
+@pytest.mark.parametrize("fp32", [False, True])
+def test_tiny_full(oracle_lib, fp32):
+    compare(oracle_lib, ms.make_config("tiny"), fp32)
+
+
+@pytest.mark.parametrize("fp32", [False, True])
+def test_decode_full(oracle_lib, fp32):
+    compare(oracle_lib, ms.make_config("decode"), fp32)
+
+
+@pytest.mark.parametrize("name", ["prefill4k", "prefill8k", "prefill16k"])
+@pytest.mark.parametrize("fp32", [False, True])
+def test_prefill_sampled(oracle_lib, name, fp32):
+    p = ms.make_config(name)
+    compare(oracle_lib, p, fp32, tokens=sample_tokens(p, n=20))
+
+
+@pytest.mark.parametrize("shape", [
+    (1, 64, 64, 1, 1),      # one expert, one token
+    (4, 192, 64, 5, 2),     # H not a multiple of 256 or 128: partial chunk and column block
+    (3, 320, 192, 40, 3),   # 5 groups; I = 3 column blocks
+    (8, 256, 128, 200, 2),  # more than 32 rows per expert: full and tail tiles
+    (2, 128, 64, 33, 2),    # 33 tokens top-2 over 2 experts: 32 + tail tiles
+])
+@pytest.mark.parametrize("fp32", [False, True])
+def test_shapes_full(oracle_lib, shape, fp32):
+    E, H, I, T, k = shape
+    compare(oracle_lib, ms.make_problem(E, H, I, T, k, seed=H + T, name="shape"), fp32)
+
+
+def test_all_tokens_one_expert(oracle_lib):
+    T, k, E = 300, 2, 8
+    ids = np.tile(np.array([[3, 6]], np.int32), (T, 1))
+    p = ms.make_problem(E, 256, 128, T, k, seed=4, topk_ids=ids, name="hot")
+    compare(oracle_lib, p, False)
+
+
+def test_invalid_ids_contribute_zero(oracle_lib):
+    p = ms.make_config("tiny")
+    p.topk_ids[3, 0] = p.E
+    p.topk_ids[10, 1] = -1
+    p.topk_ids[11, :] = 99
+    compare(oracle_lib, p, False)
+    compare(oracle_lib, p, True)
+
+
+def test_zero_tokens():
+    p = ms.make_problem(4, 64, 64, 0, 2, seed=0, name="empty")
+    d = dev_arrays(p)
+    out = bgq.expert_ffn_forward(d["x"], d["ids"], d["w"], d["w_gu"], d["s_gu"], d["b_gu"],
+                                 d["w_d"], d["s_d"], d["b_d"])
+    torch.cuda.synchronize()
+    assert out.shape == (0, 64)
+
+
+def test_deterministic_and_token_permutation_equivariant():
+    p = ms.make_config("prefill4k")
+    log("determinism + permutation equivariance on prefill4k")
+    o1, _, _ = run_forward(p)
+    o2, _, _ = run_forward(p)
+    np.testing.assert_array_equal(o1, o2)
+    perm = np.random.default_rng(3).permutation(p.T)
+    q = ms.make_config("prefill4k")
+    q.x = np.ascontiguousarray(p.x[perm])
+    q.topk_ids = np.ascontiguousarray(p.topk_ids[perm])
+    q.topk_weights = np.ascontiguousarray(p.topk_weights[perm])
+    o3, _, _ = run_forward(q)
+    np.testing.assert_array_equal(o3, o1[perm])
+
+
+def test_symmetric_down_codes_cancel():
+    """q = 8 with b = -8 s makes W_down exactly zero; the fp32 bias path must
+    cancel the +128 code offset to rounding level."""
+    p = ms.make_problem(4, 256, 128, 40, 2, seed=2, name="zero")
+    ref, _, _ = run_forward(p, fp32=True)
+    p.w_down[:] = 0x88888888
+    out, _, _ = run_forward(p, fp32=True)
+    rms = float(np.sqrt(np.mean(ref ** 2)))
+    log(f"  max|out| = {np.abs(out).max():.3g}, rms(normal) = {rms:.3g}")
+    assert np.abs(out).max() <= 1e-4 * rms

@@ -8,7 +8,7 @@ so that the 256 MB Infinity Cache cannot serve a step from the previous one.
 
 Prints ONE JSON line:
   value         whole-forward assignments/s over the timed steps (host clock,
-                synchronised on both sides), no per-stage events in that loop;
+                synchronised on both sides), no per-kernel events in that loop;
   roofline      the dominant kernel's algorithmic bytes (or flops) per launch
                 divided by its mean duration, from HIP events recorded on the
                 library's stream in a second, instrumented loop;
@@ -31,32 +31,58 @@ if ROOT not in sys.path:
 METRIC = "expert-FFN assignments/s and TFLOP/s (or HBM GB/s) vs roofline, 1 MI355X"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
-STAGES = ("moe_route_sort_tiles", "moe_gateup_geglu", "moe_down", "moe_combine")
+BM_BIG, BM_SMALL = 128, 16     # tile heights the forward routes with
 
 
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def algorithmic_work(p, touched: int):
-    """Per-launch algorithmic bytes and flops of each kernel (what the method
-    must move and compute, not what a kernel happens to re-read)."""
+def algorithmic_work(p):
+    """Per-launch algorithmic bytes and flops of each kernel: what the method
+    must move and compute for the rows that kernel owns (tiles of <= 16 rows
+    go to the skinny kernels, larger tiles to the wide ones), not what a
+    kernel happens to re-read."""
+    import numpy as np
     E, H, I, T, k = p.E, p.H, p.I, p.T, p.k
     A = T * k
     G_h, G_i = H // 64, I // 64
-    gu_expert = 2 * I * H // 2 + 2 * (2 * I * G_h * 2)      # packed codes + scales + biases
+    gu_expert = 2 * I * H // 2 + 2 * (2 * I * G_h * 2)      # codes + scales + biases
     d_expert = H * I // 2 + 2 * (H * G_i * 2)
+    ids = p.topk_ids.ravel()
+    counts = np.bincount(ids, minlength=E)
+    # rows of each expert in skinny tiles: all of them if it has <= 16 rows,
+    # else its last tile when that has <= 16 rows
+    rem = counts % BM_BIG
+    skinny_rows = np.where((rem > 0) & (rem <= BM_SMALL), rem, 0)
+    wide_rows = counts - skinny_rows
+    order = np.argsort(ids, kind="stable")
+    starts = np.concatenate([[0], np.cumsum(counts)[:-1]])
+    in_skinny = np.zeros(A, bool)
+    for e in np.nonzero(skinny_rows)[0]:
+        in_skinny[order[starts[e] + counts[e] - skinny_rows[e]: starts[e] + counts[e]]] = True
+    tok = np.arange(A) // k
+    tok_s = np.unique(tok[in_skinny]).size
+    tok_w = np.unique(tok[~in_skinny]).size
+    rs, rw = int(skinny_rows.sum()), int(wide_rows.sum())
+    es, ew = int(np.count_nonzero(skinny_rows)), int(np.count_nonzero(wide_rows))
     work = {
-        "moe_route_sort_tiles": dict(bytes=A * 4 + A * 8 + (2 * E + 1) * 4, flops=0),
-        "moe_gateup_geglu": dict(bytes=touched * gu_expert + T * H * 2 + A * I * 2,
-                                 flops=A * 4 * H * I),
-        "moe_down": dict(bytes=touched * d_expert + A * I * 2 + A * H * 4 + A * 4,
-                         flops=A * 2 * H * I),
+        "moe_route_sort_tiles": dict(bytes=A * 12 + (2 * E + 1) * 4 + T * H * 4 + T * G_h * 4,
+                                     flops=0),
+        "moe_gateup_skinny": dict(bytes=es * gu_expert + tok_s * H * 2 + rs * I * 2,
+                                  flops=rs * 4 * H * I),
+        "moe_gateup_wide": dict(bytes=ew * gu_expert + tok_w * H * 2 + rw * I * 2,
+                                flops=rw * 4 * H * I),
+        "moe_down_skinny": dict(bytes=es * d_expert + rs * I * 2 + rs * H * 4, flops=rs * 2 * H * I),
+        "moe_down_wide": dict(bytes=ew * d_expert + rw * I * 2 + rw * H * 4, flops=rw * 2 * H * I),
         "moe_combine": dict(bytes=A * H * 4 + T * H * 2 + A * 4, flops=A * H),
     }
+    touched = int(np.count_nonzero(counts))
     fwd = dict(bytes=touched * (gu_expert + d_expert) + T * H * 2 + A * 8 + T * H * 2,
                flops=A * 6 * H * I)
-    return work, fwd
+    split = dict(skinny_rows=rs, wide_rows=rw, experts_with_skinny_tile=es,
+                 wide_tiles=int(np.sum((wide_rows + BM_BIG - 1) // BM_BIG)))
+    return work, fwd, split
 
 
 def bound_of(w):
@@ -99,7 +125,6 @@ def cpu_baseline_leg(p, gpu_out, seconds_budget: float):
     import numpy as np
 
     import oracle
-    import moe_synth as ms
 
     if p.T <= 16:
         tokens = np.arange(p.T, dtype=np.int32)
@@ -137,7 +162,8 @@ def cpu_baseline_leg(p, gpu_out, seconds_budget: float):
 
 
 def main():
-    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap = argparse.ArgumentParser(description=__doc__,
+                                 formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
@@ -169,9 +195,8 @@ def main():
     A = p.T * p.k
     counts = np.bincount(p.topk_ids.ravel(), minlength=p.E)
     touched = int(np.count_nonzero(counts))
-    n_tiles = int(np.sum((counts + 31) // 32))
     log(f"workload {args.workload}: E={p.E} H={p.H} I={p.I} T={p.T} k={p.k} A={A} "
-        f"touched={touched} tiles={n_tiles}")
+        f"touched={touched}")
 
     dev = torch.device("cuda", 0)
 
@@ -193,23 +218,24 @@ def main():
         bgq.expert_ffn_forward(*sets[i % len(sets)], out=out, workspace=ws, stream=stream,
                                events=events)
 
-    # warm-up
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
 
     # timed loop: whole forward, host clock
-    torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
         step(i)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     ms_per_step = elapsed / args.steps * 1e3
+    log(f"timed loop: {args.steps} steps, {ms_per_step * 1e3:.1f} us/step")
 
     # instrumented loop: per-kernel durations from events on the same stream
+    kernels = bgq.KERNELS
     n_ev = min(args.steps, 100)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(n_ev)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(bgq.N_EVENTS)]
+           for _ in range(n_ev)]
     for row in evs:
         for e in row:
             e.record(stream)
@@ -217,20 +243,19 @@ def main():
     for i in range(n_ev):
         step(i, events=[e.cuda_event for e in evs[i]])
     torch.cuda.synchronize()
-    stage_us = {s: [] for s in STAGES}
+    kern_us = {s: [] for s in kernels}
     fwd_us = []
     for row in evs:
-        for j, s in enumerate(STAGES):
-            stage_us[s].append(row[j].elapsed_time(row[j + 1]) * 1e3)
-        fwd_us.append(row[0].elapsed_time(row[4]) * 1e3)
-    mean_us = {s: statistics.fmean(v) for s, v in stage_us.items()}
+        for j, s in enumerate(kernels):
+            kern_us[s].append(row[2 * j].elapsed_time(row[2 * j + 1]) * 1e3)
+        fwd_us.append(row[0].elapsed_time(row[-1]) * 1e3)
+    mean_us = {s: statistics.fmean(v) for s, v in kern_us.items()}
 
-    work, fwd_work = algorithmic_work(p, touched)
-    dominant = max(STAGES, key=lambda s: mean_us[s])
+    work, fwd_work, split = algorithmic_work(p)
+    dominant = max(kernels, key=lambda s: mean_us[s])
     roof = roofline_entry(work[dominant], mean_us[dominant] * 1e-6)
     roof["kernel"] = dominant
-    traffic = load_traffic(dominant, args.workload)
-    roof["traffic"] = traffic
+    roof["traffic"] = load_traffic(dominant, args.workload)
 
     fwd_s = statistics.median(fwd_us) * 1e-6
     forward = dict(
@@ -245,11 +270,14 @@ def main():
         frac=roofline_entry(fwd_work, fwd_s)["frac"],
         wall_frac=roofline_entry(fwd_work, ms_per_step * 1e-3)["frac"],
     )
-    kernels = {}
-    for s in STAGES:
-        e = roofline_entry(work[s], mean_us[s] * 1e-6)
-        kernels[s] = dict(mean_us=round(mean_us[s], 2), bound=e["bound"], achieved=e["achieved"],
-                          unit=e["unit"], frac=e["frac"])
+    kstats = {}
+    for s in kernels:
+        w = work[s]
+        entry = dict(mean_us=round(mean_us[s], 2))
+        if (w["bytes"] or w["flops"]) and mean_us[s] > 0:
+            e = roofline_entry(w, mean_us[s] * 1e-6)
+            entry.update(bound=e["bound"], achieved=e["achieved"], unit=e["unit"], frac=e["frac"])
+        kstats[s] = entry
 
     result = {
         "metric": METRIC,
@@ -267,16 +295,14 @@ def main():
         "config": {"workload": args.workload, "E": p.E, "H": p.H, "I": p.I, "T": p.T,
                    "k": p.k, "assignments": A, "group_size": 64, "bits": 4,
                    "router": ms.CONFIGS[args.workload]["router"], "seed": 0,
-                   "touched_experts": touched, "tiles_bm32": n_tiles,
-                   "input_copies": len(sets)},
+                   "touched_experts": touched, "input_copies": len(sets), **split},
         "roofline": roof,
         "forward": forward,
-        "kernels": kernels,
+        "kernels": kstats,
     }
 
     if not args.no_cpu_baseline:
         gpu_out = out.float().cpu().numpy().astype(np.float64)
-        # the last forward ran on copy (n_ev - 1) % copies: all copies hold the same data
         base, parity = cpu_baseline_leg(p, gpu_out, args.cpu_seconds)
         result["cpu_baseline"] = base
         result["parity"] = parity

@@ -20,6 +20,11 @@ __all__ = [
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoeffn.so")
 
 MOE_OK = 0
+# kernels of one forward, in launch order; the timed forward takes a start
+# and a stop event per kernel
+KERNELS = ("moe_route_sort_tiles", "moe_gateup_skinny", "moe_gateup_wide", "moe_down_skinny",
+           "moe_down_wide", "moe_combine")
+N_EVENTS = 2 * len(KERNELS)
 MOE_F_FP32_OUT = 1
 MOE_F_FP32_INTERMEDIATE = 2
 
@@ -44,7 +49,8 @@ class MoeProblem(ctypes.Structure):
 
 class MoeWsLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in
-                ("counts", "offsets", "perm", "inv_perm", "tiles", "num_tiles", "h", "y", "total")] + \
+                ("counts", "offsets", "perm", "inv_perm", "tiles", "num_tiles", "x_perm", "x_sums",
+                 "h", "h_sums", "y", "total")] + \
                [(n, ctypes.c_int32) for n in ("max_tiles", "bm_big", "bm_small", "reserved")]
 
 
@@ -205,7 +211,9 @@ def expert_ffn_forward(x, topk_ids, topk_weights, w_gateup, s_gateup, b_gateup,
         st = lib().moe_expert_ffn_forward(ctypes.byref(p), *ptrs, optr, wptr,
                                           workspace.numel(), s)
     else:
-        arr = (ctypes.c_void_p * 5)(*[ctypes.c_void_p(int(e)) for e in events])
+        if len(events) != N_EVENTS:
+            raise ValueError(f"events must hold {N_EVENTS} event handles")
+        arr = (ctypes.c_void_p * N_EVENTS)(*[ctypes.c_void_p(int(e)) for e in events])
         st = lib().moe_expert_ffn_forward_timed(ctypes.byref(p), *ptrs, optr, wptr,
                                                 workspace.numel(), s, arr)
     _check(st, "moe_expert_ffn_forward")

@@ -22,6 +22,8 @@ HIPCC_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
     "-Wall", "-Wextra", "-fno-fast-math",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA results straight into VGPRs: the per-group scale FMA reads them
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
 ]
 
 

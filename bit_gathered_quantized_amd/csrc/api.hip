@@ -23,6 +23,7 @@ moe_status check_problem(const moe_problem* p) {
     if (p->E > MOE_MAX_EXPERTS) return MOE_ERR_UNSUPPORTED;
     if (p->k > p->E) return MOE_ERR_SHAPE;
     if (p->H % moe::kGroup || p->I % moe::kGroup) return MOE_ERR_SHAPE;
+    if (p->H > moe::kMaxDim || p->I > moe::kMaxDim) return MOE_ERR_UNSUPPORTED;
     const int64_t A = static_cast<int64_t>(p->T) * p->k;
     if (A > INT32_MAX / 2) return MOE_ERR_SHAPE;
     return MOE_OK;
@@ -31,9 +32,11 @@ moe_status check_problem(const moe_problem* p) {
 moe_ws_layout make_layout(const moe_problem* p) {
     moe_ws_layout l = {};
     const int64_t A = static_cast<int64_t>(p->T) * p->k;
-    l.bm_big = moe::kBmBig;
+    // With an fp32 h the down matmul carries two activation parts; it runs
+    // on tiles of at most 64 rows (at most 4 row blocks per wave).
+    l.bm_big = (p->flags & MOE_F_FP32_INTERMEDIATE) ? moe::kBmBigF32 : moe::kBmBig;
     l.bm_small = moe::kBmSmall;
-    l.max_tiles = moe_max_tiles(A, p->E, moe::kBmBig);
+    l.max_tiles = moe_max_tiles(A, p->E, l.bm_big);
     size_t off = 0;
     auto take = [&](size_t bytes) {
         const size_t at = off;
@@ -41,13 +44,17 @@ moe_ws_layout make_layout(const moe_problem* p) {
         return at;
     };
     const size_t hbytes = (p->flags & MOE_F_FP32_INTERMEDIATE) ? 4 : 2;
+    const size_t G = p->H / moe::kGroup, GI = p->I / moe::kGroup;
     l.counts = take(sizeof(int32_t) * p->E);
     l.offsets = take(sizeof(int32_t) * (p->E + 1));
     l.perm = take(sizeof(int32_t) * A);
     l.inv_perm = take(sizeof(int32_t) * A);
     l.tiles = take(sizeof(moe_tile) * l.max_tiles);
     l.num_tiles = take(sizeof(int32_t) * 2);
+    l.x_perm = take(sizeof(uint16_t) * p->T * p->H);
+    l.x_sums = take(sizeof(float) * p->T * G);
     l.h = take(hbytes * A * p->I);
+    l.h_sums = take(sizeof(float) * A * GI);
     l.y = take(sizeof(float) * A * p->H);
     l.total = off;
     return l;
@@ -74,9 +81,14 @@ moe_status forward_impl(const moe_problem* p, const void* x, const int32_t* ids,
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     char* base = static_cast<char*>(ws);
-    auto ev = [&](int i) -> hipError_t {
-        if (!events || !events[i]) return hipSuccess;
-        return hipEventRecord(static_cast<hipEvent_t>(events[i]), s);
+    // events[2i], events[2i+1]: start and stop of kernel i
+    auto kt = [&](int i) {
+        moe::KTiming t;
+        if (events != nullptr) {
+            t.start = static_cast<hipEvent_t>(events[2 * i]);
+            t.stop = static_cast<hipEvent_t>(events[2 * i + 1]);
+        }
+        return t;
     };
 
     moe::RouteArgs r;
@@ -92,6 +104,11 @@ moe_status forward_impl(const moe_problem* p, const void* x, const int32_t* ids,
     r.inv_perm = reinterpret_cast<int32_t*>(base + l.inv_perm);
     r.tiles = reinterpret_cast<int32_t*>(base + l.tiles);
     r.num_tiles = reinterpret_cast<int32_t*>(base + l.num_tiles);
+    r.x = static_cast<const uint16_t*>(x);
+    r.T = p->T;
+    r.H = p->H;
+    r.xp = reinterpret_cast<uint16_t*>(base + l.x_perm);
+    r.xs = reinterpret_cast<float*>(base + l.x_sums);
 
     moe::FfnArgs f;
     f.T = p->T;
@@ -102,6 +119,9 @@ moe_status forward_impl(const moe_problem* p, const void* x, const int32_t* ids,
     f.max_tiles = l.max_tiles;
     f.flags = p->flags;
     f.x = static_cast<const uint16_t*>(x);
+    f.xp = r.xp;
+    f.xs = r.xs;
+    f.hs = reinterpret_cast<float*>(base + l.h_sums);
     f.ids = ids;
     f.topk_w = topk_w;
     f.w_gu = w_gu;
@@ -117,15 +137,12 @@ moe_status forward_impl(const moe_problem* p, const void* x, const int32_t* ids,
     f.y = reinterpret_cast<float*>(base + l.y);
     f.out = out;
 
-    if (ev(0) != hipSuccess) return MOE_ERR_HIP;
-    if (moe::launch_route(r, s) != hipSuccess) return MOE_ERR_HIP;
-    if (ev(1) != hipSuccess) return MOE_ERR_HIP;
-    if (moe::launch_gateup(f, s) != hipSuccess) return MOE_ERR_HIP;
-    if (ev(2) != hipSuccess) return MOE_ERR_HIP;
-    if (moe::launch_down(f, s) != hipSuccess) return MOE_ERR_HIP;
-    if (ev(3) != hipSuccess) return MOE_ERR_HIP;
-    if (moe::launch_combine(f, s) != hipSuccess) return MOE_ERR_HIP;
-    if (ev(4) != hipSuccess) return MOE_ERR_HIP;
+    if (moe::launch_route(r, s, kt(0)) != hipSuccess) return MOE_ERR_HIP;
+    if (moe::launch_gateup_skinny(f, s, kt(1)) != hipSuccess) return MOE_ERR_HIP;
+    if (moe::launch_gateup_wide(f, s, kt(2)) != hipSuccess) return MOE_ERR_HIP;
+    if (moe::launch_down_skinny(f, s, kt(3)) != hipSuccess) return MOE_ERR_HIP;
+    if (moe::launch_down_wide(f, s, kt(4)) != hipSuccess) return MOE_ERR_HIP;
+    if (moe::launch_combine(f, s, kt(5)) != hipSuccess) return MOE_ERR_HIP;
     return MOE_OK;
 }
 
@@ -170,6 +187,11 @@ moe_status moe_sort_build_tiles(const int32_t* topk_ids, int32_t T, int32_t k, i
     r.inv_perm = inv_perm;
     r.tiles = reinterpret_cast<int32_t*>(tiles);
     r.num_tiles = num_tiles;
+    r.x = nullptr;
+    r.T = T;
+    r.H = 0;
+    r.xp = nullptr;
+    r.xs = nullptr;
     return moe::launch_route(r, static_cast<hipStream_t>(stream)) == hipSuccess ? MOE_OK
                                                                                : MOE_ERR_HIP;
 }

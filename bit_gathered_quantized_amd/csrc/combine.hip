@@ -44,14 +44,13 @@ __global__ __launch_bounds__(256) void moe_combine(FfnArgs a) {
 
 }  // namespace
 
-hipError_t launch_combine(const FfnArgs& a, hipStream_t stream) {
+hipError_t launch_combine(const FfnArgs& a, hipStream_t stream, const KTiming& t) {
     const size_t total = static_cast<size_t>(a.T) * (a.H / 4);
     const dim3 grid(static_cast<unsigned>((total + 255) / 256));
     if (a.flags & MOE_F_FP32_OUT)
-        hipLaunchKernelGGL(moe_combine<true>, grid, dim3(256), 0, stream, a);
+        return launch_kernel(moe_combine<true>, grid, dim3(256), stream, t, a);
     else
-        hipLaunchKernelGGL(moe_combine<false>, grid, dim3(256), 0, stream, a);
-    return hipGetLastError();
+        return launch_kernel(moe_combine<false>, grid, dim3(256), stream, t, a);
 }
 
 }  // namespace moe

@@ -1,437 +1,826 @@
 // Gathered 4-bit quantised matmuls over expert tiles.
 //
-//   moe_gateup_geglu  h[s, n] = gelu_tanh(x[tok(s)] . Wg[e, n]) * (x[tok(s)] . Wu[e, n])
-//   moe_down          y[perm[s], m] = w[perm[s]] * (h[s] . Wd[e, m])
+//   gate|up  h[s, n] = gelu_tanh(x[tok(s)] . Wg[e, n]) * (x[tok(s)] . Wu[e, n])
+//   down     y[perm[s], m] = w[perm[s]] * (h[s] . Wd[e, m])
 //
 // Prior art: the expert-tile QMM of the Layr-Labs/mlx PR #4 page ("What":
-// BM32 expert tiles with BM16 fallback rows over sorted indices, one private
-// row count per tile), the compiled gelu-product of SwiftLM issue #236
-// ("Still missing"), and the direct weighted unsort of the PR #4 page
-// ("Measured standing").  Design for gfx950:
+// expert tiles with short fallback tiles over sorted indices, one private row
+// count per tile), the compiled gelu-product of SwiftLM issue #236 ("Still
+// missing") and the direct weighted unsort of the PR #4 page ("Measured
+// standing").  Design for gfx950:
 //
-//  * One workgroup = 4 waves = one tile x one block of output columns.  All
-//    products run on v_mfma_f32_16x16x32_bf16: a tile of at most 16 rows is
-//    one 16-row block (decode-sized tiles pay for 16 rows, not 32), a 32-row
-//    tile two.  Each output row sees the same MFMA sequence in every tile, so
-//    results are bitwise independent of how rows are grouped into tiles.
-//  * The activation tile is staged through LDS in chunks of 4 quantisation
-//    groups (256 columns), double-buffered; the gather through perm happens
-//    in the staging loads, so no gathered copy of x is ever written.
-//  * Weights go straight from HBM to registers (16-byte loads), are never
-//    staged, and are turned into MFMA operands in registers: each 4-bit code
-//    q becomes the bf16 value 128 + q exactly (codes_as_bf16).  The MFMA
-//    operand therefore carries q exactly; scale and bias are applied in fp32
-//    once per 64-column group:
-//        acc += s * P + (b - 128 s) * X,
-//    P = MFMA partial sum over the group, X = sum of the group's activations
-//    (computed while staging).  Rounding the dequantised weights to bf16
-//    instead would cost accuracy the fp32 path cannot afford.
-//  * The gate and up rows of one output column are loaded by the same wave,
-//    so the GeGLU product is formed in registers and h is written once.
-//  * The down kernel scales each row by its routing weight and writes it to
+//  * Every product runs on v_mfma_f32_16x16x32_bf16.  The weight operand is
+//    the 4-bit code itself, exactly (codes_as_bf16: 1 + q/16), decoded in
+//    registers straight from HBM loads; weights never touch LDS.  Per
+//    64-column group the fp32 accumulator takes 16 s * P (one FMA per output
+//    per group); the rest, sum_g (b - 16 s) X, is itself a small contraction
+//    over groups, run on MFMAs once per tile with both factors split into
+//    bf16 hi + lo.  Rounding dequantised weights to bf16 instead would cost
+//    the accuracy the fp32 path needs.
+//  * Activations come pre-ordered (x_perm, from the route launch) with their
+//    group sums, so nothing here reorders or sums activations on the fly.
+//  * Skinny path, tiles of <= 16 rows (decode): no LDS staging and no
+//    barrier in the K loop; each wave streams its own weight rows through a
+//    ring of kRing groups of loads in flight.
+//  * Wide path, tiles of 17..128 rows (prefill): the activation tile is
+//    staged in LDS, double-buffered; each wave owns 4 column blocks and all
+//    row blocks, so a decoded weight word feeds up to 8 row blocks and an LDS
+//    activation fragment feeds 4 MFMAs.
+//  * Both paths do the same arithmetic in the same order for every output
+//    element, so results do not depend on how rows are grouped into tiles
+//    (hence not on the order of the tokens).
+//  * Gate and up of an output column sit in the same lane: the GeGLU product
+//    is formed in registers and h is written once, already in MFMA operand
+//    order, with its group sums for the down matmul.
+//  * The down kernels scale each row by its routing weight and write it to
 //    its original (token, slot) position: the weighted unsort.
-//  * Workgroups past the device-side tile count exit at once, so the host
-//    never reads the tile count back.
+//  * Workgroups whose tile is past the device-side tile count, or belongs to
+//    the other path, exit at once: the host never reads the tile count back.
 #include "moe_internal.h"
 
 namespace moe {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kChunkGroups = 4;                 // groups per staged K chunk
-constexpr int kARows = 32;                      // staged activation rows
-constexpr int kAStride = kChunkGroups * kGroup / 2 + 4;  // u32 per LDS row (+16 B pad)
+constexpr int kRingC = 4;                  // skinny path: weight chunks in flight per wave
+constexpr int kMaxG = kMaxDim / kGroup;    // groups per row the LDS tables hold
 
 __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
 }
 
-// ---------------------------------------------------------------- staging
-// Activation rows of one tile, staged chunk by chunk.  Thread t handles row
-// t / 8 and, for each group i of the chunk, the 8 columns 8 * (t % 8) of it.
-// LDS row layout: per group 8 pieces of 8 bf16, each piece reordered by
-// permute8 to match the code order of codes_as_bf16.  Alongside, the fp32
-// sum of each (row, group) for the bias term.
-template <bool kF32>
-struct Stager {
-    // bf16 source: one 16-byte piece per group; fp32 source: two.
-    u32x4 v[kChunkGroups][kF32 ? 2 : 1];
+__device__ __forceinline__ int4 load_tile(const FfnArgs& a) {
+    if (static_cast<int>(blockIdx.x) >= min(a.num_tiles[0], a.max_tiles)) return int4{-1, 0, 0, 0};
+    return reinterpret_cast<const int4*>(a.tiles)[blockIdx.x];
+}
+
+// --------------------------------------------------------------- bias term
+// Operand of the bias contraction for one lane: 8 consecutive groups per MFMA
+// step (group 32 st + 8 q + j in element j), split into bf16 hi and lo.
+struct BiasOp {
+    u32x4 hi[kMaxBiasSteps];
+    u32x4 lo[kMaxBiasSteps];
 };
 
-template <bool kF32>
-__device__ __forceinline__ void stage_load(Stager<kF32>& st, const void* row_ptr, bool valid,
-                                           int g0, int G, int sub) {
+__device__ __forceinline__ void pack_split(const float (&v)[8], u32x4& hi, u32x4& lo) {
 #pragma unroll
-    for (int i = 0; i < kChunkGroups; ++i) {
-        const bool ok = valid && (g0 + i) < G;
-        const size_t col = static_cast<size_t>(g0 + i) * kGroup + 8 * sub;
-        if constexpr (kF32) {
-            const float* p = static_cast<const float*>(row_ptr) + col;
-            st.v[i][0] = ok ? *reinterpret_cast<const u32x4*>(p) : u32x4{0, 0, 0, 0};
-            st.v[i][1] = ok ? *reinterpret_cast<const u32x4*>(p + 4) : u32x4{0, 0, 0, 0};
-        } else {
-            const uint16_t* p = static_cast<const uint16_t*>(row_ptr) + col;
-            st.v[i][0] = ok ? *reinterpret_cast<const u32x4*>(p) : u32x4{0, 0, 0, 0};
+    for (int j = 0; j < 4; ++j) {
+        const uint16_t h0 = f32_to_bf16(v[2 * j]), h1 = f32_to_bf16(v[2 * j + 1]);
+        const uint16_t l0 = f32_to_bf16(v[2 * j] - bf16_to_f32(h0));
+        const uint16_t l1 = f32_to_bf16(v[2 * j + 1] - bf16_to_f32(h1));
+        hi[j] = static_cast<uint32_t>(h0) | (static_cast<uint32_t>(h1) << 16);
+        lo[j] = static_cast<uint32_t>(l0) | (static_cast<uint32_t>(l1) << 16);
+    }
+}
+
+// Row operand: the group sums X[g] of one activation row.  Loads use clamped
+// indices and a select, never a branch, so they stay in flight together.
+__device__ __forceinline__ void bias_from_sums(BiasOp& o, const float* X, int G, int q, int steps) {
+#pragma unroll
+    for (int st = 0; st < kMaxBiasSteps; ++st) {
+        if (st < steps) {
+            float v[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int g = 32 * st + 8 * q + j;
+                const float x = X[min(g, G - 1)];
+                v[j] = g < G ? x : 0.f;
+            }
+            pack_split(v, o.hi[st], o.lo[st]);
         }
     }
 }
 
-__device__ __forceinline__ float group_sum8(float s) {
-    s += __shfl_xor(s, 1);
-    s += __shfl_xor(s, 2);
-    s += __shfl_xor(s, 4);
-    return s;
-}
-
-// bf16 source -> one LDS array.
-__device__ __forceinline__ void stage_store(const Stager<false>& st, uint32_t* sA, uint32_t*,
-                                            float (*sX)[kARows], int r, int sub) {
+// Column operand: c[g] = b[g] - 16 s[g] of one weight row, from its LDS table
+// of (scale | bias << 16).
+__device__ __forceinline__ void bias_from_table(BiasOp& o, const uint32_t* sb, int G, int q,
+                                                int steps, bool active) {
 #pragma unroll
-    for (int i = 0; i < kChunkGroups; ++i) {
-        *reinterpret_cast<u32x4*>(sA + r * kAStride + 32 * i + 4 * sub) = permute8(st.v[i][0]);
-        const float s = group_sum8(sum8_bf16(st.v[i][0]));
-        if (sub == 0) sX[i][r] = s;
-    }
-}
-
-// fp32 source -> hi and lo bf16 LDS arrays, value = hi + lo to 16 bits.
-__device__ __forceinline__ void stage_store(const Stager<true>& st, uint32_t* sAh, uint32_t* sAl,
-                                            float (*sX)[kARows], int r, int sub) {
+    for (int st = 0; st < kMaxBiasSteps; ++st) {
+        if (st < steps) {
+            float v[8];
 #pragma unroll
-    for (int i = 0; i < kChunkGroups; ++i) {
-        u32x4 hi, lo;
-        float s = 0.f;
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            const float f0 = __uint_as_float(st.v[i][w >> 1][2 * (w & 1)]);
-            const float f1 = __uint_as_float(st.v[i][w >> 1][2 * (w & 1) + 1]);
-            const uint16_t h0 = f32_to_bf16(f0), h1 = f32_to_bf16(f1);
-            const float r0 = f0 - bf16_to_f32(h0), r1 = f1 - bf16_to_f32(h1);
-            const uint16_t l0 = f32_to_bf16(r0), l1 = f32_to_bf16(r1);
-            hi[w] = static_cast<uint32_t>(h0) | (static_cast<uint32_t>(h1) << 16);
-            lo[w] = static_cast<uint32_t>(l0) | (static_cast<uint32_t>(l1) << 16);
-            s += bf16_to_f32(h0) + bf16_to_f32(l0);
-            s += bf16_to_f32(h1) + bf16_to_f32(l1);
-        }
-        *reinterpret_cast<u32x4*>(sAh + r * kAStride + 32 * i + 4 * sub) = permute8(hi);
-        *reinterpret_cast<u32x4*>(sAl + r * kAStride + 32 * i + 4 * sub) = permute8(lo);
-        s = group_sum8(s);
-        if (sub == 0) sX[i][r] = s;
-    }
-}
-
-__device__ __forceinline__ u32x4 lds_piece(const uint32_t* sA, int row, int piece) {
-    return *reinterpret_cast<const u32x4*>(sA + row * kAStride + 4 * piece);
-}
-
-// ------------------------------------------------------------ gate | up
-// Grid: (max_tiles, I / 64).  Wave w owns h columns n0 + 16 w + [0, 16): its
-// 16 gate rows and the matching 16 up rows, as two 16-column MFMA blocks, so
-// gate and up of one output land in the same lane.  A tile of up to 16 rows
-// is one 16-row block, a 32-row tile two.  Every row goes through the same
-// sequence of 16x16x32 MFMAs whatever tile it sits in, so results do not
-// depend on the tile layout (and hence not on the order of the tokens).
-template <int RB, bool kF32H>
-__device__ __forceinline__ void gateup_tile(const FfnArgs& a, uint32_t (*sA)[kARows * kAStride],
-                                            float (*sX)[kChunkGroups][kARows], int e,
-                                            int row_begin, int rows, int n0) {
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int H = a.H, I = a.I, G = H / kGroup;
-    const int nchunks = (G + kChunkGroups - 1) / kChunkGroups;
-
-    // staging role
-    const int sr = tid >> 3, sub = tid & 7;
-    const bool svalid = sr < rows;
-    const uint16_t* xrow = a.x;
-    if (svalid) xrow = a.x + static_cast<size_t>(a.perm[row_begin + sr] / a.k) * H;
-
-    const int q = lane >> 4, lr = lane & 15;
-    const int hcol = n0 + 16 * wave + lr;
-    const size_t row_words = static_cast<size_t>(H) / 8;
-    const size_t grow = static_cast<size_t>(e) * 2 * I + hcol;   // gate row
-    const size_t urow = grow + I;                                // up row
-    const uint32_t* wg = a.w_gu + grow * row_words + 2 * q;
-    const uint32_t* wu = a.w_gu + urow * row_words + 2 * q;
-    const uint16_t* sg_p = a.s_gu + grow * G;
-    const uint16_t* bg_p = a.b_gu + grow * G;
-    const uint16_t* su_p = a.s_gu + urow * G;
-    const uint16_t* bu_p = a.b_gu + urow * G;
-
-    Stager<false> st;
-    stage_load<false>(st, xrow, svalid, 0, G, sub);
-    stage_store(st, sA[0], nullptr, sX[0], sr, sub);
-
-    f32x4 accg[RB] = {}, accu[RB] = {};
-    // per group: gate words [0,1], up words [2,3]; scale/bias of gate, up
-    u32x4 wcur[kChunkGroups], wnext[kChunkGroups];
-    uint32_t sbc[kChunkGroups][4], sbn[kChunkGroups][4];
-    auto load_w = [&](int c, u32x4 (&wv)[kChunkGroups], uint32_t (&sb)[kChunkGroups][4]) {
-#pragma unroll
-        for (int i = 0; i < kChunkGroups; ++i) {
-            const int g = c * kChunkGroups + i;
-            if (g < G) {
-                const u32x2 gw = *reinterpret_cast<const u32x2*>(wg + 8 * g);
-                const u32x2 uw = *reinterpret_cast<const u32x2*>(wu + 8 * g);
-                wv[i] = u32x4{gw[0], gw[1], uw[0], uw[1]};
-                sb[i][0] = sg_p[g];
-                sb[i][1] = bg_p[g];
-                sb[i][2] = su_p[g];
-                sb[i][3] = bu_p[g];
+            for (int j = 0; j < 8; ++j) {
+                const int g = 32 * st + 8 * q + j;
+                const uint32_t t = sb[min(g, G - 1)];
+                const float c = fmaf(-kCodeScale, bf16_to_f32(static_cast<uint16_t>(t & 0xFFFFu)),
+                                     bf16_to_f32(static_cast<uint16_t>(t >> 16)));
+                v[j] = (active && g < G) ? c : 0.f;
             }
-        }
-    };
-    load_w(0, wcur, sbc);
-    __syncthreads();
-
-    for (int c = 0; c < nchunks; ++c) {
-        const int buf = c & 1;
-        const bool more = c + 1 < nchunks;
-        if (more) {
-            stage_load<false>(st, xrow, svalid, (c + 1) * kChunkGroups, G, sub);
-            load_w(c + 1, wnext, sbn);
-        }
-        const uint32_t* A = sA[buf];
-#pragma unroll
-        for (int i = 0; i < kChunkGroups; ++i) {
-            if (c * kChunkGroups + i >= G) break;
-            f32x4 pg[RB] = {}, pu[RB] = {};
-#pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                const u32x4 bg = codes_as_bf16(wcur[i][s]);
-                const u32x4 bu = codes_as_bf16(wcur[i][2 + s]);
-#pragma unroll
-                for (int rb = 0; rb < RB; ++rb) {
-                    const u32x4 av = lds_piece(A, 16 * rb + lr, 8 * i + 2 * q + s);
-                    pg[rb] = mfma16(av, bg, pg[rb]);
-                    pu[rb] = mfma16(av, bu, pu[rb]);
-                }
-            }
-            const float sg = bf16_to_f32(sbc[i][0]), bgv = bf16_to_f32(sbc[i][1]);
-            const float su = bf16_to_f32(sbc[i][2]), buv = bf16_to_f32(sbc[i][3]);
-            const float cg = fmaf(-kCodeOffset, sg, bgv), cu = fmaf(-kCodeOffset, su, buv);
-#pragma unroll
-            for (int rb = 0; rb < RB; ++rb) {
-#pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    const float X = sX[buf][i][16 * rb + 4 * q + v];
-                    accg[rb][v] = fmaf(cg, X, fmaf(sg, pg[rb][v], accg[rb][v]));
-                    accu[rb][v] = fmaf(cu, X, fmaf(su, pu[rb][v], accu[rb][v]));
-                }
-            }
-        }
-        if (more) stage_store(st, sA[buf ^ 1], nullptr, sX[buf ^ 1], sr, sub);
-        __syncthreads();
-        if (more) {
-#pragma unroll
-            for (int i = 0; i < kChunkGroups; ++i) {
-                wcur[i] = wnext[i];
-#pragma unroll
-                for (int z = 0; z < 4; ++z) sbc[i][z] = sbn[i][z];
-            }
-        }
-    }
-
-    // GeGLU epilogue: h = gelu_tanh(gate) * up, written once.
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-            const int r = 16 * rb + 4 * q + v;
-            if (r < rows) {
-                const float hv = gelu_tanh(accg[rb][v]) * accu[rb][v];
-                const size_t o = static_cast<size_t>(row_begin + r) * I + hcol;
-                if constexpr (kF32H) static_cast<float*>(a.h)[o] = hv;
-                else static_cast<uint16_t*>(a.h)[o] = f32_to_bf16(hv);
-            }
+            pack_split(v, o.hi[st], o.lo[st]);
         }
     }
 }
 
+// sum_g c[n, g] X[m, g] for one 16x16 block: hi*hi + hi*lo + lo*hi per step.
+__device__ __forceinline__ f32x4 bias_mfma(const BiasOp& A, const BiasOp& B, int steps) {
+    f32x4 r = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int st = 0; st < kMaxBiasSteps; ++st) {
+        if (st < steps) {
+            r = mfma16(A.hi[st], B.hi[st], r);
+            r = mfma16(A.hi[st], B.lo[st], r);
+            r = mfma16(A.lo[st], B.hi[st], r);
+        }
+    }
+    return r;
+}
+
+// One 64-column group of one 16x16 block: two MFMA steps, then the scale.
+// Every path goes through exactly this sequence.
+__device__ __forceinline__ f32x4 group_step(f32x4 acc, u32x4 a0, u32x4 a1, u32x4 b0, u32x4 b1,
+                                            float s16) {
+    f32x4 p = {0.f, 0.f, 0.f, 0.f};
+    p = mfma16(a0, b0, p);
+    p = mfma16(a1, b1, p);
+#pragma unroll
+    for (int v = 0; v < 4; ++v) acc[v] = fmaf(s16, p[v], acc[v]);
+    return acc;
+}
+// Same with the activation split into hi + lo parts (fp32 h, down matmul).
+__device__ __forceinline__ f32x4 group_step2(f32x4 acc, u32x4 a0h, u32x4 a0l, u32x4 a1h,
+                                             u32x4 a1l, u32x4 b0, u32x4 b1, float s16) {
+    f32x4 p = {0.f, 0.f, 0.f, 0.f};
+    p = mfma16(a0h, b0, p);
+    p = mfma16(a0l, b0, p);
+    p = mfma16(a1h, b1, p);
+    p = mfma16(a1l, b1, p);
+#pragma unroll
+    for (int v = 0; v < 4; ++v) acc[v] = fmaf(s16, p[v], acc[v]);
+    return acc;
+}
+
+// 16 s from a table entry (scale | bias << 16).
+__device__ __forceinline__ float scale16(uint32_t t) {
+    return kCodeScale * bf16_to_f32(static_cast<uint16_t>(t & 0xFFFFu));
+}
+
+// Sum over the 16 lanes of a 16-lane row (the same value in every lane).
+__device__ __forceinline__ float sum16(float v) {
+    v += __shfl_xor(v, 1);
+    v += __shfl_xor(v, 2);
+    v += __shfl_xor(v, 4);
+    v += __shfl_xor(v, 8);
+    return v;
+}
+
+// h for (sorted row srow, column hcol), stored once in operand order; returns
+// the value the down matmul will see (bf16 h, or hi + lo), 0 if not valid.
 template <bool kF32H>
-__global__ __launch_bounds__(kThreads) void moe_gateup_geglu(FfnArgs a) {
-    __shared__ uint32_t sA[2][kARows * kAStride];
-    __shared__ float sX[2][kChunkGroups][kARows];
-    const int tile_idx = blockIdx.x;
-    if (tile_idx >= min(a.num_tiles[0], a.max_tiles)) return;
-    const int4 tile = reinterpret_cast<const int4*>(a.tiles)[tile_idx];
-    const int n0 = blockIdx.y * 64;
-    if (tile.z <= 16)
-        gateup_tile<1, kF32H>(a, sA, sX, tile.x, tile.y, tile.z, n0);
-    else
-        gateup_tile<2, kF32H>(a, sA, sX, tile.x, tile.y, tile.z, n0);
+__device__ __forceinline__ float store_h(const FfnArgs& a, size_t A, int srow, int hcol, float g,
+                                         float u, bool valid) {
+    const float hv = gelu_tanh(g) * u;
+    const size_t pos = static_cast<size_t>(srow) * a.I + (hcol & ~7) + permuted_pos(hcol & 7);
+    uint16_t* h = static_cast<uint16_t*>(a.h);
+    const uint16_t hi = f32_to_bf16(hv);
+    float seen = bf16_to_f32(hi);
+    if constexpr (kF32H) {
+        const uint16_t lo = f32_to_bf16(hv - seen);
+        seen += bf16_to_f32(lo);
+        if (valid) h[A * a.I + pos] = lo;
+    }
+    if (valid) h[pos] = hi;
+    return valid ? seen : 0.f;
 }
 
-// ------------------------------------------------------------------ down
-// Grid: (max_tiles, ceil(H / 128)).  Wave w owns output columns
-// n0 + 32 w + [0, 32) as two 16-column MFMA blocks (skipped past H); one or
-// two 16-row blocks as above.  With an fp32 h the activation operand is split
-// into bf16 hi + lo and both halves go through the MFMAs.
-template <int RB, bool kF32H>
-__device__ __forceinline__ void down_tile(const FfnArgs& a,
-                                          uint32_t (*sA)[kF32H ? 2 : 1][kARows * kAStride],
-                                          float (*sX)[kChunkGroups][kARows], const int32_t* sDst,
-                                          const float* sW, int e, int row_begin, int rows,
-                                          int n0) {
-    constexpr int kParts = kF32H ? 2 : 1;
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int H = a.H, I = a.I, G = I / kGroup;
-    const int nchunks = (G + kChunkGroups - 1) / kChunkGroups;
-    const int ncol0 = n0 + 32 * wave;
-    const bool wave_active = ncol0 < H;
+// X_h[row][group] = ((b0 + b1) + b2) + b3 over the four 16-column blocks of a
+// 64-column group of h, each block sum taken by sum16.
+__device__ __forceinline__ float hsum_of(const float* b0, const float* b1, const float* b2,
+                                         const float* b3, int r) {
+    return ((b0[r] + b1[r]) + b2[r]) + b3[r];
+}
 
-    const int sr = tid >> 3, sub = tid & 7;
-    const bool svalid = sr < rows;
-    const size_t elt = kF32H ? 4 : 2;
-    const char* hbase = static_cast<const char*>(a.h);
-    const void* hrow = hbase + static_cast<size_t>(row_begin + (svalid ? sr : 0)) * I * elt;
+// ================================================== weights through LDS
+// The MFMA operand wants lane (lr, q) to hold words 2q, 2q+1 of weight row lr
+// for each group, so lanes next to each other would read rows 1.4 KB apart:
+// every 4-lane quad would touch 4 cache lines and the vector L1 tag lookups,
+// not HBM, would set the pace.  Instead each lane loads 16 contiguous bytes
+// (4 lanes per row: a quad reads one line) and the chunk is turned into
+// operand order through a small LDS buffer private to the wave (no barrier).
+//
+// A wave owns NCB blocks of 16 weight rows; a chunk is 2 groups = 64 bytes per
+// row.  LDS entry (row, q, g) = words 2q, 2q+1 of group g of the chunk, at
+// row * 16 + 4 * (q ^ ((row >> 2) & 3)) + 2 g  (u32 units); the XOR keeps the
+// 16 rows of a fragment read on distinct banks.
+template <int NCB>
+struct WaveW {
+    uint32_t* lds;            // NCB * 16 rows x 16 u32
+    const uint32_t* src[NCB]; // this lane's load row in block cb
+    int rw;                   // row length, u32
 
-    const int q = lane >> 4, lr = lane & 15;
-    const int c0 = ncol0 + lr, c1 = c0 + 16;
-    const size_t row_words = static_cast<size_t>(I) / 8;
-    const size_t r0 = static_cast<size_t>(e) * H + (wave_active ? c0 : 0);
-    const size_t r1 = static_cast<size_t>(e) * H + (wave_active ? c1 : 0);
-    const uint32_t* w0 = a.w_d + r0 * row_words + 2 * q;
-    const uint32_t* w1 = a.w_d + r1 * row_words + 2 * q;
-    const uint16_t* s0 = a.s_d + r0 * G;
-    const uint16_t* b0 = a.b_d + r0 * G;
-    const uint16_t* s1 = a.s_d + r1 * G;
-    const uint16_t* b1 = a.b_d + r1 * G;
-
-    Stager<kF32H> st;
-    stage_load<kF32H>(st, hrow, svalid, 0, G, sub);
-    stage_store(st, sA[0][0], sA[0][kParts - 1], sX[0], sr, sub);
-
-    f32x4 acc0[RB] = {}, acc1[RB] = {};
-    u32x4 wcur[kChunkGroups], wnext[kChunkGroups];
-    uint32_t sbc[kChunkGroups][4], sbn[kChunkGroups][4];
-    auto load_w = [&](int c, u32x4 (&wv)[kChunkGroups], uint32_t (&sb)[kChunkGroups][4]) {
+    __device__ __forceinline__ void init(uint32_t* l, const uint32_t* const (&blk)[NCB],
+                                         int row_words) {
+        const int lane = threadIdx.x & 63;
+        lds = l;
+        rw = row_words;
 #pragma unroll
-        for (int i = 0; i < kChunkGroups; ++i) {
-            const int g = c * kChunkGroups + i;
-            if (g < G && wave_active) {
-                const u32x2 x0 = *reinterpret_cast<const u32x2*>(w0 + 8 * g);
-                const u32x2 x1 = *reinterpret_cast<const u32x2*>(w1 + 8 * g);
-                wv[i] = u32x4{x0[0], x0[1], x1[0], x1[1]};
-                sb[i][0] = s0[g];
-                sb[i][1] = b0[g];
-                sb[i][2] = s1[g];
-                sb[i][3] = b1[g];
-            }
+        for (int cb = 0; cb < NCB; ++cb) src[cb] = blk[cb] + (lane >> 2) * row_words;
+    }
+    // Chunk c; the last chunk of an odd group count reads a repeated piece
+    // instead of running past the row.
+    __device__ __forceinline__ void load(int c, u32x4 (&v)[NCB]) const {
+        const int off = min(16 * c + 4 * (threadIdx.x & 3), rw - 4);
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) v[cb] = *reinterpret_cast<const u32x4*>(src[cb] + off);
+    }
+    __device__ __forceinline__ void put(const u32x4 (&v)[NCB]) const {
+        const int lane = threadIdx.x & 63;
+        const int j = lane & 3, g = j >> 1, qa = 2 * (j & 1), sw = (lane >> 4) & 3;
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) {
+            uint32_t* row = lds + (16 * cb + (lane >> 2)) * 16;
+            *reinterpret_cast<u32x2*>(row + 4 * (qa ^ sw) + 2 * g) = u32x2{v[cb][0], v[cb][1]};
+            *reinterpret_cast<u32x2*>(row + 4 * ((qa + 1) ^ sw) + 2 * g) = u32x2{v[cb][2], v[cb][3]};
+        }
+    }
+    // [g0 word 2q, g0 word 2q+1, g1 word 2q, g1 word 2q+1] of row 16 cb + lr
+    __device__ __forceinline__ u32x4 get(int cb, int lr, int q) const {
+        return *reinterpret_cast<const u32x4*>(lds + (16 * cb + lr) * 16 + 4 * (q ^ ((lr >> 2) & 3)));
+    }
+};
+
+// (scale | bias << 16) of NCB blocks of 16 weight rows into a wave's table,
+// read in row order (coalesced).
+template <int NCB>
+__device__ __forceinline__ void load_sb(uint32_t (*tab)[kMaxG], const uint16_t* s, const uint16_t* b,
+                                        const size_t (&row0)[NCB], int G) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
+        const uint16_t* sp = s + row0[cb] * G;
+        const uint16_t* bp = b + row0[cb] * G;
+        for (int idx = lane; idx < 16 * G; idx += 64) {
+            const int r = idx / G, g = idx - r * G;
+            tab[16 * cb + r][g] = static_cast<uint32_t>(sp[idx]) | (static_cast<uint32_t>(bp[idx]) << 16);
+        }
+    }
+}
+
+// =========================================================== skinny paths
+struct SkinnySmem {
+    uint32_t w[4][32 * 16];     // per-wave weight transposition buffer
+    uint32_t sb[4][32][kMaxG];  // per-wave (scale | bias << 16) of its 32 weight rows
+    float blk[4][kBmSmall];     // 16-column block sums of h
+};
+
+// gate|up, tiles of <= 16 rows.  Grid (max_tiles, I / 64).  Wave w owns h
+// columns n0 + 16 w + [0, 16), i.e. block w of 64-column group blockIdx.y,
+// as two 16-row weight blocks: gate and up.
+template <bool kF32H>
+__global__ __launch_bounds__(kThreads) void moe_gateup_skinny(FfnArgs a) {
+    __shared__ SkinnySmem sm;
+    const int4 tile = load_tile(a);
+    if (tile.x < 0 || tile.z > kBmSmall) return;
+    const int e = tile.x, row_begin = tile.y, rows = tile.z;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, q = lane >> 4, lr = lane & 15;
+    const int H = a.H, I = a.I, G = H / kGroup;
+    const size_t A = static_cast<size_t>(a.T) * a.k;
+    const int hcol0 = blockIdx.y * 64 + 16 * wave, hcol = hcol0 + lr;
+
+    const size_t row0[2] = {static_cast<size_t>(e) * 2 * I + hcol0,
+                            static_cast<size_t>(e) * 2 * I + I + hcol0};
+    const uint32_t* blk[2] = {a.w_gu + row0[0] * (H / 8), a.w_gu + row0[1] * (H / 8)};
+    WaveW<2> ww;
+    ww.init(sm.w[wave], blk, H / 8);
+    u32x4 rv[kRingC][2];
+#pragma unroll
+    for (int i = 0; i < kRingC; ++i) ww.load(i, rv[i]);
+
+    // padding lanes (row >= rows) read row 0: their outputs are never stored
+    const int tok = a.perm[row_begin + min(lr, rows - 1)] / a.k;
+    const uint32_t* xa = reinterpret_cast<const uint32_t*>(a.xp) + static_cast<size_t>(tok) * (H / 2);
+    u32x4 ra[2][4];
+    auto load_a = [&](int c, int buf) {
+#pragma unroll
+        for (int gi = 0; gi < 2; ++gi) {
+            const int g = min(2 * c + gi, G - 1);
+#pragma unroll
+            for (int s = 0; s < 2; ++s)
+                ra[buf][2 * gi + s] = *reinterpret_cast<const u32x4*>(xa + 4 * (8 * g + 2 * q + s));
         }
     };
-    load_w(0, wcur, sbc);
-    __syncthreads();
+    load_a(0, 0);
 
-    for (int c = 0; c < nchunks; ++c) {
-        const int buf = c & 1;
-        const bool more = c + 1 < nchunks;
-        if (more) {
-            stage_load<kF32H>(st, hrow, svalid, (c + 1) * kChunkGroups, G, sub);
-            load_w(c + 1, wnext, sbn);
+    load_sb<2>(sm.sb[wave], a.s_gu, a.b_gu, row0, G);
+    __builtin_amdgcn_wave_barrier();
+
+    // the bias term initialises the accumulators
+    const int steps = (G + 31) / 32;
+    f32x4 accg, accu;
+    {
+        BiasOp X, C;
+        bias_from_sums(X, a.xs + static_cast<size_t>(tok) * G, G, q, steps);
+        bias_from_table(C, sm.sb[wave][lr], G, q, steps, true);
+        accg = bias_mfma(X, C, steps);
+        bias_from_table(C, sm.sb[wave][16 + lr], G, q, steps, true);
+        accu = bias_mfma(X, C, steps);
+    }
+
+    const int nch = (G + 1) / 2;
+    auto compute = [&](int slot, int abuf, int c) {
+        ww.put(rv[slot]);
+        __builtin_amdgcn_wave_barrier();
+        const u32x4 wgv = ww.get(0, lr, q), wuv = ww.get(1, lr, q);
+#pragma unroll
+        for (int gi = 0; gi < 2; ++gi) {
+            const int g = 2 * c + gi;
+            if (g < G) {
+                const float sg = scale16(sm.sb[wave][lr][g]), su = scale16(sm.sb[wave][16 + lr][g]);
+                accg = group_step(accg, ra[abuf][2 * gi], ra[abuf][2 * gi + 1],
+                                  codes_as_bf16(wgv[2 * gi]), codes_as_bf16(wgv[2 * gi + 1]), sg);
+                accu = group_step(accu, ra[abuf][2 * gi], ra[abuf][2 * gi + 1],
+                                  codes_as_bf16(wuv[2 * gi]), codes_as_bf16(wuv[2 * gi + 1]), su);
+            }
         }
-        if (wave_active) {
+        __builtin_amdgcn_wave_barrier();
+    };
+    int c0 = 0;
+    for (; c0 + kRingC <= nch; c0 += kRingC) {
 #pragma unroll
-            for (int i = 0; i < kChunkGroups; ++i) {
-                if (c * kChunkGroups + i >= G) break;
-                f32x4 p0[RB] = {}, p1[RB] = {};
+        for (int i = 0; i < kRingC; ++i) {
+            load_a(c0 + i + 1, (i + 1) & 1);
+            compute(i, i & 1, c0 + i);
+            ww.load(c0 + i + kRingC, rv[i]);
+        }
+    }
 #pragma unroll
-                for (int part = 0; part < kParts; ++part) {
-                    const uint32_t* A = sA[buf][part];
+    for (int i = 0; i < kRingC; ++i) {
+        if (c0 + i < nch) {
+            load_a(c0 + i + 1, (i + 1) & 1);
+            compute(i, i & 1, c0 + i);
+        }
+    }
+
+    // GeGLU, h once, and this wave's 16-column block sums of h per row
 #pragma unroll
-                    for (int s = 0; s < 2; ++s) {
-                        const u32x4 bw0 = codes_as_bf16(wcur[i][s]);
-                        const u32x4 bw1 = codes_as_bf16(wcur[i][2 + s]);
+    for (int v = 0; v < 4; ++v) {
+        const int r = 4 * q + v;
+        const float seen = store_h<kF32H>(a, A, row_begin + r, hcol, accg[v], accu[v], r < rows);
+        const float s = sum16(seen);
+        if (lr == 0) sm.blk[wave][r] = s;
+    }
+    __syncthreads();
+    if (tid < rows)
+        a.hs[static_cast<size_t>(row_begin + tid) * (I / kGroup) + blockIdx.y] =
+            hsum_of(sm.blk[0], sm.blk[1], sm.blk[2], sm.blk[3], tid);
+}
+
+// down, tiles of <= 16 rows.  Grid (max_tiles, ceil(H / 128)).  Wave w owns
+// output columns n0 + 32 w + [0, 32): two 16-row weight blocks.
+template <bool kF32H>
+__global__ __launch_bounds__(kThreads) void moe_down_skinny(FfnArgs a) {
+    constexpr int P = kF32H ? 2 : 1;
+    __shared__ SkinnySmem sm;
+    const int4 tile = load_tile(a);
+    if (tile.x < 0 || tile.z > kBmSmall) return;
+    const int e = tile.x, row_begin = tile.y, rows = tile.z;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, q = lane >> 4, lr = lane & 15;
+    const int H = a.H, I = a.I, G = I / kGroup;
+    const size_t A = static_cast<size_t>(a.T) * a.k;
+    const int cbase = blockIdx.y * 128 + 32 * wave;
+    if (cbase >= H) return;  // whole wave past the last column; no barrier follows
+    const int c0 = cbase + lr, c1 = c0 + 16;
+
+    const size_t row0[2] = {static_cast<size_t>(e) * H + cbase, static_cast<size_t>(e) * H + cbase + 16};
+    const uint32_t* blk[2] = {a.w_d + row0[0] * (I / 8), a.w_d + row0[1] * (I / 8)};
+    WaveW<2> ww;
+    ww.init(sm.w[wave], blk, I / 8);
+    u32x4 rv[kRingC][2];
 #pragma unroll
-                        for (int rb = 0; rb < RB; ++rb) {
-                            const u32x4 av = lds_piece(A, 16 * rb + lr, 8 * i + 2 * q + s);
-                            p0[rb] = mfma16(av, bw0, p0[rb]);
-                            p1[rb] = mfma16(av, bw1, p1[rb]);
+    for (int i = 0; i < kRingC; ++i) ww.load(i, rv[i]);
+
+    // padding lanes (row >= rows) read row 0: their outputs are never stored
+    const int arow = row_begin + min(lr, rows - 1);
+    const uint32_t* ha = reinterpret_cast<const uint32_t*>(a.h) + static_cast<size_t>(arow) * (I / 2);
+    const size_t part = A * (I / 2);  // offset of the lo half, u32
+    u32x4 ra[2][4][P];
+    auto load_a = [&](int c, int buf) {
+#pragma unroll
+        for (int gi = 0; gi < 2; ++gi) {
+            const int g = min(2 * c + gi, G - 1);
+#pragma unroll
+            for (int s = 0; s < 2; ++s)
+#pragma unroll
+                for (int pp = 0; pp < P; ++pp)
+                    ra[buf][2 * gi + s][pp] =
+                        *reinterpret_cast<const u32x4*>(ha + pp * part + 4 * (8 * g + 2 * q + s));
+        }
+    };
+    load_a(0, 0);
+
+    load_sb<2>(sm.sb[wave], a.s_d, a.b_d, row0, G);
+    __builtin_amdgcn_wave_barrier();
+
+    const int steps = (G + 31) / 32;
+    f32x4 acc0, acc1;
+    {
+        BiasOp X, C;
+        bias_from_sums(X, a.hs + static_cast<size_t>(arow) * G, G, q, steps);
+        bias_from_table(C, sm.sb[wave][lr], G, q, steps, true);
+        acc0 = bias_mfma(X, C, steps);
+        bias_from_table(C, sm.sb[wave][16 + lr], G, q, steps, true);
+        acc1 = bias_mfma(X, C, steps);
+    }
+
+    const int nch = (G + 1) / 2;
+    auto compute = [&](int slot, int abuf, int c) {
+        ww.put(rv[slot]);
+        __builtin_amdgcn_wave_barrier();
+        const u32x4 w0v = ww.get(0, lr, q), w1v = ww.get(1, lr, q);
+#pragma unroll
+        for (int gi = 0; gi < 2; ++gi) {
+            const int g = 2 * c + gi;
+            if (g < G) {
+                const float s0 = scale16(sm.sb[wave][lr][g]), s1 = scale16(sm.sb[wave][16 + lr][g]);
+                const u32x4 b00 = codes_as_bf16(w0v[2 * gi]), b01 = codes_as_bf16(w0v[2 * gi + 1]);
+                const u32x4 b10 = codes_as_bf16(w1v[2 * gi]), b11 = codes_as_bf16(w1v[2 * gi + 1]);
+                const u32x4(&x)[4][P] = ra[abuf];
+                if constexpr (kF32H) {
+                    acc0 = group_step2(acc0, x[2 * gi][0], x[2 * gi][P - 1], x[2 * gi + 1][0],
+                                       x[2 * gi + 1][P - 1], b00, b01, s0);
+                    acc1 = group_step2(acc1, x[2 * gi][0], x[2 * gi][P - 1], x[2 * gi + 1][0],
+                                       x[2 * gi + 1][P - 1], b10, b11, s1);
+                } else {
+                    acc0 = group_step(acc0, x[2 * gi][0], x[2 * gi + 1][0], b00, b01, s0);
+                    acc1 = group_step(acc1, x[2 * gi][0], x[2 * gi + 1][0], b10, b11, s1);
+                }
+            }
+        }
+        __builtin_amdgcn_wave_barrier();
+    };
+    int cc = 0;
+    for (; cc + kRingC <= nch; cc += kRingC) {
+#pragma unroll
+        for (int i = 0; i < kRingC; ++i) {
+            load_a(cc + i + 1, (i + 1) & 1);
+            compute(i, i & 1, cc + i);
+            ww.load(cc + i + kRingC, rv[i]);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < kRingC; ++i) {
+        if (cc + i < nch) {
+            load_a(cc + i + 1, (i + 1) & 1);
+            compute(i, i & 1, cc + i);
+        }
+    }
+
+    // weighted unsort
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+        const int r = 4 * q + v;
+        if (r < rows) {
+            const int32_t dst = a.perm[row_begin + r];
+            const float wt = a.topk_w[dst];
+            float* yrow = a.y + static_cast<size_t>(dst) * H;
+            yrow[c0] = wt * acc0[v];
+            yrow[c1] = wt * acc1[v];
+        }
+    }
+}
+
+// ============================================================= wide paths
+// Tiles of 17..128 rows; RB = 16-row blocks, rows / 16 rounded up to even.
+// The activation tile (RB*16 rows) is staged in LDS in chunks of 2 groups
+// (NBUF buffers); an LDS row is 16 pieces of 16 bytes plus 16 bytes of
+// padding, so the 16 rows of a fragment read fall on distinct banks.  Each
+// wave owns 4 blocks of 16 weight rows, moved through its own LDS buffer.
+constexpr int kAStride = 2 * 32 + 4;  // u32 per staged activation row
+
+template <int RB, int P, int NBUF>
+struct WideSmem {
+    uint32_t a[NBUF][P][RB * 16 * kAStride];
+    uint32_t w[4][64 * 16];
+    uint32_t sb[4][64][kMaxG];
+    float blk[2][4][kBmBig];  // [64-column group][16-column block][row]
+};
+// the largest layout any wide kernel uses
+constexpr size_t kWideSmemBytes = sizeof(WideSmem<8, 1, 2>) > sizeof(WideSmem<8, 2, 1>)
+                                      ? sizeof(WideSmem<8, 1, 2>)
+                                      : sizeof(WideSmem<8, 2, 1>);
+
+// Thread t copies piece t % 16 of rows t / 16 + 16 i.  Rows past the tile
+// read a real row and groups past G the last group: those values are never
+// used, and the loads need no branch.
+template <int RB, int P>
+struct Stager {
+    static constexpr int kPasses = RB;
+    u32x4 v[kPasses][P];
+
+    __device__ __forceinline__ void load(const uint32_t* const (&src)[kPasses], size_t part, int c,
+                                         int G) {
+        const int pc = threadIdx.x & 15;
+        const int g = min(2 * c + (pc >> 3), G - 1);
+        const int piece = 8 * g + (pc & 7);
+#pragma unroll
+        for (int i = 0; i < kPasses; ++i)
+#pragma unroll
+            for (int pp = 0; pp < P; ++pp)
+                v[i][pp] = *reinterpret_cast<const u32x4*>(src[i] + pp * part + 4 * piece);
+    }
+    template <int NBUF>
+    __device__ __forceinline__ void store(WideSmem<RB, P, NBUF>& sm, int buf) const {
+        const int pc = threadIdx.x & 15, r0 = threadIdx.x >> 4;
+#pragma unroll
+        for (int i = 0; i < kPasses; ++i)
+#pragma unroll
+            for (int pp = 0; pp < P; ++pp)
+                *reinterpret_cast<u32x4*>(&sm.a[buf][pp][(r0 + 16 * i) * kAStride + 4 * pc]) = v[i][pp];
+    }
+};
+
+template <int RB, int P, int NBUF>
+__device__ __forceinline__ u32x4 lds_frag(const WideSmem<RB, P, NBUF>& sm, int buf, int pp, int row,
+                                          int piece) {
+    return *reinterpret_cast<const u32x4*>(&sm.a[buf][pp][row * kAStride + 4 * piece]);
+}
+
+// Shared K loop of the wide paths: acc[rb][cb] over all groups for the four
+// 16-row weight blocks blk[cb] of this wave (row length K), activations staged
+// from src (P parts, `part` apart).
+template <int RB, int P, int NBUF>
+__device__ __forceinline__ void wide_kloop(WideSmem<RB, P, NBUF>& sm, Stager<RB, P>& st,
+                                           const uint32_t* const (&src)[RB], size_t part,
+                                           const uint32_t* const (&blk)[4], int K, bool active,
+                                           f32x4 (&acc)[RB][4]) {
+    constexpr int CB = 4;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, q = lane >> 4, lr = lane & 15;
+    const int G = K / kGroup;
+    const int nch = (G + 1) / 2;
+    WaveW<CB> ww;
+    ww.init(sm.w[wave], blk, K / 8);
+    u32x4 wcur[CB], wnext[CB];
+    ww.load(0, wcur);
+    __syncthreads();  // stage 0 and the scale tables are in place
+
+    for (int c = 0; c < nch; ++c) {
+        const int buf = NBUF == 2 ? (c & 1) : 0;
+        const int cn = min(c + 1, nch - 1);
+        st.load(src, part, cn, G);
+        ww.load(cn, wnext);
+        ww.put(wcur);
+        __builtin_amdgcn_wave_barrier();
+        u32x4 wq[CB];
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) wq[cb] = ww.get(cb, lr, q);
+        if (active) {
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int g = 2 * c + i;
+                if (g < G) {
+                    u32x4 b0[CB], b1[CB];
+                    float s16[CB];
+#pragma unroll
+                    for (int cb = 0; cb < CB; ++cb) {
+                        b0[cb] = codes_as_bf16(wq[cb][2 * i]);
+                        b1[cb] = codes_as_bf16(wq[cb][2 * i + 1]);
+                        s16[cb] = scale16(sm.sb[wave][16 * cb + lr][g]);
+                    }
+#pragma unroll
+                    for (int rb = 0; rb < RB; ++rb) {
+                        const int row = 16 * rb + lr;
+                        const u32x4 a0 = lds_frag(sm, buf, 0, row, 8 * i + 2 * q);
+                        const u32x4 a1 = lds_frag(sm, buf, 0, row, 8 * i + 2 * q + 1);
+                        if constexpr (P == 2) {
+                            const u32x4 a0l = lds_frag(sm, buf, 1, row, 8 * i + 2 * q);
+                            const u32x4 a1l = lds_frag(sm, buf, 1, row, 8 * i + 2 * q + 1);
+#pragma unroll
+                            for (int cb = 0; cb < CB; ++cb)
+                                acc[rb][cb] = group_step2(acc[rb][cb], a0, a0l, a1, a1l, b0[cb],
+                                                          b1[cb], s16[cb]);
+                        } else {
+#pragma unroll
+                            for (int cb = 0; cb < CB; ++cb)
+                                acc[rb][cb] = group_step(acc[rb][cb], a0, a1, b0[cb], b1[cb], s16[cb]);
                         }
                     }
                 }
-                const float sa = bf16_to_f32(sbc[i][0]), ba = bf16_to_f32(sbc[i][1]);
-                const float sb = bf16_to_f32(sbc[i][2]), bb = bf16_to_f32(sbc[i][3]);
-                const float ca = fmaf(-kCodeOffset, sa, ba), cb = fmaf(-kCodeOffset, sb, bb);
-#pragma unroll
-                for (int rb = 0; rb < RB; ++rb) {
-#pragma unroll
-                    for (int v = 0; v < 4; ++v) {
-                        const float X = sX[buf][i][16 * rb + 4 * q + v];
-                        acc0[rb][v] = fmaf(ca, X, fmaf(sa, p0[rb][v], acc0[rb][v]));
-                        acc1[rb][v] = fmaf(cb, X, fmaf(sb, p1[rb][v], acc1[rb][v]));
-                    }
-                }
             }
         }
-        if (more) stage_store(st, sA[buf ^ 1][0], sA[buf ^ 1][kParts - 1], sX[buf ^ 1], sr, sub);
-        __syncthreads();
-        if (more) {
+        __builtin_amdgcn_wave_barrier();
+        if constexpr (NBUF == 2) {
+            if (c + 1 < nch) st.store(sm, buf ^ 1);
+            __syncthreads();
+        } else {
+            __syncthreads();
+            if (c + 1 < nch) st.store(sm, 0);
+            __syncthreads();
+        }
 #pragma unroll
-            for (int i = 0; i < kChunkGroups; ++i) {
-                wcur[i] = wnext[i];
+        for (int cb = 0; cb < CB; ++cb) wcur[cb] = wnext[cb];
+    }
+}
+
+// gate|up wide.  Grid (max_tiles, ceil(I / 128)).  Wave w owns h columns
+// n0 + 32 w + [0, 32): weight blocks 0/1 = gate columns +0/+16, blocks 2/3 =
+// the matching up columns.  Waves {0,1} cover 64-column group 2*by of h,
+// waves {2,3} group 2*by + 1.
+template <int RB, bool kF32H>
+__device__ __forceinline__ void gateup_wide(const FfnArgs& a, void* smem, int e, int row_begin,
+                                            int rows) {
+    constexpr int P = 1, NBUF = 2, CB = 4;
+    auto& sm = *static_cast<WideSmem<RB, P, NBUF>*>(smem);
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, q = lane >> 4, lr = lane & 15;
+    const int H = a.H, I = a.I, G = H / kGroup;
+    const size_t A = static_cast<size_t>(a.T) * a.k;
+    const int n0 = blockIdx.y * 128;
+    const bool active = n0 + 32 * wave < I;
+    const int hbase = active ? n0 + 32 * wave : 0;
+
+    const uint32_t* src[RB];
 #pragma unroll
-                for (int z = 0; z < 4; ++z) sbc[i][z] = sbn[i][z];
+    for (int i = 0; i < RB; ++i) {
+        const int r = (tid >> 4) + 16 * i;
+        src[i] = reinterpret_cast<const uint32_t*>(a.xp) +
+                 static_cast<size_t>(a.perm[row_begin + min(r, rows - 1)] / a.k) * (H / 2);
+    }
+    Stager<RB, P> st;
+    st.load(src, 0, 0, G);
+
+    size_t row0[CB];
+    const uint32_t* blk[CB];
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+        row0[cb] = static_cast<size_t>(e) * 2 * I + hbase + 16 * (cb & 1) + (cb >> 1) * I;
+        blk[cb] = a.w_gu + row0[cb] * (H / 8);
+    }
+    load_sb<CB>(sm.sb[wave], a.s_gu, a.b_gu, row0, G);
+    __builtin_amdgcn_wave_barrier();
+
+    // the bias term initialises the accumulators
+    const int steps = (G + 31) / 32;
+    f32x4 acc[RB][CB];
+    {
+        BiasOp C[CB];
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb)
+            bias_from_table(C[cb], sm.sb[wave][16 * cb + lr], G, q, steps, active);
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+            const int r = 16 * rb + lr;
+            BiasOp X;
+            bias_from_sums(X, a.xs + static_cast<size_t>(a.perm[row_begin + min(r, rows - 1)] / a.k) * G,
+                           G, q, steps);
+#pragma unroll
+            for (int cb = 0; cb < CB; ++cb) acc[rb][cb] = bias_mfma(X, C[cb], steps);
+        }
+    }
+    st.store(sm, 0);
+
+    wide_kloop<RB, P, NBUF>(sm, st, src, 0, blk, H, active, acc);
+
+    // GeGLU epilogue and the 16-column block sums of h
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            const int hcol = hbase + 16 * half + lr;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int r = 16 * rb + 4 * q + v;
+                const float seen = store_h<kF32H>(a, A, row_begin + r, hcol, acc[rb][half][v],
+                                                  acc[rb][2 + half][v], active && r < rows);
+                const float s = sum16(seen);
+                if (lr == 0) sm.blk[wave >> 1][2 * (wave & 1) + half][r] = s;
             }
         }
     }
+    __syncthreads();
+    const int GI = I / kGroup;
+    for (int idx = tid; idx < 2 * rows; idx += kThreads) {
+        const int j = idx / rows, r = idx - j * rows, grp = 2 * blockIdx.y + j;
+        if (grp < GI)
+            a.hs[static_cast<size_t>(row_begin + r) * GI + grp] =
+                hsum_of(sm.blk[j][0], sm.blk[j][1], sm.blk[j][2], sm.blk[j][3], r);
+    }
+}
 
-    // weighted unsort: row s goes back to assignment perm[s], times its weight
-    if (!wave_active) return;
+// down wide.  Grid (max_tiles, ceil(H / 256)).  Wave w owns output columns
+// n0 + 64 w + [0, 64): four 16-row weight blocks.
+template <int RB, bool kF32H>
+__device__ __forceinline__ void down_wide(const FfnArgs& a, void* smem, int e, int row_begin,
+                                          int rows) {
+    constexpr int P = kF32H ? 2 : 1, NBUF = kF32H ? 1 : 2, CB = 4;
+    auto& sm = *static_cast<WideSmem<RB, P, NBUF>*>(smem);
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, q = lane >> 4, lr = lane & 15;
+    const int H = a.H, I = a.I, G = I / kGroup;
+    const size_t A = static_cast<size_t>(a.T) * a.k;
+    const int n0 = blockIdx.y * 256;
+    const bool active = n0 + 64 * wave < H;  // H is a multiple of 64
+    const int cbase = active ? n0 + 64 * wave : 0;
+
+    const uint32_t* src[RB];
+#pragma unroll
+    for (int i = 0; i < RB; ++i) {
+        const int r = (tid >> 4) + 16 * i;
+        src[i] = reinterpret_cast<const uint32_t*>(a.h) +
+                 static_cast<size_t>(row_begin + min(r, rows - 1)) * (I / 2);
+    }
+    const size_t part = A * (I / 2);
+    Stager<RB, P> st;
+    st.load(src, part, 0, G);
+
+    size_t row0[CB];
+    const uint32_t* blk[CB];
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+        row0[cb] = static_cast<size_t>(e) * H + cbase + 16 * cb;
+        blk[cb] = a.w_d + row0[cb] * (I / 8);
+    }
+    load_sb<CB>(sm.sb[wave], a.s_d, a.b_d, row0, G);
+    __builtin_amdgcn_wave_barrier();
+
+    const int steps = (G + 31) / 32;
+    f32x4 acc[RB][CB];
+    {
+        BiasOp C[CB];
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb)
+            bias_from_table(C[cb], sm.sb[wave][16 * cb + lr], G, q, steps, active);
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+            const int r = 16 * rb + lr;
+            BiasOp X;
+            bias_from_sums(X, a.hs + static_cast<size_t>(row_begin + min(r, rows - 1)) * G, G, q,
+                           steps);
+#pragma unroll
+            for (int cb = 0; cb < CB; ++cb) acc[rb][cb] = bias_mfma(X, C[cb], steps);
+        }
+    }
+    st.store(sm, 0);
+
+    wide_kloop<RB, P, NBUF>(sm, st, src, part, blk, I, active, acc);
+
+    if (!active) return;
+    // weighted unsort
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
             const int r = 16 * rb + 4 * q + v;
             if (r < rows) {
-                float* yrow = a.y + static_cast<size_t>(sDst[r]) * H;
-                const float wt = sW[r];
-                yrow[c0] = wt * acc0[rb][v];
-                yrow[c1] = wt * acc1[rb][v];
+                const int32_t dst = a.perm[row_begin + r];
+                const float wt = a.topk_w[dst];
+                float* yrow = a.y + static_cast<size_t>(dst) * H + cbase + lr;
+#pragma unroll
+                for (int cb = 0; cb < CB; ++cb) yrow[16 * cb] = wt * acc[rb][cb][v];
             }
         }
     }
 }
 
 template <bool kF32H>
-__global__ __launch_bounds__(kThreads) void moe_down(FfnArgs a) {
-    __shared__ uint32_t sA[2][kF32H ? 2 : 1][kARows * kAStride];
-    __shared__ float sX[2][kChunkGroups][kARows];
-    __shared__ int32_t sDst[kARows];
-    __shared__ float sW[kARows];
-    const int tile_idx = blockIdx.x;
-    if (tile_idx >= min(a.num_tiles[0], a.max_tiles)) return;
-    const int4 tile = reinterpret_cast<const int4*>(a.tiles)[tile_idx];
-    const int tid = threadIdx.x;
-    if (tid < tile.z) {
-        const int32_t dst = a.perm[tile.y + tid];
-        sDst[tid] = dst;
-        sW[tid] = a.topk_w[dst];
-    }
-    const int n0 = blockIdx.y * 128;
-    if (tile.z <= 16)
-        down_tile<1, kF32H>(a, sA, sX, sDst, sW, tile.x, tile.y, tile.z, n0);
-    else
-        down_tile<2, kF32H>(a, sA, sX, sDst, sW, tile.x, tile.y, tile.z, n0);
+__global__ __launch_bounds__(kThreads) void moe_gateup_wide(FfnArgs a) {
+    __shared__ __attribute__((aligned(16))) unsigned char smem[kWideSmemBytes];
+    const int4 tile = load_tile(a);
+    if (tile.x < 0 || tile.z <= kBmSmall) return;
+    const int rows = tile.z;
+    if (rows <= 32) gateup_wide<2, kF32H>(a, smem, tile.x, tile.y, rows);
+    else if (kF32H || rows <= 64) gateup_wide<4, kF32H>(a, smem, tile.x, tile.y, rows);
+    else if (rows <= 96) gateup_wide<6, kF32H>(a, smem, tile.x, tile.y, rows);
+    else gateup_wide<8, kF32H>(a, smem, tile.x, tile.y, rows);
+}
+
+template <bool kF32H>
+__global__ __launch_bounds__(kThreads) void moe_down_wide(FfnArgs a) {
+    __shared__ __attribute__((aligned(16))) unsigned char smem[kWideSmemBytes];
+    const int4 tile = load_tile(a);
+    if (tile.x < 0 || tile.z <= kBmSmall) return;
+    const int rows = tile.z;
+    if (rows <= 32) down_wide<2, kF32H>(a, smem, tile.x, tile.y, rows);
+    else if (kF32H || rows <= 64) down_wide<4, kF32H>(a, smem, tile.x, tile.y, rows);
+    else if (rows <= 96) down_wide<6, kF32H>(a, smem, tile.x, tile.y, rows);
+    else down_wide<8, kF32H>(a, smem, tile.x, tile.y, rows);
 }
 
 }  // namespace
 
-hipError_t launch_gateup(const FfnArgs& a, hipStream_t stream) {
+hipError_t launch_gateup_skinny(const FfnArgs& a, hipStream_t stream, const KTiming& t) {
     const dim3 grid(a.max_tiles, a.I / 64);
     if (a.flags & MOE_F_FP32_INTERMEDIATE)
-        hipLaunchKernelGGL(moe_gateup_geglu<true>, grid, dim3(kThreads), 0, stream, a);
-    else
-        hipLaunchKernelGGL(moe_gateup_geglu<false>, grid, dim3(kThreads), 0, stream, a);
-    return hipGetLastError();
+        return launch_kernel(moe_gateup_skinny<true>, grid, dim3(kThreads), stream, t, a);
+    return launch_kernel(moe_gateup_skinny<false>, grid, dim3(kThreads), stream, t, a);
 }
 
-hipError_t launch_down(const FfnArgs& a, hipStream_t stream) {
+hipError_t launch_gateup_wide(const FfnArgs& a, hipStream_t stream, const KTiming& t) {
+    const dim3 grid(a.max_tiles, (a.I + 127) / 128);
+    if (a.flags & MOE_F_FP32_INTERMEDIATE)
+        return launch_kernel(moe_gateup_wide<true>, grid, dim3(kThreads), stream, t, a);
+    return launch_kernel(moe_gateup_wide<false>, grid, dim3(kThreads), stream, t, a);
+}
+
+hipError_t launch_down_skinny(const FfnArgs& a, hipStream_t stream, const KTiming& t) {
     const dim3 grid(a.max_tiles, (a.H + 127) / 128);
     if (a.flags & MOE_F_FP32_INTERMEDIATE)
-        hipLaunchKernelGGL(moe_down<true>, grid, dim3(kThreads), 0, stream, a);
-    else
-        hipLaunchKernelGGL(moe_down<false>, grid, dim3(kThreads), 0, stream, a);
-    return hipGetLastError();
+        return launch_kernel(moe_down_skinny<true>, grid, dim3(kThreads), stream, t, a);
+    return launch_kernel(moe_down_skinny<false>, grid, dim3(kThreads), stream, t, a);
+}
+
+hipError_t launch_down_wide(const FfnArgs& a, hipStream_t stream, const KTiming& t) {
+    const dim3 grid(a.max_tiles, (a.H + 255) / 256);
+    if (a.flags & MOE_F_FP32_INTERMEDIATE)
+        return launch_kernel(moe_down_wide<true>, grid, dim3(kThreads), stream, t, a);
+    return launch_kernel(moe_down_wide<false>, grid, dim3(kThreads), stream, t, a);
 }
 
 }  // namespace moe

@@ -1,6 +1,7 @@
 // Internal declarations shared by the libmoeffn translation units.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -19,10 +20,15 @@ constexpr int kGroup = 64;      // quantisation group (columns per scale/bias)
 constexpr int kRouteThreads = 1024;
 constexpr int kRouteWaves = kRouteThreads / 64;
 
-// Tile heights used by the forward's own routing.  32-row tiles run on
-// 32x32x16 MFMAs; tiles of at most 16 rows run on 16x16x32 MFMAs.
-constexpr int kBmBig = 32;
+// Tile heights used by the forward's own routing: tiles of up to 128 rows of
+// one expert; a tile of at most 16 rows (decode-sized, or the short end of an
+// expert) takes the skinny path, larger ones the wide path.
+constexpr int kBmBig = 128;
+constexpr int kBmBigF32 = 64;  // with MOE_F_FP32_INTERMEDIATE
 constexpr int kBmSmall = 16;
+// Largest H and I the bias contraction handles (32 groups per MFMA step).
+constexpr int kMaxBiasSteps = 2;
+constexpr int kMaxDim = kMaxBiasSteps * 32 * kGroup;
 
 // ---------------------------------------------------------- bf16 helpers
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
@@ -37,21 +43,27 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
 }
 
 // ------------------------------------------------------------ dequant
-// The eight 4-bit codes of one weight word as eight bf16 values 128 + q,
-// which bf16 holds exactly (exponent 7, mantissa q).  Element order in the
-// MFMA operand is [q0, q4, q1, q5, q2, q6, q3, q7]; the activation operand is
-// stored in the same order (permute8 below), so the products still pair each
-// code with its own column.  The +128 offset is removed in fp32 per group:
-//   sum_k x_k (s q_k + b) = s * sum_k x_k (128 + q_k) + (b - 128 s) * sum_k x_k.
+// The eight 4-bit codes of one weight word as eight bf16 values 1 + q/16:
+// q goes into the top four of the seven mantissa bits of 1.0, which bf16
+// holds exactly.  Element order in the MFMA operand is
+// [q0, q4, q1, q5, q2, q6, q3, q7]; the activation operand is stored in the
+// same order (permute8 below), so each code still meets its own column.
+// With P = sum_k x_k (1 + q_k/16) and X = sum_k x_k over a 64-column group,
+//   sum_k x_k (s q_k + b) = 16 s P + (b - 16 s) X.
+// The offset 16 (rather than, say, 128 + q) keeps P close in size to the
+// part that carries information, so little is lost when X is taken out.
 __device__ __forceinline__ u32x4 codes_as_bf16(uint32_t w) {
     u32x4 r;
-    r[0] = (w & 0x000F000Fu) | 0x43004300u;
-    r[1] = ((w >> 4) & 0x000F000Fu) | 0x43004300u;
-    r[2] = ((w >> 8) & 0x000F000Fu) | 0x43004300u;
-    r[3] = ((w >> 12) & 0x000F000Fu) | 0x43004300u;
+    r[0] = ((w << 3) & 0x00780078u) | 0x3F803F80u;  // q0, q4
+    r[1] = ((w >> 1) & 0x00780078u) | 0x3F803F80u;  // q1, q5
+    r[2] = ((w >> 5) & 0x00780078u) | 0x3F803F80u;  // q2, q6
+    r[3] = ((w >> 9) & 0x00780078u) | 0x3F803F80u;  // q3, q7
     return r;
 }
-constexpr float kCodeOffset = 128.0f;
+constexpr float kCodeScale = 16.0f;
+
+// Position of column c (0..7) of an 8-column piece after permute8.
+__device__ __forceinline__ int permuted_pos(int c) { return ((c & 3) << 1) | (c >> 2); }
 
 // Reorder eight consecutive bf16 values [v0..v7] to [v0,v4,v1,v5,v2,v6,v3,v7].
 __device__ __forceinline__ u32x4 permute8(u32x4 v) {
@@ -84,17 +96,43 @@ __device__ __forceinline__ float gelu_tanh(float v) {
 }
 
 // ---------------------------------------------------- kernel launchers
+// Optional start/stop events of one kernel.  With events the kernel is
+// launched through hipExtLaunchKernelGGL, which records them with the dispatch
+// itself, so the interval is the kernel alone.
+struct KTiming {
+    hipEvent_t start = nullptr;
+    hipEvent_t stop = nullptr;
+};
+
+template <typename... Args, typename F = void (*)(Args...)>
+inline hipError_t launch_kernel(F kernel, dim3 grid, dim3 block, hipStream_t stream,
+                                const KTiming& t, Args... args) {
+    if (t.start != nullptr && t.stop != nullptr)
+        hipExtLaunchKernelGGL(kernel, grid, block, 0, stream, t.start, t.stop, 0, args...);
+    else
+        hipLaunchKernelGGL(kernel, grid, block, 0, stream, args...);
+    return hipGetLastError();
+}
+
 struct RouteArgs {
     const int32_t* ids;
     int32_t A, E, bm_big, bm_small, max_tiles;
     int32_t *counts, *offsets, *perm, *inv_perm, *tiles, *num_tiles;
+    // activation preparation (forward only; x == nullptr skips it)
+    const uint16_t* x;  // [T, H] bf16
+    int32_t T, H;
+    uint16_t* xp;       // [T, H] bf16, pieces reordered by permute8
+    float* xs;          // [T, H/64] group sums
 };
-hipError_t launch_route(const RouteArgs& a, hipStream_t stream);
+hipError_t launch_route(const RouteArgs& a, hipStream_t stream, const KTiming& t = {});
 
 struct FfnArgs {
     int32_t T, k, E, H, I, max_tiles;
     uint32_t flags;
     const uint16_t* x;
+    const uint16_t* xp;  // [T, H] x with pieces reordered by permute8
+    const float* xs;     // [T, H/64] group sums of x
+    float* hs;           // [A, I/64] group sums of h (as the down matmul sees it)
     const int32_t* ids;
     const float* topk_w;
     const uint32_t* w_gu;
@@ -106,12 +144,14 @@ struct FfnArgs {
     const int32_t* perm;
     const int32_t* tiles;
     const int32_t* num_tiles;
-    void* h;
+    void* h;             // [A, I] bf16, or hi and lo [2, A, I] bf16; pieces permuted
     float* y;
     void* out;
 };
-hipError_t launch_gateup(const FfnArgs& a, hipStream_t stream);
-hipError_t launch_down(const FfnArgs& a, hipStream_t stream);
-hipError_t launch_combine(const FfnArgs& a, hipStream_t stream);
+hipError_t launch_gateup_skinny(const FfnArgs& a, hipStream_t stream, const KTiming& t = {});
+hipError_t launch_gateup_wide(const FfnArgs& a, hipStream_t stream, const KTiming& t = {});
+hipError_t launch_down_skinny(const FfnArgs& a, hipStream_t stream, const KTiming& t = {});
+hipError_t launch_down_wide(const FfnArgs& a, hipStream_t stream, const KTiming& t = {});
+hipError_t launch_combine(const FfnArgs& a, hipStream_t stream, const KTiming& t = {});
 
 }  // namespace moe

@@ -18,6 +18,9 @@
 //   4. tiles per expert = ceil(count / bm_big), scanned; thread i emits tile i
 //      after an upper-bound search of the scanned tile offsets.
 //
+// In the forward, the other workgroups of the same launch prepare the
+// activations for the matmuls (prepare_x).
+//
 // Keys are expert ids; ids outside [0, E) get key E, which sorts after all
 // experts and gets no tiles.
 #include "moe_internal.h"
@@ -26,6 +29,15 @@ namespace moe {
 namespace {
 
 constexpr int kMaxKeys = MOE_MAX_EXPERTS + 1;
+
+constexpr int kBatch = 16;  // rows of 64 keys loaded ahead per wave
+
+// Sort key of assignment ai: its expert id, or E for an out-of-range id.
+__device__ __forceinline__ uint32_t load_key(const RouteArgs& a, int ai, int end, int E) {
+    if (ai >= end) return 0;
+    const int32_t id = a.ids[ai];
+    return (id >= 0 && id < E) ? static_cast<uint32_t>(id) : static_cast<uint32_t>(E);
+}
 
 // Lanes of the wave whose key equals this lane's key, among `active` lanes.
 __device__ __forceinline__ uint64_t match_any(uint32_t key, int nbits, uint64_t active) {
@@ -73,7 +85,32 @@ __device__ void block_exclusive_scan(const int32_t* in, int32_t* out, int n, int
     __syncthreads();
 }
 
+// Activation preparation, run by workgroups 1.. of the same launch: x in MFMA
+// operand order (each 8-column piece reordered by permute8) and the fp32 sum
+// of each (token, 64-column group), which the matmuls use for the bias term.
+// Thread p handles piece p of the [T, H/8] piece grid; the 8 pieces of a group
+// are 8 consecutive lanes.
+__device__ void prepare_x(const RouteArgs& a, int block) {
+    const int pieces_per_row = a.H / 8;
+    const int64_t p = static_cast<int64_t>(block) * kRouteThreads + threadIdx.x;
+    const int64_t total = static_cast<int64_t>(a.T) * pieces_per_row;
+    const bool ok = p < total;
+    u32x4 v = {0, 0, 0, 0};
+    if (ok) v = reinterpret_cast<const u32x4*>(a.x)[p];
+    float s = sum8_bf16(v);
+    s += __shfl_xor(s, 1);
+    s += __shfl_xor(s, 2);
+    s += __shfl_xor(s, 4);
+    if (!ok) return;
+    reinterpret_cast<u32x4*>(a.xp)[p] = permute8(v);
+    if ((p & 7) == 0) a.xs[p / 8] = s;
+}
+
 __global__ __launch_bounds__(kRouteThreads) void moe_route_sort_tiles(RouteArgs a) {
+    if (blockIdx.x > 0) {
+        prepare_x(a, blockIdx.x - 1);
+        return;
+    }
     __shared__ int32_t s_tab[kRouteWaves * kMaxKeys];  // per-wave key counts, then bases
     __shared__ int32_t s_cnt[kMaxKeys];
     __shared__ int32_t s_off[kMaxKeys + 1];
@@ -95,17 +132,20 @@ __global__ __launch_bounds__(kRouteThreads) void moe_route_sort_tiles(RouteArgs 
     const int end = min(A, beg + per);
     int32_t* tab = s_tab + wave * nkeys;
 
-    // 1. per-wave histogram
-    for (int base = beg; base < end; base += 64) {
-        const int ai = base + lane;
-        const bool act = ai < end;
-        uint32_t key = 0;
-        if (act) {
-            const int32_t id = a.ids[ai];
-            key = (id >= 0 && id < E) ? static_cast<uint32_t>(id) : static_cast<uint32_t>(E);
+    // 1. per-wave histogram.  Keys are loaded kBatch rows of 64 at a time, all
+    // loads issued before the first is used.
+    for (int base0 = beg; base0 < end; base0 += 64 * kBatch) {
+        uint32_t keys[kBatch];
+#pragma unroll
+        for (int b = 0; b < kBatch; ++b) keys[b] = load_key(a, base0 + 64 * b + lane, end, E);
+#pragma unroll
+        for (int b = 0; b < kBatch; ++b) {
+            const int base = base0 + 64 * b;
+            if (base >= end) break;
+            const bool act = base + lane < end;
+            const uint64_t m = match_any(keys[b], nbits, __ballot(act));
+            if (act && (m & below) == 0) tab[keys[b]] += __popcll(m);
         }
-        const uint64_t m = match_any(key, nbits, __ballot(act));
-        if (act && (m & below) == 0) tab[key] += __popcll(m);
     }
     __syncthreads();
 
@@ -128,22 +168,24 @@ __global__ __launch_bounds__(kRouteThreads) void moe_route_sort_tiles(RouteArgs 
     __syncthreads();
 
     // 3. stable scatter
-    for (int base = beg; base < end; base += 64) {
-        const int ai = base + lane;
-        const bool act = ai < end;
-        uint32_t key = 0;
-        if (act) {
-            const int32_t id = a.ids[ai];
-            key = (id >= 0 && id < E) ? static_cast<uint32_t>(id) : static_cast<uint32_t>(E);
+    for (int base0 = beg; base0 < end; base0 += 64 * kBatch) {
+        uint32_t keys[kBatch];
+#pragma unroll
+        for (int b = 0; b < kBatch; ++b) keys[b] = load_key(a, base0 + 64 * b + lane, end, E);
+#pragma unroll
+        for (int b = 0; b < kBatch; ++b) {
+            const int base = base0 + 64 * b;
+            if (base >= end) break;
+            const int ai = base + lane;
+            const bool act = ai < end;
+            const uint64_t m = match_any(keys[b], nbits, __ballot(act));
+            if (act) {
+                const int32_t slot = tab[keys[b]] + __popcll(m & below);
+                a.perm[slot] = ai;
+                a.inv_perm[ai] = slot;
+            }
+            if (act && (m & below) == 0) tab[keys[b]] += __popcll(m);
         }
-        const uint64_t m = match_any(key, nbits, __ballot(act));
-        int32_t slot = 0;
-        if (act) slot = tab[key] + __popcll(m & below);
-        if (act) {
-            a.perm[slot] = ai;
-            a.inv_perm[ai] = slot;
-        }
-        if (act && (m & below) == 0) tab[key] += __popcll(m);
     }
 
     // 4. counts, offsets, tiles
@@ -183,9 +225,13 @@ __global__ __launch_bounds__(kRouteThreads) void moe_route_sort_tiles(RouteArgs 
 
 }  // namespace
 
-hipError_t launch_route(const RouteArgs& a, hipStream_t stream) {
-    hipLaunchKernelGGL(moe_route_sort_tiles, dim3(1), dim3(kRouteThreads), 0, stream, a);
-    return hipGetLastError();
+hipError_t launch_route(const RouteArgs& a, hipStream_t stream, const KTiming& t) {
+    int blocks = 1;
+    if (a.x != nullptr) {
+        const int64_t pieces = static_cast<int64_t>(a.T) * (a.H / 8);
+        blocks += static_cast<int>((pieces + kRouteThreads - 1) / kRouteThreads);
+    }
+    return launch_kernel(moe_route_sort_tiles, dim3(blocks), dim3(kRouteThreads), stream, t, a);
 }
 
 }  // namespace moe

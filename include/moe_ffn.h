@@ -74,8 +74,8 @@ typedef struct {
     int32_t T;          /* tokens, >= 0                                  */
     int32_t k;          /* experts per token, 1 <= k <= E                */
     int32_t E;          /* experts, 1 <= E <= MOE_MAX_EXPERTS            */
-    int32_t H;          /* hidden size, multiple of 64                   */
-    int32_t I;          /* intermediate size, multiple of 64             */
+    int32_t H;          /* hidden size, multiple of 64, <= 4096          */
+    int32_t I;          /* intermediate size, multiple of 64, <= 4096    */
     int32_t group_size; /* must be 64                                    */
     int32_t bits;       /* must be 4                                     */
     uint32_t flags;     /* MOE_F_* below                                 */
@@ -125,16 +125,23 @@ moe_status moe_sort_build_tiles(const int32_t* topk_ids, int32_t T, int32_t k,
 size_t moe_ffn_workspace_bytes(const moe_problem* p);
 
 /* Byte offsets of the forward's intermediates inside its workspace, so that
- * callers and tests can inspect them after a forward on the same stream. */
+ * callers and tests can inspect them after a forward on the same stream.
+ * "Operand order": within every run of 8 consecutive columns, the values are
+ * stored in the order 0,4,1,5,2,6,3,7 (the column order of the matmul
+ * operands). */
 typedef struct {
     size_t counts;    /* int32 [E]                                        */
     size_t offsets;   /* int32 [E+1]                                      */
     size_t perm;      /* int32 [A]                                        */
     size_t inv_perm;  /* int32 [A]                                        */
-    size_t tiles;     /* moe_tile [max_tiles]                             */
+    size_t tiles;     /* moe_tile [max_tiles], bm_big/bm_small below      */
     size_t num_tiles; /* int32 [2]                                        */
-    size_t h;         /* [A, I] sorted order; bf16, or fp32 with
-                         MOE_F_FP32_INTERMEDIATE                          */
+    size_t x_perm;    /* bf16 [T, H]: x in operand order                  */
+    size_t x_sums;    /* fp32 [T, H/64]: sum of x over each 64-column group */
+    size_t h;         /* GeGLU output in sorted order, operand order:
+                         bf16 [A, I]; with MOE_F_FP32_INTERMEDIATE two bf16
+                         arrays [2, A, I], h = hi + lo                    */
+    size_t h_sums;    /* fp32 [A, I/64]: sum of h (hi + lo) per group     */
     size_t y;         /* fp32 [A, H] flat order a = t*k + j, already
                          multiplied by topk_weights; rows of assignments
                          with an out-of-range id are not written          */
@@ -172,10 +179,12 @@ moe_status moe_expert_ffn_forward(const moe_problem* p, const void* x,
                                   const void* s_down, const void* b_down, void* out,
                                   void* ws, size_t ws_bytes, void* stream);
 
-/* Same as moe_expert_ffn_forward, and records events[0..4] (hipEvent_t,
- * created by the caller) on `stream` before the route kernel, after it, after
- * the gate|up kernel, after the down kernel and after the combine kernel, so
- * that each stage can be timed on the stream it runs on.  events may be NULL. */
+/* Same as moe_expert_ffn_forward, with per-kernel timing: events[2i] and
+ * events[2i+1] (hipEvent_t, created by the caller) are recorded at the start
+ * and the end of kernel i, with the kernel's dispatch itself, on `stream`.
+ * The kernels, in launch order: 0 route, 1 gate|up skinny (tiles of <= 16
+ * rows), 2 gate|up wide, 3 down skinny, 4 down wide, 5 combine.  A kernel
+ * whose pair holds a NULL is not timed; events may be NULL. */
 moe_status moe_expert_ffn_forward_timed(const moe_problem* p, const void* x,
                                         const int32_t* topk_ids,
                                         const float* topk_weights,

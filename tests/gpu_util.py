@@ -67,12 +67,30 @@ def ws_view(ws, offset, count, dtype):
     return raw.view(dtype)
 
 
+OPERAND_ORDER = np.array([0, 4, 1, 5, 2, 6, 3, 7])
+
+
+def from_operand_order(a: np.ndarray) -> np.ndarray:
+    """Undo the operand order of the last axis: within every 8 columns the
+    stored order is 0,4,1,5,2,6,3,7."""
+    n = a.shape[-1]
+    src = np.empty(n, np.int64)
+    for b in range(0, n, 8):
+        src[b + OPERAND_ORDER] = b + np.arange(8)
+    return a[..., src]
+
+
 def ws_h(ws, lay, p, fp32):
+    """h [A, I] in sorted order, natural column order, as float64."""
     A = p.T * p.k
     if fp32:
-        return ws_view(ws, lay.h, A * p.I, np.float32).reshape(A, p.I).astype(np.float64)
-    bits = ws_view(ws, lay.h, A * p.I, np.uint16).reshape(A, p.I)
-    return ms.bf16_bits_to_f32(bits).astype(np.float64)
+        bits = ws_view(ws, lay.h, 2 * A * p.I, np.uint16).reshape(2, A, p.I)
+        h = (ms.bf16_bits_to_f32(bits[0]).astype(np.float64)
+             + ms.bf16_bits_to_f32(bits[1]).astype(np.float64))
+    else:
+        bits = ws_view(ws, lay.h, A * p.I, np.uint16).reshape(A, p.I)
+        h = ms.bf16_bits_to_f32(bits).astype(np.float64)
+    return from_operand_order(h)
 
 
 def ws_y_rows(ws, lay, p, rows):

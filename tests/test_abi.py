@@ -41,18 +41,21 @@ def test_workspace_layout_and_sizes():
     lay = bgq.workspace_layout(p)
     A = 2048 * 8
     assert lay.total == bgq.workspace_bytes(p)
-    offs = [lay.counts, lay.offsets, lay.perm, lay.inv_perm, lay.tiles, lay.num_tiles, lay.h, lay.y]
+    offs = [lay.counts, lay.offsets, lay.perm, lay.inv_perm, lay.tiles, lay.num_tiles,
+            lay.x_perm, lay.x_sums, lay.h, lay.h_sums, lay.y]
     assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
-    assert lay.y - lay.h >= A * 704 * 2 and lay.total - lay.y >= A * 2816 * 4
-    assert lay.max_tiles == 640 and lay.bm_big == 32 and lay.bm_small == 16
+    assert lay.x_sums - lay.x_perm >= 2048 * 2816 * 2
+    assert lay.h_sums - lay.h >= A * 704 * 2 and lay.total - lay.y >= A * 2816 * 4
+    assert lay.bm_big == 128 and lay.bm_small == 16
+    assert lay.max_tiles == A // 128 + 128
     p32 = bgq.problem(2048, 8, 128, 2816, 704, bgq.MOE_F_FP32_INTERMEDIATE)
-    assert bgq.workspace_layout(p32).total - bgq.workspace_layout(p32).y == lay.total - lay.y
-    assert bgq.workspace_layout(p32).y - bgq.workspace_layout(p32).h >= A * 704 * 4
+    l32 = bgq.workspace_layout(p32)
+    assert l32.h_sums - l32.h >= A * 704 * 4
 
 
 @pytest.mark.parametrize("kw,status", [
     (dict(bits=8), -3), (dict(group_size=32), -3), (dict(E=2000), -3), (dict(flags=8), -3),
-    (dict(H=100), -2), (dict(I=96), -2), (dict(k=0), -2), (dict(k=9, E=8), -2), (dict(T=-1), -2),
+    (dict(H=100), -2), (dict(I=96), -2), (dict(H=8192), -3), (dict(I=4160), -3), (dict(k=0), -2), (dict(k=9, E=8), -2), (dict(T=-1), -2),
 ])
 def test_bad_problem(kw, status):
     base = dict(T=4, k=2, E=8, H=256, I=128, flags=0, group_size=64, bits=4)

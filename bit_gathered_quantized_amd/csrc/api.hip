@@ -75,8 +75,8 @@ moe_status forward_impl(const moe_problem* p, const void* x, const int32_t* ids,
     if (ws_bytes < l.total) return MOE_ERR_WORKSPACE;
     const bool f32out = p->flags & MOE_F_FP32_OUT;
     if (!aligned(x, 16) || !aligned(w_gu, 16) || !aligned(w_d, 16) || !aligned(ids, 4) ||
-        !aligned(topk_w, 4) || !aligned(s_gu, 2) || !aligned(b_gu, 2) || !aligned(s_d, 2) ||
-        !aligned(b_d, 2) || !aligned(out, f32out ? 16 : 8) || !aligned(ws, kAlign))
+        !aligned(topk_w, 4) || !aligned(s_gu, 16) || !aligned(b_gu, 16) || !aligned(s_d, 16) ||
+        !aligned(b_d, 16) || !aligned(out, f32out ? 16 : 8) || !aligned(ws, kAlign))
         return MOE_ERR_ALIGN;
 
     hipStream_t s = static_cast<hipStream_t>(stream);

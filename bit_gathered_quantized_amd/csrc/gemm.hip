@@ -14,8 +14,8 @@
 //    registers straight from HBM loads; weights never touch LDS.  Per
 //    64-column group the fp32 accumulator takes 16 s * P (one FMA per output
 //    per group); the rest, sum_g (b - 16 s) X, is itself a small contraction
-//    over groups, run on MFMAs once per tile with both factors split into
-//    bf16 hi + lo.  Rounding dequantised weights to bf16 instead would cost
+//    over groups, run on MFMAs once per tile after the groups, with both
+//    factors split into bf16 hi + lo.  Rounding dequantised weights to bf16 instead would cost
 //    the accuracy the fp32 path needs.
 //  * Activations come pre-ordered (x_perm, from the route launch) with their
 //    group sums, so nothing here reorders or sums activations on the fly.
@@ -91,10 +91,10 @@ __device__ __forceinline__ void bias_from_sums(BiasOp& o, const float* X, int G,
     }
 }
 
-// Column operand: c[g] = b[g] - 16 s[g] of one weight row, from its LDS table
-// of (scale | bias << 16).
-__device__ __forceinline__ void bias_from_table(BiasOp& o, const uint32_t* sb, int G, int q,
-                                                int steps, bool active) {
+// Column operand: c[g] = b[g] - 16 s[g] of one weight row, from its rows of
+// the scale and bias tables.
+__device__ __forceinline__ void bias_from_table(BiasOp& o, const uint16_t* ts, const uint16_t* tb,
+                                                int G, int q, int steps, bool active) {
 #pragma unroll
     for (int st = 0; st < kMaxBiasSteps; ++st) {
         if (st < steps) {
@@ -102,15 +102,37 @@ __device__ __forceinline__ void bias_from_table(BiasOp& o, const uint32_t* sb, i
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 const int g = 32 * st + 8 * q + j;
-                const uint32_t t = sb[min(g, G - 1)];
-                const float c = fmaf(-kCodeScale, bf16_to_f32(static_cast<uint16_t>(t & 0xFFFFu)),
-                                     bf16_to_f32(static_cast<uint16_t>(t >> 16)));
+                const int gc = min(g, G - 1);
+                const float c = fmaf(-kCodeScale, bf16_to_f32(ts[gc]), bf16_to_f32(tb[gc]));
                 v[j] = (active && g < G) ? c : 0.f;
             }
             pack_split(v, o.hi[st], o.lo[st]);
         }
     }
 }
+
+// The group sums of one activation row as the bias operand.
+struct RowSums {
+    float v[kMaxBiasSteps][8];
+
+    __device__ __forceinline__ void load(const float* X, int G, int q) {
+#pragma unroll
+        for (int st = 0; st < kMaxBiasSteps; ++st)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) v[st][j] = X[min(32 * st + 8 * q + j, G - 1)];
+    }
+    __device__ __forceinline__ void pack(BiasOp& o, int G, int q, int steps) const {
+#pragma unroll
+        for (int st = 0; st < kMaxBiasSteps; ++st) {
+            if (st < steps) {
+                float w[8];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) w[j] = (32 * st + 8 * q + j < G) ? v[st][j] : 0.f;
+                pack_split(w, o.hi[st], o.lo[st]);
+            }
+        }
+    }
+};
 
 // sum_g c[n, g] X[m, g] for one 16x16 block: hi*hi + hi*lo + lo*hi per step.
 __device__ __forceinline__ f32x4 bias_mfma(const BiasOp& A, const BiasOp& B, int steps) {
@@ -150,10 +172,8 @@ __device__ __forceinline__ f32x4 group_step2(f32x4 acc, u32x4 a0h, u32x4 a0l, u3
     return acc;
 }
 
-// 16 s from a table entry (scale | bias << 16).
-__device__ __forceinline__ float scale16(uint32_t t) {
-    return kCodeScale * bf16_to_f32(static_cast<uint16_t>(t & 0xFFFFu));
-}
+// 16 s from a bf16 scale.
+__device__ __forceinline__ float scale16(uint16_t t) { return kCodeScale * bf16_to_f32(t); }
 
 // Sum over the 16 lanes of a 16-lane row (the same value in every lane).
 __device__ __forceinline__ float sum16(float v) {
@@ -239,28 +259,48 @@ struct WaveW {
     }
 };
 
-// (scale | bias << 16) of NCB blocks of 16 weight rows into a wave's table,
-// read in row order (coalesced).
+// Scale and bias rows of NCB blocks of 16 weight rows, copied raw into a
+// wave's LDS tables (entry (row, g) at row * G + g).  A block's 16 rows are
+// contiguous, 32 G bytes, so they move as 16-byte pieces in row order: two
+// loads per lane and table cover G <= 64.  The loads are issued early and the
+// stores made later, so their latency overlaps the first weight loads.
 template <int NCB>
-__device__ __forceinline__ void load_sb(uint32_t (*tab)[kMaxG], const uint16_t* s, const uint16_t* b,
-                                        const size_t (&row0)[NCB], int G) {
-    const int lane = threadIdx.x & 63;
+struct Tables {
+    u32x4 vs[NCB][2], vb[NCB][2];
+
+    __device__ __forceinline__ void load(const uint16_t* s, const uint16_t* b,
+                                         const size_t (&row0)[NCB], int G) {
+        const int lane = threadIdx.x & 63, np = 2 * G;
 #pragma unroll
-    for (int cb = 0; cb < NCB; ++cb) {
-        const uint16_t* sp = s + row0[cb] * G;
-        const uint16_t* bp = b + row0[cb] * G;
-        for (int idx = lane; idx < 16 * G; idx += 64) {
-            const int r = idx / G, g = idx - r * G;
-            tab[16 * cb + r][g] = static_cast<uint32_t>(sp[idx]) | (static_cast<uint32_t>(bp[idx]) << 16);
-        }
+        for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const size_t off = row0[cb] * G + 8 * min(lane + 64 * j, np - 1);
+                vs[cb][j] = *reinterpret_cast<const u32x4*>(s + off);
+                vb[cb][j] = *reinterpret_cast<const u32x4*>(b + off);
+            }
     }
-}
+    __device__ __forceinline__ void store(uint16_t* ts, uint16_t* tb, int G) const {
+        const int lane = threadIdx.x & 63, np = 2 * G;
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const int idx = lane + 64 * j;
+                if (idx < np) {
+                    *reinterpret_cast<u32x4*>(ts + cb * 16 * G + 8 * idx) = vs[cb][j];
+                    *reinterpret_cast<u32x4*>(tb + cb * 16 * G + 8 * idx) = vb[cb][j];
+                }
+            }
+    }
+};
 
 // =========================================================== skinny paths
-struct SkinnySmem {
-    uint32_t w[4][32 * 16];     // per-wave weight transposition buffer
-    uint32_t sb[4][32][kMaxG];  // per-wave (scale | bias << 16) of its 32 weight rows
-    float blk[4][kBmSmall];     // 16-column block sums of h
+struct alignas(16) SkinnySmem {
+    uint32_t w[4][32 * 16];      // per-wave weight transposition buffer
+    uint16_t ts[4][32 * kMaxG];  // per-wave scales of its 32 weight rows
+    uint16_t tb[4][32 * kMaxG];  // per-wave biases
+    float blk[4][kBmSmall];      // 16-column block sums of h
 };
 
 // gate|up, tiles of <= 16 rows.  Grid (max_tiles, I / 64).  Wave w owns h
@@ -279,6 +319,8 @@ __global__ __launch_bounds__(kThreads) void moe_gateup_skinny(FfnArgs a) {
 
     const size_t row0[2] = {static_cast<size_t>(e) * 2 * I + hcol0,
                             static_cast<size_t>(e) * 2 * I + I + hcol0};
+    Tables<2> tab;
+    tab.load(a.s_gu, a.b_gu, row0, G);
     const uint32_t* blk[2] = {a.w_gu + row0[0] * (H / 8), a.w_gu + row0[1] * (H / 8)};
     WaveW<2> ww;
     ww.init(sm.w[wave], blk, H / 8);
@@ -301,21 +343,12 @@ __global__ __launch_bounds__(kThreads) void moe_gateup_skinny(FfnArgs a) {
     };
     load_a(0, 0);
 
-    load_sb<2>(sm.sb[wave], a.s_gu, a.b_gu, row0, G);
+    uint16_t* const ts = sm.ts[wave];
+    uint16_t* const tb = sm.tb[wave];
+    tab.store(ts, tb, G);
     __builtin_amdgcn_wave_barrier();
 
-    // the bias term initialises the accumulators
-    const int steps = (G + 31) / 32;
-    f32x4 accg, accu;
-    {
-        BiasOp X, C;
-        bias_from_sums(X, a.xs + static_cast<size_t>(tok) * G, G, q, steps);
-        bias_from_table(C, sm.sb[wave][lr], G, q, steps, true);
-        accg = bias_mfma(X, C, steps);
-        bias_from_table(C, sm.sb[wave][16 + lr], G, q, steps, true);
-        accu = bias_mfma(X, C, steps);
-    }
-
+    f32x4 accg = {0.f, 0.f, 0.f, 0.f}, accu = accg;
     const int nch = (G + 1) / 2;
     auto compute = [&](int slot, int abuf, int c) {
         ww.put(rv[slot]);
@@ -325,7 +358,7 @@ __global__ __launch_bounds__(kThreads) void moe_gateup_skinny(FfnArgs a) {
         for (int gi = 0; gi < 2; ++gi) {
             const int g = 2 * c + gi;
             if (g < G) {
-                const float sg = scale16(sm.sb[wave][lr][g]), su = scale16(sm.sb[wave][16 + lr][g]);
+                const float sg = scale16(ts[lr * G + g]), su = scale16(ts[(16 + lr) * G + g]);
                 accg = group_step(accg, ra[abuf][2 * gi], ra[abuf][2 * gi + 1],
                                   codes_as_bf16(wgv[2 * gi]), codes_as_bf16(wgv[2 * gi + 1]), sg);
                 accu = group_step(accu, ra[abuf][2 * gi], ra[abuf][2 * gi + 1],
@@ -349,6 +382,19 @@ __global__ __launch_bounds__(kThreads) void moe_gateup_skinny(FfnArgs a) {
             load_a(c0 + i + 1, (i + 1) & 1);
             compute(i, i & 1, c0 + i);
         }
+    }
+
+    // the bias term, added once after the groups
+    {
+        const int steps = (G + 31) / 32;
+        BiasOp X, C;
+        RowSums xsum;
+        xsum.load(a.xs + static_cast<size_t>(tok) * G, G, q);
+        xsum.pack(X, G, q, steps);
+        bias_from_table(C, ts + lr * G, tb + lr * G, G, q, steps, true);
+        accg += bias_mfma(X, C, steps);
+        bias_from_table(C, ts + (16 + lr) * G, tb + (16 + lr) * G, G, q, steps, true);
+        accu += bias_mfma(X, C, steps);
     }
 
     // GeGLU, h once, and this wave's 16-column block sums of h per row
@@ -382,6 +428,8 @@ __global__ __launch_bounds__(kThreads) void moe_down_skinny(FfnArgs a) {
     const int c0 = cbase + lr, c1 = c0 + 16;
 
     const size_t row0[2] = {static_cast<size_t>(e) * H + cbase, static_cast<size_t>(e) * H + cbase + 16};
+    Tables<2> tab;
+    tab.load(a.s_d, a.b_d, row0, G);
     const uint32_t* blk[2] = {a.w_d + row0[0] * (I / 8), a.w_d + row0[1] * (I / 8)};
     WaveW<2> ww;
     ww.init(sm.w[wave], blk, I / 8);
@@ -408,20 +456,12 @@ __global__ __launch_bounds__(kThreads) void moe_down_skinny(FfnArgs a) {
     };
     load_a(0, 0);
 
-    load_sb<2>(sm.sb[wave], a.s_d, a.b_d, row0, G);
+    uint16_t* const ts = sm.ts[wave];
+    uint16_t* const tb = sm.tb[wave];
+    tab.store(ts, tb, G);
     __builtin_amdgcn_wave_barrier();
 
-    const int steps = (G + 31) / 32;
-    f32x4 acc0, acc1;
-    {
-        BiasOp X, C;
-        bias_from_sums(X, a.hs + static_cast<size_t>(arow) * G, G, q, steps);
-        bias_from_table(C, sm.sb[wave][lr], G, q, steps, true);
-        acc0 = bias_mfma(X, C, steps);
-        bias_from_table(C, sm.sb[wave][16 + lr], G, q, steps, true);
-        acc1 = bias_mfma(X, C, steps);
-    }
-
+    f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
     const int nch = (G + 1) / 2;
     auto compute = [&](int slot, int abuf, int c) {
         ww.put(rv[slot]);
@@ -431,7 +471,7 @@ __global__ __launch_bounds__(kThreads) void moe_down_skinny(FfnArgs a) {
         for (int gi = 0; gi < 2; ++gi) {
             const int g = 2 * c + gi;
             if (g < G) {
-                const float s0 = scale16(sm.sb[wave][lr][g]), s1 = scale16(sm.sb[wave][16 + lr][g]);
+                const float s0 = scale16(ts[lr * G + g]), s1 = scale16(ts[(16 + lr) * G + g]);
                 const u32x4 b00 = codes_as_bf16(w0v[2 * gi]), b01 = codes_as_bf16(w0v[2 * gi + 1]);
                 const u32x4 b10 = codes_as_bf16(w1v[2 * gi]), b11 = codes_as_bf16(w1v[2 * gi + 1]);
                 const u32x4(&x)[4][P] = ra[abuf];
@@ -465,6 +505,19 @@ __global__ __launch_bounds__(kThreads) void moe_down_skinny(FfnArgs a) {
         }
     }
 
+    // the bias term, added once after the groups
+    {
+        const int steps = (G + 31) / 32;
+        BiasOp X, C;
+        RowSums hsum;
+        hsum.load(a.hs + static_cast<size_t>(arow) * G, G, q);
+        hsum.pack(X, G, q, steps);
+        bias_from_table(C, ts + lr * G, tb + lr * G, G, q, steps, true);
+        acc0 += bias_mfma(X, C, steps);
+        bias_from_table(C, ts + (16 + lr) * G, tb + (16 + lr) * G, G, q, steps, true);
+        acc1 += bias_mfma(X, C, steps);
+    }
+
     // weighted unsort
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
@@ -488,12 +541,18 @@ __global__ __launch_bounds__(kThreads) void moe_down_skinny(FfnArgs a) {
 constexpr int kAStride = 2 * 32 + 4;  // u32 per staged activation row
 
 template <int RB, int P, int NBUF>
-struct WideSmem {
-    uint32_t a[NBUF][P][RB * 16 * kAStride];
+struct alignas(16) WideSmem {
+    uint32_t a[NBUF][P][RB * 16 * kAStride];  // after the K loop: group sums of the rows
     uint32_t w[4][64 * 16];
-    uint32_t sb[4][64][kMaxG];
-    float blk[2][4][kBmBig];  // [64-column group][16-column block][row]
+    uint16_t ts[4][64 * kMaxG];  // per-wave scales of its 64 weight rows
+    uint16_t tb[4][64 * kMaxG];  // per-wave biases
+    float blk[2][4][kBmBig];     // [64-column group][16-column block][row]
 };
+// row stride (floats) of the group sums staged in a[] after the K loop: 16
+// rows of a fragment read fall on distinct banks, and 8-group reads up to
+// group 63 stay inside a row
+constexpr int kXStride = kMaxG + 4;
+static_assert(kXStride <= kAStride, "group sums must fit the activation buffer");
 // the largest layout any wide kernel uses
 constexpr size_t kWideSmemBytes = sizeof(WideSmem<8, 1, 2>) > sizeof(WideSmem<8, 2, 1>)
                                       ? sizeof(WideSmem<8, 1, 2>)
@@ -574,7 +633,7 @@ __device__ __forceinline__ void wide_kloop(WideSmem<RB, P, NBUF>& sm, Stager<RB,
                     for (int cb = 0; cb < CB; ++cb) {
                         b0[cb] = codes_as_bf16(wq[cb][2 * i]);
                         b1[cb] = codes_as_bf16(wq[cb][2 * i + 1]);
-                        s16[cb] = scale16(sm.sb[wave][16 * cb + lr][g]);
+                        s16[cb] = scale16(sm.ts[wave][(16 * cb + lr) * G + g]);
                     }
 #pragma unroll
                     for (int rb = 0; rb < RB; ++rb) {
@@ -611,6 +670,58 @@ __device__ __forceinline__ void wide_kloop(WideSmem<RB, P, NBUF>& sm, Stager<RB,
     }
 }
 
+// The bias term of the wide paths, added once after the K loop.  The group
+// sums of the staged rows go through LDS (the activation buffers are free by
+// then): thread t copies groups t % 16 + 16 j of rows t / 16 + 16 i, from row
+// pointers xrow[i] (G floats each).
+template <int RB, int P, int NBUF>
+__device__ __forceinline__ void wide_bias(WideSmem<RB, P, NBUF>& sm, const float* const (&xrow)[RB],
+                                          int G, bool active, f32x4 (&acc)[RB][4]) {
+    constexpr int CB = 4;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, q = lane >> 4, lr = lane & 15;
+    float* xl = reinterpret_cast<float*>(&sm.a[0][0][0]);
+    const int pc = threadIdx.x & 15, r0 = threadIdx.x >> 4;
+#pragma unroll
+    for (int i = 0; i < RB; ++i)
+#pragma unroll
+        for (int j = 0; j < kMaxG / 16; ++j) {
+            const int g = pc + 16 * j;
+            if (g < G) xl[(r0 + 16 * i) * kXStride + g] = xrow[i][g];
+        }
+    __syncthreads();
+    const int steps = (G + 31) / 32;
+    const uint16_t* ts = sm.ts[wave];
+    const uint16_t* tb = sm.tb[wave];
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+        BiasOp C;
+        bias_from_table(C, ts + (16 * cb + lr) * G, tb + (16 * cb + lr) * G, G, q, steps, active);
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+            // 8 consecutive groups per step; reads past G stay inside the row
+            // stride and are replaced by 0
+            const float* xr = xl + (16 * rb + lr) * kXStride;
+            BiasOp X;
+#pragma unroll
+            for (int st = 0; st < kMaxBiasSteps; ++st) {
+                if (st < steps) {
+                    const f32x4 v0 = *reinterpret_cast<const f32x4*>(xr + 32 * st + 8 * q);
+                    const f32x4 v1 = *reinterpret_cast<const f32x4*>(xr + 32 * st + 8 * q + 4);
+                    float v[8];
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) {
+                        const float x = j < 4 ? v0[j] : v1[j - 4];
+                        v[j] = 32 * st + 8 * q + j < G ? x : 0.f;
+                    }
+                    pack_split(v, X.hi[st], X.lo[st]);
+                }
+            }
+            acc[rb][cb] += bias_mfma(X, C, steps);
+            __builtin_amdgcn_sched_barrier(0);  // one block at a time: registers stay low
+        }
+    }
+}
+
 // gate|up wide.  Grid (max_tiles, ceil(I / 128)).  Wave w owns h columns
 // n0 + 32 w + [0, 32): weight blocks 0/1 = gate columns +0/+16, blocks 2/3 =
 // the matching up columns.  Waves {0,1} cover 64-column group 2*by of h,
@@ -627,16 +738,6 @@ __device__ __forceinline__ void gateup_wide(const FfnArgs& a, void* smem, int e,
     const bool active = n0 + 32 * wave < I;
     const int hbase = active ? n0 + 32 * wave : 0;
 
-    const uint32_t* src[RB];
-#pragma unroll
-    for (int i = 0; i < RB; ++i) {
-        const int r = (tid >> 4) + 16 * i;
-        src[i] = reinterpret_cast<const uint32_t*>(a.xp) +
-                 static_cast<size_t>(a.perm[row_begin + min(r, rows - 1)] / a.k) * (H / 2);
-    }
-    Stager<RB, P> st;
-    st.load(src, 0, 0, G);
-
     size_t row0[CB];
     const uint32_t* blk[CB];
 #pragma unroll
@@ -644,30 +745,34 @@ __device__ __forceinline__ void gateup_wide(const FfnArgs& a, void* smem, int e,
         row0[cb] = static_cast<size_t>(e) * 2 * I + hbase + 16 * (cb & 1) + (cb >> 1) * I;
         blk[cb] = a.w_gu + row0[cb] * (H / 8);
     }
-    load_sb<CB>(sm.sb[wave], a.s_gu, a.b_gu, row0, G);
-    __builtin_amdgcn_wave_barrier();
+    Tables<CB> tab;
+    tab.load(a.s_gu, a.b_gu, row0, G);
 
-    // the bias term initialises the accumulators
-    const int steps = (G + 31) / 32;
-    f32x4 acc[RB][CB];
-    {
-        BiasOp C[CB];
+    int tok[RB];
+    const uint32_t* src[RB];
 #pragma unroll
-        for (int cb = 0; cb < CB; ++cb)
-            bias_from_table(C[cb], sm.sb[wave][16 * cb + lr], G, q, steps, active);
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-            const int r = 16 * rb + lr;
-            BiasOp X;
-            bias_from_sums(X, a.xs + static_cast<size_t>(a.perm[row_begin + min(r, rows - 1)] / a.k) * G,
-                           G, q, steps);
-#pragma unroll
-            for (int cb = 0; cb < CB; ++cb) acc[rb][cb] = bias_mfma(X, C[cb], steps);
-        }
+    for (int i = 0; i < RB; ++i) {
+        const int r = (tid >> 4) + 16 * i;
+        tok[i] = a.perm[row_begin + min(r, rows - 1)] / a.k;
+        src[i] = reinterpret_cast<const uint32_t*>(a.xp) + static_cast<size_t>(tok[i]) * (H / 2);
     }
+    Stager<RB, P> st;
+    st.load(src, 0, 0, G);
+    tab.store(sm.ts[wave], sm.tb[wave], G);
     st.store(sm, 0);
 
+    f32x4 acc[RB][CB];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) acc[rb][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
     wide_kloop<RB, P, NBUF>(sm, st, src, 0, blk, H, active, acc);
+
+    const float* xrow[RB];
+#pragma unroll
+    for (int i = 0; i < RB; ++i) xrow[i] = a.xs + static_cast<size_t>(tok[i]) * G;
+    wide_bias<RB, P, NBUF>(sm, xrow, G, active, acc);
 
     // GeGLU epilogue and the 16-column block sums of h
 #pragma unroll
@@ -709,17 +814,6 @@ __device__ __forceinline__ void down_wide(const FfnArgs& a, void* smem, int e, i
     const bool active = n0 + 64 * wave < H;  // H is a multiple of 64
     const int cbase = active ? n0 + 64 * wave : 0;
 
-    const uint32_t* src[RB];
-#pragma unroll
-    for (int i = 0; i < RB; ++i) {
-        const int r = (tid >> 4) + 16 * i;
-        src[i] = reinterpret_cast<const uint32_t*>(a.h) +
-                 static_cast<size_t>(row_begin + min(r, rows - 1)) * (I / 2);
-    }
-    const size_t part = A * (I / 2);
-    Stager<RB, P> st;
-    st.load(src, part, 0, G);
-
     size_t row0[CB];
     const uint32_t* blk[CB];
 #pragma unroll
@@ -727,29 +821,35 @@ __device__ __forceinline__ void down_wide(const FfnArgs& a, void* smem, int e, i
         row0[cb] = static_cast<size_t>(e) * H + cbase + 16 * cb;
         blk[cb] = a.w_d + row0[cb] * (I / 8);
     }
-    load_sb<CB>(sm.sb[wave], a.s_d, a.b_d, row0, G);
-    __builtin_amdgcn_wave_barrier();
+    Tables<CB> tab;
+    tab.load(a.s_d, a.b_d, row0, G);
 
-    const int steps = (G + 31) / 32;
-    f32x4 acc[RB][CB];
-    {
-        BiasOp C[CB];
+    int hrow[RB];
+    const uint32_t* src[RB];
 #pragma unroll
-        for (int cb = 0; cb < CB; ++cb)
-            bias_from_table(C[cb], sm.sb[wave][16 * cb + lr], G, q, steps, active);
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-            const int r = 16 * rb + lr;
-            BiasOp X;
-            bias_from_sums(X, a.hs + static_cast<size_t>(row_begin + min(r, rows - 1)) * G, G, q,
-                           steps);
-#pragma unroll
-            for (int cb = 0; cb < CB; ++cb) acc[rb][cb] = bias_mfma(X, C[cb], steps);
-        }
+    for (int i = 0; i < RB; ++i) {
+        const int r = (tid >> 4) + 16 * i;
+        hrow[i] = row_begin + min(r, rows - 1);
+        src[i] = reinterpret_cast<const uint32_t*>(a.h) + static_cast<size_t>(hrow[i]) * (I / 2);
     }
+    const size_t part = A * (I / 2);
+    Stager<RB, P> st;
+    st.load(src, part, 0, G);
+    tab.store(sm.ts[wave], sm.tb[wave], G);
     st.store(sm, 0);
 
+    f32x4 acc[RB][CB];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) acc[rb][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
     wide_kloop<RB, P, NBUF>(sm, st, src, part, blk, I, active, acc);
+
+    const float* xrow[RB];
+#pragma unroll
+    for (int i = 0; i < RB; ++i) xrow[i] = a.hs + static_cast<size_t>(hrow[i]) * G;
+    wide_bias<RB, P, NBUF>(sm, xrow, G, active, acc);
 
     if (!active) return;
     // weighted unsort

@@ -162,7 +162,7 @@ moe_status moe_ffn_workspace_layout(const moe_problem* p, moe_ws_layout* layout)
  *   x            bf16 [T, H]        16-byte aligned
  *   topk_ids     int32 [T, k]
  *   topk_weights fp32 [T, k]        used as given (no renormalisation)
- *   w_gateup ... b_down             see the layout above; w_* 16-byte aligned
+ *   w_gateup ... b_down             see the layout above; all six 16-byte aligned
  *   out          [T, H] bf16, or fp32 with MOE_F_FP32_OUT
  *   ws           device workspace of at least moe_ffn_workspace_bytes(p)
  *                bytes, 256-byte aligned

@@ -89,6 +89,11 @@ def test_forward_host_checks():
     bad_w = list(good)
     bad_w[3] = ctypes.c_void_p(0x10008)
     assert _forward(p, bad_w, out, ws, need) == -4
+    # scales and biases are read in 16-byte pieces
+    for i in (4, 5, 7, 8):
+        bad_s = list(good)
+        bad_s[i] = ctypes.c_void_p(0x10002)
+        assert _forward(p, bad_s, out, ws, need) == -4
     assert _forward(p, good, ctypes.c_void_p(0x20002), ws, need) == -4
     assert _forward(p, good, out, ctypes.c_void_p(0x40080), need) == -4
     # zero tokens: nothing to do, nothing touched

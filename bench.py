@@ -31,7 +31,7 @@ if ROOT not in sys.path:
 METRIC = "expert-FFN assignments/s and TFLOP/s (or HBM GB/s) vs roofline, 1 MI355X"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
-BM_BIG, BM_SMALL = 128, 16     # tile heights the forward routes with
+BM_BIG, BM_SMALL = 64, 16      # tile heights the forward routes with
 
 
 def log(msg):

@@ -50,7 +50,8 @@ moe_ws_layout make_layout(const moe_problem* p) {
     l.perm = take(sizeof(int32_t) * A);
     l.inv_perm = take(sizeof(int32_t) * A);
     l.tiles = take(sizeof(moe_tile) * l.max_tiles);
-    l.num_tiles = take(sizeof(int32_t) * 2);
+    l.tiles_skinny = take(sizeof(moe_tile) * l.max_tiles);
+    l.num_tiles = take(sizeof(int32_t) * 4);
     l.x_perm = take(sizeof(uint16_t) * p->T * p->H);
     l.x_sums = take(sizeof(float) * p->T * G);
     l.h = take(hbytes * A * p->I);
@@ -103,6 +104,7 @@ moe_status forward_impl(const moe_problem* p, const void* x, const int32_t* ids,
     r.perm = reinterpret_cast<int32_t*>(base + l.perm);
     r.inv_perm = reinterpret_cast<int32_t*>(base + l.inv_perm);
     r.tiles = reinterpret_cast<int32_t*>(base + l.tiles);
+    r.tiles_skinny = reinterpret_cast<int32_t*>(base + l.tiles_skinny);
     r.num_tiles = reinterpret_cast<int32_t*>(base + l.num_tiles);
     r.x = static_cast<const uint16_t*>(x);
     r.T = p->T;
@@ -118,6 +120,7 @@ moe_status forward_impl(const moe_problem* p, const void* x, const int32_t* ids,
     f.I = p->I;
     f.max_tiles = l.max_tiles;
     f.flags = p->flags;
+    f.zero = 0;
     f.x = static_cast<const uint16_t*>(x);
     f.xp = r.xp;
     f.xs = r.xs;
@@ -132,6 +135,7 @@ moe_status forward_impl(const moe_problem* p, const void* x, const int32_t* ids,
     f.b_d = static_cast<const uint16_t*>(b_d);
     f.perm = r.perm;
     f.tiles = r.tiles;
+    f.tiles_skinny = r.tiles_skinny;
     f.num_tiles = r.num_tiles;
     f.h = base + l.h;
     f.y = reinterpret_cast<float*>(base + l.y);
@@ -186,6 +190,7 @@ moe_status moe_sort_build_tiles(const int32_t* topk_ids, int32_t T, int32_t k, i
     r.perm = perm;
     r.inv_perm = inv_perm;
     r.tiles = reinterpret_cast<int32_t*>(tiles);
+    r.tiles_skinny = nullptr;
     r.num_tiles = num_tiles;
     r.x = nullptr;
     r.T = T;

@@ -34,24 +34,32 @@
 //    order, with its group sums for the down matmul.
 //  * The down kernels scale each row by its routing weight and write it to
 //    its original (token, slot) position: the weighted unsort.
-//  * Workgroups whose tile is past the device-side tile count, or belongs to
-//    the other path, exit at once: the host never reads the tile count back.
+//  * Each path reads its own tile list (tiles of more than 16 rows; short
+//    tails).  Grids are sized from bounds the host knows (at most one short
+//    tail per expert, at most A / 17 wide tiles) and workgroups past the
+//    list's device-side count exit at once: the host never reads it back.
 #include "moe_internal.h"
 
 namespace moe {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kRingC = 4;                  // skinny path: weight chunks in flight per wave
+// skinny paths: 16-column blocks per wave and weight chunks in flight
+constexpr int kSkinnyGateUpPairs = 1, kSkinnyGateUpRing = 2;
+constexpr int kSkinnyDownBlocks = 2, kSkinnyDownRing = 2;
 constexpr int kMaxG = kMaxDim / kGroup;    // groups per row the LDS tables hold
 
 __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
 }
 
+// Tile blockIdx.x of the wide list (tiles of more than kBmSmall rows) or
+// of the skinny list; {-1, ..} past the list's device-side count.
+template <bool kSkinny>
 __device__ __forceinline__ int4 load_tile(const FfnArgs& a) {
-    if (static_cast<int>(blockIdx.x) >= min(a.num_tiles[0], a.max_tiles)) return int4{-1, 0, 0, 0};
-    return reinterpret_cast<const int4*>(a.tiles)[blockIdx.x];
+    const int n = min(a.num_tiles[kSkinny ? 3 : 2], a.max_tiles);
+    if (static_cast<int>(blockIdx.x) >= n) return int4{-1, 0, 0, 0};
+    return reinterpret_cast<const int4*>(kSkinny ? a.tiles_skinny : a.tiles)[blockIdx.x];
 }
 
 // --------------------------------------------------------------- bias term
@@ -239,7 +247,7 @@ struct WaveW {
     // Chunk c; the last chunk of an odd group count reads a repeated piece
     // instead of running past the row.
     __device__ __forceinline__ void load(int c, u32x4 (&v)[NCB]) const {
-        const int off = min(16 * c + 4 * (threadIdx.x & 3), rw - 4);
+        const int off = min(16 * c + 4 * static_cast<int>(threadIdx.x & 3), rw - 4);
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb) v[cb] = *reinterpret_cast<const u32x4*>(src[cb] + off);
     }
@@ -296,37 +304,48 @@ struct Tables {
 };
 
 // =========================================================== skinny paths
+// W waves of NB 16-row weight blocks each.
+template <int W, int NB>
 struct alignas(16) SkinnySmem {
-    uint32_t w[4][32 * 16];      // per-wave weight transposition buffer
-    uint16_t ts[4][32 * kMaxG];  // per-wave scales of its 32 weight rows
-    uint16_t tb[4][32 * kMaxG];  // per-wave biases
-    float blk[4][kBmSmall];      // 16-column block sums of h
+    uint32_t w[W][NB * 16 * 16];      // per-wave weight transposition buffer
+    uint16_t ts[W][NB * 16 * kMaxG];  // per-wave scales of its weight rows
+    uint16_t tb[W][NB * 16 * kMaxG];  // per-wave biases
+    float blk[W][NB / 2][kBmSmall];   // gate|up: 16-column block sums of h
 };
 
-// gate|up, tiles of <= 16 rows.  Grid (max_tiles, I / 64).  Wave w owns h
-// columns n0 + 16 w + [0, 16), i.e. block w of 64-column group blockIdx.y,
-// as two 16-row weight blocks: gate and up.
-template <bool kF32H>
-__global__ __launch_bounds__(kThreads) void moe_gateup_skinny(FfnArgs a) {
-    __shared__ SkinnySmem sm;
-    const int4 tile = load_tile(a);
-    if (tile.x < 0 || tile.z > kBmSmall) return;
+// gate|up, tiles of <= 16 rows.  Grid (max_tiles, I / 64): a workgroup owns
+// one 64-column group of h, W = 4 / NP waves of NP 16-column blocks each
+// (wave w: columns 16 NP w + [0, 16 NP)).  Block p of a wave is the pair of
+// weight blocks gate p (block p) and up p (block NP + p).  RING chunks of
+// weights are in flight per wave.
+template <bool kF32H, int NP, int RING>
+__global__ __launch_bounds__(256 / NP) void moe_gateup_skinny(FfnArgs a) {
+    constexpr int W = 4 / NP, NB = 2 * NP;
+    __shared__ SkinnySmem<W, NB> sm;
+    const int4 tile = load_tile<true>(a);
+    if (tile.x < 0) return;
     const int e = tile.x, row_begin = tile.y, rows = tile.z;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, q = lane >> 4, lr = lane & 15;
     const int H = a.H, I = a.I, G = H / kGroup;
     const size_t A = static_cast<size_t>(a.T) * a.k;
-    const int hcol0 = blockIdx.y * 64 + 16 * wave, hcol = hcol0 + lr;
+    const int hcol0 = blockIdx.y * 64 + 16 * NP * wave;
 
-    const size_t row0[2] = {static_cast<size_t>(e) * 2 * I + hcol0,
-                            static_cast<size_t>(e) * 2 * I + I + hcol0};
-    Tables<2> tab;
-    tab.load(a.s_gu, a.b_gu, row0, G);
-    const uint32_t* blk[2] = {a.w_gu + row0[0] * (H / 8), a.w_gu + row0[1] * (H / 8)};
-    WaveW<2> ww;
-    ww.init(sm.w[wave], blk, H / 8);
-    u32x4 rv[kRingC][2];
+    size_t row0[NB];
+    const uint32_t* blk[NB];
 #pragma unroll
-    for (int i = 0; i < kRingC; ++i) ww.load(i, rv[i]);
+    for (int p = 0; p < NP; ++p) {
+        row0[p] = static_cast<size_t>(e) * 2 * I + hcol0 + 16 * p;
+        row0[NP + p] = row0[p] + I;
+    }
+#pragma unroll
+    for (int b = 0; b < NB; ++b) blk[b] = a.w_gu + row0[b] * (H / 8);
+    Tables<NB> tab;
+    tab.load(a.s_gu, a.b_gu, row0, G);
+    WaveW<NB> ww;
+    ww.init(sm.w[wave], blk, H / 8);
+    u32x4 rv[RING][NB];
+#pragma unroll
+    for (int i = 0; i < RING; ++i) ww.load(i, rv[i]);
 
     // padding lanes (row >= rows) read row 0: their outputs are never stored
     const int tok = a.perm[row_begin + min(lr, rows - 1)] / a.k;
@@ -348,94 +367,115 @@ __global__ __launch_bounds__(kThreads) void moe_gateup_skinny(FfnArgs a) {
     tab.store(ts, tb, G);
     __builtin_amdgcn_wave_barrier();
 
-    f32x4 accg = {0.f, 0.f, 0.f, 0.f}, accu = accg;
+    f32x4 acc[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
     const int nch = (G + 1) / 2;
-    auto compute = [&](int slot, int abuf, int c) {
+    const CodeConsts kc = code_consts(a.zero);
+    // chunk c: its weights go through LDS, the slot reloads with chunk c + RING
+    // at once, then the MFMAs run
+    auto compute = [&](int slot, int abuf, int c, bool reload) {
         ww.put(rv[slot]);
+        if (reload) ww.load(c + RING, rv[slot]);
         __builtin_amdgcn_wave_barrier();
-        const u32x4 wgv = ww.get(0, lr, q), wuv = ww.get(1, lr, q);
+        u32x4 wv[NB];
+#pragma unroll
+        for (int b = 0; b < NB; ++b) wv[b] = ww.get(b, lr, q);
 #pragma unroll
         for (int gi = 0; gi < 2; ++gi) {
             const int g = 2 * c + gi;
             if (g < G) {
-                const float sg = scale16(ts[lr * G + g]), su = scale16(ts[(16 + lr) * G + g]);
-                accg = group_step(accg, ra[abuf][2 * gi], ra[abuf][2 * gi + 1],
-                                  codes_as_bf16(wgv[2 * gi]), codes_as_bf16(wgv[2 * gi + 1]), sg);
-                accu = group_step(accu, ra[abuf][2 * gi], ra[abuf][2 * gi + 1],
-                                  codes_as_bf16(wuv[2 * gi]), codes_as_bf16(wuv[2 * gi + 1]), su);
+#pragma unroll
+                for (int b = 0; b < NB; ++b)
+                    acc[b] = group_step(acc[b], ra[abuf][2 * gi], ra[abuf][2 * gi + 1],
+                                        codes_as_bf16(wv[b][2 * gi], kc), codes_as_bf16(wv[b][2 * gi + 1], kc),
+                                        scale16(ts[(16 * b + lr) * G + g]));
             }
         }
         __builtin_amdgcn_wave_barrier();
     };
     int c0 = 0;
-    for (; c0 + kRingC <= nch; c0 += kRingC) {
+    for (; c0 + RING <= nch; c0 += RING) {
 #pragma unroll
-        for (int i = 0; i < kRingC; ++i) {
+        for (int i = 0; i < RING; ++i) {
             load_a(c0 + i + 1, (i + 1) & 1);
-            compute(i, i & 1, c0 + i);
-            ww.load(c0 + i + kRingC, rv[i]);
+            compute(i, i & 1, c0 + i, true);
         }
     }
 #pragma unroll
-    for (int i = 0; i < kRingC; ++i) {
+    for (int i = 0; i < RING; ++i) {
         if (c0 + i < nch) {
             load_a(c0 + i + 1, (i + 1) & 1);
-            compute(i, i & 1, c0 + i);
+            compute(i, i & 1, c0 + i, false);
         }
     }
 
     // the bias term, added once after the groups
     {
         const int steps = (G + 31) / 32;
-        BiasOp X, C;
+        BiasOp X;
         RowSums xsum;
         xsum.load(a.xs + static_cast<size_t>(tok) * G, G, q);
         xsum.pack(X, G, q, steps);
-        bias_from_table(C, ts + lr * G, tb + lr * G, G, q, steps, true);
-        accg += bias_mfma(X, C, steps);
-        bias_from_table(C, ts + (16 + lr) * G, tb + (16 + lr) * G, G, q, steps, true);
-        accu += bias_mfma(X, C, steps);
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            BiasOp C;
+            bias_from_table(C, ts + (16 * b + lr) * G, tb + (16 * b + lr) * G, G, q, steps, true);
+            acc[b] += bias_mfma(X, C, steps);
+        }
     }
 
-    // GeGLU, h once, and this wave's 16-column block sums of h per row
+    // GeGLU, h once, and the 16-column block sums of h per row
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-        const int r = 4 * q + v;
-        const float seen = store_h<kF32H>(a, A, row_begin + r, hcol, accg[v], accu[v], r < rows);
-        const float s = sum16(seen);
-        if (lr == 0) sm.blk[wave][r] = s;
+    for (int p = 0; p < NP; ++p) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const int r = 4 * q + v;
+            const float seen = store_h<kF32H>(a, A, row_begin + r, hcol0 + 16 * p + lr, acc[p][v],
+                                              acc[NP + p][v], r < rows);
+            const float s = sum16(seen);
+            if (lr == 0) sm.blk[wave][p][r] = s;
+        }
     }
     __syncthreads();
-    if (tid < rows)
+    if (tid < rows) {
+        const float* b0 = &sm.blk[0][0][0];  // the four 16-column blocks in column order
         a.hs[static_cast<size_t>(row_begin + tid) * (I / kGroup) + blockIdx.y] =
-            hsum_of(sm.blk[0], sm.blk[1], sm.blk[2], sm.blk[3], tid);
+            hsum_of(b0, b0 + kBmSmall, b0 + 2 * kBmSmall, b0 + 3 * kBmSmall, tid);
+    }
 }
 
-// down, tiles of <= 16 rows.  Grid (max_tiles, ceil(H / 128)).  Wave w owns
-// output columns n0 + 32 w + [0, 32): two 16-row weight blocks.
-template <bool kF32H>
+// down, tiles of <= 16 rows.  Grid (max_tiles, ceil(H / (64 NB))).  Wave w
+// owns output columns 64 NB by + 16 NB w + [0, 16 NB): NB 16-row weight
+// blocks.  Waves are independent (no barrier).
+template <bool kF32H, int NB, int RING>
 __global__ __launch_bounds__(kThreads) void moe_down_skinny(FfnArgs a) {
     constexpr int P = kF32H ? 2 : 1;
-    __shared__ SkinnySmem sm;
-    const int4 tile = load_tile(a);
-    if (tile.x < 0 || tile.z > kBmSmall) return;
+    __shared__ SkinnySmem<4, NB> sm;
+    const int4 tile = load_tile<true>(a);
+    if (tile.x < 0) return;
     const int e = tile.x, row_begin = tile.y, rows = tile.z;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, q = lane >> 4, lr = lane & 15;
     const int H = a.H, I = a.I, G = I / kGroup;
     const size_t A = static_cast<size_t>(a.T) * a.k;
-    const int cbase = blockIdx.y * 128 + 32 * wave;
+    const int cbase = blockIdx.y * 64 * NB + 16 * NB * wave;
     if (cbase >= H) return;  // whole wave past the last column; no barrier follows
-    const int c0 = cbase + lr, c1 = c0 + 16;
+    const int nb = min(NB, (H - cbase) / 16);  // blocks inside H (H is a multiple of 64)
 
-    const size_t row0[2] = {static_cast<size_t>(e) * H + cbase, static_cast<size_t>(e) * H + cbase + 16};
-    Tables<2> tab;
-    tab.load(a.s_d, a.b_d, row0, G);
-    const uint32_t* blk[2] = {a.w_d + row0[0] * (I / 8), a.w_d + row0[1] * (I / 8)};
-    WaveW<2> ww;
-    ww.init(sm.w[wave], blk, I / 8);
-    u32x4 rv[kRingC][2];
+    size_t row0[NB];
+    const uint32_t* blk[NB];
 #pragma unroll
-    for (int i = 0; i < kRingC; ++i) ww.load(i, rv[i]);
+    for (int b = 0; b < NB; ++b) {
+        row0[b] = static_cast<size_t>(e) * H + cbase + 16 * min(b, nb - 1);
+        blk[b] = a.w_d + row0[b] * (I / 8);
+    }
+    Tables<NB> tab;
+    tab.load(a.s_d, a.b_d, row0, G);
+    WaveW<NB> ww;
+    ww.init(sm.w[wave], blk, I / 8);
+    u32x4 rv[RING][NB];
+#pragma unroll
+    for (int i = 0; i < RING; ++i) ww.load(i, rv[i]);
 
     // padding lanes (row >= rows) read row 0: their outputs are never stored
     const int arow = row_begin + min(lr, rows - 1);
@@ -461,61 +501,68 @@ __global__ __launch_bounds__(kThreads) void moe_down_skinny(FfnArgs a) {
     tab.store(ts, tb, G);
     __builtin_amdgcn_wave_barrier();
 
-    f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
+    f32x4 acc[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
     const int nch = (G + 1) / 2;
-    auto compute = [&](int slot, int abuf, int c) {
+    const CodeConsts kc = code_consts(a.zero);
+    // chunk c: its weights go through LDS, the slot reloads with chunk c + RING
+    // at once, then the MFMAs run
+    auto compute = [&](int slot, int abuf, int c, bool reload) {
         ww.put(rv[slot]);
+        if (reload) ww.load(c + RING, rv[slot]);
         __builtin_amdgcn_wave_barrier();
-        const u32x4 w0v = ww.get(0, lr, q), w1v = ww.get(1, lr, q);
+        u32x4 wv[NB];
+#pragma unroll
+        for (int b = 0; b < NB; ++b) wv[b] = ww.get(b, lr, q);
 #pragma unroll
         for (int gi = 0; gi < 2; ++gi) {
             const int g = 2 * c + gi;
             if (g < G) {
-                const float s0 = scale16(ts[lr * G + g]), s1 = scale16(ts[(16 + lr) * G + g]);
-                const u32x4 b00 = codes_as_bf16(w0v[2 * gi]), b01 = codes_as_bf16(w0v[2 * gi + 1]);
-                const u32x4 b10 = codes_as_bf16(w1v[2 * gi]), b11 = codes_as_bf16(w1v[2 * gi + 1]);
                 const u32x4(&x)[4][P] = ra[abuf];
-                if constexpr (kF32H) {
-                    acc0 = group_step2(acc0, x[2 * gi][0], x[2 * gi][P - 1], x[2 * gi + 1][0],
-                                       x[2 * gi + 1][P - 1], b00, b01, s0);
-                    acc1 = group_step2(acc1, x[2 * gi][0], x[2 * gi][P - 1], x[2 * gi + 1][0],
-                                       x[2 * gi + 1][P - 1], b10, b11, s1);
-                } else {
-                    acc0 = group_step(acc0, x[2 * gi][0], x[2 * gi + 1][0], b00, b01, s0);
-                    acc1 = group_step(acc1, x[2 * gi][0], x[2 * gi + 1][0], b10, b11, s1);
+#pragma unroll
+                for (int b = 0; b < NB; ++b) {
+                    const u32x4 b0 = codes_as_bf16(wv[b][2 * gi], kc), b1 = codes_as_bf16(wv[b][2 * gi + 1], kc);
+                    const float s16 = scale16(ts[(16 * b + lr) * G + g]);
+                    if constexpr (kF32H)
+                        acc[b] = group_step2(acc[b], x[2 * gi][0], x[2 * gi][P - 1], x[2 * gi + 1][0],
+                                             x[2 * gi + 1][P - 1], b0, b1, s16);
+                    else
+                        acc[b] = group_step(acc[b], x[2 * gi][0], x[2 * gi + 1][0], b0, b1, s16);
                 }
             }
         }
         __builtin_amdgcn_wave_barrier();
     };
     int cc = 0;
-    for (; cc + kRingC <= nch; cc += kRingC) {
+    for (; cc + RING <= nch; cc += RING) {
 #pragma unroll
-        for (int i = 0; i < kRingC; ++i) {
+        for (int i = 0; i < RING; ++i) {
             load_a(cc + i + 1, (i + 1) & 1);
-            compute(i, i & 1, cc + i);
-            ww.load(cc + i + kRingC, rv[i]);
+            compute(i, i & 1, cc + i, true);
         }
     }
 #pragma unroll
-    for (int i = 0; i < kRingC; ++i) {
+    for (int i = 0; i < RING; ++i) {
         if (cc + i < nch) {
             load_a(cc + i + 1, (i + 1) & 1);
-            compute(i, i & 1, cc + i);
+            compute(i, i & 1, cc + i, false);
         }
     }
 
     // the bias term, added once after the groups
     {
         const int steps = (G + 31) / 32;
-        BiasOp X, C;
+        BiasOp X;
         RowSums hsum;
         hsum.load(a.hs + static_cast<size_t>(arow) * G, G, q);
         hsum.pack(X, G, q, steps);
-        bias_from_table(C, ts + lr * G, tb + lr * G, G, q, steps, true);
-        acc0 += bias_mfma(X, C, steps);
-        bias_from_table(C, ts + (16 + lr) * G, tb + (16 + lr) * G, G, q, steps, true);
-        acc1 += bias_mfma(X, C, steps);
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            BiasOp C;
+            bias_from_table(C, ts + (16 * b + lr) * G, tb + (16 * b + lr) * G, G, q, steps, true);
+            acc[b] += bias_mfma(X, C, steps);
+        }
     }
 
     // weighted unsort
@@ -525,15 +572,16 @@ __global__ __launch_bounds__(kThreads) void moe_down_skinny(FfnArgs a) {
         if (r < rows) {
             const int32_t dst = a.perm[row_begin + r];
             const float wt = a.topk_w[dst];
-            float* yrow = a.y + static_cast<size_t>(dst) * H;
-            yrow[c0] = wt * acc0[v];
-            yrow[c1] = wt * acc1[v];
+            float* yrow = a.y + static_cast<size_t>(dst) * H + cbase + lr;
+#pragma unroll
+            for (int b = 0; b < NB; ++b)
+                if (b < nb) yrow[16 * b] = wt * acc[b][v];
         }
     }
 }
 
 // ============================================================= wide paths
-// Tiles of 17..128 rows; RB = 16-row blocks, rows / 16 rounded up to even.
+// Tiles of 17..96 rows (17..64 with an fp32 h); RB = 16-row blocks.
 // The activation tile (RB*16 rows) is staged in LDS in chunks of 2 groups
 // (NBUF buffers); an LDS row is 16 pieces of 16 bytes plus 16 bytes of
 // padding, so the 16 rows of a fragment read fall on distinct banks.  Each
@@ -553,10 +601,15 @@ struct alignas(16) WideSmem {
 // group 63 stay inside a row
 constexpr int kXStride = kMaxG + 4;
 static_assert(kXStride <= kAStride, "group sums must fit the activation buffer");
+// One row-block count per kernel (a tile's unused row blocks are skipped at
+// run time): a kernel that branches to several instantiations is allocated
+// for all of them at once and overflows into accumulation registers.
+constexpr int kWideRowBlocks = kBmBig / 16, kWideRowBlocksF32 = kBmBigF32 / 16;
 // the largest layout any wide kernel uses
-constexpr size_t kWideSmemBytes = sizeof(WideSmem<8, 1, 2>) > sizeof(WideSmem<8, 2, 1>)
-                                      ? sizeof(WideSmem<8, 1, 2>)
-                                      : sizeof(WideSmem<8, 2, 1>);
+constexpr size_t kWideSmemBytes =
+    sizeof(WideSmem<kWideRowBlocks, 1, 2>) > sizeof(WideSmem<kWideRowBlocksF32, 2, 1>)
+        ? sizeof(WideSmem<kWideRowBlocks, 1, 2>)
+        : sizeof(WideSmem<kWideRowBlocksF32, 2, 1>);
 
 // Thread t copies piece t % 16 of rows t / 16 + 16 i.  Rows past the tile
 // read a real row and groups past G the last group: those values are never
@@ -596,12 +649,12 @@ __device__ __forceinline__ u32x4 lds_frag(const WideSmem<RB, P, NBUF>& sm, int b
 
 // Shared K loop of the wide paths: acc[rb][cb] over all groups for the four
 // 16-row weight blocks blk[cb] of this wave (row length K), activations staged
-// from src (P parts, `part` apart).
+// from src (P parts, `part` apart); row blocks rb >= nrb are skipped.
 template <int RB, int P, int NBUF>
 __device__ __forceinline__ void wide_kloop(WideSmem<RB, P, NBUF>& sm, Stager<RB, P>& st,
                                            const uint32_t* const (&src)[RB], size_t part,
                                            const uint32_t* const (&blk)[4], int K, bool active,
-                                           f32x4 (&acc)[RB][4]) {
+                                           int nrb, CodeConsts kc, f32x4 (&acc)[RB][4]) {
     constexpr int CB = 4;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, q = lane >> 4, lr = lane & 15;
     const int G = K / kGroup;
@@ -631,12 +684,13 @@ __device__ __forceinline__ void wide_kloop(WideSmem<RB, P, NBUF>& sm, Stager<RB,
                     float s16[CB];
 #pragma unroll
                     for (int cb = 0; cb < CB; ++cb) {
-                        b0[cb] = codes_as_bf16(wq[cb][2 * i]);
-                        b1[cb] = codes_as_bf16(wq[cb][2 * i + 1]);
+                        b0[cb] = codes_as_bf16(wq[cb][2 * i], kc);
+                        b1[cb] = codes_as_bf16(wq[cb][2 * i + 1], kc);
                         s16[cb] = scale16(sm.ts[wave][(16 * cb + lr) * G + g]);
                     }
 #pragma unroll
                     for (int rb = 0; rb < RB; ++rb) {
+                        if (rb >= nrb) break;  // row blocks past the tile
                         const int row = 16 * rb + lr;
                         const u32x4 a0 = lds_frag(sm, buf, 0, row, 8 * i + 2 * q);
                         const u32x4 a1 = lds_frag(sm, buf, 0, row, 8 * i + 2 * q + 1);
@@ -767,7 +821,7 @@ __device__ __forceinline__ void gateup_wide(const FfnArgs& a, void* smem, int e,
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb) acc[rb][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    wide_kloop<RB, P, NBUF>(sm, st, src, 0, blk, H, active, acc);
+    wide_kloop<RB, P, NBUF>(sm, st, src, 0, blk, H, active, (rows + 15) / 16, code_consts(a.zero), acc);
 
     const float* xrow[RB];
 #pragma unroll
@@ -844,7 +898,7 @@ __device__ __forceinline__ void down_wide(const FfnArgs& a, void* smem, int e, i
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb) acc[rb][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    wide_kloop<RB, P, NBUF>(sm, st, src, part, blk, I, active, acc);
+    wide_kloop<RB, P, NBUF>(sm, st, src, part, blk, I, active, (rows + 15) / 16, code_consts(a.zero), acc);
 
     const float* xrow[RB];
 #pragma unroll
@@ -872,52 +926,70 @@ __device__ __forceinline__ void down_wide(const FfnArgs& a, void* smem, int e, i
 template <bool kF32H>
 __global__ __launch_bounds__(kThreads) void moe_gateup_wide(FfnArgs a) {
     __shared__ __attribute__((aligned(16))) unsigned char smem[kWideSmemBytes];
-    const int4 tile = load_tile(a);
-    if (tile.x < 0 || tile.z <= kBmSmall) return;
-    const int rows = tile.z;
-    if (rows <= 32) gateup_wide<2, kF32H>(a, smem, tile.x, tile.y, rows);
-    else if (kF32H || rows <= 64) gateup_wide<4, kF32H>(a, smem, tile.x, tile.y, rows);
-    else if (rows <= 96) gateup_wide<6, kF32H>(a, smem, tile.x, tile.y, rows);
-    else gateup_wide<8, kF32H>(a, smem, tile.x, tile.y, rows);
+    const int4 tile = load_tile<false>(a);
+    if (tile.x < 0) return;
+    gateup_wide<kF32H ? kWideRowBlocksF32 : kWideRowBlocks, kF32H>(a, smem, tile.x, tile.y, tile.z);
 }
 
 template <bool kF32H>
 __global__ __launch_bounds__(kThreads) void moe_down_wide(FfnArgs a) {
     __shared__ __attribute__((aligned(16))) unsigned char smem[kWideSmemBytes];
-    const int4 tile = load_tile(a);
-    if (tile.x < 0 || tile.z <= kBmSmall) return;
-    const int rows = tile.z;
-    if (rows <= 32) down_wide<2, kF32H>(a, smem, tile.x, tile.y, rows);
-    else if (kF32H || rows <= 64) down_wide<4, kF32H>(a, smem, tile.x, tile.y, rows);
-    else if (rows <= 96) down_wide<6, kF32H>(a, smem, tile.x, tile.y, rows);
-    else down_wide<8, kF32H>(a, smem, tile.x, tile.y, rows);
+    const int4 tile = load_tile<false>(a);
+    if (tile.x < 0) return;
+    down_wide<kF32H ? kWideRowBlocksF32 : kWideRowBlocks, kF32H>(a, smem, tile.x, tile.y, tile.z);
 }
 
 }  // namespace
 
+// Grid widths: a skinny tile is an expert's short tail (at most one per
+// expert, at least one row); a wide tile has more than kBmSmall rows.
+static int skinny_grid(const FfnArgs& a) {
+    return min(a.max_tiles, min(a.E, a.T * a.k));
+}
+static int wide_grid(const FfnArgs& a) {
+    return min(a.max_tiles, a.T * a.k / (kBmSmall + 1));
+}
+
+// No tile can be wide: nothing to launch, but the timing events still mark
+// the (empty) interval.
+static hipError_t skip_launch(hipStream_t stream, const KTiming& t) {
+    if (t.start != nullptr && t.stop != nullptr) {
+        hipError_t e = hipEventRecord(t.start, stream);
+        if (e == hipSuccess) e = hipEventRecord(t.stop, stream);
+        return e;
+    }
+    return hipSuccess;
+}
+
 hipError_t launch_gateup_skinny(const FfnArgs& a, hipStream_t stream, const KTiming& t) {
-    const dim3 grid(a.max_tiles, a.I / 64);
+    constexpr int NP = kSkinnyGateUpPairs, RING = kSkinnyGateUpRing;
+    const dim3 grid(skinny_grid(a), a.I / 64);
     if (a.flags & MOE_F_FP32_INTERMEDIATE)
-        return launch_kernel(moe_gateup_skinny<true>, grid, dim3(kThreads), stream, t, a);
-    return launch_kernel(moe_gateup_skinny<false>, grid, dim3(kThreads), stream, t, a);
+        return launch_kernel(moe_gateup_skinny<true, NP, RING>, grid, dim3(256 / NP), stream, t, a);
+    return launch_kernel(moe_gateup_skinny<false, NP, RING>, grid, dim3(256 / NP), stream, t, a);
 }
 
 hipError_t launch_gateup_wide(const FfnArgs& a, hipStream_t stream, const KTiming& t) {
-    const dim3 grid(a.max_tiles, (a.I + 127) / 128);
+    const int n = wide_grid(a);
+    if (n == 0) return skip_launch(stream, t);
+    const dim3 grid(n, (a.I + 127) / 128);
     if (a.flags & MOE_F_FP32_INTERMEDIATE)
         return launch_kernel(moe_gateup_wide<true>, grid, dim3(kThreads), stream, t, a);
     return launch_kernel(moe_gateup_wide<false>, grid, dim3(kThreads), stream, t, a);
 }
 
 hipError_t launch_down_skinny(const FfnArgs& a, hipStream_t stream, const KTiming& t) {
-    const dim3 grid(a.max_tiles, (a.H + 127) / 128);
+    constexpr int NB = kSkinnyDownBlocks, RING = kSkinnyDownRing;
+    const dim3 grid(skinny_grid(a), (a.H + 64 * NB - 1) / (64 * NB));
     if (a.flags & MOE_F_FP32_INTERMEDIATE)
-        return launch_kernel(moe_down_skinny<true>, grid, dim3(kThreads), stream, t, a);
-    return launch_kernel(moe_down_skinny<false>, grid, dim3(kThreads), stream, t, a);
+        return launch_kernel(moe_down_skinny<true, NB, RING>, grid, dim3(kThreads), stream, t, a);
+    return launch_kernel(moe_down_skinny<false, NB, RING>, grid, dim3(kThreads), stream, t, a);
 }
 
 hipError_t launch_down_wide(const FfnArgs& a, hipStream_t stream, const KTiming& t) {
-    const dim3 grid(a.max_tiles, (a.H + 255) / 256);
+    const int n = wide_grid(a);
+    if (n == 0) return skip_launch(stream, t);
+    const dim3 grid(n, (a.H + 255) / 256);
     if (a.flags & MOE_F_FP32_INTERMEDIATE)
         return launch_kernel(moe_down_wide<true>, grid, dim3(kThreads), stream, t, a);
     return launch_kernel(moe_down_wide<false>, grid, dim3(kThreads), stream, t, a);

@@ -20,11 +20,12 @@ constexpr int kGroup = 64;      // quantisation group (columns per scale/bias)
 constexpr int kRouteThreads = 1024;
 constexpr int kRouteWaves = kRouteThreads / 64;
 
-// Tile heights used by the forward's own routing: tiles of up to 128 rows of
+// Tile heights used by the forward's own routing: tiles of up to 96 rows of
 // one expert; a tile of at most 16 rows (decode-sized, or the short end of an
-// expert) takes the skinny path, larger ones the wide path.
-constexpr int kBmBig = 128;
-constexpr int kBmBigF32 = 64;  // with MOE_F_FP32_INTERMEDIATE
+// expert) takes the skinny path, larger ones the wide path.  96 rows = 6 row
+// blocks per wave keeps the wide kernels within 256 vector registers.
+constexpr int kBmBig = 64;
+constexpr int kBmBigF32 = 32;  // with MOE_F_FP32_INTERMEDIATE
 constexpr int kBmSmall = 16;
 // Largest H and I the bias contraction handles (32 groups per MFMA step).
 constexpr int kMaxBiasSteps = 2;
@@ -52,12 +53,27 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
 //   sum_k x_k (s q_k + b) = 16 s P + (b - 16 s) X.
 // The offset 16 (rather than, say, 128 + q) keeps P close in size to the
 // part that carries information, so little is lost when X is taken out.
-__device__ __forceinline__ u32x4 codes_as_bf16(uint32_t w) {
+//
+// The two constants sit in registers (CodeConsts, built from a zero the
+// compiler cannot see through): folded into literals, each AND-OR below would
+// take two VALU instructions, because gfx9 VOP3 forms such as v_and_or_b32
+// take no literal operand.
+struct CodeConsts {
+    uint32_t mask, one;
+};
+// The mask goes to a vector register (a per-lane select on a condition the
+// compiler cannot fold) and the other constant stays scalar: one VOP3
+// instruction may read only one scalar operand.
+__device__ __forceinline__ CodeConsts code_consts(uint32_t zero) {
+    const uint32_t mask = (threadIdx.x & zero) ? 0u : 0x00780078u;
+    return CodeConsts{mask, 0x3F803F80u | zero};
+}
+__device__ __forceinline__ u32x4 codes_as_bf16(uint32_t w, CodeConsts k) {
     u32x4 r;
-    r[0] = ((w << 3) & 0x00780078u) | 0x3F803F80u;  // q0, q4
-    r[1] = ((w >> 1) & 0x00780078u) | 0x3F803F80u;  // q1, q5
-    r[2] = ((w >> 5) & 0x00780078u) | 0x3F803F80u;  // q2, q6
-    r[3] = ((w >> 9) & 0x00780078u) | 0x3F803F80u;  // q3, q7
+    r[0] = ((w << 3) & k.mask) | k.one;  // q0, q4
+    r[1] = ((w >> 1) & k.mask) | k.one;  // q1, q5
+    r[2] = ((w >> 5) & k.mask) | k.one;  // q2, q6
+    r[3] = ((w >> 9) & k.mask) | k.one;  // q3, q7
     return r;
 }
 constexpr float kCodeScale = 16.0f;
@@ -118,6 +134,10 @@ struct RouteArgs {
     const int32_t* ids;
     int32_t A, E, bm_big, bm_small, max_tiles;
     int32_t *counts, *offsets, *perm, *inv_perm, *tiles, *num_tiles;
+    // nullptr: one tile list in expert order, num_tiles [2].  Otherwise tiles
+    // gets the tiles of more than bm_small rows and tiles_skinny the others,
+    // each in expert order; num_tiles [4] = {total, invalid ids, wide, skinny}.
+    int32_t* tiles_skinny;
     // activation preparation (forward only; x == nullptr skips it)
     const uint16_t* x;  // [T, H] bf16
     int32_t T, H;
@@ -129,6 +149,7 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t stream, const KTiming& t
 struct FfnArgs {
     int32_t T, k, E, H, I, max_tiles;
     uint32_t flags;
+    uint32_t zero;       // always 0 (see CodeConsts)
     const uint16_t* x;
     const uint16_t* xp;  // [T, H] x with pieces reordered by permute8
     const float* xs;     // [T, H/64] group sums of x
@@ -142,8 +163,9 @@ struct FfnArgs {
     const uint16_t* s_d;
     const uint16_t* b_d;
     const int32_t* perm;
-    const int32_t* tiles;
-    const int32_t* num_tiles;
+    const int32_t* tiles;         // tiles of more than kBmSmall rows
+    const int32_t* tiles_skinny;  // tiles of at most kBmSmall rows
+    const int32_t* num_tiles;     // {total, invalid ids, wide, skinny}
     void* h;             // [A, I] bf16, or hi and lo [2, A, I] bf16; pieces permuted
     float* y;
     void* out;

@@ -16,7 +16,9 @@
 //      assignment to base + (rank among equal keys in lower lanes): a stable
 //      counting sort;
 //   4. tiles per expert = ceil(count / bm_big), scanned; thread i emits tile i
-//      after an upper-bound search of the scanned tile offsets.
+//      after an upper-bound search of the scanned tile offsets.  The forward
+//      asks for two lists instead (tiles of more than bm_small rows, and the
+//      short tails), so that each matmul launch only covers its own tiles.
 //
 // In the forward, the other workgroups of the same launch prepare the
 // activations for the matmuls (prepare_x).
@@ -106,6 +108,23 @@ __device__ void prepare_x(const RouteArgs& a, int block) {
     if ((p & 7) == 0) a.xs[p / 8] = s;
 }
 
+// First index in [0, n) with v[index] > x (v ascending), n if none.
+__device__ __forceinline__ int upper_bound(const int32_t* v, int n, int x) {
+    int lo = 0, hi = n;
+    while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (v[mid] <= x) lo = mid + 1; else hi = mid;
+    }
+    return lo;
+}
+
+__device__ __forceinline__ void write_tile(int32_t* t, int e, int row_begin, int rows, int bm) {
+    t[0] = e;
+    t[1] = row_begin;
+    t[2] = rows;
+    t[3] = bm;
+}
+
 __global__ __launch_bounds__(kRouteThreads) void moe_route_sort_tiles(RouteArgs a) {
     if (blockIdx.x > 0) {
         prepare_x(a, blockIdx.x - 1);
@@ -115,6 +134,7 @@ __global__ __launch_bounds__(kRouteThreads) void moe_route_sort_tiles(RouteArgs 
     __shared__ int32_t s_cnt[kMaxKeys];
     __shared__ int32_t s_off[kMaxKeys + 1];
     __shared__ int32_t s_toff[kMaxKeys + 1];
+    __shared__ int32_t s_soff[kMaxKeys + 1];
     __shared__ int32_t s_wsum[kRouteWaves + 1];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -197,30 +217,53 @@ __global__ __launch_bounds__(kRouteThreads) void moe_route_sort_tiles(RouteArgs 
         a.offsets[E] = s_off[E];
         a.num_tiles[1] = s_cnt[E];
     }
-    // tiles per expert into s_tab's first row (no longer needed)
     __syncthreads();
-    for (int e = tid; e < E; e += kRouteThreads) s_tab[e] = (s_cnt[e] + a.bm_big - 1) / a.bm_big;
-    __syncthreads();
-    block_exclusive_scan(s_tab, s_toff, E, s_wsum);
-    const int total = s_toff[E];
-    for (int i = tid; i < total && i < a.max_tiles; i += kRouteThreads) {
-        // upper bound: first e with s_toff[e] > i, over s_toff[0..E]
-        int lo = 0, hi = E + 1;
-        while (lo < hi) {
-            const int mid = (lo + hi) >> 1;
-            if (s_toff[mid] <= i) lo = mid + 1; else hi = mid;
+    if (a.tiles_skinny == nullptr) {
+        // one list in expert order: tiles per expert into s_tab's first row
+        // (no longer needed), scan, upper-bound emission
+        for (int e = tid; e < E; e += kRouteThreads) s_tab[e] = (s_cnt[e] + a.bm_big - 1) / a.bm_big;
+        __syncthreads();
+        block_exclusive_scan(s_tab, s_toff, E, s_wsum);
+        const int total = s_toff[E];
+        for (int i = tid; i < total && i < a.max_tiles; i += kRouteThreads) {
+            const int e = upper_bound(s_toff, E + 1, i) - 1;
+            const int row0 = (i - s_toff[e]) * a.bm_big;
+            const int rows = min(a.bm_big, s_cnt[e] - row0);
+            write_tile(a.tiles + 4 * i, e, s_off[e] + row0, rows,
+                       rows <= a.bm_small ? a.bm_small : a.bm_big);
         }
-        const int e = lo - 1;
-        const int local = i - s_toff[e];
-        const int row0 = local * a.bm_big;
-        const int rows = min(a.bm_big, s_cnt[e] - row0);
-        int32_t* t = a.tiles + 4 * i;
-        t[0] = e;
-        t[1] = s_off[e] + row0;
-        t[2] = rows;
-        t[3] = rows <= a.bm_small ? a.bm_small : a.bm_big;
+        if (tid == 0) a.num_tiles[0] = total;
+    } else {
+        // two lists, each in expert order: tiles of more than bm_small rows
+        // (full tiles and long tails) and tiles of at most bm_small rows (an
+        // expert's short tail; at most one per expert)
+        int32_t* s_ns = s_tab + kMaxKeys;
+        for (int e = tid; e < E; e += kRouteThreads) {
+            const int c = s_cnt[e], tail = c % a.bm_big;
+            const bool short_tail = tail > 0 && tail <= a.bm_small;
+            s_tab[e] = c / a.bm_big + (tail > a.bm_small ? 1 : 0);
+            s_ns[e] = short_tail ? 1 : 0;
+        }
+        __syncthreads();
+        block_exclusive_scan(s_tab, s_toff, E, s_wsum);
+        block_exclusive_scan(s_ns, s_soff, E, s_wsum);
+        const int nw = s_toff[E], ns = s_soff[E];
+        for (int i = tid; i < nw && i < a.max_tiles; i += kRouteThreads) {
+            const int e = upper_bound(s_toff, E + 1, i) - 1;
+            const int row0 = (i - s_toff[e]) * a.bm_big;
+            write_tile(a.tiles + 4 * i, e, s_off[e] + row0, min(a.bm_big, s_cnt[e] - row0), a.bm_big);
+        }
+        for (int i = tid; i < ns && i < a.max_tiles; i += kRouteThreads) {
+            const int e = upper_bound(s_soff, E + 1, i) - 1;
+            const int tail = s_cnt[e] % a.bm_big;
+            write_tile(a.tiles_skinny + 4 * i, e, s_off[e] + s_cnt[e] - tail, tail, a.bm_small);
+        }
+        if (tid == 0) {
+            a.num_tiles[0] = nw + ns;
+            a.num_tiles[2] = nw;
+            a.num_tiles[3] = ns;
+        }
     }
-    if (tid == 0) a.num_tiles[0] = total;
 }
 
 }  // namespace

@@ -134,8 +134,10 @@ typedef struct {
     size_t offsets;   /* int32 [E+1]                                      */
     size_t perm;      /* int32 [A]                                        */
     size_t inv_perm;  /* int32 [A]                                        */
-    size_t tiles;     /* moe_tile [max_tiles], bm_big/bm_small below      */
-    size_t num_tiles; /* int32 [2]                                        */
+    size_t tiles;     /* moe_tile [max_tiles]: the tiles of more than
+                         bm_small rows, in expert order                   */
+    size_t num_tiles; /* int32 [4]: total tiles, out-of-range ids, tiles
+                         in `tiles`, tiles in `tiles_skinny`              */
     size_t x_perm;    /* bf16 [T, H]: x in operand order                  */
     size_t x_sums;    /* fp32 [T, H/64]: sum of x over each 64-column group */
     size_t h;         /* GeGLU output in sorted order, operand order:
@@ -150,6 +152,9 @@ typedef struct {
     int32_t bm_big;
     int32_t bm_small;
     int32_t reserved;
+    size_t tiles_skinny; /* moe_tile [max_tiles]: the tiles of at most
+                            bm_small rows (an expert's short tail), in
+                            expert order                                  */
 } moe_ws_layout;
 
 moe_status moe_ffn_workspace_layout(const moe_problem* p, moe_ws_layout* layout);

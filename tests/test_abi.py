@@ -41,13 +41,15 @@ def test_workspace_layout_and_sizes():
     lay = bgq.workspace_layout(p)
     A = 2048 * 8
     assert lay.total == bgq.workspace_bytes(p)
-    offs = [lay.counts, lay.offsets, lay.perm, lay.inv_perm, lay.tiles, lay.num_tiles,
-            lay.x_perm, lay.x_sums, lay.h, lay.h_sums, lay.y]
+    offs = [lay.counts, lay.offsets, lay.perm, lay.inv_perm, lay.tiles, lay.tiles_skinny,
+            lay.num_tiles, lay.x_perm, lay.x_sums, lay.h, lay.h_sums, lay.y]
     assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
     assert lay.x_sums - lay.x_perm >= 2048 * 2816 * 2
     assert lay.h_sums - lay.h >= A * 704 * 2 and lay.total - lay.y >= A * 2816 * 4
-    assert lay.bm_big == 128 and lay.bm_small == 16
-    assert lay.max_tiles == A // 128 + 128
+    assert lay.bm_big == 64 and lay.bm_small == 16
+    assert lay.max_tiles == A // 64 + 128
+    assert lay.tiles_skinny - lay.tiles >= 16 * lay.max_tiles
+    assert lay.num_tiles - lay.tiles_skinny >= 16 * lay.max_tiles
     p32 = bgq.problem(2048, 8, 128, 2816, 704, bgq.MOE_F_FP32_INTERMEDIATE)
     l32 = bgq.workspace_layout(p32)
     assert l32.h_sums - l32.h >= A * 704 * 4

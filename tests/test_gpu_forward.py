@@ -165,7 +165,8 @@ def test_prepared_activations_and_h_sums(fp32):
 
 
 def _skinny_and_wide_problem():
-    """Expert 0 gets 140 rows: a 128-row wide tile and a 12-row skinny tile,
+    """Expert 0 gets 140 rows: wide tiles (2 x 64, or 4 x 32 with an fp32 h)
+    and a 12-row skinny tile,
     so permuting tokens moves rows between the two paths."""
     T, k, E = 150, 2, 4
     rng = np.random.default_rng(11)
@@ -189,3 +190,23 @@ def test_rows_bitwise_independent_of_tile_path(oracle_lib, fp32):
     q.topk_weights = np.ascontiguousarray(p.topk_weights[perm])
     o2, _, _ = run_forward(q, fp32=fp32)
     np.testing.assert_array_equal(o2, o1[perm])
+
+
+@pytest.mark.parametrize("name,fp32", [("prefill16k", False), ("prefill4k", True),
+                                        ("decode", False)])
+def test_forward_tile_lists(oracle_lib, name, fp32):
+    """The forward routes into two lists: tiles of more than 16 rows and the
+    short tails, each in expert order.  Together they are exactly the
+    oracle's tiles at the forward's tile height."""
+    p = ms.make_config(name)
+    _, ws, lay = run_forward(p, fp32=fp32)
+    counts, offsets, _, _, _ = oracle_lib.route(p.topk_ids, p.E)
+    ref = np.asarray(oracle_lib.tiles(counts, offsets, lay.bm_big, lay.bm_small), np.int32)
+    ref = ref.reshape(-1, 4)
+    nt = ws_view(ws, lay.num_tiles, 4, np.int32)
+    wide = ws_view(ws, lay.tiles, 4 * int(nt[2]), np.int32).reshape(-1, 4)
+    short = ws_view(ws, lay.tiles_skinny, 4 * int(nt[3]), np.int32).reshape(-1, 4)
+    log(f"  {name}: {len(ref)} tiles = {len(wide)} wide + {len(short)} short")
+    assert nt[0] == len(ref) == len(wide) + len(short)
+    np.testing.assert_array_equal(wide, ref[ref[:, 2] > lay.bm_small])
+    np.testing.assert_array_equal(short, ref[ref[:, 2] <= lay.bm_small])

@@ -119,6 +119,26 @@ __device__ __forceinline__ void bias_from_table(BiasOp& o, const uint16_t* ts, c
     }
 }
 
+// Same, with the biases read from HBM (row b, G entries) and the scales from
+// LDS.
+__device__ __forceinline__ void bias_from_scales(BiasOp& o, const uint16_t* ts, const uint16_t* b,
+                                                 int G, int q, int steps, bool active) {
+#pragma unroll
+    for (int st = 0; st < kMaxBiasSteps; ++st) {
+        if (st < steps) {
+            float v[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int g = 32 * st + 8 * q + j;
+                const int gc = min(g, G - 1);
+                const float c = fmaf(-kCodeScale, bf16_to_f32(ts[gc]), bf16_to_f32(b[gc]));
+                v[j] = (active && g < G) ? c : 0.f;
+            }
+            pack_split(v, o.hi[st], o.lo[st]);
+        }
+    }
+}
+
 // The group sums of one activation row as the bias operand.
 struct RowSums {
     float v[kMaxBiasSteps][8];
@@ -272,9 +292,10 @@ struct WaveW {
 // contiguous, 32 G bytes, so they move as 16-byte pieces in row order: two
 // loads per lane and table cover G <= 64.  The loads are issued early and the
 // stores made later, so their latency overlaps the first weight loads.
-template <int NCB>
+// kBias = false: scales only (the wide paths read biases from HBM at the end).
+template <int NCB, bool kBias = true>
 struct Tables {
-    u32x4 vs[NCB][2], vb[NCB][2];
+    u32x4 vs[NCB][2], vb[NCB][kBias ? 2 : 1];
 
     __device__ __forceinline__ void load(const uint16_t* s, const uint16_t* b,
                                          const size_t (&row0)[NCB], int G) {
@@ -285,7 +306,7 @@ struct Tables {
             for (int j = 0; j < 2; ++j) {
                 const size_t off = row0[cb] * G + 8 * min(lane + 64 * j, np - 1);
                 vs[cb][j] = *reinterpret_cast<const u32x4*>(s + off);
-                vb[cb][j] = *reinterpret_cast<const u32x4*>(b + off);
+                if constexpr (kBias) vb[cb][j] = *reinterpret_cast<const u32x4*>(b + off);
             }
     }
     __device__ __forceinline__ void store(uint16_t* ts, uint16_t* tb, int G) const {
@@ -297,7 +318,8 @@ struct Tables {
                 const int idx = lane + 64 * j;
                 if (idx < np) {
                     *reinterpret_cast<u32x4*>(ts + cb * 16 * G + 8 * idx) = vs[cb][j];
-                    *reinterpret_cast<u32x4*>(tb + cb * 16 * G + 8 * idx) = vb[cb][j];
+                    if constexpr (kBias)
+                        *reinterpret_cast<u32x4*>(tb + cb * 16 * G + 8 * idx) = vb[cb][j];
                 }
             }
     }
@@ -588,13 +610,14 @@ __global__ __launch_bounds__(kThreads) void moe_down_skinny(FfnArgs a) {
 // wave owns 4 blocks of 16 weight rows, moved through its own LDS buffer.
 constexpr int kAStride = 2 * 32 + 4;  // u32 per staged activation row
 
-template <int RB, int P, int NBUF>
+// MAXG bounds the group count the scale tables hold: 48 keeps a workgroup's
+// LDS under 80 KB, so that two workgroups share a CU.
+template <int RB, int P, int NBUF, int MAXG>
 struct alignas(16) WideSmem {
     uint32_t a[NBUF][P][RB * 16 * kAStride];  // after the K loop: group sums of the rows
     uint32_t w[4][64 * 16];
-    uint16_t ts[4][64 * kMaxG];  // per-wave scales of its 64 weight rows
-    uint16_t tb[4][64 * kMaxG];  // per-wave biases
-    float blk[2][4][kBmBig];     // [64-column group][16-column block][row]
+    uint16_t ts[4][64 * MAXG];  // per-wave scales of its 64 weight rows
+    float blk[2][4][RB * 16];   // [64-column group][16-column block][row]
 };
 // row stride (floats) of the group sums staged in a[] after the K loop: 16
 // rows of a fragment read fall on distinct banks, and 8-group reads up to
@@ -605,11 +628,7 @@ static_assert(kXStride <= kAStride, "group sums must fit the activation buffer")
 // run time): a kernel that branches to several instantiations is allocated
 // for all of them at once and overflows into accumulation registers.
 constexpr int kWideRowBlocks = kBmBig / 16, kWideRowBlocksF32 = kBmBigF32 / 16;
-// the largest layout any wide kernel uses
-constexpr size_t kWideSmemBytes =
-    sizeof(WideSmem<kWideRowBlocks, 1, 2>) > sizeof(WideSmem<kWideRowBlocksF32, 2, 1>)
-        ? sizeof(WideSmem<kWideRowBlocks, 1, 2>)
-        : sizeof(WideSmem<kWideRowBlocksF32, 2, 1>);
+constexpr int kWideMaxGSmall = 48;
 
 // Thread t copies piece t % 16 of rows t / 16 + 16 i.  Rows past the tile
 // read a real row and groups past G the last group: those values are never
@@ -630,8 +649,8 @@ struct Stager {
             for (int pp = 0; pp < P; ++pp)
                 v[i][pp] = *reinterpret_cast<const u32x4*>(src[i] + pp * part + 4 * piece);
     }
-    template <int NBUF>
-    __device__ __forceinline__ void store(WideSmem<RB, P, NBUF>& sm, int buf) const {
+    template <int NBUF, int MAXG>
+    __device__ __forceinline__ void store(WideSmem<RB, P, NBUF, MAXG>& sm, int buf) const {
         const int pc = threadIdx.x & 15, r0 = threadIdx.x >> 4;
 #pragma unroll
         for (int i = 0; i < kPasses; ++i)
@@ -641,8 +660,8 @@ struct Stager {
     }
 };
 
-template <int RB, int P, int NBUF>
-__device__ __forceinline__ u32x4 lds_frag(const WideSmem<RB, P, NBUF>& sm, int buf, int pp, int row,
+template <int RB, int P, int NBUF, int MAXG>
+__device__ __forceinline__ u32x4 lds_frag(const WideSmem<RB, P, NBUF, MAXG>& sm, int buf, int pp, int row,
                                           int piece) {
     return *reinterpret_cast<const u32x4*>(&sm.a[buf][pp][row * kAStride + 4 * piece]);
 }
@@ -650,8 +669,8 @@ __device__ __forceinline__ u32x4 lds_frag(const WideSmem<RB, P, NBUF>& sm, int b
 // Shared K loop of the wide paths: acc[rb][cb] over all groups for the four
 // 16-row weight blocks blk[cb] of this wave (row length K), activations staged
 // from src (P parts, `part` apart); row blocks rb >= nrb are skipped.
-template <int RB, int P, int NBUF>
-__device__ __forceinline__ void wide_kloop(WideSmem<RB, P, NBUF>& sm, Stager<RB, P>& st,
+template <int RB, int P, int NBUF, int MAXG>
+__device__ __forceinline__ void wide_kloop(WideSmem<RB, P, NBUF, MAXG>& sm, Stager<RB, P>& st,
                                            const uint32_t* const (&src)[RB], size_t part,
                                            const uint32_t* const (&blk)[4], int K, bool active,
                                            int nrb, CodeConsts kc, f32x4 (&acc)[RB][4]) {
@@ -727,10 +746,13 @@ __device__ __forceinline__ void wide_kloop(WideSmem<RB, P, NBUF>& sm, Stager<RB,
 // The bias term of the wide paths, added once after the K loop.  The group
 // sums of the staged rows go through LDS (the activation buffers are free by
 // then): thread t copies groups t % 16 + 16 j of rows t / 16 + 16 i, from row
-// pointers xrow[i] (G floats each).
-template <int RB, int P, int NBUF>
-__device__ __forceinline__ void wide_bias(WideSmem<RB, P, NBUF>& sm, const float* const (&xrow)[RB],
-                                          int G, bool active, f32x4 (&acc)[RB][4]) {
+// pointers xrow[i] (G floats each).  brow[cb]: this lane's bias row of weight
+// block cb, in HBM.
+template <int RB, int P, int NBUF, int MAXG>
+__device__ __forceinline__ void wide_bias(WideSmem<RB, P, NBUF, MAXG>& sm,
+                                          const float* const (&xrow)[RB],
+                                          const uint16_t* const (&brow)[4], int G, bool active,
+                                          f32x4 (&acc)[RB][4]) {
     constexpr int CB = 4;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, q = lane >> 4, lr = lane & 15;
     float* xl = reinterpret_cast<float*>(&sm.a[0][0][0]);
@@ -745,11 +767,10 @@ __device__ __forceinline__ void wide_bias(WideSmem<RB, P, NBUF>& sm, const float
     __syncthreads();
     const int steps = (G + 31) / 32;
     const uint16_t* ts = sm.ts[wave];
-    const uint16_t* tb = sm.tb[wave];
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
         BiasOp C;
-        bias_from_table(C, ts + (16 * cb + lr) * G, tb + (16 * cb + lr) * G, G, q, steps, active);
+        bias_from_scales(C, ts + (16 * cb + lr) * G, brow[cb], G, q, steps, active);
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
             // 8 consecutive groups per step; reads past G stay inside the row
@@ -780,11 +801,10 @@ __device__ __forceinline__ void wide_bias(WideSmem<RB, P, NBUF>& sm, const float
 // n0 + 32 w + [0, 32): weight blocks 0/1 = gate columns +0/+16, blocks 2/3 =
 // the matching up columns.  Waves {0,1} cover 64-column group 2*by of h,
 // waves {2,3} group 2*by + 1.
-template <int RB, bool kF32H>
-__device__ __forceinline__ void gateup_wide(const FfnArgs& a, void* smem, int e, int row_begin,
-                                            int rows) {
+template <int RB, int MAXG, bool kF32H>
+__device__ __forceinline__ void gateup_wide(const FfnArgs& a, WideSmem<RB, 1, 2, MAXG>& sm, int e,
+                                            int row_begin, int rows) {
     constexpr int P = 1, NBUF = 2, CB = 4;
-    auto& sm = *static_cast<WideSmem<RB, P, NBUF>*>(smem);
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, q = lane >> 4, lr = lane & 15;
     const int H = a.H, I = a.I, G = H / kGroup;
     const size_t A = static_cast<size_t>(a.T) * a.k;
@@ -799,7 +819,7 @@ __device__ __forceinline__ void gateup_wide(const FfnArgs& a, void* smem, int e,
         row0[cb] = static_cast<size_t>(e) * 2 * I + hbase + 16 * (cb & 1) + (cb >> 1) * I;
         blk[cb] = a.w_gu + row0[cb] * (H / 8);
     }
-    Tables<CB> tab;
+    Tables<CB, false> tab;
     tab.load(a.s_gu, a.b_gu, row0, G);
 
     int tok[RB];
@@ -812,7 +832,7 @@ __device__ __forceinline__ void gateup_wide(const FfnArgs& a, void* smem, int e,
     }
     Stager<RB, P> st;
     st.load(src, 0, 0, G);
-    tab.store(sm.ts[wave], sm.tb[wave], G);
+    tab.store(sm.ts[wave], nullptr, G);
     st.store(sm, 0);
 
     f32x4 acc[RB][CB];
@@ -821,12 +841,15 @@ __device__ __forceinline__ void gateup_wide(const FfnArgs& a, void* smem, int e,
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb) acc[rb][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    wide_kloop<RB, P, NBUF>(sm, st, src, 0, blk, H, active, (rows + 15) / 16, code_consts(a.zero), acc);
+    wide_kloop<RB, P, NBUF, MAXG>(sm, st, src, 0, blk, H, active, (rows + 15) / 16, code_consts(a.zero), acc);
 
     const float* xrow[RB];
 #pragma unroll
     for (int i = 0; i < RB; ++i) xrow[i] = a.xs + static_cast<size_t>(tok[i]) * G;
-    wide_bias<RB, P, NBUF>(sm, xrow, G, active, acc);
+    const uint16_t* brow[CB];
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) brow[cb] = a.b_gu + (row0[cb] + lr) * G;
+    wide_bias<RB, P, NBUF, MAXG>(sm, xrow, brow, G, active, acc);
 
     // GeGLU epilogue and the 16-column block sums of h
 #pragma unroll
@@ -856,11 +879,11 @@ __device__ __forceinline__ void gateup_wide(const FfnArgs& a, void* smem, int e,
 
 // down wide.  Grid (max_tiles, ceil(H / 256)).  Wave w owns output columns
 // n0 + 64 w + [0, 64): four 16-row weight blocks.
-template <int RB, bool kF32H>
-__device__ __forceinline__ void down_wide(const FfnArgs& a, void* smem, int e, int row_begin,
-                                          int rows) {
+template <int RB, int MAXG, bool kF32H>
+__device__ __forceinline__ void down_wide(const FfnArgs& a,
+                                          WideSmem<RB, kF32H ? 2 : 1, kF32H ? 1 : 2, MAXG>& sm,
+                                          int e, int row_begin, int rows) {
     constexpr int P = kF32H ? 2 : 1, NBUF = kF32H ? 1 : 2, CB = 4;
-    auto& sm = *static_cast<WideSmem<RB, P, NBUF>*>(smem);
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, q = lane >> 4, lr = lane & 15;
     const int H = a.H, I = a.I, G = I / kGroup;
     const size_t A = static_cast<size_t>(a.T) * a.k;
@@ -875,7 +898,7 @@ __device__ __forceinline__ void down_wide(const FfnArgs& a, void* smem, int e, i
         row0[cb] = static_cast<size_t>(e) * H + cbase + 16 * cb;
         blk[cb] = a.w_d + row0[cb] * (I / 8);
     }
-    Tables<CB> tab;
+    Tables<CB, false> tab;
     tab.load(a.s_d, a.b_d, row0, G);
 
     int hrow[RB];
@@ -889,7 +912,7 @@ __device__ __forceinline__ void down_wide(const FfnArgs& a, void* smem, int e, i
     const size_t part = A * (I / 2);
     Stager<RB, P> st;
     st.load(src, part, 0, G);
-    tab.store(sm.ts[wave], sm.tb[wave], G);
+    tab.store(sm.ts[wave], nullptr, G);
     st.store(sm, 0);
 
     f32x4 acc[RB][CB];
@@ -898,12 +921,15 @@ __device__ __forceinline__ void down_wide(const FfnArgs& a, void* smem, int e, i
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb) acc[rb][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    wide_kloop<RB, P, NBUF>(sm, st, src, part, blk, I, active, (rows + 15) / 16, code_consts(a.zero), acc);
+    wide_kloop<RB, P, NBUF, MAXG>(sm, st, src, part, blk, I, active, (rows + 15) / 16, code_consts(a.zero), acc);
 
     const float* xrow[RB];
 #pragma unroll
     for (int i = 0; i < RB; ++i) xrow[i] = a.hs + static_cast<size_t>(hrow[i]) * G;
-    wide_bias<RB, P, NBUF>(sm, xrow, G, active, acc);
+    const uint16_t* brow[CB];
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) brow[cb] = a.b_d + (row0[cb] + lr) * G;
+    wide_bias<RB, P, NBUF, MAXG>(sm, xrow, brow, G, active, acc);
 
     if (!active) return;
     // weighted unsort
@@ -923,20 +949,22 @@ __device__ __forceinline__ void down_wide(const FfnArgs& a, void* smem, int e, i
     }
 }
 
-template <bool kF32H>
-__global__ __launch_bounds__(kThreads) void moe_gateup_wide(FfnArgs a) {
-    __shared__ __attribute__((aligned(16))) unsigned char smem[kWideSmemBytes];
+template <bool kF32H, int MAXG>
+__global__ __launch_bounds__(kThreads, MAXG <= kWideMaxGSmall ? 2 : 1) void moe_gateup_wide(FfnArgs a) {
+    constexpr int RB = kF32H ? kWideRowBlocksF32 : kWideRowBlocks;
+    __shared__ WideSmem<RB, 1, 2, MAXG> sm;
     const int4 tile = load_tile<false>(a);
     if (tile.x < 0) return;
-    gateup_wide<kF32H ? kWideRowBlocksF32 : kWideRowBlocks, kF32H>(a, smem, tile.x, tile.y, tile.z);
+    gateup_wide<RB, MAXG, kF32H>(a, sm, tile.x, tile.y, tile.z);
 }
 
-template <bool kF32H>
-__global__ __launch_bounds__(kThreads) void moe_down_wide(FfnArgs a) {
-    __shared__ __attribute__((aligned(16))) unsigned char smem[kWideSmemBytes];
+template <bool kF32H, int MAXG>
+__global__ __launch_bounds__(kThreads, MAXG <= kWideMaxGSmall ? 2 : 1) void moe_down_wide(FfnArgs a) {
+    constexpr int RB = kF32H ? kWideRowBlocksF32 : kWideRowBlocks;
+    __shared__ WideSmem<RB, kF32H ? 2 : 1, kF32H ? 1 : 2, MAXG> sm;
     const int4 tile = load_tile<false>(a);
     if (tile.x < 0) return;
-    down_wide<kF32H ? kWideRowBlocksF32 : kWideRowBlocks, kF32H>(a, smem, tile.x, tile.y, tile.z);
+    down_wide<RB, MAXG, kF32H>(a, sm, tile.x, tile.y, tile.z);
 }
 
 }  // namespace
@@ -973,9 +1001,12 @@ hipError_t launch_gateup_wide(const FfnArgs& a, hipStream_t stream, const KTimin
     const int n = wide_grid(a);
     if (n == 0) return skip_launch(stream, t);
     const dim3 grid(n, (a.I + 127) / 128);
-    if (a.flags & MOE_F_FP32_INTERMEDIATE)
-        return launch_kernel(moe_gateup_wide<true>, grid, dim3(kThreads), stream, t, a);
-    return launch_kernel(moe_gateup_wide<false>, grid, dim3(kThreads), stream, t, a);
+    const bool f32 = a.flags & MOE_F_FP32_INTERMEDIATE, small = a.H / kGroup <= kWideMaxGSmall;
+    if (f32)
+        return small ? launch_kernel(moe_gateup_wide<true, kWideMaxGSmall>, grid, dim3(kThreads), stream, t, a)
+                     : launch_kernel(moe_gateup_wide<true, kMaxG>, grid, dim3(kThreads), stream, t, a);
+    return small ? launch_kernel(moe_gateup_wide<false, kWideMaxGSmall>, grid, dim3(kThreads), stream, t, a)
+                 : launch_kernel(moe_gateup_wide<false, kMaxG>, grid, dim3(kThreads), stream, t, a);
 }
 
 hipError_t launch_down_skinny(const FfnArgs& a, hipStream_t stream, const KTiming& t) {
@@ -990,9 +1021,12 @@ hipError_t launch_down_wide(const FfnArgs& a, hipStream_t stream, const KTiming&
     const int n = wide_grid(a);
     if (n == 0) return skip_launch(stream, t);
     const dim3 grid(n, (a.H + 255) / 256);
-    if (a.flags & MOE_F_FP32_INTERMEDIATE)
-        return launch_kernel(moe_down_wide<true>, grid, dim3(kThreads), stream, t, a);
-    return launch_kernel(moe_down_wide<false>, grid, dim3(kThreads), stream, t, a);
+    const bool f32 = a.flags & MOE_F_FP32_INTERMEDIATE, small = a.I / kGroup <= kWideMaxGSmall;
+    if (f32)
+        return small ? launch_kernel(moe_down_wide<true, kWideMaxGSmall>, grid, dim3(kThreads), stream, t, a)
+                     : launch_kernel(moe_down_wide<true, kMaxG>, grid, dim3(kThreads), stream, t, a);
+    return small ? launch_kernel(moe_down_wide<false, kWideMaxGSmall>, grid, dim3(kThreads), stream, t, a)
+                 : launch_kernel(moe_down_wide<false, kMaxG>, grid, dim3(kThreads), stream, t, a);
 }
 
 }  // namespace moe

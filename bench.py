@@ -161,6 +161,68 @@ def cpu_baseline_leg(p, gpu_out, seconds_budget: float):
     return base, parity
 
 
+def timed_loop(fn, steps):
+    import torch
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        fn(i)
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / steps
+
+
+def extra_legs(args, p, sets, prob, ws, out, stream):
+    """The same workload through the device router, the SwiGLU epilogue and
+    HIP-graph replays of the forward (host clock, same input rotation)."""
+    import numpy as np
+    import torch
+
+    import bit_gathered_quantized_amd as bgq
+
+    A = p.T * p.k
+    steps = max(20, min(args.steps, 200))
+    res = {}
+    # device router at the workload's shape
+    rng = np.random.default_rng(7)
+    logits = torch.from_numpy(rng.standard_normal((p.T, p.E)).astype(np.float32)).cuda()
+    ids = torch.empty((p.T, p.k), dtype=torch.int32, device="cuda")
+    wts = torch.empty((p.T, p.k), dtype=torch.float32, device="cuda")
+    for _ in range(3):
+        bgq.router_topk(logits, p.k, ids, wts, stream=stream)
+    sec = timed_loop(lambda i: bgq.router_topk(logits, p.k, ids, wts, stream=stream), steps)
+    res["router_topk"] = dict(us_per_call=round(sec * 1e6, 2), tokens_per_s=round(p.T / sec, 1),
+                              shape=[p.T, p.E, p.k])
+    # SwiGLU epilogue instead of GeGLU
+    for i in range(3):
+        bgq.expert_ffn_forward(*sets[i % len(sets)], swiglu=True, out=out, workspace=ws,
+                               stream=stream)
+    sec = timed_loop(lambda i: bgq.expert_ffn_forward(*sets[i % len(sets)], swiglu=True, out=out,
+                                                      workspace=ws, stream=stream), steps)
+    res["swiglu_forward"] = dict(ms_per_step=round(sec * 1e3, 5),
+                                 assignments_per_s=round(A / sec, 1))
+    # the whole forward as one HIP graph per input copy
+    graphs = []
+    cs = torch.cuda.Stream()
+    cs.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cs):
+        for st in sets:
+            bgq.expert_ffn_forward(*st, out=out, workspace=ws, stream=cs)
+        torch.cuda.synchronize()
+        for st in sets:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=cs):
+                bgq.expert_ffn_forward(*st, out=out, workspace=ws, stream=cs)
+            graphs.append(g)
+    torch.cuda.current_stream().wait_stream(cs)
+    torch.cuda.synchronize()
+    for g in graphs:
+        g.replay()
+    sec = timed_loop(lambda i: graphs[i % len(graphs)].replay(), steps)
+    res["graph_forward"] = dict(ms_per_step=round(sec * 1e3, 5),
+                                assignments_per_s=round(A / sec, 1))
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__,
                                  formatter_class=argparse.RawDescriptionHelpFormatter)
@@ -172,6 +234,9 @@ def main():
     ap.add_argument("--copies", type=int, default=4, help="input copies rotated across steps")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="instead of the forward, copy MIB MiB device-to-device 5 times "
+                         "(the reference kernel for scaling HBM byte counters)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -190,6 +255,17 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     bgq.lib()  # fail loudly if the HIP library is missing
+
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration": {"bytes_read": n, "bytes_written": n, "launches": 5}}),
+              flush=True)
+        return
 
     p = ms.make_config(args.workload, seed=0)
     A = p.T * p.k
@@ -300,6 +376,8 @@ def main():
         "forward": forward,
         "kernels": kstats,
     }
+
+    result["extras"] = extra_legs(args, p, sets, prob, ws, out, stream)
 
     if not args.no_cpu_baseline:
         gpu_out = out.float().cpu().numpy().astype(np.float64)

@@ -12,9 +12,9 @@ import os
 from typing import Optional, Sequence
 
 __all__ = [
-    "MoeError", "lib", "LIB_PATH", "MOE_F_FP32_OUT", "MOE_F_FP32_INTERMEDIATE",
+    "MoeError", "lib", "LIB_PATH", "MOE_F_FP32_OUT", "MOE_F_FP32_INTERMEDIATE", "MOE_F_SWIGLU",
     "max_tiles", "workspace_bytes", "workspace_layout", "sort_build_tiles",
-    "expert_ffn_forward", "status_string", "EXPORTED_SYMBOLS",
+    "expert_ffn_forward", "router_topk", "status_string", "EXPORTED_SYMBOLS",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoeffn.so")
@@ -27,11 +27,12 @@ KERNELS = ("moe_route_sort_tiles", "moe_gateup_skinny", "moe_gateup_wide", "moe_
 N_EVENTS = 2 * len(KERNELS)
 MOE_F_FP32_OUT = 1
 MOE_F_FP32_INTERMEDIATE = 2
+MOE_F_SWIGLU = 4
 
 EXPORTED_SYMBOLS = (
     "moe_max_tiles", "moe_sort_build_tiles", "moe_ffn_workspace_bytes",
     "moe_ffn_workspace_layout", "moe_expert_ffn_forward",
-    "moe_expert_ffn_forward_timed", "moe_status_string",
+    "moe_expert_ffn_forward_timed", "moe_router_topk", "moe_status_string",
 )
 
 
@@ -82,6 +83,8 @@ def lib():
         L.moe_expert_ffn_forward_timed.restype = i32
         L.moe_status_string.argtypes = [i32]
         L.moe_status_string.restype = ctypes.c_char_p
+        L.moe_router_topk.argtypes = [P, i32, i32, i32, P, P, P]
+        L.moe_router_topk.restype = i32
         _lib = L
     return _lib
 
@@ -139,6 +142,26 @@ def _dev_ptr(t, name: str, itemsize: Optional[int] = None, shape: Optional[Seque
     return ctypes.c_void_p(t.data_ptr())
 
 
+def router_topk(logits, k: int, ids=None, weights=None, stream=None):
+    """Softmax top-k routing on the GPU: logits fp32 [T, E] -> (ids int32 [T, k],
+    weights fp32 [T, k])."""
+    torch = _torch()
+    T, E = logits.shape
+    if logits.dtype != torch.float32:
+        raise ValueError("logits must be float32")
+    if ids is None:
+        ids = torch.empty((T, k), dtype=torch.int32, device=logits.device)
+    if weights is None:
+        weights = torch.empty((T, k), dtype=torch.float32, device=logits.device)
+    st = lib().moe_router_topk(_dev_ptr(logits, "logits", 4, (T, E)), T, E, k,
+                               _dev_ptr(ids, "ids", 4, (T, k)),
+                               _dev_ptr(weights, "weights", 4, (T, k)),
+                               ctypes.c_void_p(_stream(stream)))
+    if st != 0:
+        raise MoeError(st, "moe_router_topk")
+    return ids, weights
+
+
 def sort_build_tiles(topk_ids, E: int, bm_big: int = 32, bm_small: int = 16, stream=None):
     """Route/sort/tile on the GPU.  Returns a dict of device tensors:
     counts [E], offsets [E+1], perm [A], inv_perm [A], tiles [max_tiles, 4],
@@ -172,19 +195,21 @@ def sort_build_tiles(topk_ids, E: int, bm_big: int = 32, bm_small: int = 16, str
 
 def expert_ffn_forward(x, topk_ids, topk_weights, w_gateup, s_gateup, b_gateup,
                        w_down, s_down, b_down, *, fp32_out: bool = False,
-                       fp32_intermediate: bool = False, out=None, workspace=None,
-                       stream=None, events=None):
+                       fp32_intermediate: bool = False, swiglu: bool = False, out=None,
+                       workspace=None, stream=None, events=None):
     """Expert FFN forward.  Shapes: x [T, H] (2-byte), topk_ids int32 [T, k],
     topk_weights fp32 [T, k], w_gateup 4-byte [E, 2I, H/8], s/b_gateup 2-byte
     [E, 2I, H/64], w_down 4-byte [E, H, I/8], s/b_down 2-byte [E, H, I/64].
-    Returns out [T, H] (bf16, or fp32 with fp32_out).  `workspace` is a uint8
+    Returns out [T, H] (bf16, or fp32 with fp32_out); swiglu selects
+    h = silu(g) * u instead of gelu_tanh(g) * u.  `workspace` is a uint8
     device tensor of at least workspace_bytes() bytes (allocated if None)."""
     torch = _torch()
     T, H = x.shape
     k = topk_ids.shape[1]
     E, I2, hw = w_gateup.shape
     I = I2 // 2
-    flags = (MOE_F_FP32_OUT if fp32_out else 0) | (MOE_F_FP32_INTERMEDIATE if fp32_intermediate else 0)
+    flags = ((MOE_F_FP32_OUT if fp32_out else 0) | (MOE_F_FP32_INTERMEDIATE if fp32_intermediate else 0)
+             | (MOE_F_SWIGLU if swiglu else 0))
     p = problem(T, k, E, H, I, flags)
     if topk_ids.dtype != torch.int32 or topk_weights.dtype != torch.float32:
         raise ValueError("topk_ids must be int32 and topk_weights float32")

@@ -18,7 +18,8 @@ bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 moe_status check_problem(const moe_problem* p) {
     if (!p) return MOE_ERR_NULL;
     if (p->bits != 4 || p->group_size != moe::kGroup) return MOE_ERR_UNSUPPORTED;
-    if (p->flags & ~(MOE_F_FP32_OUT | MOE_F_FP32_INTERMEDIATE)) return MOE_ERR_UNSUPPORTED;
+    if (p->flags & ~(MOE_F_FP32_OUT | MOE_F_FP32_INTERMEDIATE | MOE_F_SWIGLU))
+        return MOE_ERR_UNSUPPORTED;
     if (p->T < 0 || p->k < 1 || p->E < 1 || p->H < 1 || p->I < 1) return MOE_ERR_SHAPE;
     if (p->E > MOE_MAX_EXPERTS) return MOE_ERR_UNSUPPORTED;
     if (p->k > p->E) return MOE_ERR_SHAPE;
@@ -232,6 +233,20 @@ moe_status moe_expert_ffn_forward_timed(const moe_problem* p, const void* x,
                                         void* const* events) {
     return forward_impl(p, x, topk_ids, topk_weights, w_gateup, s_gateup, b_gateup, w_down,
                         s_down, b_down, out, ws, ws_bytes, stream, events);
+}
+
+moe_status moe_router_topk(const float* logits, int32_t T, int32_t E, int32_t k,
+                           int32_t* topk_ids, float* topk_weights, void* stream) {
+    if (T < 0 || E < 1 || k < 1 || k > E) return MOE_ERR_SHAPE;
+    if (E > MOE_MAX_EXPERTS || k > moe::kRouterMaxK) return MOE_ERR_UNSUPPORTED;
+    if (T == 0) return MOE_OK;
+    if (!logits || !topk_ids || !topk_weights) return MOE_ERR_NULL;
+    if (!aligned(logits, 4) || !aligned(topk_ids, 4) || !aligned(topk_weights, 4))
+        return MOE_ERR_ALIGN;
+    if (static_cast<int64_t>(T) * E > INT32_MAX) return MOE_ERR_SHAPE;
+    const hipError_t e = moe::launch_router_topk(logits, T, E, k, topk_ids, topk_weights,
+                                                  static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
 const char* moe_status_string(moe_status s) {

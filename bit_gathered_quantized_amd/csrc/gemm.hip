@@ -1,6 +1,7 @@
 // Gathered 4-bit quantised matmuls over expert tiles.
 //
-//   gate|up  h[s, n] = gelu_tanh(x[tok(s)] . Wg[e, n]) * (x[tok(s)] . Wu[e, n])
+//   gate|up  h[s, n] = act(x[tok(s)] . Wg[e, n]) * (x[tok(s)] . Wu[e, n]),
+//            act = gelu_tanh (GeGLU), or silu with MOE_F_SWIGLU (SwiGLU)
 //   down     y[perm[s], m] = w[perm[s]] * (h[s] . Wd[e, m])
 //
 // Prior art: the expert-tile QMM of the Layr-Labs/mlx PR #4 page ("What":
@@ -217,7 +218,7 @@ __device__ __forceinline__ float sum16(float v) {
 template <bool kF32H>
 __device__ __forceinline__ float store_h(const FfnArgs& a, size_t A, int srow, int hcol, float g,
                                          float u, bool valid) {
-    const float hv = gelu_tanh(g) * u;
+    const float hv = ((a.flags & MOE_F_SWIGLU) ? silu(g) : gelu_tanh(g)) * u;
     const size_t pos = static_cast<size_t>(srow) * a.I + (hcol & ~7) + permuted_pos(hcol & 7);
     uint16_t* h = static_cast<uint16_t*>(a.h);
     const uint16_t hi = f32_to_bf16(hv);

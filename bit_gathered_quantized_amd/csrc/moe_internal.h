@@ -111,6 +111,9 @@ __device__ __forceinline__ float gelu_tanh(float v) {
     return v / (1.0f + expf(-2.0f * z));
 }
 
+// SiLU in fp32: v * sigmoid(v) = v / (1 + exp(-v)).
+__device__ __forceinline__ float silu(float v) { return v / (1.0f + expf(-v)); }
+
 // ---------------------------------------------------- kernel launchers
 // Optional start/stop events of one kernel.  With events the kernel is
 // launched through hipExtLaunchKernelGGL, which records them with the dispatch
@@ -175,5 +178,8 @@ hipError_t launch_gateup_wide(const FfnArgs& a, hipStream_t stream, const KTimin
 hipError_t launch_down_skinny(const FfnArgs& a, hipStream_t stream, const KTiming& t = {});
 hipError_t launch_down_wide(const FfnArgs& a, hipStream_t stream, const KTiming& t = {});
 hipError_t launch_combine(const FfnArgs& a, hipStream_t stream, const KTiming& t = {});
+hipError_t launch_router_topk(const float* logits, int32_t T, int32_t E, int32_t k, int32_t* ids,
+                              float* weights, hipStream_t stream);
+constexpr int kRouterMaxK = 64;
 
 }  // namespace moe

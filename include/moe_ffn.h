@@ -87,6 +87,11 @@ typedef struct {
 /* the GeGLU intermediate h is kept in fp32 instead of bf16 (the
  * fp32-accumulator path); combine with MOE_F_FP32_OUT for a full-fp32 result */
 #define MOE_F_FP32_INTERMEDIATE 2u
+/* SwiGLU instead of GeGLU: h = silu(g) * u with silu(v) = v / (1 + exp(-v))
+ * (SwiftLM issue #236, "What #27 set out to do" (2) and "Already on main":
+ * the compiled SiLU product; mlx-node PR #168: the MoE switch GLU through the
+ * fused SwiGLU kernel) */
+#define MOE_F_SWIGLU 4u
 
 /* Upper bound on the number of tiles for A assignments over E experts with
  * tile height bm_big: floor(A / bm_big) + min(E, A).  Returns -1 on bad input. */
@@ -119,6 +124,25 @@ moe_status moe_sort_build_tiles(const int32_t* topk_ids, int32_t T, int32_t k,
                                 int32_t* inv_perm, moe_tile* tiles,
                                 int32_t max_tiles, int32_t* num_tiles,
                                 void* stream);
+
+/*
+ * Device router: softmax top-k with renormalised weights, feeding
+ * moe_sort_build_tiles / moe_expert_ffn_forward.  The pages do not define the
+ * router; this is the usual top-k softmax gate (the fused top-k candidate
+ * selection of the mlx-node PR #168 page is its nearest relative there).
+ *
+ *   logits        fp32 [T, E]   4-byte aligned; NaN ranks as -inf
+ *   topk_ids      int32 [T, k]  the k largest logits of each row, in order of
+ *                               descending logit, the lower id first on ties
+ *   topk_weights  fp32 [T, k]   exp(l_j - m) / sum_i exp(l_i - m) over the k
+ *                               chosen (m the row's largest logit): the
+ *                               softmax over E renormalised over the k
+ *
+ * Requires 1 <= k <= min(E, 64), E <= MOE_MAX_EXPERTS.  T = 0 is valid.
+ * Deterministic; enqueued on `stream`, nothing allocated.
+ */
+moe_status moe_router_topk(const float* logits, int32_t T, int32_t E, int32_t k,
+                           int32_t* topk_ids, float* topk_weights, void* stream);
 
 /* Bytes of device workspace moe_expert_ffn_forward needs for problem p
  * (0 on invalid p). */

@@ -52,7 +52,11 @@ def _load():
         lib.oracle_weight.restype = dbl
         lib.oracle_gelu_tanh.argtypes = [dbl]
         lib.oracle_gelu_tanh.restype = dbl
-        lib.oracle_ffn_tokens.argtypes = [i32] * 6 + [P] * 9 + [P, i32, P, P, P]
+        lib.oracle_silu.argtypes = [dbl]
+        lib.oracle_silu.restype = dbl
+        lib.oracle_router_topk.argtypes = [P, i32, i32, i32, P, P]
+        lib.oracle_router_topk.restype = ctypes.c_int
+        lib.oracle_ffn_tokens.argtypes = [i32] * 6 + [P] * 9 + [P, i32, i32, P, P, P]
         lib.oracle_ffn_tokens.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -111,9 +115,29 @@ def gelu_tanh(v: float) -> float:
     return float(_load().oracle_gelu_tanh(float(v)))
 
 
+def silu(v: float) -> float:
+    return float(_load().oracle_silu(float(v)))
+
+
+ACTIVATIONS = {"gelu": 0, "silu": 1}
+
+
+def router_topk(logits: np.ndarray, k: int):
+    """Softmax top-k routing: (ids int32 [T, k], weights float64 [T, k])."""
+    logits = np.ascontiguousarray(logits, dtype=np.float32)
+    T, E = logits.shape
+    ids = np.zeros((max(T, 1), k), np.int32)
+    w = np.zeros((max(T, 1), k))
+    rc = _load().oracle_router_topk(_ptr(logits), T, E, k, _ptr(ids), _ptr(w))
+    if rc != 0:
+        raise ValueError(f"oracle_router_topk failed ({rc})")
+    return ids[:T], w[:T]
+
+
 def ffn_tokens(p, tokens=None, want_h: bool = True, want_y: bool = True,
-               want_out: bool = True):
-    """Expert FFN for a list of tokens of problem ``p`` (a moe_synth.Problem).
+               want_out: bool = True, act: str = "gelu"):
+    """Expert FFN for a list of tokens of problem ``p`` (a moe_synth.Problem);
+    act "gelu" (GeGLU, h = gelu_tanh(g) u) or "silu" (SwiGLU, h = silu(g) u).
 
     Returns dict with h [n*k, I], y [n*k, H] (unweighted), out [n, H]; row
     i*k + j belongs to assignment tokens[i]*k + j.
@@ -130,7 +154,8 @@ def ffn_tokens(p, tokens=None, want_h: bool = True, want_y: bool = True,
                                               p.b_down)]
     assert arrs[1].dtype == np.int32 and arrs[2].dtype == np.float32
     rc = _load().oracle_ffn_tokens(p.T, p.k, p.E, p.H, p.I, p.gs, *[_ptr(a) for a in arrs],
-                                   _ptr(tokens), n, _ptr(h), _ptr(y), _ptr(out))
+                                   _ptr(tokens), n, ACTIVATIONS[act], _ptr(h), _ptr(y),
+                                   _ptr(out))
     if rc != 0:
         raise ValueError(f"oracle_ffn_tokens failed ({rc})")
     return dict(h=h, y=y, out=out, tokens=tokens)

@@ -28,6 +28,10 @@
  *           gelu_tanh(v) = 0.5 v (1 + tanh(sqrt(2/pi) (v + 0.044715 v^3)))
  *           (SwiftLM issue #236, "Still missing": activation(xGate) * xUp with
  *           activation = geluApproximate).
+ *   SwiGLU  h = silu(g) * u, silu(v) = v / (1 + exp(-v)), when act = 1 (the
+ *           SwiGLU product of SwiftLM issue #236, "What #27 set out to do" (2)
+ *           and "Already on main"; mlx-node PR #168's MoE switch GLU).  The
+ *           pages do not spell out SiLU; this is its usual definition.
  *   down    y[a, m] = W_d[e, m, :] . h
  *   combine out[t, m] = sum_j w[t, j] * y[t*k + j, m]  (SwiftLM issue #236
  *           "Already on main": weightedExpertSum; PR #4 "Measured standing":
@@ -152,6 +156,8 @@ double oracle_gelu_tanh(double v) {
     return 0.5 * v * (1.0 + tanh(k0 * (v + 0.044715 * v * v * v)));
 }
 
+double oracle_silu(double v) { return v / (1.0 + exp(-v)); }
+
 /* dot(W[e, n, :], v) over K columns, v in double. */
 static double row_dot(const uint32_t* P, const uint16_t* S, const uint16_t* B,
                       int64_t rows, int64_t K, int32_t gs, int64_t e, int64_t n,
@@ -167,7 +173,8 @@ static double row_dot(const uint32_t* P, const uint16_t* S, const uint16_t* B,
 /*
  * Expert FFN for the listed tokens.  For list entry i (token t = tokens[i])
  * and slot j, assignment a = t*k + j is stored at row r = i*k + j of
- *   h   [ntok*k, I]  gelu_tanh(g) * u        (NULL to skip)
+ *   h   [ntok*k, I]  act(g) * u, act = gelu_tanh (act 0) or silu (act 1)
+ *                    (NULL to skip)
  *   y   [ntok*k, H]  unweighted expert output (NULL to skip)
  *   out [ntok, H]    sum_j w[t, j] * y[t*k+j] (NULL to skip)
  * Rows of an assignment with an out-of-range expert id are zero.
@@ -177,8 +184,9 @@ int oracle_ffn_tokens(int32_t T, int32_t k, int32_t E, int32_t H, int32_t I,
                       const float* w, const uint32_t* w_gu, const uint16_t* s_gu,
                       const uint16_t* b_gu, const uint32_t* w_d,
                       const uint16_t* s_d, const uint16_t* b_d,
-                      const int32_t* tokens, int32_t ntok, double* h, double* y,
-                      double* out) {
+                      const int32_t* tokens, int32_t ntok, int32_t act, double* h,
+                      double* y, double* out) {
+    if (act != 0 && act != 1) return ORACLE_ERR_ARG;
     if (T < 0 || k <= 0 || E <= 0 || H <= 0 || I <= 0 || gs <= 0 || H % gs ||
         I % gs || H % 8 || I % 8 || ntok < 0 || (ntok > 0 && !tokens))
         return ORACLE_ERR_ARG;
@@ -208,7 +216,7 @@ int oracle_ffn_tokens(int32_t T, int32_t k, int32_t E, int32_t H, int32_t I,
             for (int64_t n = 0; n < I; ++n) {
                 double g = row_dot(w_gu, s_gu, b_gu, 2 * (int64_t)I, H, gs, e, n, xv);
                 double u = row_dot(w_gu, s_gu, b_gu, 2 * (int64_t)I, H, gs, e, I + n, xv);
-                hv[n] = oracle_gelu_tanh(g) * u;
+                hv[n] = (act ? oracle_silu(g) : oracle_gelu_tanh(g)) * u;
             }
             for (int64_t m = 0; m < H; ++m)
                 yy[r * H + m] = row_dot(w_d, s_d, b_d, H, I, gs, e, m, hv);
@@ -239,5 +247,43 @@ int oracle_ffn_tokens(int32_t T, int32_t k, int32_t E, int32_t H, int32_t I,
         }
     }
     free(yy);
+    return ORACLE_OK;
+}
+
+/* ------------------------------------------------------------- router */
+
+/*
+ * Softmax top-k routing of one logits row per token, in double: the k largest
+ * logits (ties to the lower expert id), in order of descending logit, with
+ * weights exp(l_i - m) / sum over the k chosen of exp(l_j - m), m the largest
+ * logit.  That is the softmax over all E experts renormalised over the chosen
+ * k: the full softmax denominator cancels.  The pages do not define the
+ * router; this is the usual top-k softmax gate with renormalised weights (the
+ * fused top-k candidate selection of the mlx-node PR #168 page is its nearest
+ * relative there).
+ */
+int oracle_router_topk(const float* logits, int32_t T, int32_t E, int32_t k,
+                       int32_t* ids, double* weights) {
+    if (T < 0 || E <= 0 || k <= 0 || k > E || (T > 0 && (!logits || !ids || !weights)))
+        return ORACLE_ERR_ARG;
+    for (int64_t t = 0; t < T; ++t) {
+        const float* l = logits + t * E;
+        int32_t* id = ids + t * k;
+        /* selection: repeatedly take the largest remaining logit, lowest id on ties */
+        for (int32_t j = 0; j < k; ++j) {
+            int32_t best = -1;
+            for (int32_t e = 0; e < E; ++e) {
+                int taken = 0;
+                for (int32_t i = 0; i < j; ++i) taken |= (id[i] == e);
+                if (taken) continue;
+                if (best < 0 || (double)l[e] > (double)l[best]) best = e;
+            }
+            id[j] = best;
+        }
+        const double m = (double)l[id[0]];
+        double sum = 0.0;
+        for (int32_t j = 0; j < k; ++j) sum += exp((double)l[id[j]] - m);
+        for (int32_t j = 0; j < k; ++j) weights[t * k + j] = exp((double)l[id[j]] - m) / sum;
+    }
     return ORACLE_OK;
 }

@@ -44,18 +44,19 @@ def dev_arrays(p, dev="cuda"):
     )
 
 
-def run_forward(p, fp32=False, d=None, workspace=None):
+def run_forward(p, fp32=False, d=None, workspace=None, swiglu=False):
     """Run the forward; return (out as float64 numpy, workspace tensor, layout)."""
     if d is None:
         d = dev_arrays(p)
     flags = (bgq.MOE_F_FP32_OUT | bgq.MOE_F_FP32_INTERMEDIATE) if fp32 else 0
+    flags |= bgq.MOE_F_SWIGLU if swiglu else 0
     prob = bgq.problem(p.T, p.k, p.E, p.H, p.I, flags)
     lay = bgq.workspace_layout(prob)
     if workspace is None:
         workspace = torch.zeros(max(lay.total, 256), dtype=torch.uint8, device="cuda")
     out = bgq.expert_ffn_forward(d["x"], d["ids"], d["w"], d["w_gu"], d["s_gu"], d["b_gu"],
                                  d["w_d"], d["s_d"], d["b_d"], fp32_out=fp32,
-                                 fp32_intermediate=fp32, workspace=workspace)
+                                 fp32_intermediate=fp32, swiglu=swiglu, workspace=workspace)
     torch.cuda.synchronize()
     o = out.float().cpu().numpy().astype(np.float64)
     return o, workspace, lay

@@ -57,6 +57,7 @@ def test_workspace_layout_and_sizes():
 
 @pytest.mark.parametrize("kw,status", [
     (dict(bits=8), -3), (dict(group_size=32), -3), (dict(E=2000), -3), (dict(flags=8), -3),
+    (dict(flags=16), -3),
     (dict(H=100), -2), (dict(I=96), -2), (dict(H=8192), -3), (dict(I=4160), -3), (dict(k=0), -2), (dict(k=9, E=8), -2), (dict(T=-1), -2),
 ])
 def test_bad_problem(kw, status):
@@ -127,3 +128,17 @@ def test_status_strings():
     for s in range(-6, 1):
         assert bgq.status_string(s) and "unknown" not in bgq.status_string(s)
     assert "unknown" in bgq.status_string(-99)
+
+
+def test_router_host_checks():
+    L = bgq.lib()
+    P = ctypes.c_void_p
+    d = P(0x10000)
+    assert L.moe_router_topk(d, -1, 8, 2, d, d, None) == -2
+    assert L.moe_router_topk(d, 4, 8, 9, d, d, None) == -2
+    assert L.moe_router_topk(d, 4, 8, 0, d, d, None) == -2
+    assert L.moe_router_topk(d, 4, 2000, 8, d, d, None) == -3
+    assert L.moe_router_topk(d, 4, 128, 65, d, d, None) == -3
+    assert L.moe_router_topk(None, 4, 8, 2, d, d, None) == -1
+    assert L.moe_router_topk(d, 4, 8, 2, P(0x10002), d, None) == -4
+    assert L.moe_router_topk(None, 0, 8, 2, None, None, None) == 0

@@ -18,12 +18,12 @@ from gpu_util import (assert_bf16_close, assert_fp32_close, bf16_excess, dev_arr
 pytestmark = pytest.mark.gpu
 
 
-def compare(oracle_lib, p, fp32, tokens=None):
+def compare(oracle_lib, p, fp32, tokens=None, swiglu=False):
     log(f"forward: {p.name} E={p.E} H={p.H} I={p.I} T={p.T} k={p.k} fp32={fp32} "
-        f"tokens={'all' if tokens is None else len(tokens)}")
-    out, ws, lay = run_forward(p, fp32=fp32)
+        f"swiglu={swiglu} tokens={'all' if tokens is None else len(tokens)}")
+    out, ws, lay = run_forward(p, fp32=fp32, swiglu=swiglu)
     toks = np.arange(p.T, dtype=np.int32) if tokens is None else tokens
-    ref = oracle_lib.ffn_tokens(p, toks)
+    ref = oracle_lib.ffn_tokens(p, toks, act="silu" if swiglu else "gelu")
     rows = (toks[:, None] * p.k + np.arange(p.k)[None, :]).ravel()
     valid = ((p.topk_ids.ravel()[rows] >= 0) & (p.topk_ids.ravel()[rows] < p.E))
     # h: sorted order -> flat order through inv_perm
@@ -210,3 +210,16 @@ def test_forward_tile_lists(oracle_lib, name, fp32):
     assert nt[0] == len(ref) == len(wide) + len(short)
     np.testing.assert_array_equal(wide, ref[ref[:, 2] > lay.bm_small])
     np.testing.assert_array_equal(short, ref[ref[:, 2] <= lay.bm_small])
+
+
+@pytest.mark.parametrize("name,fp32", [("tiny", False), ("tiny", True), ("decode", False),
+                                        ("decode", True)])
+def test_swiglu_full(oracle_lib, name, fp32):
+    """SwiGLU epilogue (h = silu(g) * u) against the oracle, all tokens."""
+    compare(oracle_lib, ms.make_config(name), fp32, swiglu=True)
+
+
+@pytest.mark.parametrize("name", ["prefill4k", "prefill16k"])
+def test_swiglu_prefill_sampled(oracle_lib, name):
+    p = ms.make_config(name)
+    compare(oracle_lib, p, False, tokens=sample_tokens(p), swiglu=True)

@@ -39,7 +39,11 @@ def torch_gelu_tanh(v: np.ndarray) -> np.ndarray:
     return torch.nn.functional.gelu(torch.from_numpy(v), approximate="tanh").numpy()
 
 
-def brute_force_out(p) -> np.ndarray:
+def torch_silu(v: np.ndarray) -> np.ndarray:
+    return torch.nn.functional.silu(torch.from_numpy(v)).numpy()
+
+
+def brute_force_out(p, act="gelu") -> np.ndarray:
     """Dense, unrouted recomputation: every token through every expert, then
     out[t] = sum_e C[t, e] * FFN_e(x_t) with C[t, e] = sum_j [ids[t,j] == e] w[t,j]."""
     x = ms.bf16_bits_to_f32(p.x).astype(np.float64)
@@ -53,7 +57,8 @@ def brute_force_out(p) -> np.ndarray:
     out = np.zeros((p.T, p.H))
     for e in range(p.E):
         gu = x @ Wgu[e].T
-        hid = torch_gelu_tanh(gu[:, : p.I]) * gu[:, p.I:]
+        gate = gu[:, : p.I]
+        hid = (torch_gelu_tanh(gate) if act == "gelu" else torch_silu(gate)) * gu[:, p.I:]
         out += C[:, e: e + 1] * (hid @ Wd[e].T)
     return out
 
@@ -224,6 +229,34 @@ def test_gelu_matches_torch_tanh_approximation(oracle_lib):
     assert 3e-4 < d < 5e-4
 
 
+# ------------------------------------------------------------------- SiLU
+def test_silu_closed_forms(oracle_lib):
+    assert oracle_lib.silu(0.0) == 0.0
+    for v in np.linspace(-6, 6, 97):
+        # v sigmoid(v) - (-v) sigmoid(-v) = v (sigmoid(v) + sigmoid(-v)) = v
+        assert abs(oracle_lib.silu(v) - oracle_lib.silu(-v) - v) <= 4e-15 * max(1, abs(v))
+    assert oracle_lib.silu(50.0) == 50.0
+    assert abs(oracle_lib.silu(-50.0)) < 1e-19
+    # the slope at 0 is sigmoid(0) = 1/2
+    assert abs(oracle_lib.silu(1e-8) / 1e-8 - 0.5) < 1e-8
+
+
+def test_silu_matches_torch(oracle_lib):
+    v = np.linspace(-12, 12, 1001)
+    got = np.array([oracle_lib.silu(t) for t in v])
+    np.testing.assert_allclose(got, torch_silu(v), rtol=1e-14, atol=1e-15)
+
+
+@pytest.mark.parametrize("seed", [0, 3])
+def test_swiglu_matches_brute_force(oracle_lib, seed):
+    p = ms.make_config("tiny", seed=seed)
+    r = oracle_lib.ffn_tokens(p, act="silu")
+    ref = brute_force_out(p, act="silu")
+    assert rel_err(r["out"], ref) < 1e-12
+    # and it is not the GeGLU result
+    assert rel_err(r["out"], brute_force_out(p)) > 1e-2
+
+
 # ------------------------------------------------------------------- FFN
 def test_single_expert_is_dense_ffn(oracle_lib):
     """E = 1, k = 1: the routed FFN reduces to a dense quantised FFN."""
@@ -300,3 +333,40 @@ def test_token_subset_is_consistent(oracle_lib):
     rows = (toks[:, None] * p.k + np.arange(p.k)[None, :]).ravel()
     np.testing.assert_array_equal(sub["h"], full["h"][rows])
     np.testing.assert_array_equal(sub["y"], full["y"][rows])
+
+
+# ----------------------------------------------------------------- router
+def test_router_hand_example(oracle_lib):
+    """Ties go to the lower id; weights are the renormalised softmax of the
+    chosen logits: [1, 1, e^-2] / (2 + e^-2)."""
+    ids, w = oracle_lib.router_topk(np.array([[0.0, 3.0, 3.0, 1.0]], np.float32), 3)
+    assert ids.tolist() == [[1, 2, 3]]
+    d = 2 + math.exp(-2)
+    np.testing.assert_allclose(w[0], [1 / d, 1 / d, math.exp(-2) / d], rtol=1e-15)
+
+
+def test_router_full_k_is_softmax(oracle_lib):
+    rng = np.random.default_rng(21)
+    logits = rng.standard_normal((33, 8)).astype(np.float32) * 3
+    ids, w = oracle_lib.router_topk(logits, 8)
+    ref = torch.softmax(torch.from_numpy(logits.astype(np.float64)), dim=1).numpy()
+    np.testing.assert_allclose(w, np.take_along_axis(ref, ids.astype(np.int64), axis=1),
+                               rtol=1e-13)
+
+
+@pytest.mark.parametrize("E,k", [(128, 8), (64, 1), (1024, 64), (5, 5)])
+def test_router_matches_library_routines(oracle_lib, E, k):
+    rng = np.random.default_rng(E + k)
+    logits = rng.standard_normal((40, E)).astype(np.float32)
+    logits[::7, : E // 2] = 0.5  # ties inside and across the chosen set
+    ids, w = oracle_lib.router_topk(logits, k)
+    ref_ids = np.argsort(-logits, axis=1, kind="stable")[:, :k]
+    np.testing.assert_array_equal(ids, ref_ids)
+    sel = np.take_along_axis(logits, ref_ids, axis=1).astype(np.float64)
+    ref_w = torch.softmax(torch.from_numpy(sel), dim=1).numpy()
+    np.testing.assert_allclose(w, ref_w, rtol=1e-13)
+    np.testing.assert_allclose(w.sum(axis=1), 1.0, rtol=1e-14)
+    # a constant shift of a row changes nothing
+    ids2, w2 = oracle_lib.router_topk(logits + np.float32(4.0), k)
+    np.testing.assert_array_equal(ids2, ids)
+    np.testing.assert_allclose(w2, w, rtol=1e-6)

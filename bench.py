@@ -200,6 +200,17 @@ def extra_legs(args, p, sets, prob, ws, out, stream):
                                                       workspace=ws, stream=stream), steps)
     res["swiglu_forward"] = dict(ms_per_step=round(sec * 1e3, 5),
                                  assignments_per_s=round(A / sec, 1))
+    # the pre-sorted entry, given each copy's expert-sorted order
+    flat = p.topk_ids.ravel()
+    keys = np.where((flat >= 0) & (flat < p.E), flat, p.E)
+    order = torch.from_numpy(np.argsort(keys, kind="stable").astype(np.int32)).cuda()
+    for i in range(3):
+        bgq.expert_ffn_forward(*sets[i % len(sets)], out=out, workspace=ws, stream=stream,
+                               sorted_order=order)
+    sec = timed_loop(lambda i: bgq.expert_ffn_forward(*sets[i % len(sets)], out=out, workspace=ws,
+                                                      stream=stream, sorted_order=order), steps)
+    res["presorted_forward"] = dict(ms_per_step=round(sec * 1e3, 5),
+                                    assignments_per_s=round(A / sec, 1))
     # the whole forward as one HIP graph per input copy
     graphs = []
     cs = torch.cuda.Stream()

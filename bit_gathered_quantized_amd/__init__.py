@@ -32,7 +32,8 @@ MOE_F_SWIGLU = 4
 EXPORTED_SYMBOLS = (
     "moe_max_tiles", "moe_sort_build_tiles", "moe_ffn_workspace_bytes",
     "moe_ffn_workspace_layout", "moe_expert_ffn_forward",
-    "moe_expert_ffn_forward_timed", "moe_router_topk", "moe_status_string",
+    "moe_expert_ffn_forward_timed", "moe_expert_ffn_forward_presorted", "moe_router_topk",
+    "moe_status_string",
 )
 
 
@@ -81,6 +82,8 @@ def lib():
         L.moe_expert_ffn_forward.restype = i32
         L.moe_expert_ffn_forward_timed.argtypes = fwd + [P]
         L.moe_expert_ffn_forward_timed.restype = i32
+        L.moe_expert_ffn_forward_presorted.argtypes = fwd[:4] + [P] + fwd[4:]
+        L.moe_expert_ffn_forward_presorted.restype = i32
         L.moe_status_string.argtypes = [i32]
         L.moe_status_string.restype = ctypes.c_char_p
         L.moe_router_topk.argtypes = [P, i32, i32, i32, P, P, P]
@@ -196,12 +199,14 @@ def sort_build_tiles(topk_ids, E: int, bm_big: int = 32, bm_small: int = 16, str
 def expert_ffn_forward(x, topk_ids, topk_weights, w_gateup, s_gateup, b_gateup,
                        w_down, s_down, b_down, *, fp32_out: bool = False,
                        fp32_intermediate: bool = False, swiglu: bool = False, out=None,
-                       workspace=None, stream=None, events=None):
+                       workspace=None, stream=None, events=None, sorted_order=None):
     """Expert FFN forward.  Shapes: x [T, H] (2-byte), topk_ids int32 [T, k],
     topk_weights fp32 [T, k], w_gateup 4-byte [E, 2I, H/8], s/b_gateup 2-byte
     [E, 2I, H/64], w_down 4-byte [E, H, I/8], s/b_down 2-byte [E, H, I/64].
     Returns out [T, H] (bf16, or fp32 with fp32_out); swiglu selects
-    h = silu(g) * u instead of gelu_tanh(g) * u.  `workspace` is a uint8
+    h = silu(g) * u instead of gelu_tanh(g) * u.  With sorted_order (int32
+    [T*k], slot -> flat assignment, sorted by expert) the pre-sorted entry is
+    used.  `workspace` is a uint8
     device tensor of at least workspace_bytes() bytes (allocated if None)."""
     torch = _torch()
     T, H = x.shape
@@ -233,6 +238,16 @@ def expert_ffn_forward(x, topk_ids, topk_weights, w_gateup, s_gateup, b_gateup,
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=x.device)
     wptr = _dev_ptr(workspace, "workspace", 1)
     s = ctypes.c_void_p(_stream(stream))
+    if sorted_order is not None:
+        if events is not None:
+            raise ValueError("events are not supported with sorted_order")
+        if sorted_order.dtype != torch.int32:
+            raise ValueError("sorted_order must be int32")
+        sp = _dev_ptr(sorted_order, "sorted_order", 4, (T * k,))
+        st = lib().moe_expert_ffn_forward_presorted(ctypes.byref(p), *ptrs[:3], sp, *ptrs[3:],
+                                                    optr, wptr, workspace.numel(), s)
+        _check(st, "moe_expert_ffn_forward_presorted")
+        return out
     if events is None:
         st = lib().moe_expert_ffn_forward(ctypes.byref(p), *ptrs, optr, wptr,
                                           workspace.numel(), s)

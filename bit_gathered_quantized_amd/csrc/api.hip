@@ -52,7 +52,7 @@ moe_ws_layout make_layout(const moe_problem* p) {
     l.inv_perm = take(sizeof(int32_t) * A);
     l.tiles = take(sizeof(moe_tile) * l.max_tiles);
     l.tiles_skinny = take(sizeof(moe_tile) * l.max_tiles);
-    l.num_tiles = take(sizeof(int32_t) * 4);
+    l.num_tiles = take(sizeof(int32_t) * 8);
     l.x_perm = take(sizeof(uint16_t) * p->T * p->H);
     l.x_sums = take(sizeof(float) * p->T * G);
     l.h = take(hbytes * A * p->I);
@@ -66,12 +66,14 @@ moe_status forward_impl(const moe_problem* p, const void* x, const int32_t* ids,
                         const float* topk_w, const uint32_t* w_gu, const void* s_gu,
                         const void* b_gu, const uint32_t* w_d, const void* s_d,
                         const void* b_d, void* out, void* ws, size_t ws_bytes, void* stream,
-                        void* const* events) {
+                        void* const* events, const int32_t* presorted, bool want_presorted) {
     const moe_status st = check_problem(p);
     if (st != MOE_OK) return st;
     if (p->T == 0) return MOE_OK;
     if (!x || !ids || !topk_w || !w_gu || !s_gu || !b_gu || !w_d || !s_d || !b_d || !out)
         return MOE_ERR_NULL;
+    if (want_presorted && !presorted) return MOE_ERR_NULL;
+    if (presorted && !aligned(presorted, 4)) return MOE_ERR_ALIGN;
     if (!ws) return MOE_ERR_WORKSPACE;
     const moe_ws_layout l = make_layout(p);
     if (ws_bytes < l.total) return MOE_ERR_WORKSPACE;
@@ -107,6 +109,7 @@ moe_status forward_impl(const moe_problem* p, const void* x, const int32_t* ids,
     r.tiles = reinterpret_cast<int32_t*>(base + l.tiles);
     r.tiles_skinny = reinterpret_cast<int32_t*>(base + l.tiles_skinny);
     r.num_tiles = reinterpret_cast<int32_t*>(base + l.num_tiles);
+    r.presorted = presorted;
     r.x = static_cast<const uint16_t*>(x);
     r.T = p->T;
     r.H = p->H;
@@ -192,6 +195,7 @@ moe_status moe_sort_build_tiles(const int32_t* topk_ids, int32_t T, int32_t k, i
     r.inv_perm = inv_perm;
     r.tiles = reinterpret_cast<int32_t*>(tiles);
     r.tiles_skinny = nullptr;
+    r.presorted = nullptr;
     r.num_tiles = num_tiles;
     r.x = nullptr;
     r.T = T;
@@ -221,7 +225,18 @@ moe_status moe_expert_ffn_forward(const moe_problem* p, const void* x, const int
                                   const uint32_t* w_down, const void* s_down, const void* b_down,
                                   void* out, void* ws, size_t ws_bytes, void* stream) {
     return forward_impl(p, x, topk_ids, topk_weights, w_gateup, s_gateup, b_gateup, w_down,
-                        s_down, b_down, out, ws, ws_bytes, stream, nullptr);
+                        s_down, b_down, out, ws, ws_bytes, stream, nullptr, nullptr, false);
+}
+
+moe_status moe_expert_ffn_forward_presorted(const moe_problem* p, const void* x,
+                                            const int32_t* topk_ids, const float* topk_weights,
+                                            const int32_t* sorted_order,
+                                            const uint32_t* w_gateup, const void* s_gateup,
+                                            const void* b_gateup, const uint32_t* w_down,
+                                            const void* s_down, const void* b_down, void* out,
+                                            void* ws, size_t ws_bytes, void* stream) {
+    return forward_impl(p, x, topk_ids, topk_weights, w_gateup, s_gateup, b_gateup, w_down,
+                        s_down, b_down, out, ws, ws_bytes, stream, nullptr, sorted_order, true);
 }
 
 moe_status moe_expert_ffn_forward_timed(const moe_problem* p, const void* x,
@@ -232,7 +247,7 @@ moe_status moe_expert_ffn_forward_timed(const moe_problem* p, const void* x,
                                         void* ws, size_t ws_bytes, void* stream,
                                         void* const* events) {
     return forward_impl(p, x, topk_ids, topk_weights, w_gateup, s_gateup, b_gateup, w_down,
-                        s_down, b_down, out, ws, ws_bytes, stream, events);
+                        s_down, b_down, out, ws, ws_bytes, stream, events, nullptr, false);
 }
 
 moe_status moe_router_topk(const float* logits, int32_t T, int32_t E, int32_t k,

@@ -141,6 +141,11 @@ struct RouteArgs {
     // gets the tiles of more than bm_small rows and tiles_skinny the others,
     // each in expert order; num_tiles [4] = {total, invalid ids, wide, skinny}.
     int32_t* tiles_skinny;
+    // A caller's slot -> assignment order, sorted by expert (or nullptr).
+    // Checked on the device: num_tiles[4] = 0 if used, 1 if not sorted or out
+    // of range, 2 if not a permutation; in both failure cases the kernel sorts
+    // by itself.
+    const int32_t* presorted;
     // activation preparation (forward only; x == nullptr skips it)
     const uint16_t* x;  // [T, H] bf16
     int32_t T, H;

@@ -108,6 +108,34 @@ __device__ void prepare_x(const RouteArgs& a, int block) {
     if ((p & 7) == 0) a.xs[p / 8] = s;
 }
 
+// Key of flat assignment a (its expert id, or E for an out-of-range id).
+__device__ __forceinline__ int32_t key_of(const RouteArgs& a, int32_t ai) {
+    const int32_t id = a.ids[ai];
+    return (id >= 0 && id < a.E) ? id : a.E;
+}
+
+// A caller's sorted order: every slot names an assignment in [0, A) and the
+// keys along it never decrease (the adjacent-pair scan of the Layr-Labs/mlx
+// PR #4 page's fail-safe, "Deep-review round": a strided scan of adjacent
+// pairs holds exactly when the whole order is non-decreasing).  Every thread
+// of the block calls it.
+__device__ bool presorted_order_ok(const RouteArgs& a) {
+    const int A = a.A;
+    bool ok = true;
+    for (int s = threadIdx.x; s < A; s += kRouteThreads) {
+        const int32_t a0 = a.presorted[s];
+        if (a0 < 0 || a0 >= A) {
+            ok = false;
+            continue;
+        }
+        if (s + 1 < A) {
+            const int32_t a1 = a.presorted[s + 1];
+            if (a1 < 0 || a1 >= A || key_of(a, a0) > key_of(a, a1)) ok = false;
+        }
+    }
+    return __syncthreads_and(ok);
+}
+
 // First index in [0, n) with v[index] > x (v ascending), n if none.
 __device__ __forceinline__ int upper_bound(const int32_t* v, int n, int x) {
     int lo = 0, hi = n;
@@ -187,7 +215,26 @@ __global__ __launch_bounds__(kRouteThreads) void moe_route_sort_tiles(RouteArgs 
     }
     __syncthreads();
 
-    // 3. stable scatter
+    // 3. the caller's sorted order, if it is one (it must also be a
+    // permutation: checked after writing inv_perm), else the stable scatter
+    int32_t order_status = 0;
+    if (a.presorted != nullptr) {
+        order_status = presorted_order_ok(a) ? 0 : 1;
+        if (order_status == 0) {
+            for (int s = tid; s < A; s += kRouteThreads) {
+                const int32_t ai = a.presorted[s];
+                a.perm[s] = ai;
+                a.inv_perm[ai] = s;
+            }
+            __threadfence_block();
+            __syncthreads();
+            bool bij = true;
+            for (int s = tid; s < A; s += kRouteThreads)
+                if (a.inv_perm[a.presorted[s]] != s) bij = false;
+            order_status = __syncthreads_and(bij) ? 0 : 2;
+        }
+    }
+    if (a.presorted == nullptr || order_status != 0)
     for (int base0 = beg; base0 < end; base0 += 64 * kBatch) {
         uint32_t keys[kBatch];
 #pragma unroll
@@ -216,6 +263,7 @@ __global__ __launch_bounds__(kRouteThreads) void moe_route_sort_tiles(RouteArgs 
     if (tid == 0) {
         a.offsets[E] = s_off[E];
         a.num_tiles[1] = s_cnt[E];
+        if (a.presorted != nullptr) a.num_tiles[4] = order_status;
     }
     __syncthreads();
     if (a.tiles_skinny == nullptr) {

@@ -160,8 +160,12 @@ typedef struct {
     size_t inv_perm;  /* int32 [A]                                        */
     size_t tiles;     /* moe_tile [max_tiles]: the tiles of more than
                          bm_small rows, in expert order                   */
-    size_t num_tiles; /* int32 [4]: total tiles, out-of-range ids, tiles
-                         in `tiles`, tiles in `tiles_skinny`              */
+    size_t num_tiles; /* int32 [8]: total tiles, out-of-range ids, tiles
+                         in `tiles`, tiles in `tiles_skinny`, and the
+                         order check of the pre-sorted entry (0 used,
+                         1 not sorted or out of range, 2 not a
+                         permutation; the route launch then sorted by
+                         itself); [5..7] unused                           */
     size_t x_perm;    /* bf16 [T, H]: x in operand order                  */
     size_t x_sums;    /* fp32 [T, H/64]: sum of x over each 64-column group */
     size_t h;         /* GeGLU output in sorted order, operand order:
@@ -207,6 +211,32 @@ moe_status moe_expert_ffn_forward(const moe_problem* p, const void* x,
                                   const void* b_gateup, const uint32_t* w_down,
                                   const void* s_down, const void* b_down, void* out,
                                   void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * The forward on assignments the caller has already sorted by expert, the
+ * input the expert-tile kernel of the Layr-Labs/mlx PR #4 page takes ("What":
+ * sorted indices).  Arguments as moe_expert_ffn_forward, plus
+ *
+ *   sorted_order  int32 [T*k]  slot -> flat assignment a = t*k + j, with the
+ *                              expert ids topk_ids[sorted_order[s]]
+ *                              non-decreasing in s (ids outside [0, E) last);
+ *                              any order within an expert; 4-byte aligned
+ *
+ * The route launch checks the order on the device, as the page's fail-safe
+ * does ("Deep-review round": a strided adjacent-pair scan, which holds exactly
+ * when the order is globally non-decreasing), and also that it is a
+ * permutation.  If a check fails it records why in the workspace's
+ * num_tiles[4] and sorts by itself, so the result is always correct and the
+ * host never waits.  Results are bit-identical to moe_expert_ffn_forward's
+ * (they do not depend on the order of rows within an expert).
+ */
+moe_status moe_expert_ffn_forward_presorted(const moe_problem* p, const void* x,
+                                            const int32_t* topk_ids, const float* topk_weights,
+                                            const int32_t* sorted_order,
+                                            const uint32_t* w_gateup, const void* s_gateup,
+                                            const void* b_gateup, const uint32_t* w_down,
+                                            const void* s_down, const void* b_down, void* out,
+                                            void* ws, size_t ws_bytes, void* stream);
 
 /* Same as moe_expert_ffn_forward, with per-kernel timing: events[2i] and
  * events[2i+1] (hipEvent_t, created by the caller) are recorded at the start

@@ -142,3 +142,18 @@ def test_router_host_checks():
     assert L.moe_router_topk(None, 4, 8, 2, d, d, None) == -1
     assert L.moe_router_topk(d, 4, 8, 2, P(0x10002), d, None) == -4
     assert L.moe_router_topk(None, 0, 8, 2, None, None, None) == 0
+
+
+def test_presorted_host_checks():
+    L = bgq.lib()
+    p = bgq.problem(4, 2, 8, 256, 128)
+    need = bgq.workspace_bytes(p)
+    good = [ctypes.c_void_p(0x10000)] * 9
+    out, ws = ctypes.c_void_p(0x20000), ctypes.c_void_p(0x40000)
+    P = ctypes.c_void_p
+
+    def call(order):
+        return L.moe_expert_ffn_forward_presorted(ctypes.byref(p), *good[:3], order, *good[3:],
+                                                  out, ws, need, None)
+    assert call(None) == -1
+    assert call(P(0x10002)) == -4

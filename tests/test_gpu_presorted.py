@@ -1,0 +1,77 @@
+"""The pre-sorted entry: a caller's order sorted by expert is used as given
+(any order within an expert), results equal the regular forward bit for bit;
+orders that are not sorted, out of range or not a permutation are detected
+on the device (workspace num_tiles[4]) and sorted there, again with equal
+results."""
+import numpy as np
+import pytest
+import torch
+
+import bit_gathered_quantized_amd as bgq
+import moe_synth as ms
+from gpu_util import dev_arrays, log, ws_view
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(p, d, order=None):
+    prob = bgq.problem(p.T, p.k, p.E, p.H, p.I, 0)
+    ws = torch.zeros(bgq.workspace_bytes(prob), dtype=torch.uint8, device="cuda")
+    so = None if order is None else torch.from_numpy(np.ascontiguousarray(order, np.int32)).cuda()
+    out = bgq.expert_ffn_forward(d["x"], d["ids"], d["w"], d["w_gu"], d["s_gu"], d["b_gu"],
+                                 d["w_d"], d["s_d"], d["b_d"], workspace=ws, sorted_order=so)
+    torch.cuda.synchronize()
+    lay = bgq.workspace_layout(prob)
+    status = int(ws_view(ws, lay.num_tiles, 8, np.int32)[4]) if order is not None else None
+    perm = ws_view(ws, lay.perm, p.T * p.k, np.int32)
+    return out.clone(), status, perm
+
+
+def _sorted_orders(p, oracle_lib):
+    _, _, stable, _, _ = oracle_lib.route(p.topk_ids, p.E)
+    rng = np.random.default_rng(17)
+    keys = np.where((p.topk_ids.ravel() >= 0) & (p.topk_ids.ravel() < p.E), p.topk_ids.ravel(), p.E)
+    # a sorted order with each expert's rows shuffled
+    shuffled = stable.copy()
+    ks = keys[stable]
+    for e in np.unique(ks):
+        idx = np.nonzero(ks == e)[0]
+        shuffled[idx] = rng.permutation(stable[idx])
+    return stable, shuffled
+
+
+@pytest.mark.parametrize("name", ["decode", "prefill16k"])
+def test_presorted_orders_used_and_bitwise_equal(oracle_lib, name):
+    p = ms.make_config(name)
+    d = dev_arrays(p)
+    ref, _, _ = _run(p, d)
+    stable, shuffled = _sorted_orders(p, oracle_lib)
+    for order in (stable, shuffled):
+        out, status, perm = _run(p, d, order)
+        log(f"  {name}: status {status}")
+        assert status == 0
+        np.testing.assert_array_equal(perm, order)
+        assert torch.equal(out, ref)
+
+
+def test_presorted_bad_orders_fall_back(oracle_lib):
+    p = ms.make_config("prefill4k")
+    d = dev_arrays(p)
+    ref, _, _ = _run(p, d)
+    stable, _ = _sorted_orders(p, oracle_lib)
+    A = p.T * p.k
+    rng = np.random.default_rng(2)
+    unsorted = rng.permutation(A).astype(np.int32)
+    out_of_range = stable.copy()
+    out_of_range[A // 2] = A + 5
+    negative = stable.copy()
+    negative[-1] = -1
+    dup = stable.copy()
+    dup[1] = dup[0]  # same expert (the first slots share one), still sorted: not a permutation
+    assert p.topk_ids.ravel()[stable[0]] == p.topk_ids.ravel()[stable[1]]
+    for order, want in ((unsorted, 1), (out_of_range, 1), (negative, 1), (dup, 2)):
+        out, status, perm = _run(p, d, order)
+        log(f"  bad order: status {status} (want {want})")
+        assert status == want
+        np.testing.assert_array_equal(perm, stable)  # the device sorted by itself
+        assert torch.equal(out, ref)

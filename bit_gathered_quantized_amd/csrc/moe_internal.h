@@ -124,13 +124,18 @@ struct KTiming {
 };
 
 template <typename... Args, typename F = void (*)(Args...)>
+inline hipError_t launch_kernel_lds(F kernel, dim3 grid, dim3 block, size_t lds, hipStream_t stream,
+                                    const KTiming& t, Args... args) {
+    if (t.start != nullptr && t.stop != nullptr)
+        hipExtLaunchKernelGGL(kernel, grid, block, lds, stream, t.start, t.stop, 0, args...);
+    else
+        hipLaunchKernelGGL(kernel, grid, block, lds, stream, args...);
+    return hipGetLastError();
+}
+template <typename... Args, typename F = void (*)(Args...)>
 inline hipError_t launch_kernel(F kernel, dim3 grid, dim3 block, hipStream_t stream,
                                 const KTiming& t, Args... args) {
-    if (t.start != nullptr && t.stop != nullptr)
-        hipExtLaunchKernelGGL(kernel, grid, block, 0, stream, t.start, t.stop, 0, args...);
-    else
-        hipLaunchKernelGGL(kernel, grid, block, 0, stream, args...);
-    return hipGetLastError();
+    return launch_kernel_lds(kernel, grid, block, 0, stream, t, args...);
 }
 
 struct RouteArgs {
@@ -153,6 +158,7 @@ struct RouteArgs {
     float* xs;          // [T, H/64] group sums
 };
 hipError_t launch_route(const RouteArgs& a, hipStream_t stream, const KTiming& t = {});
+size_t route_lds_bytes(int E);
 
 struct FfnArgs {
     int32_t T, k, E, H, I, max_tiles;

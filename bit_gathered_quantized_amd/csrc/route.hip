@@ -7,14 +7,12 @@
 // Here the input is the raw top-k id array, so the kernel also sorts:
 //
 //   1. each wave owns a contiguous segment of the assignments and counts the
-//      keys in it, 64 at a time, grouping equal keys with a wave match-any
-//      (one ballot per key bit) -- no atomics, so counts are exact and the
-//      work is deterministic;
+//      keys in it with LDS atomic adds (counts do not depend on their order);
 //   2. per-key totals and an exclusive scan give counts and offsets, and a
 //      scan over waves gives each (wave, key) its first sorted slot;
 //   3. each wave walks its segment again in order and scatters every
-//      assignment to base + (rank among equal keys in lower lanes): a stable
-//      counting sort;
+//      assignment to base + (rank among equal keys in lower lanes, from a
+//      wave match-any: one ballot per key bit): a stable counting sort;
 //   4. tiles per expert = ceil(count / bm_big), scanned; thread i emits tile i
 //      after an upper-bound search of the scanned tile offsets.  The forward
 //      asks for two lists instead (tiles of more than bm_small rows, and the
@@ -30,7 +28,6 @@
 namespace moe {
 namespace {
 
-constexpr int kMaxKeys = MOE_MAX_EXPERTS + 1;
 
 constexpr int kBatch = 16;  // rows of 64 keys loaded ahead per wave
 
@@ -158,16 +155,18 @@ __global__ __launch_bounds__(kRouteThreads) void moe_route_sort_tiles(RouteArgs 
         prepare_x(a, blockIdx.x - 1);
         return;
     }
-    __shared__ int32_t s_tab[kRouteWaves * kMaxKeys];  // per-wave key counts, then bases
-    __shared__ int32_t s_cnt[kMaxKeys];
-    __shared__ int32_t s_off[kMaxKeys + 1];
-    __shared__ int32_t s_toff[kMaxKeys + 1];
-    __shared__ int32_t s_soff[kMaxKeys + 1];
-    __shared__ int32_t s_wsum[kRouteWaves + 1];
-
+    // LDS sized by E at launch (route_lds_bytes), so that the activation
+    // workgroups of the same launch are not held to one per CU
+    extern __shared__ int32_t route_lds[];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int E = a.E, A = a.A;
     const int nkeys = E + 1;
+    int32_t* const s_tab = route_lds;                       // [waves][nkeys] counts, then bases
+    int32_t* const s_cnt = s_tab + kRouteWaves * nkeys;     // [nkeys]
+    int32_t* const s_off = s_cnt + nkeys;                   // [nkeys + 1]
+    int32_t* const s_toff = s_off + nkeys + 1;              // [nkeys + 1]
+    int32_t* const s_soff = s_toff + nkeys + 1;             // [nkeys + 1]
+    int32_t* const s_wsum = s_soff + nkeys + 1;             // [waves + 1]
     const int nbits = 32 - __clz(E);  // bits of the largest key, E
     const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
 
@@ -180,20 +179,16 @@ __global__ __launch_bounds__(kRouteThreads) void moe_route_sort_tiles(RouteArgs 
     const int end = min(A, beg + per);
     int32_t* tab = s_tab + wave * nkeys;
 
-    // 1. per-wave histogram.  Keys are loaded kBatch rows of 64 at a time, all
+    // 1. per-wave histogram: LDS atomic adds (a count does not depend on the
+    // order of the adds).  Keys are loaded kBatch rows of 64 at a time, all
     // loads issued before the first is used.
     for (int base0 = beg; base0 < end; base0 += 64 * kBatch) {
         uint32_t keys[kBatch];
 #pragma unroll
         for (int b = 0; b < kBatch; ++b) keys[b] = load_key(a, base0 + 64 * b + lane, end, E);
 #pragma unroll
-        for (int b = 0; b < kBatch; ++b) {
-            const int base = base0 + 64 * b;
-            if (base >= end) break;
-            const bool act = base + lane < end;
-            const uint64_t m = match_any(keys[b], nbits, __ballot(act));
-            if (act && (m & below) == 0) tab[keys[b]] += __popcll(m);
-        }
+        for (int b = 0; b < kBatch; ++b)
+            if (base0 + 64 * b + lane < end) atomicAdd(&tab[keys[b]], 1);
     }
     __syncthreads();
 
@@ -285,7 +280,7 @@ __global__ __launch_bounds__(kRouteThreads) void moe_route_sort_tiles(RouteArgs 
         // two lists, each in expert order: tiles of more than bm_small rows
         // (full tiles and long tails) and tiles of at most bm_small rows (an
         // expert's short tail; at most one per expert)
-        int32_t* s_ns = s_tab + kMaxKeys;
+        int32_t* s_ns = s_tab + nkeys;
         for (int e = tid; e < E; e += kRouteThreads) {
             const int c = s_cnt[e], tail = c % a.bm_big;
             const bool short_tail = tail > 0 && tail <= a.bm_small;
@@ -316,13 +311,26 @@ __global__ __launch_bounds__(kRouteThreads) void moe_route_sort_tiles(RouteArgs 
 
 }  // namespace
 
+size_t route_lds_bytes(int E) {
+    const size_t nkeys = static_cast<size_t>(E) + 1;
+    return sizeof(int32_t) * (kRouteWaves * nkeys + nkeys + 3 * (nkeys + 1) + kRouteWaves + 1);
+}
+
 hipError_t launch_route(const RouteArgs& a, hipStream_t stream, const KTiming& t) {
     int blocks = 1;
     if (a.x != nullptr) {
         const int64_t pieces = static_cast<int64_t>(a.T) * (a.H / 8);
         blocks += static_cast<int>((pieces + kRouteThreads - 1) / kRouteThreads);
     }
-    return launch_kernel(moe_route_sort_tiles, dim3(blocks), dim3(kRouteThreads), stream, t, a);
+    const size_t lds = route_lds_bytes(a.E);
+    if (lds > 64 * 1024) {
+        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(moe_route_sort_tiles),
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                 static_cast<int>(lds));
+        if (e != hipSuccess) return e;
+    }
+    return launch_kernel_lds(moe_route_sort_tiles, dim3(blocks), dim3(kRouteThreads), lds, stream,
+                             t, a);
 }
 
 }  // namespace moe

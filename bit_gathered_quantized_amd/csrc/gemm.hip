@@ -798,18 +798,18 @@ __device__ __forceinline__ void wide_bias(WideSmem<RB, P, NBUF, MAXG>& sm,
     }
 }
 
-// gate|up wide.  Grid (max_tiles, ceil(I / 128)).  Wave w owns h columns
+// gate|up wide, column block `by` of 128 h columns (ceil(I / 128) blocks).  Wave w owns h columns
 // n0 + 32 w + [0, 32): weight blocks 0/1 = gate columns +0/+16, blocks 2/3 =
 // the matching up columns.  Waves {0,1} cover 64-column group 2*by of h,
 // waves {2,3} group 2*by + 1.
 template <int RB, int MAXG, bool kF32H>
 __device__ __forceinline__ void gateup_wide(const FfnArgs& a, WideSmem<RB, 1, 2, MAXG>& sm, int e,
-                                            int row_begin, int rows) {
+                                            int row_begin, int rows, int by) {
     constexpr int P = 1, NBUF = 2, CB = 4;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, q = lane >> 4, lr = lane & 15;
     const int H = a.H, I = a.I, G = H / kGroup;
     const size_t A = static_cast<size_t>(a.T) * a.k;
-    const int n0 = blockIdx.y * 128;
+    const int n0 = by * 128;
     const bool active = n0 + 32 * wave < I;
     const int hbase = active ? n0 + 32 * wave : 0;
 
@@ -871,24 +871,24 @@ __device__ __forceinline__ void gateup_wide(const FfnArgs& a, WideSmem<RB, 1, 2,
     __syncthreads();
     const int GI = I / kGroup;
     for (int idx = tid; idx < 2 * rows; idx += kThreads) {
-        const int j = idx / rows, r = idx - j * rows, grp = 2 * blockIdx.y + j;
+        const int j = idx / rows, r = idx - j * rows, grp = 2 * by + j;
         if (grp < GI)
             a.hs[static_cast<size_t>(row_begin + r) * GI + grp] =
                 hsum_of(sm.blk[j][0], sm.blk[j][1], sm.blk[j][2], sm.blk[j][3], r);
     }
 }
 
-// down wide.  Grid (max_tiles, ceil(H / 256)).  Wave w owns output columns
+// down wide, column block `by` of 256 output columns (ceil(H / 256) blocks).  Wave w owns output columns
 // n0 + 64 w + [0, 64): four 16-row weight blocks.
 template <int RB, int MAXG, bool kF32H>
 __device__ __forceinline__ void down_wide(const FfnArgs& a,
                                           WideSmem<RB, kF32H ? 2 : 1, kF32H ? 1 : 2, MAXG>& sm,
-                                          int e, int row_begin, int rows) {
+                                          int e, int row_begin, int rows, int by) {
     constexpr int P = kF32H ? 2 : 1, NBUF = kF32H ? 1 : 2, CB = 4;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, q = lane >> 4, lr = lane & 15;
     const int H = a.H, I = a.I, G = I / kGroup;
     const size_t A = static_cast<size_t>(a.T) * a.k;
-    const int n0 = blockIdx.y * 256;
+    const int n0 = by * 256;
     const bool active = n0 + 64 * wave < H;  // H is a multiple of 64
     const int cbase = active ? n0 + 64 * wave : 0;
 
@@ -950,22 +950,45 @@ __device__ __forceinline__ void down_wide(const FfnArgs& a,
     }
 }
 
+// XCD-aware order of the wide work.  Workgroups go to the 8 XCDs round-robin
+// by linear id, and each XCD has its own L2: XCD x takes the contiguous run
+// [x * share, (x + 1) * share) of the (tile, column block) items, column block
+// fastest, so that a tile's column blocks (one activation tile) and an
+// expert's consecutive tiles (one set of weights) meet in the same L2.  The
+// share comes from the device-side tile count; the grid holds a multiple of 8
+// workgroups, at least as many as items.
+constexpr int kXcds = 8;
+
+__device__ __forceinline__ bool wide_work(const FfnArgs& a, int ncol, int& tile, int& col) {
+    const int total = min(a.num_tiles[2], a.max_tiles) * ncol;
+    const int share = (total + kXcds - 1) / kXcds;
+    const int L = blockIdx.x, i = L / kXcds;
+    if (i >= share) return false;
+    const int item = (L % kXcds) * share + i;
+    if (item >= total) return false;
+    tile = item / ncol;
+    col = item - tile * ncol;
+    return true;
+}
+
 template <bool kF32H, int MAXG>
 __global__ __launch_bounds__(kThreads, MAXG <= kWideMaxGSmall ? 2 : 1) void moe_gateup_wide(FfnArgs a) {
     constexpr int RB = kF32H ? kWideRowBlocksF32 : kWideRowBlocks;
     __shared__ WideSmem<RB, 1, 2, MAXG> sm;
-    const int4 tile = load_tile<false>(a);
-    if (tile.x < 0) return;
-    gateup_wide<RB, MAXG, kF32H>(a, sm, tile.x, tile.y, tile.z);
+    int ti, by;
+    if (!wide_work(a, (a.I + 127) / 128, ti, by)) return;
+    const int4 tile = reinterpret_cast<const int4*>(a.tiles)[ti];
+    gateup_wide<RB, MAXG, kF32H>(a, sm, tile.x, tile.y, tile.z, by);
 }
 
 template <bool kF32H, int MAXG>
 __global__ __launch_bounds__(kThreads, MAXG <= kWideMaxGSmall ? 2 : 1) void moe_down_wide(FfnArgs a) {
     constexpr int RB = kF32H ? kWideRowBlocksF32 : kWideRowBlocks;
     __shared__ WideSmem<RB, kF32H ? 2 : 1, kF32H ? 1 : 2, MAXG> sm;
-    const int4 tile = load_tile<false>(a);
-    if (tile.x < 0) return;
-    down_wide<RB, MAXG, kF32H>(a, sm, tile.x, tile.y, tile.z);
+    int ti, by;
+    if (!wide_work(a, (a.H + 255) / 256, ti, by)) return;
+    const int4 tile = reinterpret_cast<const int4*>(a.tiles)[ti];
+    down_wide<RB, MAXG, kF32H>(a, sm, tile.x, tile.y, tile.z, by);
 }
 
 }  // namespace
@@ -1001,7 +1024,8 @@ hipError_t launch_gateup_skinny(const FfnArgs& a, hipStream_t stream, const KTim
 hipError_t launch_gateup_wide(const FfnArgs& a, hipStream_t stream, const KTiming& t) {
     const int n = wide_grid(a);
     if (n == 0) return skip_launch(stream, t);
-    const dim3 grid(n, (a.I + 127) / 128);
+    const int items = n * ((a.I + 127) / 128);
+    const dim3 grid((items + kXcds - 1) / kXcds * kXcds);
     const bool f32 = a.flags & MOE_F_FP32_INTERMEDIATE, small = a.H / kGroup <= kWideMaxGSmall;
     if (f32)
         return small ? launch_kernel(moe_gateup_wide<true, kWideMaxGSmall>, grid, dim3(kThreads), stream, t, a)
@@ -1021,7 +1045,8 @@ hipError_t launch_down_skinny(const FfnArgs& a, hipStream_t stream, const KTimin
 hipError_t launch_down_wide(const FfnArgs& a, hipStream_t stream, const KTiming& t) {
     const int n = wide_grid(a);
     if (n == 0) return skip_launch(stream, t);
-    const dim3 grid(n, (a.H + 255) / 256);
+    const int items = n * ((a.H + 255) / 256);
+    const dim3 grid((items + kXcds - 1) / kXcds * kXcds);
     const bool f32 = a.flags & MOE_F_FP32_INTERMEDIATE, small = a.I / kGroup <= kWideMaxGSmall;
     if (f32)
         return small ? launch_kernel(moe_down_wide<true, kWideMaxGSmall>, grid, dim3(kThreads), stream, t, a)

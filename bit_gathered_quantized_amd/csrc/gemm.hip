@@ -11,28 +11,29 @@
 // standing").  Design for gfx950:
 //
 //  * Every product runs on v_mfma_f32_16x16x32_bf16.  The weight operand is
-//    the 4-bit code itself, exactly (codes_as_bf16: 1 + q/16), decoded in
-//    registers straight from HBM loads; weights never touch LDS.  Per
-//    64-column group the fp32 accumulator takes 16 s * P (one FMA per output
-//    per group); the rest, sum_g (b - 16 s) X, is itself a small contraction
-//    over groups, run on MFMAs once per tile after the groups, with both
-//    factors split into bf16 hi + lo.  Rounding dequantised weights to bf16 instead would cost
-//    the accuracy the fp32 path needs.
+//    the 4-bit code itself, exactly (codes_as_bf16: 16 + q), decoded in
+//    registers.  Per 64-column group the fp32 accumulator takes s * P (one
+//    FMA per output per group); the rest, sum_g (b - 16 s) X, is itself a
+//    small contraction over groups, run on MFMAs once per tile after the
+//    groups, with both factors split into bf16 hi + lo.  Rounding dequantised
+//    weights to bf16 instead would cost the accuracy the fp32 path needs.
 //  * Activations come pre-ordered (x_perm, from the route launch) with their
 //    group sums, so nothing here reorders or sums activations on the fly.
-//  * Skinny path, tiles of <= 16 rows (decode): no LDS staging and no
-//    barrier in the K loop; each wave streams its own weight rows through a
-//    ring of kRing groups of loads in flight.
-//  * Wide path, tiles of 17..128 rows (prefill): the activation tile is
+//  * Skinny path, tiles of <= 16 rows (decode): no activation staging and
+//    no barrier in the K loop; each wave streams its own weight rows (16-byte
+//    coalesced loads, turned into operand order through a per-wave LDS
+//    buffer) with RING chunks of loads in flight.
+//  * Wide path, tiles of 17..64 rows (prefill): the activation tile is
 //    staged in LDS, double-buffered; each wave owns 4 column blocks and all
-//    row blocks, so a decoded weight word feeds up to 8 row blocks and an LDS
-//    activation fragment feeds 4 MFMAs.
+//    row blocks, so a decoded weight word feeds every row block and an LDS
+//    activation fragment feeds 4 MFMAs; weights go through a per-wave LDS
+//    transpose as on the skinny path.
 //  * Both paths do the same arithmetic in the same order for every output
 //    element, so results do not depend on how rows are grouped into tiles
 //    (hence not on the order of the tokens).
-//  * Gate and up of an output column sit in the same lane: the GeGLU product
-//    is formed in registers and h is written once, already in MFMA operand
-//    order, with its group sums for the down matmul.
+//  * Gate and up of an output column sit in the same lane: the GeGLU (or
+//    SwiGLU) product is formed in registers and h is written once, already
+//    in MFMA operand order, with its group sums for the down matmul.
 //  * The down kernels scale each row by its routing weight and write it to
 //    its original (token, slot) position: the weighted unsort.
 //  * Each path reads its own tile list (tiles of more than 16 rows; short
@@ -112,7 +113,7 @@ __device__ __forceinline__ void bias_from_table(BiasOp& o, const uint16_t* ts, c
             for (int j = 0; j < 8; ++j) {
                 const int g = 32 * st + 8 * q + j;
                 const int gc = min(g, G - 1);
-                const float c = fmaf(-kCodeScale, bf16_to_f32(ts[gc]), bf16_to_f32(tb[gc]));
+                const float c = fmaf(-kCodeOffset, bf16_to_f32(ts[gc]), bf16_to_f32(tb[gc]));
                 v[j] = (active && g < G) ? c : 0.f;
             }
             pack_split(v, o.hi[st], o.lo[st]);
@@ -132,7 +133,7 @@ __device__ __forceinline__ void bias_from_scales(BiasOp& o, const uint16_t* ts, 
             for (int j = 0; j < 8; ++j) {
                 const int g = 32 * st + 8 * q + j;
                 const int gc = min(g, G - 1);
-                const float c = fmaf(-kCodeScale, bf16_to_f32(ts[gc]), bf16_to_f32(b[gc]));
+                const float c = fmaf(-kCodeOffset, bf16_to_f32(ts[gc]), bf16_to_f32(b[gc]));
                 v[j] = (active && g < G) ? c : 0.f;
             }
             pack_split(v, o.hi[st], o.lo[st]);
@@ -201,8 +202,8 @@ __device__ __forceinline__ f32x4 group_step2(f32x4 acc, u32x4 a0h, u32x4 a0l, u3
     return acc;
 }
 
-// 16 s from a bf16 scale.
-__device__ __forceinline__ float scale16(uint16_t t) { return kCodeScale * bf16_to_f32(t); }
+// A bf16 scale as the factor of P.
+__device__ __forceinline__ float scale16(uint16_t t) { return bf16_to_f32(t); }
 
 // Sum over the 16 lanes of a 16-lane row (the same value in every lane).
 __device__ __forceinline__ float sum16(float v) {
@@ -616,7 +617,7 @@ constexpr int kAStride = 2 * 32 + 4;  // u32 per staged activation row
 template <int RB, int P, int NBUF, int MAXG>
 struct alignas(16) WideSmem {
     uint32_t a[NBUF][P][RB * 16 * kAStride];  // after the K loop: group sums of the rows
-    uint32_t w[4][64 * 16];
+    uint32_t w[4][64 * 16];     // per-wave weight transposition buffer
     uint16_t ts[4][64 * MAXG];  // per-wave scales of its 64 weight rows
     float blk[2][4][RB * 16];   // [64-column group][16-column block][row]
 };

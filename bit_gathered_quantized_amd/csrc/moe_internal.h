@@ -44,13 +44,13 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
 }
 
 // ------------------------------------------------------------ dequant
-// The eight 4-bit codes of one weight word as eight bf16 values 1 + q/16:
-// q goes into the top four of the seven mantissa bits of 1.0, which bf16
+// The eight 4-bit codes of one weight word as eight bf16 values 16 + q:
+// q goes into the top four of the seven mantissa bits of 16.0, which bf16
 // holds exactly.  Element order in the MFMA operand is
 // [q0, q4, q1, q5, q2, q6, q3, q7]; the activation operand is stored in the
 // same order (permute8 below), so each code still meets its own column.
-// With P = sum_k x_k (1 + q_k/16) and X = sum_k x_k over a 64-column group,
-//   sum_k x_k (s q_k + b) = 16 s P + (b - 16 s) X.
+// With P = sum_k x_k (16 + q_k) and X = sum_k x_k over a 64-column group,
+//   sum_k x_k (s q_k + b) = s P + (b - 16 s) X.
 // The offset 16 (rather than, say, 128 + q) keeps P close in size to the
 // part that carries information, so little is lost when X is taken out.
 //
@@ -66,7 +66,7 @@ struct CodeConsts {
 // instruction may read only one scalar operand.
 __device__ __forceinline__ CodeConsts code_consts(uint32_t zero) {
     const uint32_t mask = (threadIdx.x & zero) ? 0u : 0x00780078u;
-    return CodeConsts{mask, 0x3F803F80u | zero};
+    return CodeConsts{mask, 0x41804180u | zero};
 }
 __device__ __forceinline__ u32x4 codes_as_bf16(uint32_t w, CodeConsts k) {
     u32x4 r;
@@ -76,7 +76,7 @@ __device__ __forceinline__ u32x4 codes_as_bf16(uint32_t w, CodeConsts k) {
     r[3] = ((w >> 9) & k.mask) | k.one;  // q3, q7
     return r;
 }
-constexpr float kCodeScale = 16.0f;
+constexpr float kCodeOffset = 16.0f;  // the 16 of 16 + q
 
 // Position of column c (0..7) of an 8-column piece after permute8.
 __device__ __forceinline__ int permuted_pos(int c) { return ((c & 3) << 1) | (c >> 2); }

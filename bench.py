@@ -40,8 +40,8 @@ def log(msg):
 
 def algorithmic_work(p):
     """Per-launch algorithmic bytes and flops of each kernel: what the method
-    must move and compute for the rows that kernel owns (tiles of <= 16 rows
-    go to the skinny kernels, larger tiles to the wide ones), not what a
+    must move and compute for the rows that kernel owns (experts of <= 16
+    rows go to the skinny kernels, larger ones to the wide kernels), not what a
     kernel happens to re-read."""
     import numpy as np
     E, H, I, T, k = p.E, p.H, p.I, p.T, p.k
@@ -51,16 +51,12 @@ def algorithmic_work(p):
     d_expert = H * I // 2 + 2 * (H * G_i * 2)
     ids = p.topk_ids.ravel()
     counts = np.bincount(ids, minlength=E)
-    # rows of each expert in skinny tiles: all of them if it has <= 16 rows,
-    # else its last tile when that has <= 16 rows
-    rem = counts % BM_BIG
-    skinny_rows = np.where((rem > 0) & (rem <= BM_SMALL), rem, 0)
+    # experts of <= 16 rows run as one skinny tile, larger ones in wide
+    # tiles; batches of <= 16 tokens run every expert on the skinny path
+    skinny_max = A if T <= BM_SMALL else BM_SMALL
+    skinny_rows = np.where(counts <= skinny_max, counts, 0)
     wide_rows = counts - skinny_rows
-    order = np.argsort(ids, kind="stable")
-    starts = np.concatenate([[0], np.cumsum(counts)[:-1]])
-    in_skinny = np.zeros(A, bool)
-    for e in np.nonzero(skinny_rows)[0]:
-        in_skinny[order[starts[e] + counts[e] - skinny_rows[e]: starts[e] + counts[e]]] = True
+    in_skinny = np.isin(ids, np.nonzero((counts > 0) & (counts <= skinny_max))[0])
     tok = np.arange(A) // k
     tok_s = np.unique(tok[in_skinny]).size
     tok_w = np.unique(tok[~in_skinny]).size

@@ -53,7 +53,7 @@ class MoeWsLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in
                 ("counts", "offsets", "perm", "inv_perm", "tiles", "num_tiles", "x_perm", "x_sums",
                  "h", "h_sums", "y", "total")] + \
-               [(n, ctypes.c_int32) for n in ("max_tiles", "bm_big", "bm_small", "reserved")] + \
+               [(n, ctypes.c_int32) for n in ("max_tiles", "bm_big", "bm_small", "max_skinny")] + \
                [("tiles_skinny", ctypes.c_size_t)]
 
 

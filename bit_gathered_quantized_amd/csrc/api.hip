@@ -38,6 +38,7 @@ moe_ws_layout make_layout(const moe_problem* p) {
     l.bm_big = (p->flags & MOE_F_FP32_INTERMEDIATE) ? moe::kBmBigF32 : moe::kBmBig;
     l.bm_small = moe::kBmSmall;
     l.max_tiles = moe_max_tiles(A, p->E, l.bm_big);
+    l.max_skinny = moe_max_tiles(A, p->E, l.bm_small);
     size_t off = 0;
     auto take = [&](size_t bytes) {
         const size_t at = off;
@@ -51,7 +52,7 @@ moe_ws_layout make_layout(const moe_problem* p) {
     l.perm = take(sizeof(int32_t) * A);
     l.inv_perm = take(sizeof(int32_t) * A);
     l.tiles = take(sizeof(moe_tile) * l.max_tiles);
-    l.tiles_skinny = take(sizeof(moe_tile) * l.max_tiles);
+    l.tiles_skinny = take(sizeof(moe_tile) * l.max_skinny);
     l.num_tiles = take(sizeof(int32_t) * 8);
     l.x_perm = take(sizeof(uint16_t) * p->T * p->H);
     l.x_sums = take(sizeof(float) * p->T * G);
@@ -102,6 +103,12 @@ moe_status forward_impl(const moe_problem* p, const void* x, const int32_t* ids,
     r.bm_big = l.bm_big;
     r.bm_small = l.bm_small;
     r.max_tiles = l.max_tiles;
+    r.max_skinny = l.max_skinny;
+    // At most bm_small tokens: no expert has more rows unless a token repeats
+    // an id, so every expert takes the skinny path (in tiles of bm_small) and
+    // the wide launches are left out.
+    const bool skinny_only = p->T <= l.bm_small;
+    r.skinny_max_rows = skinny_only ? INT32_MAX : l.bm_small;
     r.counts = reinterpret_cast<int32_t*>(base + l.counts);
     r.offsets = reinterpret_cast<int32_t*>(base + l.offsets);
     r.perm = reinterpret_cast<int32_t*>(base + l.perm);
@@ -123,6 +130,8 @@ moe_status forward_impl(const moe_problem* p, const void* x, const int32_t* ids,
     f.H = p->H;
     f.I = p->I;
     f.max_tiles = l.max_tiles;
+    f.max_skinny = l.max_skinny;
+    f.skinny_only = skinny_only ? 1 : 0;
     f.flags = p->flags;
     f.zero = 0;
     f.x = static_cast<const uint16_t*>(x);
@@ -195,6 +204,8 @@ moe_status moe_sort_build_tiles(const int32_t* topk_ids, int32_t T, int32_t k, i
     r.inv_perm = inv_perm;
     r.tiles = reinterpret_cast<int32_t*>(tiles);
     r.tiles_skinny = nullptr;
+    r.max_skinny = 0;
+    r.skinny_max_rows = bm_small;
     r.presorted = nullptr;
     r.num_tiles = num_tiles;
     r.x = nullptr;

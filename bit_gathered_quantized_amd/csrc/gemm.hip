@@ -36,10 +36,11 @@
 //    in MFMA operand order, with its group sums for the down matmul.
 //  * The down kernels scale each row by its routing weight and write it to
 //    its original (token, slot) position: the weighted unsort.
-//  * Each path reads its own tile list (tiles of more than 16 rows; short
-//    tails).  Grids are sized from bounds the host knows (at most one short
-//    tail per expert, at most A / 17 wide tiles) and workgroups past the
-//    list's device-side count exit at once: the host never reads it back.
+//  * Each path reads its own tile list (experts of more than 16 rows, cut
+//    into near-equal tiles; experts of 1..16 rows).  Grids are sized from
+//    bounds the host knows (at most one skinny tile per expert, at most
+//    A / 17 wide tiles) and workgroups past the list's device-side count exit
+//    at once: the host never reads it back.
 #include "moe_internal.h"
 
 namespace moe {
@@ -59,7 +60,7 @@ __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
 // of the skinny list; {-1, ..} past the list's device-side count.
 template <bool kSkinny>
 __device__ __forceinline__ int4 load_tile(const FfnArgs& a) {
-    const int n = min(a.num_tiles[kSkinny ? 3 : 2], a.max_tiles);
+    const int n = kSkinny ? min(a.num_tiles[3], a.max_skinny) : min(a.num_tiles[2], a.max_tiles);
     if (static_cast<int>(blockIdx.x) >= n) return int4{-1, 0, 0, 0};
     return reinterpret_cast<const int4*>(kSkinny ? a.tiles_skinny : a.tiles)[blockIdx.x];
 }
@@ -994,13 +995,16 @@ __global__ __launch_bounds__(kThreads, MAXG <= kWideMaxGSmall ? 2 : 1) void moe_
 
 }  // namespace
 
-// Grid widths: a skinny tile is an expert's short tail (at most one per
-// expert, at least one row); a wide tile has more than kBmSmall rows.
+// Grid widths: a skinny tile is a whole expert of <= 16 rows (at most one per
+// expert, at least one row), or with skinny_only a piece of <= 16 rows of
+// one (at most one short piece per expert); a wide tile has more than
+// kBmSmall rows.
 static int skinny_grid(const FfnArgs& a) {
-    return min(a.max_tiles, min(a.E, a.T * a.k));
+    const int A = a.T * a.k;
+    return min(a.max_skinny, min(a.E, A) + (a.skinny_only ? A / kBmSmall : 0));
 }
 static int wide_grid(const FfnArgs& a) {
-    return min(a.max_tiles, a.T * a.k / (kBmSmall + 1));
+    return a.skinny_only ? 0 : min(a.max_tiles, a.T * a.k / (kBmSmall + 1));
 }
 
 // No tile can be wide: nothing to launch, but the timing events still mark

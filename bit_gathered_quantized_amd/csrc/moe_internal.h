@@ -20,10 +20,12 @@ constexpr int kGroup = 64;      // quantisation group (columns per scale/bias)
 constexpr int kRouteThreads = 1024;
 constexpr int kRouteWaves = kRouteThreads / 64;
 
-// Tile heights used by the forward's own routing: tiles of up to 96 rows of
-// one expert; a tile of at most 16 rows (decode-sized, or the short end of an
-// expert) takes the skinny path, larger ones the wide path.  96 rows = 6 row
-// blocks per wave keeps the wide kernels within 256 vector registers.
+// Tile heights used by the forward's own routing: an expert of at most 16
+// rows is one skinny tile; a larger one is cut into ceil(rows / 64) wide
+// tiles of near-equal height (17..64 rows each), so no expert leaves a short
+// tail that reads its weights once more.  64 rows = 4 row blocks per wave
+// keeps the wide kernels within 256 vector registers (32 rows with fp32
+// intermediates).
 constexpr int kBmBig = 64;
 constexpr int kBmBigF32 = 32;  // with MOE_F_FP32_INTERMEDIATE
 constexpr int kBmSmall = 16;
@@ -142,10 +144,13 @@ struct RouteArgs {
     const int32_t* ids;
     int32_t A, E, bm_big, bm_small, max_tiles;
     int32_t *counts, *offsets, *perm, *inv_perm, *tiles, *num_tiles;
-    // nullptr: one tile list in expert order, num_tiles [2].  Otherwise tiles
-    // gets the tiles of more than bm_small rows and tiles_skinny the others,
-    // each in expert order; num_tiles [4] = {total, invalid ids, wide, skinny}.
+    // nullptr: one tile list in expert order, num_tiles [2].  Otherwise experts
+    // of more than skinny_max_rows rows go to tiles (balanced, bm_big at
+    // most), the others to tiles_skinny in tiles of bm_small (at most
+    // max_skinny entries), each list in expert order; num_tiles [4] =
+    // {total, invalid ids, wide, skinny}.
     int32_t* tiles_skinny;
+    int32_t skinny_max_rows, max_skinny;
     // A caller's slot -> assignment order, sorted by expert (or nullptr).
     // Checked on the device: num_tiles[4] = 0 if used, 1 if not sorted or out
     // of range, 2 if not a permutation; in both failure cases the kernel sorts
@@ -162,6 +167,8 @@ size_t route_lds_bytes(int E);
 
 struct FfnArgs {
     int32_t T, k, E, H, I, max_tiles;
+    int32_t max_skinny;   // capacity of tiles_skinny
+    int32_t skinny_only;  // 1: every tile is skinny, the wide launches are skipped
     uint32_t flags;
     uint32_t zero;       // always 0 (see CodeConsts)
     const uint16_t* x;

@@ -15,8 +15,10 @@
 //      wave match-any: one ballot per key bit): a stable counting sort;
 //   4. tiles per expert = ceil(count / bm_big), scanned; thread i emits tile i
 //      after an upper-bound search of the scanned tile offsets.  The forward
-//      asks for two lists instead (tiles of more than bm_small rows, and the
-//      short tails), so that each matmul launch only covers its own tiles.
+//      asks for two lists instead, with balanced tiles: experts of at most
+//      bm_small rows get one short tile, larger experts ceil(count / bm_big)
+//      tiles of near-equal size, so that each matmul launch only covers its
+//      own tiles and no expert's weights are read again for a short tail.
 //
 // In the forward, the other workgroups of the same launch prepare the
 // activations for the matmuls (prepare_x).
@@ -277,15 +279,20 @@ __global__ __launch_bounds__(kRouteThreads) void moe_route_sort_tiles(RouteArgs 
         }
         if (tid == 0) a.num_tiles[0] = total;
     } else {
-        // two lists, each in expert order: tiles of more than bm_small rows
-        // (full tiles and long tails) and tiles of at most bm_small rows (an
-        // expert's short tail; at most one per expert)
+        // two lists, each in expert order.  An expert of at most bm_small rows
+        // is one short tile; a larger one is cut into ceil(c / bm_big) tiles
+        // of near-equal size (the first c % n one row longer), every one of
+        // them above bm_small rows: no expert ends in a short tail that would
+        // read its weights once more for a few rows.
+        // Experts of more than skinny_max_rows rows are wide (normally
+        // skinny_max_rows = bm_small; when it is larger, the short list holds
+        // consecutive tiles of bm_small rows, the last one shorter).
         int32_t* s_ns = s_tab + nkeys;
         for (int e = tid; e < E; e += kRouteThreads) {
-            const int c = s_cnt[e], tail = c % a.bm_big;
-            const bool short_tail = tail > 0 && tail <= a.bm_small;
-            s_tab[e] = c / a.bm_big + (tail > a.bm_small ? 1 : 0);
-            s_ns[e] = short_tail ? 1 : 0;
+            const int c = s_cnt[e];
+            const bool wide = c > a.skinny_max_rows;
+            s_tab[e] = wide ? (c + a.bm_big - 1) / a.bm_big : 0;
+            s_ns[e] = wide ? 0 : (c + a.bm_small - 1) / a.bm_small;
         }
         __syncthreads();
         block_exclusive_scan(s_tab, s_toff, E, s_wsum);
@@ -293,13 +300,16 @@ __global__ __launch_bounds__(kRouteThreads) void moe_route_sort_tiles(RouteArgs 
         const int nw = s_toff[E], ns = s_soff[E];
         for (int i = tid; i < nw && i < a.max_tiles; i += kRouteThreads) {
             const int e = upper_bound(s_toff, E + 1, i) - 1;
-            const int row0 = (i - s_toff[e]) * a.bm_big;
-            write_tile(a.tiles + 4 * i, e, s_off[e] + row0, min(a.bm_big, s_cnt[e] - row0), a.bm_big);
+            const int c = s_cnt[e], n = s_toff[e + 1] - s_toff[e], j = i - s_toff[e];
+            const int base = c / n, extra = c - base * n;
+            const int row0 = j * base + min(j, extra);
+            write_tile(a.tiles + 4 * i, e, s_off[e] + row0, base + (j < extra ? 1 : 0), a.bm_big);
         }
-        for (int i = tid; i < ns && i < a.max_tiles; i += kRouteThreads) {
+        for (int i = tid; i < ns && i < a.max_skinny; i += kRouteThreads) {
             const int e = upper_bound(s_soff, E + 1, i) - 1;
-            const int tail = s_cnt[e] % a.bm_big;
-            write_tile(a.tiles_skinny + 4 * i, e, s_off[e] + s_cnt[e] - tail, tail, a.bm_small);
+            const int row0 = (i - s_soff[e]) * a.bm_small;
+            write_tile(a.tiles_skinny + 4 * i, e, s_off[e] + row0, min(a.bm_small, s_cnt[e] - row0),
+                       a.bm_small);
         }
         if (tid == 0) {
             a.num_tiles[0] = nw + ns;

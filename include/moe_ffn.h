@@ -158,8 +158,10 @@ typedef struct {
     size_t offsets;   /* int32 [E+1]                                      */
     size_t perm;      /* int32 [A]                                        */
     size_t inv_perm;  /* int32 [A]                                        */
-    size_t tiles;     /* moe_tile [max_tiles]: the tiles of more than
-                         bm_small rows, in expert order                   */
+    size_t tiles;     /* moe_tile [max_tiles]: the tiles of the experts of
+                         more than bm_small rows, ceil(count / bm_big) of
+                         near-equal size per expert, in expert order
+                         (empty when T <= bm_small)                       */
     size_t num_tiles; /* int32 [8]: total tiles, out-of-range ids, tiles
                          in `tiles`, tiles in `tiles_skinny`, and the
                          order check of the pre-sorted entry (0 used,
@@ -179,10 +181,14 @@ typedef struct {
     int32_t max_tiles;
     int32_t bm_big;
     int32_t bm_small;
-    int32_t reserved;
-    size_t tiles_skinny; /* moe_tile [max_tiles]: the tiles of at most
-                            bm_small rows (an expert's short tail), in
-                            expert order                                  */
+    int32_t max_skinny;
+    size_t tiles_skinny; /* moe_tile [max_skinny]: tiles of at most bm_small
+                            rows, in expert order: one per expert of 1 to
+                            bm_small rows.  When T <= bm_small (no expert
+                            can have more rows unless a token repeats an
+                            id) every expert is put here instead, in
+                            consecutive tiles of bm_small rows, the last
+                            one shorter, and `tiles` stays empty         */
 } moe_ws_layout;
 
 moe_status moe_ffn_workspace_layout(const moe_problem* p, moe_ws_layout* layout);

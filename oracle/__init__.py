@@ -105,6 +105,34 @@ def tiles(counts: np.ndarray, offsets: np.ndarray, bm_big: int = 32, bm_small: i
     return out[:n]
 
 
+def forward_tiles(counts: np.ndarray, offsets: np.ndarray, bm_big: int, bm_small: int,
+                  short_only: bool = False):
+    """The forward's own tile lists, written out plainly: an expert of
+    1..bm_small rows is one short tile; a larger one is cut into
+    n = ceil(count / bm_big) tiles, tile j holding count // n rows plus one
+    if j < count % n, consecutively.  With short_only (the forward's choice
+    for batches of at most bm_small tokens) every expert goes to the short
+    list instead, as consecutive tiles of bm_small rows, the last one
+    shorter.  Returns (wide [m, 4], short [s, 4])."""
+    wide, short = [], []
+    for e, c in enumerate(np.asarray(counts).tolist()):
+        o = int(offsets[e])
+        if c == 0:
+            continue
+        if c <= bm_small or short_only:
+            for r0 in range(0, c, bm_small):
+                short.append([e, o + r0, min(bm_small, c - r0), bm_small])
+            continue
+        n = -(-c // bm_big)
+        base, extra = divmod(c, n)
+        row = o
+        for j in range(n):
+            r = base + (1 if j < extra else 0)
+            wide.append([e, row, r, bm_big])
+            row += r
+    return (np.array(wide, np.int32).reshape(-1, 4), np.array(short, np.int32).reshape(-1, 4))
+
+
 def weight(P: np.ndarray, S: np.ndarray, B: np.ndarray, gs: int, e: int, n: int, c: int) -> float:
     """One dequantised weight W[e, n, c] of a packed [E, rows, K/8] matrix."""
     E, rows, kw = P.shape

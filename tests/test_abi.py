@@ -49,7 +49,9 @@ def test_workspace_layout_and_sizes():
     assert lay.bm_big == 64 and lay.bm_small == 16
     assert lay.max_tiles == A // 64 + 128
     assert lay.tiles_skinny - lay.tiles >= 16 * lay.max_tiles
-    assert lay.num_tiles - lay.tiles_skinny >= 16 * lay.max_tiles
+    assert lay.num_tiles - lay.tiles_skinny >= 16 * lay.max_skinny
+    # the short list holds every expert in 16-row pieces when T <= 16
+    assert lay.max_skinny == bgq.max_tiles(p.T * p.k, p.E, lay.bm_small)
     p32 = bgq.problem(2048, 8, 128, 2816, 704, bgq.MOE_F_FP32_INTERMEDIATE)
     l32 = bgq.workspace_layout(p32)
     assert l32.h_sums - l32.h >= A * 704 * 4

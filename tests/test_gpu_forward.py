@@ -5,6 +5,8 @@ tokens (all k assignments of each), in the same launch configuration the
 benchmark times.  Intermediates (h in sorted order, weighted y in flat
 order) are read from the documented workspace layout and compared too.
 """
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -56,6 +58,46 @@ def test_tiny_full(oracle_lib, fp32):
 @pytest.mark.parametrize("fp32", [False, True])
 def test_decode_full(oracle_lib, fp32):
     compare(oracle_lib, ms.make_config("decode"), fp32)
+
+
+@pytest.mark.parametrize("fp32", [False, True])
+def test_small_batch_repeated_ids(oracle_lib, fp32):
+    """At most 16 tokens the forward routes every expert to the skinny path;
+    an expert gets more than 16 rows only when tokens repeat an id, and is
+    then cut into 16-row pieces (here expert 3, 26 rows)."""
+    T, k, E = 6, 8, 8
+    ids = np.full((T, k), 3, np.int32)
+    ids[:, 4:] = 5
+    ids[4:, 4:] = np.arange(4)[None, :] + 1
+    ids[0, 7] = 7
+    p = ms.make_problem(E, 256, 128, T, k, seed=21, topk_ids=ids, name="repeats")
+    _, ws, lay = run_forward(p, fp32=fp32)
+    counts = np.bincount(ids.ravel(), minlength=E)
+    assert counts[3] == 26
+    nt = ws_view(ws, lay.num_tiles, 4, np.int32)
+    assert nt[2] == 0 and nt[3] == np.sum(-(-counts // 16))
+    compare(oracle_lib, p, fp32)
+
+
+@pytest.mark.parametrize("fp32", [False, True])
+def test_small_batch_matches_large(oracle_lib, fp32):
+    """The 8 decode tokens give the same bits when 24 more tokens join them
+    (then the larger experts take the wide path)."""
+    a = ms.make_config("decode")
+    b = ms.make_problem(a.E, a.H, a.I, 32, a.k, seed=3, name="decode+24")
+    for f in ("w_gateup", "s_gateup", "b_gateup", "w_down", "s_down", "b_down"):
+        setattr(b, f, getattr(a, f))
+    b.x[:8] = a.x
+    b.topk_ids[:8] = a.topk_ids
+    b.topk_weights[:8] = a.topk_weights
+    b.topk_ids[8:, 0] = a.topk_ids[0, 0]  # one expert of 25 rows
+    b.topk_ids[8:, 1:] = np.where(b.topk_ids[8:, 1:] == a.topk_ids[0, 0], (a.topk_ids[0, 0] + 1) % a.E,
+                                  b.topk_ids[8:, 1:])
+    assert all(len(set(r)) == a.k for r in b.topk_ids.tolist())
+    oa, _, _ = run_forward(a, fp32=fp32)
+    ob, ws, lay = run_forward(b, fp32=fp32)
+    assert ws_view(ws, lay.num_tiles, 4, np.int32)[2] >= 1
+    np.testing.assert_array_equal(ob[:8], oa)
 
 
 # Two GPU memory faults, causes not found by reading the code (every kernel's
@@ -164,52 +206,64 @@ def test_prepared_activations_and_h_sums(fp32):
     assert np.abs(hs - href).max() <= 1e-5 * np.abs(href).max()
 
 
-def _skinny_and_wide_problem():
-    """Expert 0 gets 140 rows: wide tiles (2 x 64, or 4 x 32 with an fp32 h)
-    and a 12-row skinny tile,
-    so permuting tokens moves rows between the two paths."""
-    T, k, E = 150, 2, 4
+def _expert0_rows(n_extra):
+    """20 tokens, 10 of them routed to expert 0 (slot 0); n_extra more tokens
+    also go to expert 0, which moves its rows from the skinny path (10 rows)
+    to the wide path (10 + n_extra rows)."""
+    T, k, E = 20 + n_extra, 2, 4
     rng = np.random.default_rng(11)
     ids = np.zeros((T, k), np.int32)
     ids[:, 1] = rng.integers(1, E, size=T)
-    ids[140:, 0] = (ids[140:, 1] % (E - 1)) + 1
-    ids[140:, 1] = np.where(ids[140:, 0] == ids[140:, 1], 0, ids[140:, 1])
-    return ms.make_problem(E, 256, 128, T, k, seed=12, topk_ids=ids, name="mixed")
+    ids[10:20, 0] = ids[10:20, 1] % (E - 1) + 1
+    ids[10:20, 1] = np.where(ids[10:20, 0] == ids[10:20, 1], 0, ids[10:20, 1])
+    ids[10:20, 1] = np.where(ids[10:20, 1] == 0, 3, ids[10:20, 1])
+    p = ms.make_problem(E, 256, 128, T, k, seed=12, topk_ids=ids, name=f"e0+{n_extra}")
+    return p
 
 
 @pytest.mark.parametrize("fp32", [False, True])
 def test_rows_bitwise_independent_of_tile_path(oracle_lib, fp32):
-    p = _skinny_and_wide_problem()
-    counts = np.bincount(p.topk_ids.ravel(), minlength=p.E)
-    assert counts[0] == 140 or counts[0] == 140 + np.sum(p.topk_ids[140:] == 0)
-    o1 = compare(oracle_lib, p, fp32)
-    perm = np.random.default_rng(5).permutation(p.T)
-    q = _skinny_and_wide_problem()
-    q.x = np.ascontiguousarray(p.x[perm])
-    q.topk_ids = np.ascontiguousarray(p.topk_ids[perm])
-    q.topk_weights = np.ascontiguousarray(p.topk_weights[perm])
-    o2, _, _ = run_forward(q, fp32=fp32)
-    np.testing.assert_array_equal(o2, o1[perm])
+    """The same token's output is bit-identical whether its expert's rows run
+    as one skinny tile (10 rows) or in wide tiles (10 + 30 rows)."""
+    a = _expert0_rows(0)
+    b = _expert0_rows(30)
+    b.x[:20] = a.x
+    b.topk_weights[:20] = a.topk_weights
+    for f in ("w_gateup", "s_gateup", "b_gateup", "w_down", "s_down", "b_down"):
+        setattr(b, f, getattr(a, f))
+    assert np.array_equal(b.topk_ids[:20], a.topk_ids)
+    assert np.count_nonzero(a.topk_ids == 0) == 10 and np.count_nonzero(b.topk_ids == 0) == 40
+    oa = compare(oracle_lib, a, fp32)
+    ob = compare(oracle_lib, b, fp32)
+    np.testing.assert_array_equal(ob[:20], oa)
+    # and a token permutation only permutes the output
+    perm = np.random.default_rng(5).permutation(b.T)
+    q = dataclasses.replace(b)
+    q.x = np.ascontiguousarray(b.x[perm])
+    q.topk_ids = np.ascontiguousarray(b.topk_ids[perm])
+    q.topk_weights = np.ascontiguousarray(b.topk_weights[perm])
+    oq, _, _ = run_forward(q, fp32=fp32)
+    np.testing.assert_array_equal(oq, ob[perm])
 
 
 @pytest.mark.parametrize("name,fp32", [("prefill16k", False), ("prefill4k", True),
-                                        ("decode", False)])
+                                        ("decode", False), ("tiny", False)])
 def test_forward_tile_lists(oracle_lib, name, fp32):
-    """The forward routes into two lists: tiles of more than 16 rows and the
-    short tails, each in expert order.  Together they are exactly the
-    oracle's tiles at the forward's tile height."""
+    """The forward routes into two lists, each in expert order: experts of
+    more than 16 rows cut into near-equal tiles, and experts of 1..16 rows.
+    Bit-exact against the oracle's plain statement of that rule."""
     p = ms.make_config(name)
     _, ws, lay = run_forward(p, fp32=fp32)
     counts, offsets, _, _, _ = oracle_lib.route(p.topk_ids, p.E)
-    ref = np.asarray(oracle_lib.tiles(counts, offsets, lay.bm_big, lay.bm_small), np.int32)
-    ref = ref.reshape(-1, 4)
+    rw, rs = oracle_lib.forward_tiles(counts, offsets, lay.bm_big, lay.bm_small,
+                                      short_only=p.T <= lay.bm_small)
     nt = ws_view(ws, lay.num_tiles, 4, np.int32)
     wide = ws_view(ws, lay.tiles, 4 * int(nt[2]), np.int32).reshape(-1, 4)
     short = ws_view(ws, lay.tiles_skinny, 4 * int(nt[3]), np.int32).reshape(-1, 4)
-    log(f"  {name}: {len(ref)} tiles = {len(wide)} wide + {len(short)} short")
-    assert nt[0] == len(ref) == len(wide) + len(short)
-    np.testing.assert_array_equal(wide, ref[ref[:, 2] > lay.bm_small])
-    np.testing.assert_array_equal(short, ref[ref[:, 2] <= lay.bm_small])
+    log(f"  {name}: {len(wide)} wide + {len(short)} short tiles")
+    assert nt[0] == len(rw) + len(rs)
+    np.testing.assert_array_equal(wide, rw)
+    np.testing.assert_array_equal(short, rs)
 
 
 @pytest.mark.parametrize("name,fp32", [("tiny", False), ("tiny", True), ("decode", False),

@@ -370,3 +370,39 @@ def test_router_matches_library_routines(oracle_lib, E, k):
     ids2, w2 = oracle_lib.router_topk(logits + np.float32(4.0), k)
     np.testing.assert_array_equal(ids2, ids)
     np.testing.assert_allclose(w2, w, rtol=1e-6)
+
+
+# ---------------------------------------------------- forward tile lists
+def test_forward_tiles_hand_example(oracle_lib):
+    """bm_big 64, bm_small 16; counts 0, 5, 16, 17, 64, 65, 130 (offsets are
+    their running sum): experts 1 and 2 are short tiles; 17 and 64 one tile
+    each; 65 -> 33 + 32; 130 -> 44 + 43 + 43."""
+    counts = np.array([0, 5, 16, 17, 64, 65, 130], np.int32)
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    wide, short = oracle_lib.forward_tiles(counts, offsets, 64, 16)
+    assert short.tolist() == [[1, 0, 5, 16], [2, 5, 16, 16]]
+    assert wide.tolist() == [[3, 21, 17, 64], [4, 38, 64, 64], [5, 102, 33, 64], [5, 135, 32, 64],
+                             [6, 167, 44, 64], [6, 211, 43, 64], [6, 254, 43, 64]]
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_forward_tiles_invariants(oracle_lib, seed):
+    rng = np.random.default_rng(seed)
+    counts = rng.integers(0, 300, size=50).astype(np.int32)
+    counts[rng.integers(0, 50, 10)] = rng.integers(0, 17, 10)
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    wide, short = oracle_lib.forward_tiles(counts, offsets, 64, 16)
+    for e, c in enumerate(counts):
+        w = wide[wide[:, 0] == e]
+        s = short[short[:, 0] == e]
+        if c == 0:
+            assert len(w) == len(s) == 0
+        elif c <= 16:
+            assert len(w) == 0 and s.tolist() == [[e, offsets[e], c, 16]]
+        else:
+            assert len(s) == 0 and len(w) == -(-c // 64)
+            assert np.all(w[:, 2] > 16) and np.all(w[:, 2] <= 64)
+            assert w[:, 2].max() - w[:, 2].min() <= 1
+            # consecutive, covering the expert's rows exactly
+            assert w[0, 1] == offsets[e] and np.all(w[1:, 1] == w[:-1, 1] + w[:-1, 2])
+            assert w[:, 2].sum() == c

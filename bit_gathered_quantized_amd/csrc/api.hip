@@ -57,7 +57,7 @@ moe_ws_layout make_layout(const moe_problem* p) {
     l.x_perm = take(sizeof(uint16_t) * p->T * p->H);
     l.x_sums = take(sizeof(float) * p->T * G);
     l.h = take(hbytes * A * p->I);
-    l.h_sums = take(sizeof(float) * A * GI);
+    l.h_sums = take(sizeof(float) * A * (p->I / 16));
     l.y = take(sizeof(float) * A * p->H);
     l.total = off;
     return l;

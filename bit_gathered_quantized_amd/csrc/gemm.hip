@@ -19,10 +19,11 @@
 //    weights to bf16 instead would cost the accuracy the fp32 path needs.
 //  * Activations come pre-ordered (x_perm, from the route launch) with their
 //    group sums, so nothing here reorders or sums activations on the fly.
-//  * Skinny path, tiles of <= 16 rows (decode): no activation staging and
-//    no barrier in the K loop; each wave streams its own weight rows (16-byte
-//    coalesced loads, turned into operand order through a per-wave LDS
-//    buffer) with RING chunks of loads in flight.
+//  * Skinny path, tiles of <= 16 rows (decode): one wave per workgroup, no
+//    activation staging and no barrier; each wave streams its own weight
+//    rows (16-byte coalesced loads, turned into operand order through a
+//    small LDS buffer) with RING chunks of loads in flight, and issues the
+//    MFMA chains of a chunk's groups and blocks together.
 //  * Wide path, tiles of 17..64 rows (prefill): the activation tile is
 //    staged in LDS, double-buffered; each wave owns 4 column blocks and all
 //    row blocks, so a decoded weight word feeds every row block and an LDS
@@ -33,7 +34,8 @@
 //    (hence not on the order of the tokens).
 //  * Gate and up of an output column sit in the same lane: the GeGLU (or
 //    SwiGLU) product is formed in registers and h is written once, already
-//    in MFMA operand order, with its group sums for the down matmul.
+//    in MFMA operand order, with its 16-column block sums, from which the
+//    down matmul forms the group sums it needs.
 //  * The down kernels scale each row by its routing weight and write it to
 //    its original (token, slot) position: the weighted unsort.
 //  * Each path reads its own tile list (experts of more than 16 rows, cut
@@ -47,8 +49,9 @@ namespace moe {
 namespace {
 
 constexpr int kThreads = 256;
-// skinny paths: 16-column blocks per wave and weight chunks in flight
-constexpr int kSkinnyGateUpPairs = 1, kSkinnyGateUpRing = 2;
+// skinny paths (one wave per workgroup): 16-column weight blocks per wave
+// and weight chunks in flight
+constexpr int kSkinnyGateUpRing = 2;
 constexpr int kSkinnyDownBlocks = 2, kSkinnyDownRing = 2;
 constexpr int kMaxG = kMaxDim / kGroup;    // groups per row the LDS tables hold
 
@@ -142,6 +145,13 @@ __device__ __forceinline__ void bias_from_scales(BiasOp& o, const uint16_t* ts, 
     }
 }
 
+// Group sum g of h from its four 16-column block sums (h_sums row X16):
+// ((b0 + b1) + b2) + b3, the one order every path uses.
+__device__ __forceinline__ float group_of_blocks(const float* X16, int g) {
+    const f32x4 b = *reinterpret_cast<const f32x4*>(X16 + 4 * g);
+    return ((b[0] + b[1]) + b[2]) + b[3];
+}
+
 // The group sums of one activation row as the bias operand.
 struct RowSums {
     float v[kMaxBiasSteps][8];
@@ -151,6 +161,13 @@ struct RowSums {
         for (int st = 0; st < kMaxBiasSteps; ++st)
 #pragma unroll
             for (int j = 0; j < 8; ++j) v[st][j] = X[min(32 * st + 8 * q + j, G - 1)];
+    }
+    // from the 16-column block sums of the row (4 G floats)
+    __device__ __forceinline__ void load_blocks(const float* X16, int G, int q) {
+#pragma unroll
+        for (int st = 0; st < kMaxBiasSteps; ++st)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) v[st][j] = group_of_blocks(X16, min(32 * st + 8 * q + j, G - 1));
     }
     __device__ __forceinline__ void pack(BiasOp& o, int G, int q, int steps) const {
 #pragma unroll
@@ -203,6 +220,31 @@ __device__ __forceinline__ f32x4 group_step2(f32x4 acc, u32x4 a0h, u32x4 a0l, u3
     return acc;
 }
 
+// Both groups of one chunk for NB weight blocks: the MFMA chains of all
+// (block, group) pairs are issued together, then each block takes its two
+// scaled products in group order -- group_step's arithmetic, pair by pair.
+template <int NB>
+__device__ __forceinline__ void chunk_steps(f32x4 (&acc)[NB], const u32x4 (&x)[4], const u32x4 (&wv)[NB],
+                                            const float (&s16)[NB][2], CodeConsts kc) {
+    f32x4 p[NB][2];
+#pragma unroll
+    for (int gi = 0; gi < 2; ++gi)
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+            p[b][gi] = mfma16(x[2 * gi], codes_as_bf16(wv[b][2 * gi], kc), f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+    for (int gi = 0; gi < 2; ++gi)
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+            p[b][gi] = mfma16(x[2 * gi + 1], codes_as_bf16(wv[b][2 * gi + 1], kc), p[b][gi]);
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int gi = 0; gi < 2; ++gi)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) acc[b][v] = fmaf(s16[b][gi], p[b][gi][v], acc[b][v]);
+}
+
 // A bf16 scale as the factor of P.
 __device__ __forceinline__ float scale16(uint16_t t) { return bf16_to_f32(t); }
 
@@ -232,13 +274,6 @@ __device__ __forceinline__ float store_h(const FfnArgs& a, size_t A, int srow, i
     }
     if (valid) h[pos] = hi;
     return valid ? seen : 0.f;
-}
-
-// X_h[row][group] = ((b0 + b1) + b2) + b3 over the four 16-column blocks of a
-// 64-column group of h, each block sum taken by sum16.
-__device__ __forceinline__ float hsum_of(const float* b0, const float* b1, const float* b2,
-                                         const float* b3, int r) {
-    return ((b0[r] + b1[r]) + b2[r]) + b3[r];
 }
 
 // ================================================== weights through LDS
@@ -329,45 +364,40 @@ struct Tables {
 };
 
 // =========================================================== skinny paths
-// W waves of NB 16-row weight blocks each.
-template <int W, int NB>
+// One wave's LDS: NB 16-row weight blocks.
+template <int NB>
 struct alignas(16) SkinnySmem {
-    uint32_t w[W][NB * 16 * 16];      // per-wave weight transposition buffer
-    uint16_t ts[W][NB * 16 * kMaxG];  // per-wave scales of its weight rows
-    uint16_t tb[W][NB * 16 * kMaxG];  // per-wave biases
-    float blk[W][NB / 2][kBmSmall];   // gate|up: 16-column block sums of h
+    uint32_t w[NB * 16 * 16];      // weight transposition buffer
+    uint16_t ts[NB * 16 * kMaxG];  // scales of the wave's weight rows
+    uint16_t tb[NB * 16 * kMaxG];  // biases
 };
 
-// gate|up, tiles of <= 16 rows.  Grid (max_tiles, I / 64): a workgroup owns
-// one 64-column group of h, W = 4 / NP waves of NP 16-column blocks each
-// (wave w: columns 16 NP w + [0, 16 NP)).  Block p of a wave is the pair of
-// weight blocks gate p (block p) and up p (block NP + p).  RING chunks of
-// weights are in flight per wave.
-template <bool kF32H, int NP, int RING>
-__global__ __launch_bounds__(256 / NP) void moe_gateup_skinny(FfnArgs a) {
-    constexpr int W = 4 / NP, NB = 2 * NP;
-    __shared__ SkinnySmem<W, NB> sm;
+// gate|up, tiles of <= 16 rows.  Grid (skinny tiles, I / 16): one wave per
+// workgroup owns 16 columns of h, i.e. weight block gate (rows n0 .. n0 + 15)
+// and block up (rows I + n0 ..), and writes their 16-column block sums of h.
+// RING chunks of weights are in flight.
+template <bool kF32H, int RING>
+__global__ __launch_bounds__(64) void moe_gateup_skinny(FfnArgs a) {
+    constexpr int NB = 2;
+    __shared__ SkinnySmem<NB> sm;
     const int4 tile = load_tile<true>(a);
     if (tile.x < 0) return;
     const int e = tile.x, row_begin = tile.y, rows = tile.z;
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, q = lane >> 4, lr = lane & 15;
+    const int lane = threadIdx.x & 63, q = lane >> 4, lr = lane & 15;
     const int H = a.H, I = a.I, G = H / kGroup;
     const size_t A = static_cast<size_t>(a.T) * a.k;
-    const int hcol0 = blockIdx.y * 64 + 16 * NP * wave;
+    const int hcol0 = blockIdx.y * 16;
 
     size_t row0[NB];
     const uint32_t* blk[NB];
-#pragma unroll
-    for (int p = 0; p < NP; ++p) {
-        row0[p] = static_cast<size_t>(e) * 2 * I + hcol0 + 16 * p;
-        row0[NP + p] = row0[p] + I;
-    }
+    row0[0] = static_cast<size_t>(e) * 2 * I + hcol0;
+    row0[1] = row0[0] + I;
 #pragma unroll
     for (int b = 0; b < NB; ++b) blk[b] = a.w_gu + row0[b] * (H / 8);
     Tables<NB> tab;
     tab.load(a.s_gu, a.b_gu, row0, G);
     WaveW<NB> ww;
-    ww.init(sm.w[wave], blk, H / 8);
+    ww.init(sm.w, blk, H / 8);
     u32x4 rv[RING][NB];
 #pragma unroll
     for (int i = 0; i < RING; ++i) ww.load(i, rv[i]);
@@ -387,9 +417,7 @@ __global__ __launch_bounds__(256 / NP) void moe_gateup_skinny(FfnArgs a) {
     };
     load_a(0, 0);
 
-    uint16_t* const ts = sm.ts[wave];
-    uint16_t* const tb = sm.tb[wave];
-    tab.store(ts, tb, G);
+    tab.store(sm.ts, sm.tb, G);
     __builtin_amdgcn_wave_barrier();
 
     f32x4 acc[NB];
@@ -398,7 +426,7 @@ __global__ __launch_bounds__(256 / NP) void moe_gateup_skinny(FfnArgs a) {
     const int nch = (G + 1) / 2;
     const CodeConsts kc = code_consts(a.zero);
     // chunk c: its weights go through LDS, the slot reloads with chunk c + RING
-    // at once, then the MFMAs run
+    // at once, then the MFMAs run (an odd G ends with a one-group chunk)
     auto compute = [&](int slot, int abuf, int c, bool reload) {
         ww.put(rv[slot]);
         if (reload) ww.load(c + RING, rv[slot]);
@@ -406,16 +434,18 @@ __global__ __launch_bounds__(256 / NP) void moe_gateup_skinny(FfnArgs a) {
         u32x4 wv[NB];
 #pragma unroll
         for (int b = 0; b < NB; ++b) wv[b] = ww.get(b, lr, q);
+        if (2 * c + 1 < G) {
+            float s16[NB][2];
 #pragma unroll
-        for (int gi = 0; gi < 2; ++gi) {
-            const int g = 2 * c + gi;
-            if (g < G) {
+            for (int b = 0; b < NB; ++b)
 #pragma unroll
-                for (int b = 0; b < NB; ++b)
-                    acc[b] = group_step(acc[b], ra[abuf][2 * gi], ra[abuf][2 * gi + 1],
-                                        codes_as_bf16(wv[b][2 * gi], kc), codes_as_bf16(wv[b][2 * gi + 1], kc),
-                                        scale16(ts[(16 * b + lr) * G + g]));
-            }
+                for (int gi = 0; gi < 2; ++gi) s16[b][gi] = scale16(sm.ts[(16 * b + lr) * G + 2 * c + gi]);
+            chunk_steps<NB>(acc, ra[abuf], wv, s16, kc);
+        } else {
+#pragma unroll
+            for (int b = 0; b < NB; ++b)
+                acc[b] = group_step(acc[b], ra[abuf][0], ra[abuf][1], codes_as_bf16(wv[b][0], kc),
+                                    codes_as_bf16(wv[b][1], kc), scale16(sm.ts[(16 * b + lr) * G + 2 * c]));
         }
         __builtin_amdgcn_wave_barrier();
     };
@@ -445,46 +475,35 @@ __global__ __launch_bounds__(256 / NP) void moe_gateup_skinny(FfnArgs a) {
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
             BiasOp C;
-            bias_from_table(C, ts + (16 * b + lr) * G, tb + (16 * b + lr) * G, G, q, steps, true);
+            bias_from_table(C, sm.ts + (16 * b + lr) * G, sm.tb + (16 * b + lr) * G, G, q, steps, true);
             acc[b] += bias_mfma(X, C, steps);
         }
     }
 
-    // GeGLU, h once, and the 16-column block sums of h per row
+    // GeGLU, h once, and the 16-column block sum of h per row
 #pragma unroll
-    for (int p = 0; p < NP; ++p) {
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-            const int r = 4 * q + v;
-            const float seen = store_h<kF32H>(a, A, row_begin + r, hcol0 + 16 * p + lr, acc[p][v],
-                                              acc[NP + p][v], r < rows);
-            const float s = sum16(seen);
-            if (lr == 0) sm.blk[wave][p][r] = s;
-        }
-    }
-    __syncthreads();
-    if (tid < rows) {
-        const float* b0 = &sm.blk[0][0][0];  // the four 16-column blocks in column order
-        a.hs[static_cast<size_t>(row_begin + tid) * (I / kGroup) + blockIdx.y] =
-            hsum_of(b0, b0 + kBmSmall, b0 + 2 * kBmSmall, b0 + 3 * kBmSmall, tid);
+    for (int v = 0; v < 4; ++v) {
+        const int r = 4 * q + v;
+        const float seen = store_h<kF32H>(a, A, row_begin + r, hcol0 + lr, acc[0][v], acc[1][v], r < rows);
+        const float s = sum16(seen);
+        if (lr == 0 && r < rows) a.hs[static_cast<size_t>(row_begin + r) * (I / 16) + blockIdx.y] = s;
     }
 }
 
-// down, tiles of <= 16 rows.  Grid (max_tiles, ceil(H / (64 NB))).  Wave w
-// owns output columns 64 NB by + 16 NB w + [0, 16 NB): NB 16-row weight
-// blocks.  Waves are independent (no barrier).
+// down, tiles of <= 16 rows.  Grid (skinny tiles, ceil(H / (16 NB))): one
+// wave per workgroup owns output columns 16 NB by + [0, 16 NB), NB 16-row
+// weight blocks.
 template <bool kF32H, int NB, int RING>
-__global__ __launch_bounds__(kThreads) void moe_down_skinny(FfnArgs a) {
+__global__ __launch_bounds__(64) void moe_down_skinny(FfnArgs a) {
     constexpr int P = kF32H ? 2 : 1;
-    __shared__ SkinnySmem<4, NB> sm;
+    __shared__ SkinnySmem<NB> sm;
     const int4 tile = load_tile<true>(a);
     if (tile.x < 0) return;
     const int e = tile.x, row_begin = tile.y, rows = tile.z;
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, q = lane >> 4, lr = lane & 15;
+    const int lane = threadIdx.x & 63, q = lane >> 4, lr = lane & 15;
     const int H = a.H, I = a.I, G = I / kGroup;
     const size_t A = static_cast<size_t>(a.T) * a.k;
-    const int cbase = blockIdx.y * 64 * NB + 16 * NB * wave;
-    if (cbase >= H) return;  // whole wave past the last column; no barrier follows
+    const int cbase = blockIdx.y * 16 * NB;
     const int nb = min(NB, (H - cbase) / 16);  // blocks inside H (H is a multiple of 64)
 
     size_t row0[NB];
@@ -497,7 +516,7 @@ __global__ __launch_bounds__(kThreads) void moe_down_skinny(FfnArgs a) {
     Tables<NB> tab;
     tab.load(a.s_d, a.b_d, row0, G);
     WaveW<NB> ww;
-    ww.init(sm.w[wave], blk, I / 8);
+    ww.init(sm.w, blk, I / 8);
     u32x4 rv[RING][NB];
 #pragma unroll
     for (int i = 0; i < RING; ++i) ww.load(i, rv[i]);
@@ -521,8 +540,8 @@ __global__ __launch_bounds__(kThreads) void moe_down_skinny(FfnArgs a) {
     };
     load_a(0, 0);
 
-    uint16_t* const ts = sm.ts[wave];
-    uint16_t* const tb = sm.tb[wave];
+    uint16_t* const ts = sm.ts;
+    uint16_t* const tb = sm.tb;
     tab.store(ts, tb, G);
     __builtin_amdgcn_wave_barrier();
 
@@ -540,20 +559,35 @@ __global__ __launch_bounds__(kThreads) void moe_down_skinny(FfnArgs a) {
         u32x4 wv[NB];
 #pragma unroll
         for (int b = 0; b < NB; ++b) wv[b] = ww.get(b, lr, q);
+        if constexpr (!kF32H) {
+            if (2 * c + 1 < G) {
+                float s16[NB][2];
+                u32x4 x[4];
 #pragma unroll
-        for (int gi = 0; gi < 2; ++gi) {
-            const int g = 2 * c + gi;
-            if (g < G) {
-                const u32x4(&x)[4][P] = ra[abuf];
+                for (int j = 0; j < 4; ++j) x[j] = ra[abuf][j][0];
 #pragma unroll
-                for (int b = 0; b < NB; ++b) {
-                    const u32x4 b0 = codes_as_bf16(wv[b][2 * gi], kc), b1 = codes_as_bf16(wv[b][2 * gi + 1], kc);
-                    const float s16 = scale16(ts[(16 * b + lr) * G + g]);
-                    if constexpr (kF32H)
+                for (int b = 0; b < NB; ++b)
+#pragma unroll
+                    for (int gi = 0; gi < 2; ++gi) s16[b][gi] = scale16(ts[(16 * b + lr) * G + 2 * c + gi]);
+                chunk_steps<NB>(acc, x, wv, s16, kc);
+            } else {
+#pragma unroll
+                for (int b = 0; b < NB; ++b)
+                    acc[b] = group_step(acc[b], ra[abuf][0][0], ra[abuf][1][0], codes_as_bf16(wv[b][0], kc),
+                                        codes_as_bf16(wv[b][1], kc), scale16(ts[(16 * b + lr) * G + 2 * c]));
+            }
+        } else {
+#pragma unroll
+            for (int gi = 0; gi < 2; ++gi) {
+                const int g = 2 * c + gi;
+                if (g < G) {
+                    const u32x4(&x)[4][P] = ra[abuf];
+#pragma unroll
+                    for (int b = 0; b < NB; ++b) {
+                        const u32x4 b0 = codes_as_bf16(wv[b][2 * gi], kc), b1 = codes_as_bf16(wv[b][2 * gi + 1], kc);
                         acc[b] = group_step2(acc[b], x[2 * gi][0], x[2 * gi][P - 1], x[2 * gi + 1][0],
-                                             x[2 * gi + 1][P - 1], b0, b1, s16);
-                    else
-                        acc[b] = group_step(acc[b], x[2 * gi][0], x[2 * gi + 1][0], b0, b1, s16);
+                                             x[2 * gi + 1][P - 1], b0, b1, scale16(ts[(16 * b + lr) * G + g]));
+                    }
                 }
             }
         }
@@ -580,7 +614,7 @@ __global__ __launch_bounds__(kThreads) void moe_down_skinny(FfnArgs a) {
         const int steps = (G + 31) / 32;
         BiasOp X;
         RowSums hsum;
-        hsum.load(a.hs + static_cast<size_t>(arow) * G, G, q);
+        hsum.load_blocks(a.hs + static_cast<size_t>(arow) * (I / 16), G, q);
         hsum.pack(X, G, q, steps);
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
@@ -620,7 +654,6 @@ struct alignas(16) WideSmem {
     uint32_t a[NBUF][P][RB * 16 * kAStride];  // after the K loop: group sums of the rows
     uint32_t w[4][64 * 16];     // per-wave weight transposition buffer
     uint16_t ts[4][64 * MAXG];  // per-wave scales of its 64 weight rows
-    float blk[2][4][RB * 16];   // [64-column group][16-column block][row]
 };
 // row stride (floats) of the group sums staged in a[] after the K loop: 16
 // rows of a fragment read fall on distinct banks, and 8-group reads up to
@@ -749,9 +782,9 @@ __device__ __forceinline__ void wide_kloop(WideSmem<RB, P, NBUF, MAXG>& sm, Stag
 // The bias term of the wide paths, added once after the K loop.  The group
 // sums of the staged rows go through LDS (the activation buffers are free by
 // then): thread t copies groups t % 16 + 16 j of rows t / 16 + 16 i, from row
-// pointers xrow[i] (G floats each).  brow[cb]: this lane's bias row of weight
-// block cb, in HBM.
-template <int RB, int P, int NBUF, int MAXG>
+// pointers xrow[i] (G floats each, or with kBlocks 4 G block sums of h).
+// brow[cb]: this lane's bias row of weight block cb, in HBM.
+template <int RB, int P, int NBUF, int MAXG, bool kBlocks>
 __device__ __forceinline__ void wide_bias(WideSmem<RB, P, NBUF, MAXG>& sm,
                                           const float* const (&xrow)[RB],
                                           const uint16_t* const (&brow)[4], int G, bool active,
@@ -765,7 +798,7 @@ __device__ __forceinline__ void wide_bias(WideSmem<RB, P, NBUF, MAXG>& sm,
 #pragma unroll
         for (int j = 0; j < kMaxG / 16; ++j) {
             const int g = pc + 16 * j;
-            if (g < G) xl[(r0 + 16 * i) * kXStride + g] = xrow[i][g];
+            if (g < G) xl[(r0 + 16 * i) * kXStride + g] = kBlocks ? group_of_blocks(xrow[i], g) : xrow[i][g];
         }
     __syncthreads();
     const int steps = (G + 31) / 32;
@@ -852,7 +885,7 @@ __device__ __forceinline__ void gateup_wide(const FfnArgs& a, WideSmem<RB, 1, 2,
     const uint16_t* brow[CB];
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) brow[cb] = a.b_gu + (row0[cb] + lr) * G;
-    wide_bias<RB, P, NBUF, MAXG>(sm, xrow, brow, G, active, acc);
+    wide_bias<RB, P, NBUF, MAXG, false>(sm, xrow, brow, G, active, acc);
 
     // GeGLU epilogue and the 16-column block sums of h
 #pragma unroll
@@ -866,17 +899,10 @@ __device__ __forceinline__ void gateup_wide(const FfnArgs& a, WideSmem<RB, 1, 2,
                 const float seen = store_h<kF32H>(a, A, row_begin + r, hcol, acc[rb][half][v],
                                                   acc[rb][2 + half][v], active && r < rows);
                 const float s = sum16(seen);
-                if (lr == 0) sm.blk[wave >> 1][2 * (wave & 1) + half][r] = s;
+                if (lr == 0 && active && r < rows)
+                    a.hs[static_cast<size_t>(row_begin + r) * (I / 16) + hbase / 16 + half] = s;
             }
         }
-    }
-    __syncthreads();
-    const int GI = I / kGroup;
-    for (int idx = tid; idx < 2 * rows; idx += kThreads) {
-        const int j = idx / rows, r = idx - j * rows, grp = 2 * by + j;
-        if (grp < GI)
-            a.hs[static_cast<size_t>(row_begin + r) * GI + grp] =
-                hsum_of(sm.blk[j][0], sm.blk[j][1], sm.blk[j][2], sm.blk[j][3], r);
     }
 }
 
@@ -928,11 +954,11 @@ __device__ __forceinline__ void down_wide(const FfnArgs& a,
 
     const float* xrow[RB];
 #pragma unroll
-    for (int i = 0; i < RB; ++i) xrow[i] = a.hs + static_cast<size_t>(hrow[i]) * G;
+    for (int i = 0; i < RB; ++i) xrow[i] = a.hs + static_cast<size_t>(hrow[i]) * (I / 16);
     const uint16_t* brow[CB];
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) brow[cb] = a.b_d + (row0[cb] + lr) * G;
-    wide_bias<RB, P, NBUF, MAXG>(sm, xrow, brow, G, active, acc);
+    wide_bias<RB, P, NBUF, MAXG, true>(sm, xrow, brow, G, active, acc);
 
     if (!active) return;
     // weighted unsort
@@ -1019,11 +1045,11 @@ static hipError_t skip_launch(hipStream_t stream, const KTiming& t) {
 }
 
 hipError_t launch_gateup_skinny(const FfnArgs& a, hipStream_t stream, const KTiming& t) {
-    constexpr int NP = kSkinnyGateUpPairs, RING = kSkinnyGateUpRing;
-    const dim3 grid(skinny_grid(a), a.I / 64);
+    constexpr int RING = kSkinnyGateUpRing;
+    const dim3 grid(skinny_grid(a), a.I / 16);
     if (a.flags & MOE_F_FP32_INTERMEDIATE)
-        return launch_kernel(moe_gateup_skinny<true, NP, RING>, grid, dim3(256 / NP), stream, t, a);
-    return launch_kernel(moe_gateup_skinny<false, NP, RING>, grid, dim3(256 / NP), stream, t, a);
+        return launch_kernel(moe_gateup_skinny<true, RING>, grid, dim3(64), stream, t, a);
+    return launch_kernel(moe_gateup_skinny<false, RING>, grid, dim3(64), stream, t, a);
 }
 
 hipError_t launch_gateup_wide(const FfnArgs& a, hipStream_t stream, const KTiming& t) {
@@ -1041,10 +1067,11 @@ hipError_t launch_gateup_wide(const FfnArgs& a, hipStream_t stream, const KTimin
 
 hipError_t launch_down_skinny(const FfnArgs& a, hipStream_t stream, const KTiming& t) {
     constexpr int NB = kSkinnyDownBlocks, RING = kSkinnyDownRing;
-    const dim3 grid(skinny_grid(a), (a.H + 64 * NB - 1) / (64 * NB));
+    static_assert(kGroup % (16 * NB) == 0, "H (a multiple of 64) must split into whole column blocks");
+    const dim3 grid(skinny_grid(a), a.H / (16 * NB));
     if (a.flags & MOE_F_FP32_INTERMEDIATE)
-        return launch_kernel(moe_down_skinny<true, NB, RING>, grid, dim3(kThreads), stream, t, a);
-    return launch_kernel(moe_down_skinny<false, NB, RING>, grid, dim3(kThreads), stream, t, a);
+        return launch_kernel(moe_down_skinny<true, NB, RING>, grid, dim3(64), stream, t, a);
+    return launch_kernel(moe_down_skinny<false, NB, RING>, grid, dim3(64), stream, t, a);
 }
 
 hipError_t launch_down_wide(const FfnArgs& a, hipStream_t stream, const KTiming& t) {

@@ -173,7 +173,9 @@ typedef struct {
     size_t h;         /* GeGLU output in sorted order, operand order:
                          bf16 [A, I]; with MOE_F_FP32_INTERMEDIATE two bf16
                          arrays [2, A, I], h = hi + lo                    */
-    size_t h_sums;    /* fp32 [A, I/64]: sum of h (hi + lo) per group     */
+    size_t h_sums;    /* fp32 [A, I/16]: sum of h (hi + lo) over each
+                         16-column block (in column order); the sum of a
+                         64-column group is ((b0 + b1) + b2) + b3        */
     size_t y;         /* fp32 [A, H] flat order a = t*k + j, already
                          multiplied by topk_weights; rows of assignments
                          with an out-of-range id are not written          */

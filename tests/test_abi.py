@@ -46,6 +46,7 @@ def test_workspace_layout_and_sizes():
     assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
     assert lay.x_sums - lay.x_perm >= 2048 * 2816 * 2
     assert lay.h_sums - lay.h >= A * 704 * 2 and lay.total - lay.y >= A * 2816 * 4
+    assert lay.y - lay.h_sums >= A * (704 // 16) * 4  # 16-column block sums of h
     assert lay.bm_big == 64 and lay.bm_small == 16
     assert lay.max_tiles == A // 64 + 128
     assert lay.tiles_skinny - lay.tiles >= 16 * lay.max_tiles

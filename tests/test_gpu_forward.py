@@ -191,7 +191,7 @@ def test_symmetric_down_codes_cancel():
 @pytest.mark.parametrize("fp32", [False, True])
 def test_prepared_activations_and_h_sums(fp32):
     """The route launch's x in operand order and group sums, and the gate|up
-    kernels' group sums of h, against their definitions."""
+    kernels' 16-column block sums of h, against their definitions."""
     p = ms.make_config("prefill4k")
     out, ws, lay = run_forward(p, fp32=fp32)
     xp = ws_view(ws, lay.x_perm, p.T * p.H, np.uint16).reshape(p.T, p.H)
@@ -201,8 +201,8 @@ def test_prepared_activations_and_h_sums(fp32):
     assert np.abs(xs - ref).max() <= 1e-5 * np.abs(ref).max()
     A = p.T * p.k
     h = ws_h(ws, lay, p, fp32)
-    hs = ws_view(ws, lay.h_sums, A * p.I // 64, np.float32).reshape(A, -1)
-    href = h.reshape(A, -1, 64).sum(-1)
+    hs = ws_view(ws, lay.h_sums, A * p.I // 16, np.float32).reshape(A, -1)
+    href = h.reshape(A, -1, 16).sum(-1)
     assert np.abs(hs - href).max() <= 1e-5 * np.abs(href).max()
 
 

@@ -86,6 +86,29 @@ __device__ void block_exclusive_scan(const int32_t* in, int32_t* out, int n, int
     __syncthreads();
 }
 
+// The same by one wave alone (lane l scans a contiguous run of n / 64 entries);
+// in and out must not overlap.
+__device__ void wave_exclusive_scan(const int32_t* in, int32_t* out, int n) {
+    const int lane = threadIdx.x & 63;
+    const int per = (n + 63) / 64;
+    const int b = min(n, lane * per), e = min(n, b + per);
+    int32_t s = 0;
+    for (int i = b; i < e; ++i) s += in[i];
+    int32_t inc = s;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int32_t t = __shfl_up(inc, d);
+        if (lane >= d) inc += t;
+    }
+    int32_t run = inc - s;
+    for (int i = b; i < e; ++i) {
+        const int32_t v = in[i];
+        out[i] = run;
+        run += v;
+    }
+    if (lane == 63) out[n] = inc;
+}
+
 // Activation preparation, run by workgroups 1.. of the same launch: x in MFMA
 // operand order (each 8-column piece reordered by permute8) and the fp32 sum
 // of each (token, 64-column group), which the matmuls use for the bias term.
@@ -152,6 +175,90 @@ __device__ __forceinline__ void write_tile(int32_t* t, int e, int row_begin, int
     t[3] = bm;
 }
 
+// Counts, offsets and the tile lists from the per-key totals (s_cnt) and
+// their exclusive scan (s_off), by the first NT threads: the whole block, or
+// wave 0 alone (NT = 64, no barriers).
+template <int NT>
+__device__ void emit_tiles(const RouteArgs& a, int32_t* s_tab, const int32_t* s_cnt, const int32_t* s_off,
+                           int32_t* s_toff, int32_t* s_soff, int32_t* s_wsum, int32_t order_status) {
+    const int tid = threadIdx.x, E = a.E, nkeys = E + 1;
+    auto sync = [] {
+        if constexpr (NT == 64) __builtin_amdgcn_wave_barrier(); else __syncthreads();
+    };
+    auto scan = [&](const int32_t* in, int32_t* out, int n) {
+        if constexpr (NT == 64) {
+            wave_exclusive_scan(in, out, n);
+            __builtin_amdgcn_wave_barrier();
+        } else {
+            block_exclusive_scan(in, out, n, s_wsum);
+        }
+    };
+    for (int e = tid; e < E; e += NT) {
+        a.counts[e] = s_cnt[e];
+        a.offsets[e] = s_off[e];
+    }
+    if (tid == 0) {
+        a.offsets[E] = s_off[E];
+        a.num_tiles[1] = s_cnt[E];
+        if (a.presorted != nullptr) a.num_tiles[4] = order_status;
+    }
+    sync();
+    if (a.tiles_skinny == nullptr) {
+        // one list in expert order: tiles per expert into s_tab's first row
+        // (no longer needed), scan, upper-bound emission
+        for (int e = tid; e < E; e += NT) s_tab[e] = (s_cnt[e] + a.bm_big - 1) / a.bm_big;
+        sync();
+        scan(s_tab, s_toff, E);
+        const int total = s_toff[E];
+        for (int i = tid; i < total && i < a.max_tiles; i += NT) {
+            const int e = upper_bound(s_toff, E + 1, i) - 1;
+            const int row0 = (i - s_toff[e]) * a.bm_big;
+            const int rows = min(a.bm_big, s_cnt[e] - row0);
+            write_tile(a.tiles + 4 * i, e, s_off[e] + row0, rows,
+                       rows <= a.bm_small ? a.bm_small : a.bm_big);
+        }
+        if (tid == 0) a.num_tiles[0] = total;
+    } else {
+        // two lists, each in expert order.  An expert of at most bm_small rows
+        // is one short tile; a larger one is cut into ceil(c / bm_big) tiles
+        // of near-equal size (the first c % n one row longer), every one of
+        // them above bm_small rows: no expert ends in a short tail that would
+        // read its weights once more for a few rows.
+        // Experts of more than skinny_max_rows rows are wide (normally
+        // skinny_max_rows = bm_small; when it is larger, the short list holds
+        // consecutive tiles of bm_small rows, the last one shorter).
+        int32_t* s_ns = s_tab + nkeys;
+        for (int e = tid; e < E; e += NT) {
+            const int c = s_cnt[e];
+            const bool wide = c > a.skinny_max_rows;
+            s_tab[e] = wide ? (c + a.bm_big - 1) / a.bm_big : 0;
+            s_ns[e] = wide ? 0 : (c + a.bm_small - 1) / a.bm_small;
+        }
+        sync();
+        scan(s_tab, s_toff, E);
+        scan(s_ns, s_soff, E);
+        const int nw = s_toff[E], ns = s_soff[E];
+        for (int i = tid; i < nw && i < a.max_tiles; i += NT) {
+            const int e = upper_bound(s_toff, E + 1, i) - 1;
+            const int c = s_cnt[e], n = s_toff[e + 1] - s_toff[e], j = i - s_toff[e];
+            const int base = c / n, extra = c - base * n;
+            const int row0 = j * base + min(j, extra);
+            write_tile(a.tiles + 4 * i, e, s_off[e] + row0, base + (j < extra ? 1 : 0), a.bm_big);
+        }
+        for (int i = tid; i < ns && i < a.max_skinny; i += NT) {
+            const int e = upper_bound(s_soff, E + 1, i) - 1;
+            const int row0 = (i - s_soff[e]) * a.bm_small;
+            write_tile(a.tiles_skinny + 4 * i, e, s_off[e] + row0, min(a.bm_small, s_cnt[e] - row0),
+                       a.bm_small);
+        }
+        if (tid == 0) {
+            a.num_tiles[0] = nw + ns;
+            a.num_tiles[2] = nw;
+            a.num_tiles[3] = ns;
+        }
+    }
+}
+
 __global__ __launch_bounds__(kRouteThreads) void moe_route_sort_tiles(RouteArgs a) {
     if (blockIdx.x > 0) {
         prepare_x(a, blockIdx.x - 1);
@@ -171,6 +278,28 @@ __global__ __launch_bounds__(kRouteThreads) void moe_route_sort_tiles(RouteArgs 
     int32_t* const s_wsum = s_soff + nkeys + 1;             // [waves + 1]
     const int nbits = 32 - __clz(E);  // bits of the largest key, E
     const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+
+    if (A <= 64 && a.presorted == nullptr) {
+        // one row of keys: wave 0 alone, a match-any gives each key's count
+        // (at its lowest lane) and each assignment's rank among equal keys
+        if (wave != 0) return;
+        for (int i = lane; i < nkeys; i += 64) s_cnt[i] = 0;
+        const bool act = lane < A;
+        const uint32_t key = act ? load_key(a, lane, A, E) : static_cast<uint32_t>(E);
+        const uint64_t m = match_any(key, nbits, __ballot(act));
+        __builtin_amdgcn_wave_barrier();
+        if (act && (m & below) == 0) s_cnt[key] = __popcll(m);
+        __builtin_amdgcn_wave_barrier();
+        wave_exclusive_scan(s_cnt, s_off, nkeys);
+        __builtin_amdgcn_wave_barrier();
+        if (act) {
+            const int32_t slot = s_off[key] + __popcll(m & below);
+            a.perm[slot] = lane;
+            a.inv_perm[lane] = slot;
+        }
+        emit_tiles<64>(a, s_tab, s_cnt, s_off, s_toff, s_soff, s_wsum, 0);
+        return;
+    }
 
     for (int i = tid; i < kRouteWaves * nkeys; i += kRouteThreads) s_tab[i] = 0;
     __syncthreads();
@@ -253,70 +382,7 @@ __global__ __launch_bounds__(kRouteThreads) void moe_route_sort_tiles(RouteArgs 
     }
 
     // 4. counts, offsets, tiles
-    for (int e = tid; e < E; e += kRouteThreads) {
-        a.counts[e] = s_cnt[e];
-        a.offsets[e] = s_off[e];
-    }
-    if (tid == 0) {
-        a.offsets[E] = s_off[E];
-        a.num_tiles[1] = s_cnt[E];
-        if (a.presorted != nullptr) a.num_tiles[4] = order_status;
-    }
-    __syncthreads();
-    if (a.tiles_skinny == nullptr) {
-        // one list in expert order: tiles per expert into s_tab's first row
-        // (no longer needed), scan, upper-bound emission
-        for (int e = tid; e < E; e += kRouteThreads) s_tab[e] = (s_cnt[e] + a.bm_big - 1) / a.bm_big;
-        __syncthreads();
-        block_exclusive_scan(s_tab, s_toff, E, s_wsum);
-        const int total = s_toff[E];
-        for (int i = tid; i < total && i < a.max_tiles; i += kRouteThreads) {
-            const int e = upper_bound(s_toff, E + 1, i) - 1;
-            const int row0 = (i - s_toff[e]) * a.bm_big;
-            const int rows = min(a.bm_big, s_cnt[e] - row0);
-            write_tile(a.tiles + 4 * i, e, s_off[e] + row0, rows,
-                       rows <= a.bm_small ? a.bm_small : a.bm_big);
-        }
-        if (tid == 0) a.num_tiles[0] = total;
-    } else {
-        // two lists, each in expert order.  An expert of at most bm_small rows
-        // is one short tile; a larger one is cut into ceil(c / bm_big) tiles
-        // of near-equal size (the first c % n one row longer), every one of
-        // them above bm_small rows: no expert ends in a short tail that would
-        // read its weights once more for a few rows.
-        // Experts of more than skinny_max_rows rows are wide (normally
-        // skinny_max_rows = bm_small; when it is larger, the short list holds
-        // consecutive tiles of bm_small rows, the last one shorter).
-        int32_t* s_ns = s_tab + nkeys;
-        for (int e = tid; e < E; e += kRouteThreads) {
-            const int c = s_cnt[e];
-            const bool wide = c > a.skinny_max_rows;
-            s_tab[e] = wide ? (c + a.bm_big - 1) / a.bm_big : 0;
-            s_ns[e] = wide ? 0 : (c + a.bm_small - 1) / a.bm_small;
-        }
-        __syncthreads();
-        block_exclusive_scan(s_tab, s_toff, E, s_wsum);
-        block_exclusive_scan(s_ns, s_soff, E, s_wsum);
-        const int nw = s_toff[E], ns = s_soff[E];
-        for (int i = tid; i < nw && i < a.max_tiles; i += kRouteThreads) {
-            const int e = upper_bound(s_toff, E + 1, i) - 1;
-            const int c = s_cnt[e], n = s_toff[e + 1] - s_toff[e], j = i - s_toff[e];
-            const int base = c / n, extra = c - base * n;
-            const int row0 = j * base + min(j, extra);
-            write_tile(a.tiles + 4 * i, e, s_off[e] + row0, base + (j < extra ? 1 : 0), a.bm_big);
-        }
-        for (int i = tid; i < ns && i < a.max_skinny; i += kRouteThreads) {
-            const int e = upper_bound(s_soff, E + 1, i) - 1;
-            const int row0 = (i - s_soff[e]) * a.bm_small;
-            write_tile(a.tiles_skinny + 4 * i, e, s_off[e] + row0, min(a.bm_small, s_cnt[e] - row0),
-                       a.bm_small);
-        }
-        if (tid == 0) {
-            a.num_tiles[0] = nw + ns;
-            a.num_tiles[2] = nw;
-            a.num_tiles[3] = ns;
-        }
-    }
+    emit_tiles<kRouteThreads>(a, s_tab, s_cnt, s_off, s_toff, s_soff, s_wsum, order_status);
 }
 
 }  // namespace

@@ -52,6 +52,18 @@ def test_route_fuzz(oracle_lib, T, k, E):
     check_route(oracle_lib, ids, E)
 
 
+@pytest.mark.parametrize("T,k,E,lo,hi", [(8, 8, 128, 0, 128), (7, 9, 1024, -2, 1030), (64, 1, 1, 0, 1),
+                                         (5, 3, 2, -1, 3), (1, 64, 64, 0, 64), (2, 32, 4, 0, 4),
+                                         (1, 63, 1000, 990, 1001)])
+def test_route_one_row(oracle_lib, T, k, E, lo, hi):
+    """At most 64 assignments (one wave does the whole sort), with repeated
+    and out-of-range ids."""
+    rng = np.random.default_rng(T * 131 + k * 7 + E)
+    ids = rng.integers(lo, hi, size=(T, k)).astype(np.int32)
+    for bm in [(32, 16), (64, 16), (1, 1)]:
+        check_route(oracle_lib, ids, E, *bm)
+
+
 @pytest.mark.parametrize("bm_big,bm_small", [(64, 16), (16, 16), (128, 32), (1, 1), (7, 3)])
 def test_route_tile_sizes(oracle_lib, bm_big, bm_small):
     c = ms.CONFIGS["prefill16k"]

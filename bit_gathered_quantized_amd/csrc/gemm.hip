@@ -716,20 +716,21 @@ __device__ __forceinline__ void wide_kloop(WideSmem<RB, P, NBUF, MAXG>& sm, Stag
     const int nch = (G + 1) / 2;
     WaveW<CB> ww;
     ww.init(sm.w[wave], blk, K / 8);
-    u32x4 wcur[CB], wnext[CB];
-    ww.load(0, wcur);
+    // chunk c + 1's weights arrive in registers while chunk c is multiplied and
+    // go to the wave's LDS buffer after it (chunk c's reads are done by then)
+    u32x4 wn[CB];
+    ww.load(0, wn);
+    ww.put(wn);
     __syncthreads();  // stage 0 and the scale tables are in place
 
     for (int c = 0; c < nch; ++c) {
         const int buf = NBUF == 2 ? (c & 1) : 0;
         const int cn = min(c + 1, nch - 1);
-        st.load(src, part, cn, G);
-        ww.load(cn, wnext);
-        ww.put(wcur);
-        __builtin_amdgcn_wave_barrier();
         u32x4 wq[CB];
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb) wq[cb] = ww.get(cb, lr, q);
+        st.load(src, part, cn, G);
+        ww.load(cn, wn);
         if (active) {
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
@@ -766,6 +767,7 @@ __device__ __forceinline__ void wide_kloop(WideSmem<RB, P, NBUF, MAXG>& sm, Stag
             }
         }
         __builtin_amdgcn_wave_barrier();
+        if (c + 1 < nch) ww.put(wn);
         if constexpr (NBUF == 2) {
             if (c + 1 < nch) st.store(sm, buf ^ 1);
             __syncthreads();
@@ -774,8 +776,6 @@ __device__ __forceinline__ void wide_kloop(WideSmem<RB, P, NBUF, MAXG>& sm, Stag
             if (c + 1 < nch) st.store(sm, 0);
             __syncthreads();
         }
-#pragma unroll
-        for (int cb = 0; cb < CB; ++cb) wcur[cb] = wnext[cb];
     }
 }
 

@@ -127,6 +127,8 @@ def test_prefill_sampled(oracle_lib, name, fp32):
     (3, 320, 192, 40, 3),   # 5 groups; I = 3 column blocks
     (8, 256, 128, 200, 2),  # more than 32 rows per expert: full and tail tiles
     (2, 128, 64, 33, 2),    # 33 tokens top-2 over 2 experts: 32 + tail tiles
+    (2, 4096, 256, 40, 1),  # 64 groups per gate|up row: the large-table wide kernels
+    (2, 256, 4096, 40, 1),  # 64 groups per down row
 ])
 @pytest.mark.parametrize("fp32", [False, True])
 def test_shapes_full(oracle_lib, shape, fp32):

@@ -80,6 +80,31 @@ def test_small_batch_repeated_ids(oracle_lib, fp32):
 
 
 @pytest.mark.parametrize("fp32", [False, True])
+def test_sixteen_and_seventeen_tokens(oracle_lib, fp32):
+    """16 tokens run every expert on the skinny path (expert 0: one 16-row
+    tile); a 17th token makes expert 0 a 17-row wide tile.  Both match the
+    oracle, and the first 16 tokens' outputs are the same bits."""
+    E, k = 4, 2
+    def problem(T):
+        ids = np.zeros((T, k), np.int32)
+        ids[:, 1] = 1 + np.arange(T) % 3
+        return ms.make_problem(E, 256, 128, T, k, seed=31, topk_ids=ids, name=f"t{T}")
+    a, b = problem(16), problem(17)
+    for f in ("w_gateup", "s_gateup", "b_gateup", "w_down", "s_down", "b_down"):
+        setattr(b, f, getattr(a, f))
+    b.x[:16] = a.x
+    b.topk_weights[:16] = a.topk_weights
+    oa = compare(oracle_lib, a, fp32)
+    ob = compare(oracle_lib, b, fp32)
+    _, wa, la = run_forward(a, fp32=fp32)
+    _, wb, lb = run_forward(b, fp32=fp32)
+    na = ws_view(wa, la.num_tiles, 4, np.int32)
+    nb = ws_view(wb, lb.num_tiles, 4, np.int32)
+    assert na[2] == 0 and nb[2] >= 1
+    np.testing.assert_array_equal(ob[:16], oa)
+
+
+@pytest.mark.parametrize("fp32", [False, True])
 def test_small_batch_matches_large(oracle_lib, fp32):
     """The 8 decode tokens give the same bits when 24 more tokens join them
     (then the larger experts take the wide path)."""

@@ -59,6 +59,7 @@ moe_ws_layout make_layout(const moe_problem* p) {
     l.h = take(hbytes * A * p->I);
     l.h_sums = take(sizeof(float) * A * (p->I / 16));
     l.y = take(sizeof(float) * A * p->H);
+    l.route_hist = take(sizeof(int32_t) * moe::route_count_wgs(A) * (static_cast<size_t>(p->E) + 1));
     l.total = off;
     return l;
 }
@@ -117,6 +118,8 @@ moe_status forward_impl(const moe_problem* p, const void* x, const int32_t* ids,
     r.tiles_skinny = reinterpret_cast<int32_t*>(base + l.tiles_skinny);
     r.num_tiles = reinterpret_cast<int32_t*>(base + l.num_tiles);
     r.presorted = presorted;
+    r.count_wgs = presorted != nullptr ? 0 : moe::route_count_wgs(r.A);
+    r.hist = reinterpret_cast<int32_t*>(base + l.route_hist);
     r.x = static_cast<const uint16_t*>(x);
     r.T = p->T;
     r.H = p->H;
@@ -207,6 +210,8 @@ moe_status moe_sort_build_tiles(const int32_t* topk_ids, int32_t T, int32_t k, i
     r.max_skinny = 0;
     r.skinny_max_rows = bm_small;
     r.presorted = nullptr;
+    r.count_wgs = 0;
+    r.hist = nullptr;
     r.num_tiles = num_tiles;
     r.x = nullptr;
     r.T = T;

@@ -156,6 +156,11 @@ struct RouteArgs {
     // of range, 2 if not a permutation; in both failure cases the kernel sorts
     // by itself.
     const int32_t* presorted;
+    // count_wgs > 0: the sort spreads over that many workgroups of
+    // kRouteSegment assignments, counts in hist [count_wgs][E + 1] (forward
+    // only, no caller's order); 0: one workgroup sorts
+    int32_t count_wgs;
+    int32_t* hist;
     // activation preparation (forward only; x == nullptr skips it)
     const uint16_t* x;  // [T, H] bf16
     int32_t T, H;
@@ -163,6 +168,9 @@ struct RouteArgs {
     float* xs;          // [T, H/64] group sums
 };
 hipError_t launch_route(const RouteArgs& a, hipStream_t stream, const KTiming& t = {});
+constexpr int kRouteSegment = kRouteThreads;  // assignments per counting workgroup
+constexpr int64_t kRouteMultiMin = 2048;      // larger A sorts over several workgroups
+int route_count_wgs(int64_t A);
 size_t route_lds_bytes(int E);
 
 struct FfnArgs {

@@ -385,6 +385,83 @@ __global__ __launch_bounds__(kRouteThreads) void moe_route_sort_tiles(RouteArgs 
     emit_tiles<kRouteThreads>(a, s_tab, s_cnt, s_off, s_toff, s_soff, s_wsum, order_status);
 }
 
+// ---------------------------------------------------------------------------
+// Large A (the forward, without a caller's order): the sort spreads over
+// count_wgs workgroups of kRouteSegment assignments each (one row of 64 per
+// wave), in two launches.  moe_route_count: each workgroup's per-key counts of
+// its segment into hist[wg][key]; the activation workgroups of the forward
+// ride in the same launch.  moe_route_scatter: each workgroup forms the totals
+// and its own base per key from hist (sums in workgroup order, so the sort is
+// the same stable sort), ranks its rows with a wave match-any and scatters;
+// workgroup 0 also writes counts, offsets and the tile lists.
+__global__ __launch_bounds__(kRouteThreads) void moe_route_count(RouteArgs a) {
+    if (static_cast<int>(blockIdx.x) >= a.count_wgs) {
+        prepare_x(a, blockIdx.x - a.count_wgs);
+        return;
+    }
+    extern __shared__ int32_t route_lds[];
+    const int tid = threadIdx.x, E = a.E, nkeys = E + 1;
+    int32_t* const s_cnt = route_lds;  // [nkeys]
+    for (int i = tid; i < nkeys; i += kRouteThreads) s_cnt[i] = 0;
+    __syncthreads();
+    const int ai = blockIdx.x * kRouteSegment + tid;
+    if (ai < a.A) atomicAdd(&s_cnt[load_key(a, ai, a.A, E)], 1);
+    __syncthreads();
+    int32_t* const h = a.hist + static_cast<size_t>(blockIdx.x) * nkeys;
+    for (int i = tid; i < nkeys; i += kRouteThreads) h[i] = s_cnt[i];
+}
+
+__global__ __launch_bounds__(kRouteThreads) void moe_route_scatter(RouteArgs a) {
+    extern __shared__ int32_t route_lds[];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int E = a.E, nkeys = E + 1, wg = blockIdx.x;
+    int32_t* const s_tab = route_lds;                       // [waves][nkeys]
+    int32_t* const s_cnt = s_tab + kRouteWaves * nkeys;     // [nkeys]
+    int32_t* const s_off = s_cnt + nkeys;                   // [nkeys + 1]
+    int32_t* const s_toff = s_off + nkeys + 1;              // [nkeys + 1]
+    int32_t* const s_soff = s_toff + nkeys + 1;             // [nkeys + 1]
+    int32_t* const s_wsum = s_soff + nkeys + 1;             // [waves + 1]
+    const int nbits = 32 - __clz(E);
+    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    for (int i = tid; i < kRouteWaves * nkeys; i += kRouteThreads) s_tab[i] = 0;
+    __syncthreads();
+    // this workgroup's rows: wave w owns row w (assignments beg + 64 w + lane)
+    const int ai = wg * kRouteSegment + tid;
+    const bool act = ai < a.A;
+    const uint32_t key = act ? load_key(a, ai, a.A, E) : static_cast<uint32_t>(E);
+    if (act) atomicAdd(&s_tab[wave * nkeys + key], 1);
+    // totals, and the rows of this key in the workgroups before this one
+    for (int k = tid; k < nkeys; k += kRouteThreads) {
+        int32_t tot = 0, before = 0;
+#pragma unroll 16
+        for (int w = 0; w < a.count_wgs; ++w) {  // unrolled: the loads go out together
+            const int32_t c = a.hist[static_cast<size_t>(w) * nkeys + k];
+            tot += c;
+            before += w < wg ? c : 0;
+        }
+        s_cnt[k] = tot;
+        s_toff[k] = before;  // scratch until the tile emission
+    }
+    __syncthreads();
+    block_exclusive_scan(s_cnt, s_off, nkeys, s_wsum);
+    for (int k = tid; k < nkeys; k += kRouteThreads) {
+        int32_t run = s_off[k] + s_toff[k];
+        for (int w = 0; w < kRouteWaves; ++w) {
+            const int32_t c = s_tab[w * nkeys + k];
+            s_tab[w * nkeys + k] = run;
+            run += c;
+        }
+    }
+    __syncthreads();
+    const uint64_t m = match_any(key, nbits, __ballot(act));
+    if (act) {
+        const int32_t slot = s_tab[wave * nkeys + key] + __popcll(m & below);
+        a.perm[slot] = ai;
+        a.inv_perm[ai] = slot;
+    }
+    if (wg == 0) emit_tiles<kRouteThreads>(a, s_tab, s_cnt, s_off, s_toff, s_soff, s_wsum, 0);
+}
+
 }  // namespace
 
 size_t route_lds_bytes(int E) {
@@ -392,13 +469,38 @@ size_t route_lds_bytes(int E) {
     return sizeof(int32_t) * (kRouteWaves * nkeys + nkeys + 3 * (nkeys + 1) + kRouteWaves + 1);
 }
 
+int route_count_wgs(int64_t A) {
+    return A > kRouteMultiMin ? static_cast<int>((A + kRouteSegment - 1) / kRouteSegment) : 0;
+}
+
 hipError_t launch_route(const RouteArgs& a, hipStream_t stream, const KTiming& t) {
-    int blocks = 1;
+    int prep = 0;
     if (a.x != nullptr) {
         const int64_t pieces = static_cast<int64_t>(a.T) * (a.H / 8);
-        blocks += static_cast<int>((pieces + kRouteThreads - 1) / kRouteThreads);
+        prep = static_cast<int>((pieces + kRouteThreads - 1) / kRouteThreads);
     }
     const size_t lds = route_lds_bytes(a.E);
+    if (a.count_wgs > 0) {
+        if (a.presorted != nullptr || a.hist == nullptr || a.count_wgs != route_count_wgs(a.A))
+            return hipErrorInvalidValue;
+        if (lds > 64 * 1024) {
+            const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(moe_route_scatter),
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                     static_cast<int>(lds));
+            if (e != hipSuccess) return e;
+        }
+        if (t.start != nullptr && hipEventRecord(t.start, stream) != hipSuccess) return hipGetLastError();
+        const size_t lds1 = sizeof(int32_t) * (static_cast<size_t>(a.E) + 1);
+        hipLaunchKernelGGL(moe_route_count, dim3(a.count_wgs + prep), dim3(kRouteThreads), lds1, stream, a);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(moe_route_scatter, dim3(a.count_wgs), dim3(kRouteThreads), lds, stream, a);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        if (t.stop != nullptr) return hipEventRecord(t.stop, stream);
+        return hipSuccess;
+    }
+    const int blocks = 1 + prep;
     if (lds > 64 * 1024) {
         const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(moe_route_sort_tiles),
                                                  hipFuncAttributeMaxDynamicSharedMemorySize,

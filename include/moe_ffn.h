@@ -191,6 +191,9 @@ typedef struct {
                             id) every expert is put here instead, in
                             consecutive tiles of bm_small rows, the last
                             one shorter, and `tiles` stays empty         */
+    size_t route_hist;   /* int32 [ceil(A/1024), E+1] when A > 2048 (else
+                            empty): per-key counts of each 1024-assignment
+                            segment, for the route launches              */
 } moe_ws_layout;
 
 moe_status moe_ffn_workspace_layout(const moe_problem* p, moe_ws_layout* layout);

@@ -42,10 +42,14 @@ def test_workspace_layout_and_sizes():
     A = 2048 * 8
     assert lay.total == bgq.workspace_bytes(p)
     offs = [lay.counts, lay.offsets, lay.perm, lay.inv_perm, lay.tiles, lay.tiles_skinny,
-            lay.num_tiles, lay.x_perm, lay.x_sums, lay.h, lay.h_sums, lay.y]
+            lay.num_tiles, lay.x_perm, lay.x_sums, lay.h, lay.h_sums, lay.y, lay.route_hist]
     assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
     assert lay.x_sums - lay.x_perm >= 2048 * 2816 * 2
-    assert lay.h_sums - lay.h >= A * 704 * 2 and lay.total - lay.y >= A * 2816 * 4
+    assert lay.h_sums - lay.h >= A * 704 * 2 and lay.route_hist - lay.y >= A * 2816 * 4
+    # per-key counts of each 1024-assignment segment for the route launches
+    assert lay.total - lay.route_hist >= (A // 1024) * 129 * 4
+    small = bgq.workspace_layout(bgq.problem(256, 8, 128, 2816, 704))
+    assert small.total == small.route_hist  # 2048 assignments: one workgroup sorts
     assert lay.y - lay.h_sums >= A * (704 // 16) * 4  # 16-column block sums of h
     assert lay.bm_big == 64 and lay.bm_small == 16
     assert lay.max_tiles == A // 64 + 128

@@ -79,6 +79,25 @@ def test_small_batch_repeated_ids(oracle_lib, fp32):
     compare(oracle_lib, p, fp32)
 
 
+def test_forward_route_invalid_ids_large(oracle_lib):
+    """Out-of-range ids in a batch sorted by several workgroups: same sort and
+    tiles as the oracle, outputs of the valid slots within tolerance."""
+    T, k, E = 700, 4, 16
+    rng = np.random.default_rng(17)
+    ids = rng.integers(-2, E + 3, size=(T, k)).astype(np.int32)
+    p = ms.make_problem(E, 256, 128, T, k, seed=19, topk_ids=ids, name="invalid-large")
+    compare(oracle_lib, p, False, tokens=sample_tokens(p, n=40))
+    _, ws, lay = run_forward(p)
+    counts, offsets, operm, oinv, obad = oracle_lib.route(p.topk_ids, p.E)
+    nt = ws_view(ws, lay.num_tiles, 4, np.int32)
+    assert nt[1] == obad > 0
+    np.testing.assert_array_equal(ws_view(ws, lay.perm, T * k, np.int32), operm)
+    np.testing.assert_array_equal(ws_view(ws, lay.inv_perm, T * k, np.int32), oinv)
+    rw, rs = oracle_lib.forward_tiles(counts, offsets, lay.bm_big, lay.bm_small)
+    np.testing.assert_array_equal(ws_view(ws, lay.tiles, 4 * int(nt[2]), np.int32).reshape(-1, 4), rw)
+    np.testing.assert_array_equal(ws_view(ws, lay.tiles_skinny, 4 * int(nt[3]), np.int32).reshape(-1, 4), rs)
+
+
 @pytest.mark.parametrize("fp32", [False, True])
 def test_sixteen_and_seventeen_tokens(oracle_lib, fp32):
     """16 tokens run every expert on the skinny path (expert 0: one 16-row
@@ -284,6 +303,13 @@ def test_forward_tile_lists(oracle_lib, name, fp32):
     counts, offsets, _, _, _ = oracle_lib.route(p.topk_ids, p.E)
     rw, rs = oracle_lib.forward_tiles(counts, offsets, lay.bm_big, lay.bm_small,
                                       short_only=p.T <= lay.bm_small)
+    # the forward's own sort (several workgroups above 2048 assignments)
+    _, _, operm, oinv, obad = oracle_lib.route(p.topk_ids, p.E)
+    A = p.T * p.k
+    np.testing.assert_array_equal(ws_view(ws, lay.counts, p.E, np.int32), counts)
+    np.testing.assert_array_equal(ws_view(ws, lay.offsets, p.E + 1, np.int32), offsets)
+    np.testing.assert_array_equal(ws_view(ws, lay.perm, A, np.int32), operm)
+    np.testing.assert_array_equal(ws_view(ws, lay.inv_perm, A, np.int32), oinv)
     nt = ws_view(ws, lay.num_tiles, 4, np.int32)
     wide = ws_view(ws, lay.tiles, 4 * int(nt[2]), np.int32).reshape(-1, 4)
     short = ws_view(ws, lay.tiles_skinny, 4 * int(nt[3]), np.int32).reshape(-1, 4)

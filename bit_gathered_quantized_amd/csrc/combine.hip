@@ -20,15 +20,28 @@ __global__ __launch_bounds__(256) void moe_combine(FfnArgs a) {
     const int t = static_cast<int>(idx / H4);
     const int c4 = static_cast<int>(idx - static_cast<size_t>(t) * H4);
     float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int j = 0; j < a.k; ++j) {
-        const size_t asg = static_cast<size_t>(t) * a.k + j;
-        const int32_t id = a.ids[asg];
-        if (id < 0 || id >= a.E) continue;
-        const float4 v = reinterpret_cast<const float4*>(a.y + asg * a.H)[c4];
-        s.x += v.x;
-        s.y += v.y;
-        s.z += v.z;
-        s.w += v.w;
+    // eight slots at a time: all their loads are issued before the first add
+    // (rows of out-of-range slots are read but not added)
+    for (int j0 = 0; j0 < a.k; j0 += 8) {
+        float4 v[8];
+        bool ok[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int j = j0 + u;
+            const size_t asg = static_cast<size_t>(t) * a.k + min(j, a.k - 1);
+            const int32_t id = a.ids[asg];
+            ok[u] = j < a.k && id >= 0 && id < a.E;
+            v[u] = reinterpret_cast<const float4*>(a.y + asg * a.H)[c4];
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            if (ok[u]) {
+                s.x += v[u].x;
+                s.y += v[u].y;
+                s.z += v[u].z;
+                s.w += v[u].w;
+            }
+        }
     }
     if constexpr (kF32Out) {
         reinterpret_cast<float4*>(static_cast<float*>(a.out) + static_cast<size_t>(t) * a.H)[c4] = s;

@@ -416,9 +416,26 @@ __global__ __launch_bounds__(64) void moe_gateup_skinny(FfnArgs a) {
         }
     };
     load_a(0, 0);
+    // the bias term's row sums, loaded early; the term itself is formed as soon
+    // as the tables are in place and added after the groups (the same
+    // arithmetic as forming it there), so no load waits at the end
+    const int steps = (G + 31) / 32;
+    RowSums xsum;
+    xsum.load(a.xs + static_cast<size_t>(tok) * G, G, q);
 
     tab.store(sm.ts, sm.tb, G);
     __builtin_amdgcn_wave_barrier();
+    f32x4 bterm[NB];
+    {
+        BiasOp X;
+        xsum.pack(X, G, q, steps);
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            BiasOp C;
+            bias_from_table(C, sm.ts + (16 * b + lr) * G, sm.tb + (16 * b + lr) * G, G, q, steps, true);
+            bterm[b] = bias_mfma(X, C, steps);
+        }
+    }
 
     f32x4 acc[NB];
 #pragma unroll
@@ -466,19 +483,8 @@ __global__ __launch_bounds__(64) void moe_gateup_skinny(FfnArgs a) {
     }
 
     // the bias term, added once after the groups
-    {
-        const int steps = (G + 31) / 32;
-        BiasOp X;
-        RowSums xsum;
-        xsum.load(a.xs + static_cast<size_t>(tok) * G, G, q);
-        xsum.pack(X, G, q, steps);
 #pragma unroll
-        for (int b = 0; b < NB; ++b) {
-            BiasOp C;
-            bias_from_table(C, sm.ts + (16 * b + lr) * G, sm.tb + (16 * b + lr) * G, G, q, steps, true);
-            acc[b] += bias_mfma(X, C, steps);
-        }
-    }
+    for (int b = 0; b < NB; ++b) acc[b] += bterm[b];
 
     // GeGLU, h once, and the 16-column block sum of h per row
 #pragma unroll

@@ -162,12 +162,19 @@ struct RowSums {
 #pragma unroll
             for (int j = 0; j < 8; ++j) v[st][j] = X[min(32 * st + 8 * q + j, G - 1)];
     }
-    // from the 16-column block sums of the row (4 G floats)
-    __device__ __forceinline__ void load_blocks(const float* X16, int G, int q) {
+    // from the 16-column block sums of the row (4 G floats); steps past the
+    // ones used are left unread
+    __device__ __forceinline__ void load_blocks(const float* X16, int G, int q, int steps) {
 #pragma unroll
-        for (int st = 0; st < kMaxBiasSteps; ++st)
+        for (int st = 0; st < kMaxBiasSteps; ++st) {
+            if (st < steps) {
 #pragma unroll
-            for (int j = 0; j < 8; ++j) v[st][j] = group_of_blocks(X16, min(32 * st + 8 * q + j, G - 1));
+                for (int j = 0; j < 8; ++j) v[st][j] = group_of_blocks(X16, min(32 * st + 8 * q + j, G - 1));
+            } else {
+#pragma unroll
+                for (int j = 0; j < 8; ++j) v[st][j] = 0.f;
+            }
+        }
     }
     __device__ __forceinline__ void pack(BiasOp& o, int G, int q, int steps) const {
 #pragma unroll
@@ -545,11 +552,26 @@ __global__ __launch_bounds__(64) void moe_down_skinny(FfnArgs a) {
         }
     };
     load_a(0, 0);
+    // the bias term early, as in the gate|up kernel
+    const int steps = (G + 31) / 32;
+    RowSums hsum;
+    hsum.load_blocks(a.hs + static_cast<size_t>(arow) * (I / 16), G, q, steps);
 
     uint16_t* const ts = sm.ts;
     uint16_t* const tb = sm.tb;
     tab.store(ts, tb, G);
     __builtin_amdgcn_wave_barrier();
+    f32x4 bterm[NB];
+    {
+        BiasOp X;
+        hsum.pack(X, G, q, steps);
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            BiasOp C;
+            bias_from_table(C, ts + (16 * b + lr) * G, tb + (16 * b + lr) * G, G, q, steps, true);
+            bterm[b] = bias_mfma(X, C, steps);
+        }
+    }
 
     f32x4 acc[NB];
 #pragma unroll
@@ -616,19 +638,8 @@ __global__ __launch_bounds__(64) void moe_down_skinny(FfnArgs a) {
     }
 
     // the bias term, added once after the groups
-    {
-        const int steps = (G + 31) / 32;
-        BiasOp X;
-        RowSums hsum;
-        hsum.load_blocks(a.hs + static_cast<size_t>(arow) * (I / 16), G, q);
-        hsum.pack(X, G, q, steps);
 #pragma unroll
-        for (int b = 0; b < NB; ++b) {
-            BiasOp C;
-            bias_from_table(C, ts + (16 * b + lr) * G, tb + (16 * b + lr) * G, G, q, steps, true);
-            acc[b] += bias_mfma(X, C, steps);
-        }
-    }
+    for (int b = 0; b < NB; ++b) acc[b] += bterm[b];
 
     // weighted unsort
 #pragma unroll

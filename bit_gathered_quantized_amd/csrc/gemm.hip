@@ -377,6 +377,8 @@ struct alignas(16) SkinnySmem {
     uint32_t w[NB * 16 * 16];      // weight transposition buffer
     uint16_t ts[NB * 16 * kMaxG];  // scales of the wave's weight rows
     uint16_t tb[NB * 16 * kMaxG];  // biases
+    int32_t dst[kBmSmall];         // down: destination slot of each row
+    float wt[kBmSmall];            // down: its routing weight
 };
 
 // gate|up, tiles of <= 16 rows.  Grid (skinny tiles, I / 16): one wave per
@@ -536,6 +538,13 @@ __global__ __launch_bounds__(64) void moe_down_skinny(FfnArgs a) {
 
     // padding lanes (row >= rows) read row 0: their outputs are never stored
     const int arow = row_begin + min(lr, rows - 1);
+    // destination slot and routing weight of each row, read now and kept in
+    // LDS for the epilogue
+    if (lane < kBmSmall) {
+        const int32_t d = a.perm[row_begin + min(lane, rows - 1)];
+        sm.dst[lane] = d;
+        sm.wt[lane] = a.topk_w[d];
+    }
     const uint32_t* ha = reinterpret_cast<const uint32_t*>(a.h) + static_cast<size_t>(arow) * (I / 2);
     const size_t part = A * (I / 2);  // offset of the lo half, u32
     u32x4 ra[2][4][P];
@@ -641,14 +650,13 @@ __global__ __launch_bounds__(64) void moe_down_skinny(FfnArgs a) {
 #pragma unroll
     for (int b = 0; b < NB; ++b) acc[b] += bterm[b];
 
-    // weighted unsort
+    // weighted unsort (destinations and weights read before the K loop)
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
         const int r = 4 * q + v;
         if (r < rows) {
-            const int32_t dst = a.perm[row_begin + r];
-            const float wt = a.topk_w[dst];
-            float* yrow = a.y + static_cast<size_t>(dst) * H + cbase + lr;
+            float* yrow = a.y + static_cast<size_t>(sm.dst[r]) * H + cbase + lr;
+            const float wt = sm.wt[r];
 #pragma unroll
             for (int b = 0; b < NB; ++b)
                 if (b < nb) yrow[16 * b] = wt * acc[b][v];

@@ -61,11 +61,13 @@ __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
 
 // Tile blockIdx.x of the wide list (tiles of more than kBmSmall rows) or
 // of the skinny list; {-1, ..} past the list's device-side count.
+// The entry and the count are read together (the grid never exceeds the
+// list's capacity, so the entry read stays inside it).
 template <bool kSkinny>
 __device__ __forceinline__ int4 load_tile(const FfnArgs& a) {
+    const int4 t = reinterpret_cast<const int4*>(kSkinny ? a.tiles_skinny : a.tiles)[blockIdx.x];
     const int n = kSkinny ? min(a.num_tiles[3], a.max_skinny) : min(a.num_tiles[2], a.max_tiles);
-    if (static_cast<int>(blockIdx.x) >= n) return int4{-1, 0, 0, 0};
-    return reinterpret_cast<const int4*>(kSkinny ? a.tiles_skinny : a.tiles)[blockIdx.x];
+    return static_cast<int>(blockIdx.x) < n ? t : int4{-1, 0, 0, 0};
 }
 
 // --------------------------------------------------------------- bias term

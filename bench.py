@@ -76,8 +76,23 @@ def algorithmic_work(p):
     touched = int(np.count_nonzero(counts))
     fwd = dict(bytes=touched * (gu_expert + d_expert) + T * H * 2 + A * 8 + T * H * 2,
                flops=A * 6 * H * I)
+    # tile heights of the forward's tiling (wide tiles near-equal per expert)
+    hist = {"skinny 1-4": 0, "skinny 5-8": 0, "skinny 9-16": 0,
+            "wide 17-32": 0, "wide 33-48": 0, "wide 49-64": 0}
+    for c in counts.tolist():
+        if c == 0:
+            continue
+        if c <= skinny_max:
+            for r0 in range(0, c, BM_SMALL):
+                r = min(BM_SMALL, c - r0)
+                hist["skinny 1-4" if r <= 4 else "skinny 5-8" if r <= 8 else "skinny 9-16"] += 1
+            continue
+        n = -(-c // BM_BIG)
+        for j in range(n):
+            r = c // n + (1 if j < c % n else 0)
+            hist["wide 17-32" if r <= 32 else "wide 33-48" if r <= 48 else "wide 49-64"] += 1
     split = dict(skinny_rows=rs, wide_rows=rw, experts_with_skinny_tile=es,
-                 wide_tiles=int(np.sum((wide_rows + BM_BIG - 1) // BM_BIG)))
+                 wide_tiles=int(np.sum((wide_rows + BM_BIG - 1) // BM_BIG)), tile_rows=hist)
     return work, fwd, split
 
 
@@ -115,6 +130,17 @@ def load_traffic(kernel: str, workload: str):
         return None
 
 
+def host_cpu() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline_leg(p, gpu_out, seconds_budget: float):
     """The oracle (as it stands) on this host's cores, on a bounded sample of
     the same workload; the same run checks the GPU output."""
@@ -145,13 +171,28 @@ def cpu_baseline_leg(p, gpu_out, seconds_budget: float):
             break
     med = statistics.median(times)
     n_asg = tokens.size * p.k
+    one_thread = None
+    if p.T <= 64:  # the small configurations: also one core
+        cores = oracle.num_threads()
+        oracle.set_num_threads(1)
+        t1 = []
+        t_start = time.perf_counter()
+        while len(t1) < 20 and (len(t1) < 2 or time.perf_counter() - t_start < seconds_budget / 2):
+            t0 = time.perf_counter()
+            oracle.ffn_tokens(p, tokens, want_h=False, want_y=False)
+            t1.append(time.perf_counter() - t0)
+        oracle.set_num_threads(cores)
+        one_thread = round(n_asg / statistics.median(t1), 3)
     got = gpu_out[tokens]
     rms = float(np.sqrt(np.mean(ref ** 2)))
     allow = np.exp2(np.floor(np.log2(np.maximum(np.maximum(np.abs(got), np.abs(ref)), 1e-38))) - 8)
     excess = float(np.max(np.abs(got - ref) - allow)) / rms
     base = dict(value=round(n_asg / med, 3), unit="assignments/s", cores=oracle.num_threads(),
                 kind="oracle", sample=f"{sample}; median of {len(times)} runs",
-                seconds_per_run=round(med, 4))
+                seconds_per_run=round(med, 4), host_cpu=host_cpu(),
+                affinity=len(os.sched_getaffinity(0)))
+    if one_thread is not None:
+        base["one_thread_value"] = one_thread
     parity = dict(tokens=int(tokens.size), bf16_excess_over_rms=round(excess, 6), bar=2e-2,
                   ok=bool(excess <= 2e-2))
     return base, parity

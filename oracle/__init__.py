@@ -44,6 +44,8 @@ def _load():
         P = ctypes.c_void_p
         i32, i64, dbl = ctypes.c_int32, ctypes.c_int64, ctypes.c_double
         lib.oracle_num_threads.restype = ctypes.c_int
+        lib.oracle_set_num_threads.argtypes = [ctypes.c_int]
+        lib.oracle_set_num_threads.restype = None
         lib.oracle_route.argtypes = [P, i64, i32, P, P, P, P, P]
         lib.oracle_route.restype = ctypes.c_int
         lib.oracle_tiles.argtypes = [P, P, i32, i32, i32, P, i64, P]
@@ -68,6 +70,12 @@ def _ptr(a: Optional[np.ndarray]):
 
 def num_threads() -> int:
     return int(_load().oracle_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """Threads of the following calls (timing only: every result is the same
+    for any thread count)."""
+    _load().oracle_set_num_threads(int(n))
 
 
 def route(ids: np.ndarray, E: int):

@@ -69,6 +69,15 @@ int oracle_num_threads(void) {
 #endif
 }
 
+/* Threads for the following calls (timing only; results do not depend on it). */
+void oracle_set_num_threads(int n) {
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 /* ---------------------------------------------------------------- route */
 
 int oracle_route(const int32_t* ids, int64_t A, int32_t E,

@@ -46,7 +46,7 @@ moe_ws_layout make_layout(const moe_problem* p) {
         return at;
     };
     const size_t hbytes = (p->flags & MOE_F_FP32_INTERMEDIATE) ? 4 : 2;
-    const size_t G = p->H / moe::kGroup, GI = p->I / moe::kGroup;
+    const size_t G = p->H / moe::kGroup;
     l.counts = take(sizeof(int32_t) * p->E);
     l.offsets = take(sizeof(int32_t) * (p->E + 1));
     l.perm = take(sizeof(int32_t) * A);

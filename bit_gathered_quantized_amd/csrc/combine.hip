@@ -46,12 +46,8 @@ __global__ __launch_bounds__(256) void moe_combine(FfnArgs a) {
     if constexpr (kF32Out) {
         reinterpret_cast<float4*>(static_cast<float*>(a.out) + static_cast<size_t>(t) * a.H)[c4] = s;
     } else {
-        const uint32_t lo = static_cast<uint32_t>(f32_to_bf16(s.x)) |
-                            (static_cast<uint32_t>(f32_to_bf16(s.y)) << 16);
-        const uint32_t hi = static_cast<uint32_t>(f32_to_bf16(s.z)) |
-                            (static_cast<uint32_t>(f32_to_bf16(s.w)) << 16);
         reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.out) + static_cast<size_t>(t) * a.H)[c4] =
-            u32x2{lo, hi};
+            u32x2{pack_bf16x2(s.x, s.y), pack_bf16x2(s.z, s.w)};
     }
 }
 

@@ -55,6 +55,18 @@ constexpr int kSkinnyGateUpRing = 2;
 constexpr int kSkinnyDownBlocks = 2, kSkinnyDownRing = 2;
 constexpr int kMaxG = kMaxDim / kGroup;    // groups per row the LDS tables hold
 
+// A buffer resource over n bytes at p (p the same in every lane): a 16-byte
+// load through it at a byte offset at or past n returns zeros and reads no
+// memory.  Word 3 = 0x00020000: 32-bit data format, no swizzle.
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+__device__ __forceinline__ Rsrc make_rsrc(const void* p, uint32_t n) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, static_cast<int>(n), 0x00020000);
+}
+// 16 bytes at byte offset voff + soff (soff the same in every lane).
+__device__ __forceinline__ u32x4 load16(Rsrc r, uint32_t voff, uint32_t soff) {
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+
 __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
 }
@@ -81,34 +93,15 @@ struct BiasOp {
 __device__ __forceinline__ void pack_split(const float (&v)[8], u32x4& hi, u32x4& lo) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        const uint16_t h0 = f32_to_bf16(v[2 * j]), h1 = f32_to_bf16(v[2 * j + 1]);
-        const uint16_t l0 = f32_to_bf16(v[2 * j] - bf16_to_f32(h0));
-        const uint16_t l1 = f32_to_bf16(v[2 * j + 1] - bf16_to_f32(h1));
-        hi[j] = static_cast<uint32_t>(h0) | (static_cast<uint32_t>(h1) << 16);
-        lo[j] = static_cast<uint32_t>(l0) | (static_cast<uint32_t>(l1) << 16);
-    }
-}
-
-// Row operand: the group sums X[g] of one activation row.  Loads use clamped
-// indices and a select, never a branch, so they stay in flight together.
-__device__ __forceinline__ void bias_from_sums(BiasOp& o, const float* X, int G, int q, int steps) {
-#pragma unroll
-    for (int st = 0; st < kMaxBiasSteps; ++st) {
-        if (st < steps) {
-            float v[8];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int g = 32 * st + 8 * q + j;
-                const float x = X[min(g, G - 1)];
-                v[j] = g < G ? x : 0.f;
-            }
-            pack_split(v, o.hi[st], o.lo[st]);
-        }
+        hi[j] = pack_bf16x2(v[2 * j], v[2 * j + 1]);
+        lo[j] = pack_bf16x2(v[2 * j] - __uint_as_float(hi[j] << 16),
+                            v[2 * j + 1] - __uint_as_float(hi[j] & 0xFFFF0000u));
     }
 }
 
 // Column operand: c[g] = b[g] - 16 s[g] of one weight row, from its rows of
-// the scale and bias tables.
+// the scale and bias tables.  Groups past G repeat the last group: the row
+// operand is zero there, so those (finite) products add nothing.
 __device__ __forceinline__ void bias_from_table(BiasOp& o, const uint16_t* ts, const uint16_t* tb,
                                                 int G, int q, int steps, bool active) {
 #pragma unroll
@@ -117,10 +110,9 @@ __device__ __forceinline__ void bias_from_table(BiasOp& o, const uint16_t* ts, c
             float v[8];
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
-                const int g = 32 * st + 8 * q + j;
-                const int gc = min(g, G - 1);
+                const int gc = min(32 * st + 8 * q + j, G - 1);
                 const float c = fmaf(-kCodeOffset, bf16_to_f32(ts[gc]), bf16_to_f32(tb[gc]));
-                v[j] = (active && g < G) ? c : 0.f;
+                v[j] = active ? c : 0.f;
             }
             pack_split(v, o.hi[st], o.lo[st]);
         }
@@ -137,10 +129,9 @@ __device__ __forceinline__ void bias_from_scales(BiasOp& o, const uint16_t* ts, 
             float v[8];
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
-                const int g = 32 * st + 8 * q + j;
-                const int gc = min(g, G - 1);
+                const int gc = min(32 * st + 8 * q + j, G - 1);
                 const float c = fmaf(-kCodeOffset, bf16_to_f32(ts[gc]), bf16_to_f32(b[gc]));
-                v[j] = (active && g < G) ? c : 0.f;
+                v[j] = active ? c : 0.f;
             }
             pack_split(v, o.hi[st], o.lo[st]);
         }
@@ -299,24 +290,25 @@ __device__ __forceinline__ float store_h(const FfnArgs& a, size_t A, int srow, i
 // 16 rows of a fragment read on distinct banks.
 template <int NCB>
 struct WaveW {
-    uint32_t* lds;            // NCB * 16 rows x 16 u32
-    const uint32_t* src[NCB]; // this lane's load row in block cb
-    int rw;                   // row length, u32
+    uint32_t* lds;   // NCB * 16 rows x 16 u32
+    Rsrc blk[NCB];   // block cb: its 16 weight rows
+    uint32_t voff;   // this lane's load row and piece, bytes
 
-    __device__ __forceinline__ void init(uint32_t* l, const uint32_t* const (&blk)[NCB],
+    // blocks at blk_ptr[cb] (the same in every lane), rows of row_words u32
+    __device__ __forceinline__ void init(uint32_t* l, const uint32_t* const (&blk_ptr)[NCB],
                                          int row_words) {
         const int lane = threadIdx.x & 63;
         lds = l;
-        rw = row_words;
 #pragma unroll
-        for (int cb = 0; cb < NCB; ++cb) src[cb] = blk[cb] + (lane >> 2) * row_words;
+        for (int cb = 0; cb < NCB; ++cb) blk[cb] = make_rsrc(blk_ptr[cb], 64u * row_words);
+        voff = 4u * ((lane >> 2) * row_words + 4 * (lane & 3));
     }
-    // Chunk c; the last chunk of an odd group count reads a repeated piece
-    // instead of running past the row.
+    // Chunk c.  Pieces past a row's end (the second group of the last chunk of
+    // an odd group count, chunks past the last) read the next row or, past the
+    // block, zeros; they are never used.
     __device__ __forceinline__ void load(int c, u32x4 (&v)[NCB]) const {
-        const int off = min(16 * c + 4 * static_cast<int>(threadIdx.x & 3), rw - 4);
 #pragma unroll
-        for (int cb = 0; cb < NCB; ++cb) v[cb] = *reinterpret_cast<const u32x4*>(src[cb] + off);
+        for (int cb = 0; cb < NCB; ++cb) v[cb] = load16(blk[cb], voff, 64u * c);
     }
     __device__ __forceinline__ void put(const u32x4 (&v)[NCB]) const {
         const int lane = threadIdx.x & 63;
@@ -346,15 +338,19 @@ struct Tables {
 
     __device__ __forceinline__ void load(const uint16_t* s, const uint16_t* b,
                                          const size_t (&row0)[NCB], int G) {
-        const int lane = threadIdx.x & 63, np = 2 * G;
+        const int lane = threadIdx.x & 63;
+        const uint32_t n = 32u * G;  // 16 rows of G bf16; pieces past it read zeros
 #pragma unroll
-        for (int cb = 0; cb < NCB; ++cb)
+        for (int cb = 0; cb < NCB; ++cb) {
+            const Rsrc rs = make_rsrc(s + row0[cb] * G, n);
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                const size_t off = row0[cb] * G + 8 * min(lane + 64 * j, np - 1);
-                vs[cb][j] = *reinterpret_cast<const u32x4*>(s + off);
-                if constexpr (kBias) vb[cb][j] = *reinterpret_cast<const u32x4*>(b + off);
+            for (int j = 0; j < 2; ++j) vs[cb][j] = load16(rs, 16u * (lane + 64 * j), 0);
+            if constexpr (kBias) {
+                const Rsrc rb = make_rsrc(b + row0[cb] * G, n);
+#pragma unroll
+                for (int j = 0; j < 2; ++j) vb[cb][j] = load16(rb, 16u * (lane + 64 * j), 0);
             }
+        }
     }
     __device__ __forceinline__ void store(uint16_t* ts, uint16_t* tb, int G) const {
         const int lane = threadIdx.x & 63, np = 2 * G;
@@ -417,13 +413,14 @@ __global__ __launch_bounds__(64) void moe_gateup_skinny(FfnArgs a) {
     const int tok = a.perm[row_begin + min(lr, rows - 1)] / a.k;
     const uint32_t* xa = reinterpret_cast<const uint32_t*>(a.xp) + static_cast<size_t>(tok) * (H / 2);
     u32x4 ra[2][4];
+    // this lane's pieces of group g start at xq + 32 g (g the same in every lane)
+    const uint32_t* const xq = xa + 8 * q;
     auto load_a = [&](int c, int buf) {
 #pragma unroll
         for (int gi = 0; gi < 2; ++gi) {
-            const int g = min(2 * c + gi, G - 1);
+            const uint32_t* const xg = xq + static_cast<uint32_t>(32 * min(2 * c + gi, G - 1));
 #pragma unroll
-            for (int s = 0; s < 2; ++s)
-                ra[buf][2 * gi + s] = *reinterpret_cast<const u32x4*>(xa + 4 * (8 * g + 2 * q + s));
+            for (int s = 0; s < 2; ++s) ra[buf][2 * gi + s] = *reinterpret_cast<const u32x4*>(xg + 4 * s);
         }
     };
     load_a(0, 0);
@@ -451,18 +448,18 @@ __global__ __launch_bounds__(64) void moe_gateup_skinny(FfnArgs a) {
     f32x4 acc[NB];
 #pragma unroll
     for (int b = 0; b < NB; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const int nch = (G + 1) / 2;
+    const int nfull = G / 2, nch = (G + 1) / 2;
     const CodeConsts kc = code_consts(a.zero);
     // chunk c: its weights go through LDS, the slot reloads with chunk c + RING
     // at once, then the MFMAs run (an odd G ends with a one-group chunk)
-    auto compute = [&](int slot, int abuf, int c, bool reload) {
+    auto compute = [&](int slot, int abuf, int c, bool reload, bool full) {
         ww.put(rv[slot]);
         if (reload) ww.load(c + RING, rv[slot]);
         __builtin_amdgcn_wave_barrier();
         u32x4 wv[NB];
 #pragma unroll
         for (int b = 0; b < NB; ++b) wv[b] = ww.get(b, lr, q);
-        if (2 * c + 1 < G) {
+        if (full) {
             float s16[NB][2];
 #pragma unroll
             for (int b = 0; b < NB; ++b)
@@ -477,19 +474,21 @@ __global__ __launch_bounds__(64) void moe_gateup_skinny(FfnArgs a) {
         }
         __builtin_amdgcn_wave_barrier();
     };
+    // the loop runs full chunks only; the rest (at most RING chunks, the last
+    // one a single group when G is odd) follows without reloads
     int c0 = 0;
-    for (; c0 + RING <= nch; c0 += RING) {
+    for (; c0 + RING <= nfull; c0 += RING) {
 #pragma unroll
         for (int i = 0; i < RING; ++i) {
             load_a(c0 + i + 1, (i + 1) & 1);
-            compute(i, i & 1, c0 + i, true);
+            compute(i, i & 1, c0 + i, true, true);
         }
     }
 #pragma unroll
     for (int i = 0; i < RING; ++i) {
         if (c0 + i < nch) {
             load_a(c0 + i + 1, (i + 1) & 1);
-            compute(i, i & 1, c0 + i, false);
+            compute(i, i & 1, c0 + i, false, c0 + i < nfull);
         }
     }
 
@@ -550,16 +549,19 @@ __global__ __launch_bounds__(64) void moe_down_skinny(FfnArgs a) {
     const uint32_t* ha = reinterpret_cast<const uint32_t*>(a.h) + static_cast<size_t>(arow) * (I / 2);
     const size_t part = A * (I / 2);  // offset of the lo half, u32
     u32x4 ra[2][4][P];
+    // this lane's pieces of group g start at hq[pp] + 32 g (g the same in every lane)
+    const uint32_t* hq[P];
+#pragma unroll
+    for (int pp = 0; pp < P; ++pp) hq[pp] = ha + pp * part + 8 * q;
     auto load_a = [&](int c, int buf) {
 #pragma unroll
         for (int gi = 0; gi < 2; ++gi) {
-            const int g = min(2 * c + gi, G - 1);
+            const uint32_t goff = 32 * min(2 * c + gi, G - 1);
 #pragma unroll
             for (int s = 0; s < 2; ++s)
 #pragma unroll
                 for (int pp = 0; pp < P; ++pp)
-                    ra[buf][2 * gi + s][pp] =
-                        *reinterpret_cast<const u32x4*>(ha + pp * part + 4 * (8 * g + 2 * q + s));
+                    ra[buf][2 * gi + s][pp] = *reinterpret_cast<const u32x4*>(hq[pp] + goff + 4 * s);
         }
     };
     load_a(0, 0);
@@ -587,11 +589,11 @@ __global__ __launch_bounds__(64) void moe_down_skinny(FfnArgs a) {
     f32x4 acc[NB];
 #pragma unroll
     for (int b = 0; b < NB; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const int nch = (G + 1) / 2;
+    const int nfull = G / 2, nch = (G + 1) / 2;
     const CodeConsts kc = code_consts(a.zero);
     // chunk c: its weights go through LDS, the slot reloads with chunk c + RING
-    // at once, then the MFMAs run
-    auto compute = [&](int slot, int abuf, int c, bool reload) {
+    // at once, then the MFMAs run (an odd G ends with a one-group chunk)
+    auto compute = [&](int slot, int abuf, int c, bool reload, bool full) {
         ww.put(rv[slot]);
         if (reload) ww.load(c + RING, rv[slot]);
         __builtin_amdgcn_wave_barrier();
@@ -599,7 +601,7 @@ __global__ __launch_bounds__(64) void moe_down_skinny(FfnArgs a) {
 #pragma unroll
         for (int b = 0; b < NB; ++b) wv[b] = ww.get(b, lr, q);
         if constexpr (!kF32H) {
-            if (2 * c + 1 < G) {
+            if (full) {
                 float s16[NB][2];
                 u32x4 x[4];
 #pragma unroll
@@ -619,7 +621,7 @@ __global__ __launch_bounds__(64) void moe_down_skinny(FfnArgs a) {
 #pragma unroll
             for (int gi = 0; gi < 2; ++gi) {
                 const int g = 2 * c + gi;
-                if (g < G) {
+                if (gi == 0 || full) {
                     const u32x4(&x)[4][P] = ra[abuf];
 #pragma unroll
                     for (int b = 0; b < NB; ++b) {
@@ -633,18 +635,18 @@ __global__ __launch_bounds__(64) void moe_down_skinny(FfnArgs a) {
         __builtin_amdgcn_wave_barrier();
     };
     int cc = 0;
-    for (; cc + RING <= nch; cc += RING) {
+    for (; cc + RING <= nfull; cc += RING) {
 #pragma unroll
         for (int i = 0; i < RING; ++i) {
             load_a(cc + i + 1, (i + 1) & 1);
-            compute(i, i & 1, cc + i, true);
+            compute(i, i & 1, cc + i, true, true);
         }
     }
 #pragma unroll
     for (int i = 0; i < RING; ++i) {
         if (cc + i < nch) {
             load_a(cc + i + 1, (i + 1) & 1);
-            compute(i, i & 1, cc + i, false);
+            compute(i, i & 1, cc + i, false, cc + i < nfull);
         }
     }
 
@@ -868,7 +870,8 @@ template <int RB, int MAXG, bool kF32H>
 __device__ __forceinline__ void gateup_wide(const FfnArgs& a, WideSmem<RB, 1, 2, MAXG>& sm, int e,
                                             int row_begin, int rows, int by) {
     constexpr int P = 1, NBUF = 2, CB = 4;
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, q = lane >> 4, lr = lane & 15;
+    const int tid = threadIdx.x, lane = tid & 63, q = lane >> 4, lr = lane & 15;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: weight rows are per wave
     const int H = a.H, I = a.I, G = H / kGroup;
     const size_t A = static_cast<size_t>(a.T) * a.k;
     const int n0 = by * 128;
@@ -940,7 +943,8 @@ __device__ __forceinline__ void down_wide(const FfnArgs& a,
                                           WideSmem<RB, kF32H ? 2 : 1, kF32H ? 1 : 2, MAXG>& sm,
                                           int e, int row_begin, int rows, int by) {
     constexpr int P = kF32H ? 2 : 1, NBUF = kF32H ? 1 : 2, CB = 4;
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, q = lane >> 4, lr = lane & 15;
+    const int tid = threadIdx.x, lane = tid & 63, q = lane >> 4, lr = lane & 15;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: weight rows are per wave
     const int H = a.H, I = a.I, G = I / kGroup;
     const size_t A = static_cast<size_t>(a.T) * a.k;
     const int n0 = by * 256;

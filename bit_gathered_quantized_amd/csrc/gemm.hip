@@ -67,19 +67,33 @@ __device__ __forceinline__ u32x4 load16(Rsrc r, uint32_t voff, uint32_t soff) {
     return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
 }
 
+// Start of a skinny chunk: nothing moves across.  The memory counter a wave
+// waits on retires loads in issue order, so a wait for one load is a wait for
+// every earlier one.  Without the fence the scheduler lifts the weight reload
+// above the next chunk's activation loads, or a chunk's LDS put (and the wait
+// for its weights) above the previous chunk's arithmetic; either way a chunk
+// waits for weights it needs only later, and the ring is shallower than it
+// looks.
+__device__ __forceinline__ void chunk_fence() { __builtin_amdgcn_sched_barrier(0); }
+
 __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
 }
 
-// Tile blockIdx.x of the wide list (tiles of more than kBmSmall rows) or
-// of the skinny list; {-1, ..} past the list's device-side count.
-// The entry and the count are read together (the grid never exceeds the
-// list's capacity, so the entry read stays inside it).
-template <bool kSkinny>
-__device__ __forceinline__ int4 load_tile(const FfnArgs& a) {
-    const int4 t = reinterpret_cast<const int4*>(kSkinny ? a.tiles_skinny : a.tiles)[blockIdx.x];
-    const int n = kSkinny ? min(a.num_tiles[3], a.max_skinny) : min(a.num_tiles[2], a.max_tiles);
-    return static_cast<int>(blockIdx.x) < n ? t : int4{-1, 0, 0, 0};
+// Skinny work item blockIdx.x: tile blockIdx.x / ncb of the skinny list
+// (tiles of at most kBmSmall rows), column block blockIdx.x % ncb; tile
+// {-1, ..} past the list's device-side count.  Column blocks vary fastest, so
+// the workgroups past the count are the last ones dispatched: the dispatcher
+// hands runs of consecutive workgroups to one CU, and exiting workgroups
+// spread through the grid left whole CUs without work.  The entry and the
+// count are read together (the grid never exceeds the list's capacity, so the
+// entry read stays inside it).
+__device__ __forceinline__ int4 load_skinny_tile(const FfnArgs& a, int ncb, int& cb) {
+    const int ti = static_cast<int>(blockIdx.x) / ncb;
+    cb = static_cast<int>(blockIdx.x) - ti * ncb;
+    const int4 t = reinterpret_cast<const int4*>(a.tiles_skinny)[ti];
+    const int n = min(a.num_tiles[3], a.max_skinny);
+    return ti < n ? t : int4{-1, 0, 0, 0};
 }
 
 // --------------------------------------------------------------- bias term
@@ -379,21 +393,23 @@ struct alignas(16) SkinnySmem {
     float wt[kBmSmall];            // down: its routing weight
 };
 
-// gate|up, tiles of <= 16 rows.  Grid (skinny tiles, I / 16): one wave per
-// workgroup owns 16 columns of h, i.e. weight block gate (rows n0 .. n0 + 15)
-// and block up (rows I + n0 ..), and writes their 16-column block sums of h.
+// gate|up, tiles of <= 16 rows.  Grid: skinny tiles x I / 16 column blocks;
+// one wave per workgroup owns 16 columns of h, i.e. weight block gate (rows
+// n0 .. n0 + 15) and block up (rows I + n0 ..), and writes their 16-column
+// block sums of h.
 // RING chunks of weights are in flight.
 template <bool kF32H, int RING>
-__global__ __launch_bounds__(64) void moe_gateup_skinny(FfnArgs a) {
+__global__ __launch_bounds__(64, 3) void moe_gateup_skinny(FfnArgs a) {
     constexpr int NB = 2;
     __shared__ SkinnySmem<NB> sm;
-    const int4 tile = load_tile<true>(a);
+    int cb;
+    const int4 tile = load_skinny_tile(a, a.I / 16, cb);
     if (tile.x < 0) return;
     const int e = tile.x, row_begin = tile.y, rows = tile.z;
     const int lane = threadIdx.x & 63, q = lane >> 4, lr = lane & 15;
     const int H = a.H, I = a.I, G = H / kGroup;
     const size_t A = static_cast<size_t>(a.T) * a.k;
-    const int hcol0 = blockIdx.y * 16;
+    const int hcol0 = cb * 16;
 
     size_t row0[NB];
     const uint32_t* blk[NB];
@@ -453,6 +469,7 @@ __global__ __launch_bounds__(64) void moe_gateup_skinny(FfnArgs a) {
     // chunk c: its weights go through LDS, the slot reloads with chunk c + RING
     // at once, then the MFMAs run (an odd G ends with a one-group chunk)
     auto compute = [&](int slot, int abuf, int c, bool reload, bool full) {
+        chunk_fence();
         ww.put(rv[slot]);
         if (reload) ww.load(c + RING, rv[slot]);
         __builtin_amdgcn_wave_barrier();
@@ -474,21 +491,23 @@ __global__ __launch_bounds__(64) void moe_gateup_skinny(FfnArgs a) {
         }
         __builtin_amdgcn_wave_barrier();
     };
-    // the loop runs full chunks only; the rest (at most RING chunks, the last
-    // one a single group when G is odd) follows without reloads
+    // the loop runs full chunks only, U per trip (a multiple of the ring and
+    // of the two activation buffers); the rest (at most U chunks, the last one
+    // a single group when G is odd) follows
+    constexpr int U = RING % 2 == 0 ? RING : 2 * RING;
     int c0 = 0;
-    for (; c0 + RING <= nfull; c0 += RING) {
+    for (; c0 + U <= nfull; c0 += U) {
 #pragma unroll
-        for (int i = 0; i < RING; ++i) {
+        for (int i = 0; i < U; ++i) {
             load_a(c0 + i + 1, (i + 1) & 1);
-            compute(i, i & 1, c0 + i, true, true);
+            compute(i % RING, i & 1, c0 + i, true, true);
         }
     }
 #pragma unroll
-    for (int i = 0; i < RING; ++i) {
+    for (int i = 0; i < U; ++i) {
         if (c0 + i < nch) {
             load_a(c0 + i + 1, (i + 1) & 1);
-            compute(i, i & 1, c0 + i, false, c0 + i < nfull);
+            compute(i % RING, i & 1, c0 + i, c0 + i + RING < nch, c0 + i < nfull);
         }
     }
 
@@ -502,24 +521,25 @@ __global__ __launch_bounds__(64) void moe_gateup_skinny(FfnArgs a) {
         const int r = 4 * q + v;
         const float seen = store_h<kF32H>(a, A, row_begin + r, hcol0 + lr, acc[0][v], acc[1][v], r < rows);
         const float s = sum16(seen);
-        if (lr == 0 && r < rows) a.hs[static_cast<size_t>(row_begin + r) * (I / 16) + blockIdx.y] = s;
+        if (lr == 0 && r < rows) a.hs[static_cast<size_t>(row_begin + r) * (I / 16) + cb] = s;
     }
 }
 
-// down, tiles of <= 16 rows.  Grid (skinny tiles, ceil(H / (16 NB))): one
-// wave per workgroup owns output columns 16 NB by + [0, 16 NB), NB 16-row
-// weight blocks.
+// down, tiles of <= 16 rows.  Grid: skinny tiles x H / (16 NB) column
+// blocks; one wave per workgroup owns output columns 16 NB cb + [0, 16 NB),
+// NB 16-row weight blocks.
 template <bool kF32H, int NB, int RING>
-__global__ __launch_bounds__(64) void moe_down_skinny(FfnArgs a) {
+__global__ __launch_bounds__(64, kF32H ? 2 : 3) void moe_down_skinny(FfnArgs a) {
     constexpr int P = kF32H ? 2 : 1;
     __shared__ SkinnySmem<NB> sm;
-    const int4 tile = load_tile<true>(a);
+    int cb;
+    const int4 tile = load_skinny_tile(a, a.H / (16 * NB), cb);
     if (tile.x < 0) return;
     const int e = tile.x, row_begin = tile.y, rows = tile.z;
     const int lane = threadIdx.x & 63, q = lane >> 4, lr = lane & 15;
     const int H = a.H, I = a.I, G = I / kGroup;
     const size_t A = static_cast<size_t>(a.T) * a.k;
-    const int cbase = blockIdx.y * 16 * NB;
+    const int cbase = cb * 16 * NB;
     const int nb = min(NB, (H - cbase) / 16);  // blocks inside H (H is a multiple of 64)
 
     size_t row0[NB];
@@ -594,6 +614,7 @@ __global__ __launch_bounds__(64) void moe_down_skinny(FfnArgs a) {
     // chunk c: its weights go through LDS, the slot reloads with chunk c + RING
     // at once, then the MFMAs run (an odd G ends with a one-group chunk)
     auto compute = [&](int slot, int abuf, int c, bool reload, bool full) {
+        chunk_fence();
         ww.put(rv[slot]);
         if (reload) ww.load(c + RING, rv[slot]);
         __builtin_amdgcn_wave_barrier();
@@ -634,19 +655,21 @@ __global__ __launch_bounds__(64) void moe_down_skinny(FfnArgs a) {
         }
         __builtin_amdgcn_wave_barrier();
     };
+    // full chunks in the loop, U per trip, then the rest (as in gate|up)
+    constexpr int U = RING % 2 == 0 ? RING : 2 * RING;
     int cc = 0;
-    for (; cc + RING <= nfull; cc += RING) {
+    for (; cc + U <= nfull; cc += U) {
 #pragma unroll
-        for (int i = 0; i < RING; ++i) {
+        for (int i = 0; i < U; ++i) {
             load_a(cc + i + 1, (i + 1) & 1);
-            compute(i, i & 1, cc + i, true, true);
+            compute(i % RING, i & 1, cc + i, true, true);
         }
     }
 #pragma unroll
-    for (int i = 0; i < RING; ++i) {
+    for (int i = 0; i < U; ++i) {
         if (cc + i < nch) {
             load_a(cc + i + 1, (i + 1) & 1);
-            compute(i, i & 1, cc + i, false, cc + i < nfull);
+            compute(i % RING, i & 1, cc + i, cc + i + RING < nch, cc + i < nfull);
         }
     }
 
@@ -1077,7 +1100,7 @@ static hipError_t skip_launch(hipStream_t stream, const KTiming& t) {
 
 hipError_t launch_gateup_skinny(const FfnArgs& a, hipStream_t stream, const KTiming& t) {
     constexpr int RING = kSkinnyGateUpRing;
-    const dim3 grid(skinny_grid(a), a.I / 16);
+    const dim3 grid(skinny_grid(a) * (a.I / 16));
     if (a.flags & MOE_F_FP32_INTERMEDIATE)
         return launch_kernel(moe_gateup_skinny<true, RING>, grid, dim3(64), stream, t, a);
     return launch_kernel(moe_gateup_skinny<false, RING>, grid, dim3(64), stream, t, a);
@@ -1099,7 +1122,7 @@ hipError_t launch_gateup_wide(const FfnArgs& a, hipStream_t stream, const KTimin
 hipError_t launch_down_skinny(const FfnArgs& a, hipStream_t stream, const KTiming& t) {
     constexpr int NB = kSkinnyDownBlocks, RING = kSkinnyDownRing;
     static_assert(kGroup % (16 * NB) == 0, "H (a multiple of 64) must split into whole column blocks");
-    const dim3 grid(skinny_grid(a), a.H / (16 * NB));
+    const dim3 grid(skinny_grid(a) * (a.H / (16 * NB)));
     if (a.flags & MOE_F_FP32_INTERMEDIATE)
         return launch_kernel(moe_down_skinny<true, NB, RING>, grid, dim3(64), stream, t, a);
     return launch_kernel(moe_down_skinny<false, NB, RING>, grid, dim3(64), stream, t, a);

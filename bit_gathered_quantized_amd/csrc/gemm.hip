@@ -45,6 +45,8 @@
 //    at once: the host never reads it back.
 #include "moe_internal.h"
 
+#include <type_traits>
+
 namespace moe {
 namespace {
 
@@ -126,25 +128,6 @@ __device__ __forceinline__ void bias_from_table(BiasOp& o, const uint16_t* ts, c
             for (int j = 0; j < 8; ++j) {
                 const int gc = min(32 * st + 8 * q + j, G - 1);
                 const float c = fmaf(-kCodeOffset, bf16_to_f32(ts[gc]), bf16_to_f32(tb[gc]));
-                v[j] = active ? c : 0.f;
-            }
-            pack_split(v, o.hi[st], o.lo[st]);
-        }
-    }
-}
-
-// Same, with the biases read from HBM (row b, G entries) and the scales from
-// LDS.
-__device__ __forceinline__ void bias_from_scales(BiasOp& o, const uint16_t* ts, const uint16_t* b,
-                                                 int G, int q, int steps, bool active) {
-#pragma unroll
-    for (int st = 0; st < kMaxBiasSteps; ++st) {
-        if (st < steps) {
-            float v[8];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int gc = min(32 * st + 8 * q + j, G - 1);
-                const float c = fmaf(-kCodeOffset, bf16_to_f32(ts[gc]), bf16_to_f32(b[gc]));
                 v[j] = active ? c : 0.f;
             }
             pack_split(v, o.hi[st], o.lo[st]);
@@ -704,8 +687,38 @@ constexpr int kAStride = 2 * 32 + 4;  // u32 per staged activation row
 template <int RB, int P, int NBUF, int MAXG>
 struct alignas(16) WideSmem {
     uint32_t a[NBUF][P][RB * 16 * kAStride];  // after the K loop: group sums of the rows
-    uint32_t w[4][64 * 16];     // per-wave weight transposition buffer
+    uint32_t w[4][64 * 16];     // per-wave weight transposition buffer; after the K loop
+                                // the wave's bias rows, one block at a time
     uint16_t ts[4][64 * MAXG];  // per-wave scales of its 64 weight rows
+    int32_t dst[RB * 16];       // down: destination slot of each row
+    float wt[RB * 16];          // down: its routing weight
+};
+
+// Bias rows of a wave's four weight blocks (16 rows x G bf16 each, contiguous),
+// read raw as 16-byte pieces (lane l holds pieces l and l + 64 of each block)
+// while the last chunk is multiplied, and turned into operand order through
+// the wave's LDS buffer once the K loop is done.
+template <int CB>
+struct BiasRows {
+    u32x4 v[CB][2];
+
+    // blk[cb]: the block's first bias (the same in every lane)
+    __device__ __forceinline__ void load(const uint16_t* const (&blk)[CB], int G) {
+        const int lane = threadIdx.x & 63;
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) {
+            const Rsrc r = make_rsrc(blk[cb], 32u * G);  // pieces past the block read zeros
+#pragma unroll
+            for (int j = 0; j < 2; ++j) v[cb][j] = load16(r, 16u * (lane + 64 * j), 0);
+        }
+    }
+    // block cb to buf as 16 rows of G (pieces past the block are not stored)
+    __device__ __forceinline__ void store(uint16_t* buf, int cb, int G) const {
+        const int lane = threadIdx.x & 63;
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+            if (lane + 64 * j < 2 * G) *reinterpret_cast<u32x4*>(buf + 8 * (lane + 64 * j)) = v[cb][j];
+    }
 };
 // row stride (floats) of the group sums staged in a[] after the K loop: 16
 // rows of a fragment read fall on distinct banks, and 8-group reads up to
@@ -757,11 +770,11 @@ __device__ __forceinline__ u32x4 lds_frag(const WideSmem<RB, P, NBUF, MAXG>& sm,
 // Shared K loop of the wide paths: acc[rb][cb] over all groups for the four
 // 16-row weight blocks blk[cb] of this wave (row length K), activations staged
 // from src (P parts, `part` apart); row blocks rb >= nrb are skipped.
-template <int RB, int P, int NBUF, int MAXG>
+template <int RB, int P, int NBUF, int MAXG, class Last>
 __device__ __forceinline__ void wide_kloop(WideSmem<RB, P, NBUF, MAXG>& sm, Stager<RB, P>& st,
                                            const uint32_t* const (&src)[RB], size_t part,
                                            const uint32_t* const (&blk)[4], int K, bool active,
-                                           int nrb, CodeConsts kc, f32x4 (&acc)[RB][4]) {
+                                           int nrb, CodeConsts kc, f32x4 (&acc)[RB][4], Last&& last) {
     constexpr int CB = 4;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, q = lane >> 4, lr = lane & 15;
     const int G = K / kGroup;
@@ -775,14 +788,21 @@ __device__ __forceinline__ void wide_kloop(WideSmem<RB, P, NBUF, MAXG>& sm, Stag
     ww.put(wn);
     __syncthreads();  // stage 0 and the scale tables are in place
 
-    for (int c = 0; c < nch; ++c) {
+    // chunk c; the last one (peeled, so that the next-chunk registers are free
+    // for the epilogue's loads) issues no loads of its own
+    auto chunk = [&](int c, auto last_tag) {
+        constexpr bool kLast = decltype(last_tag)::value;
         const int buf = NBUF == 2 ? (c & 1) : 0;
-        const int cn = min(c + 1, nch - 1);
         u32x4 wq[CB];
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb) wq[cb] = ww.get(cb, lr, q);
-        st.load(src, part, cn, G);
-        ww.load(cn, wn);
+        // the next chunk's loads; during the last chunk, the epilogue's
+        if constexpr (!kLast) {
+            st.load(src, part, c + 1, G);
+            ww.load(c + 1, wn);
+        } else {
+            last();
+        }
         if (active) {
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
@@ -819,28 +839,29 @@ __device__ __forceinline__ void wide_kloop(WideSmem<RB, P, NBUF, MAXG>& sm, Stag
             }
         }
         __builtin_amdgcn_wave_barrier();
-        if (c + 1 < nch) ww.put(wn);
+        if constexpr (!kLast) ww.put(wn);
         if constexpr (NBUF == 2) {
-            if (c + 1 < nch) st.store(sm, buf ^ 1);
+            if constexpr (!kLast) st.store(sm, buf ^ 1);
             __syncthreads();
         } else {
             __syncthreads();
-            if (c + 1 < nch) st.store(sm, 0);
+            if constexpr (!kLast) st.store(sm, 0);
             __syncthreads();
         }
-    }
+    };
+    for (int c = 0; c + 1 < nch; ++c) chunk(c, std::false_type{});
+    chunk(nch - 1, std::true_type{});
 }
 
 // The bias term of the wide paths, added once after the K loop.  The group
 // sums of the staged rows go through LDS (the activation buffers are free by
 // then): thread t copies groups t % 16 + 16 j of rows t / 16 + 16 i, from row
 // pointers xrow[i] (G floats each, or with kBlocks 4 G block sums of h).
-// brow[cb]: this lane's bias row of weight block cb, in HBM.
+// br: the wave's bias rows, prefetched during the last chunk.
 template <int RB, int P, int NBUF, int MAXG, bool kBlocks>
 __device__ __forceinline__ void wide_bias(WideSmem<RB, P, NBUF, MAXG>& sm,
-                                          const float* const (&xrow)[RB],
-                                          const uint16_t* const (&brow)[4], int G, bool active,
-                                          f32x4 (&acc)[RB][4]) {
+                                          const float* const (&xrow)[RB], const BiasRows<4>& br,
+                                          int G, bool active, f32x4 (&acc)[RB][4]) {
     constexpr int CB = 4;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, q = lane >> 4, lr = lane & 15;
     float* xl = reinterpret_cast<float*>(&sm.a[0][0][0]);
@@ -855,10 +876,14 @@ __device__ __forceinline__ void wide_bias(WideSmem<RB, P, NBUF, MAXG>& sm,
     __syncthreads();
     const int steps = (G + 31) / 32;
     const uint16_t* ts = sm.ts[wave];
+    uint16_t* const wb = reinterpret_cast<uint16_t*>(sm.w[wave]);
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
+        br.store(wb, cb, G);
+        __builtin_amdgcn_wave_barrier();
         BiasOp C;
-        bias_from_scales(C, ts + (16 * cb + lr) * G, brow[cb], G, q, steps, active);
+        bias_from_table(C, ts + (16 * cb + lr) * G, wb + lr * G, G, q, steps, active);
+        __builtin_amdgcn_wave_barrier();
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
             // 8 consecutive groups per step; reads past G stay inside the row
@@ -930,15 +955,17 @@ __device__ __forceinline__ void gateup_wide(const FfnArgs& a, WideSmem<RB, 1, 2,
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb) acc[rb][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    wide_kloop<RB, P, NBUF, MAXG>(sm, st, src, 0, blk, H, active, (rows + 15) / 16, code_consts(a.zero), acc);
+    const uint16_t* bblk[CB];
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) bblk[cb] = a.b_gu + row0[cb] * G;
+    BiasRows<CB> br;
+    wide_kloop<RB, P, NBUF, MAXG>(sm, st, src, 0, blk, H, active, (rows + 15) / 16, code_consts(a.zero), acc,
+                                  [&] { br.load(bblk, G); });
 
     const float* xrow[RB];
 #pragma unroll
     for (int i = 0; i < RB; ++i) xrow[i] = a.xs + static_cast<size_t>(tok[i]) * G;
-    const uint16_t* brow[CB];
-#pragma unroll
-    for (int cb = 0; cb < CB; ++cb) brow[cb] = a.b_gu + (row0[cb] + lr) * G;
-    wide_bias<RB, P, NBUF, MAXG, false>(sm, xrow, brow, G, active, acc);
+    wide_bias<RB, P, NBUF, MAXG, false>(sm, xrow, br, G, active, acc);
 
     // GeGLU epilogue and the 16-column block sums of h
 #pragma unroll
@@ -992,6 +1019,13 @@ __device__ __forceinline__ void down_wide(const FfnArgs& a,
         hrow[i] = row_begin + min(r, rows - 1);
         src[i] = reinterpret_cast<const uint32_t*>(a.h) + static_cast<size_t>(hrow[i]) * (I / 2);
     }
+    // destination slot and routing weight of each row, kept in LDS for the
+    // epilogue (the K loop's first barrier publishes them)
+    if (tid < RB * 16) {
+        const int32_t d = a.perm[row_begin + min(tid, rows - 1)];
+        sm.dst[tid] = d;
+        sm.wt[tid] = a.topk_w[d];
+    }
     const size_t part = A * (I / 2);
     Stager<RB, P> st;
     st.load(src, part, 0, G);
@@ -1004,26 +1038,28 @@ __device__ __forceinline__ void down_wide(const FfnArgs& a,
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb) acc[rb][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    wide_kloop<RB, P, NBUF, MAXG>(sm, st, src, part, blk, I, active, (rows + 15) / 16, code_consts(a.zero), acc);
+    const uint16_t* bblk[CB];
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) bblk[cb] = a.b_d + row0[cb] * G;
+    BiasRows<CB> br;
+    wide_kloop<RB, P, NBUF, MAXG>(sm, st, src, part, blk, I, active, (rows + 15) / 16, code_consts(a.zero), acc,
+                                  [&] { br.load(bblk, G); });
 
     const float* xrow[RB];
 #pragma unroll
     for (int i = 0; i < RB; ++i) xrow[i] = a.hs + static_cast<size_t>(hrow[i]) * (I / 16);
-    const uint16_t* brow[CB];
-#pragma unroll
-    for (int cb = 0; cb < CB; ++cb) brow[cb] = a.b_d + (row0[cb] + lr) * G;
-    wide_bias<RB, P, NBUF, MAXG, true>(sm, xrow, brow, G, active, acc);
+    wide_bias<RB, P, NBUF, MAXG, true>(sm, xrow, br, G, active, acc);
 
     if (!active) return;
-    // weighted unsort
+    // weighted unsort (destinations and weights read before the K loop)
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
             const int r = 16 * rb + 4 * q + v;
             if (r < rows) {
-                const int32_t dst = a.perm[row_begin + r];
-                const float wt = a.topk_w[dst];
+                const int32_t dst = sm.dst[r];
+                const float wt = sm.wt[r];
                 float* yrow = a.y + static_cast<size_t>(dst) * H + cbase + lr;
 #pragma unroll
                 for (int cb = 0; cb < CB; ++cb) yrow[16 * cb] = wt * acc[rb][cb][v];

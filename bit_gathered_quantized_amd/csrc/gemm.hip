@@ -861,7 +861,7 @@ __device__ __forceinline__ void wide_kloop(WideSmem<RB, P, NBUF, MAXG>& sm, Stag
 template <int RB, int P, int NBUF, int MAXG, bool kBlocks>
 __device__ __forceinline__ void wide_bias(WideSmem<RB, P, NBUF, MAXG>& sm,
                                           const float* const (&xrow)[RB], const BiasRows<4>& br,
-                                          int G, bool active, f32x4 (&acc)[RB][4]) {
+                                          int G, bool active, int nrb, f32x4 (&acc)[RB][4]) {
     constexpr int CB = 4;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, q = lane >> 4, lr = lane & 15;
     float* xl = reinterpret_cast<float*>(&sm.a[0][0][0]);
@@ -875,6 +875,27 @@ __device__ __forceinline__ void wide_bias(WideSmem<RB, P, NBUF, MAXG>& sm,
         }
     __syncthreads();
     const int steps = (G + 31) / 32;
+    // row operands once per row block (8 consecutive groups per step; reads
+    // past G stay inside the row stride and are replaced by 0)
+    BiasOp X[RB];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+        const float* xr = xl + (16 * rb + lr) * kXStride;
+#pragma unroll
+        for (int st = 0; st < kMaxBiasSteps; ++st) {
+            if (st < steps) {
+                const f32x4 v0 = *reinterpret_cast<const f32x4*>(xr + 32 * st + 8 * q);
+                const f32x4 v1 = *reinterpret_cast<const f32x4*>(xr + 32 * st + 8 * q + 4);
+                float v[8];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const float x = j < 4 ? v0[j] : v1[j - 4];
+                    v[j] = 32 * st + 8 * q + j < G ? x : 0.f;
+                }
+                pack_split(v, X[rb].hi[st], X[rb].lo[st]);
+            }
+        }
+    }
     const uint16_t* ts = sm.ts[wave];
     uint16_t* const wb = reinterpret_cast<uint16_t*>(sm.w[wave]);
 #pragma unroll
@@ -886,27 +907,10 @@ __device__ __forceinline__ void wide_bias(WideSmem<RB, P, NBUF, MAXG>& sm,
         __builtin_amdgcn_wave_barrier();
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
-            // 8 consecutive groups per step; reads past G stay inside the row
-            // stride and are replaced by 0
-            const float* xr = xl + (16 * rb + lr) * kXStride;
-            BiasOp X;
-#pragma unroll
-            for (int st = 0; st < kMaxBiasSteps; ++st) {
-                if (st < steps) {
-                    const f32x4 v0 = *reinterpret_cast<const f32x4*>(xr + 32 * st + 8 * q);
-                    const f32x4 v1 = *reinterpret_cast<const f32x4*>(xr + 32 * st + 8 * q + 4);
-                    float v[8];
-#pragma unroll
-                    for (int j = 0; j < 8; ++j) {
-                        const float x = j < 4 ? v0[j] : v1[j - 4];
-                        v[j] = 32 * st + 8 * q + j < G ? x : 0.f;
-                    }
-                    pack_split(v, X.hi[st], X.lo[st]);
-                }
-            }
-            acc[rb][cb] += bias_mfma(X, C, steps);
-            __builtin_amdgcn_sched_barrier(0);  // one block at a time: registers stay low
+            if (rb >= nrb) break;  // row blocks past the tile
+            acc[rb][cb] += bias_mfma(X[rb], C, steps);
         }
+        __builtin_amdgcn_sched_barrier(0);  // one weight block at a time: registers stay low
     }
 }
 
@@ -965,7 +969,7 @@ __device__ __forceinline__ void gateup_wide(const FfnArgs& a, WideSmem<RB, 1, 2,
     const float* xrow[RB];
 #pragma unroll
     for (int i = 0; i < RB; ++i) xrow[i] = a.xs + static_cast<size_t>(tok[i]) * G;
-    wide_bias<RB, P, NBUF, MAXG, false>(sm, xrow, br, G, active, acc);
+    wide_bias<RB, P, NBUF, MAXG, false>(sm, xrow, br, G, active, (rows + 15) / 16, acc);
 
     // GeGLU epilogue and the 16-column block sums of h
 #pragma unroll
@@ -1048,7 +1052,7 @@ __device__ __forceinline__ void down_wide(const FfnArgs& a,
     const float* xrow[RB];
 #pragma unroll
     for (int i = 0; i < RB; ++i) xrow[i] = a.hs + static_cast<size_t>(hrow[i]) * (I / 16);
-    wide_bias<RB, P, NBUF, MAXG, true>(sm, xrow, br, G, active, acc);
+    wide_bias<RB, P, NBUF, MAXG, true>(sm, xrow, br, G, active, (rows + 15) / 16, acc);
 
     if (!active) return;
     // weighted unsort (destinations and weights read before the K loop)

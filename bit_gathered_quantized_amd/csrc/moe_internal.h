@@ -113,14 +113,20 @@ __device__ __forceinline__ float sum8_bf16(u32x4 v) {
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
 // tanh-approximate GELU in fp32: 0.5 v (1 + tanh(z)) = v / (1 + exp(-2 z)),
-// z = sqrt(2/pi) (v + 0.044715 v^3).
+// z = sqrt(2/pi) (v + 0.044715 v^3).  exp(-2 z) is 2^(-2 z log2 e) on the
+// hardware base-2 exponential and the quotient is v times the hardware
+// reciprocal: each within a few ulp, far below the rounding of h that follows
+// (bf16, or 16 bits as hi + lo).  Large |v| give v or -0 (the exponential
+// saturates to 0 or +inf, whose reciprocal is 0).
 __device__ __forceinline__ float gelu_tanh(float v) {
     const float z = 0.7978845608028654f * (v + 0.044715f * v * v * v);
-    return v / (1.0f + expf(-2.0f * z));
+    return v * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-2.8853900817779268f * z));
 }
 
-// SiLU in fp32: v * sigmoid(v) = v / (1 + exp(-v)).
-__device__ __forceinline__ float silu(float v) { return v / (1.0f + expf(-v)); }
+// SiLU in fp32: v * sigmoid(v) = v / (1 + exp(-v)), evaluated the same way.
+__device__ __forceinline__ float silu(float v) {
+    return v * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * v));
+}
 
 // ---------------------------------------------------- kernel launchers
 // Optional start/stop events of one kernel.  With events the kernel is

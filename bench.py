@@ -46,7 +46,7 @@ def algorithmic_work(p):
     import numpy as np
     E, H, I, T, k = p.E, p.H, p.I, p.T, p.k
     A = T * k
-    G_h, G_i = H // 64, I // 64
+    G_h, G_i = H // p.gs, I // p.gs
     gu_expert = 2 * I * H // 2 + 2 * (2 * I * G_h * 2)      # codes + scales + biases
     d_expert = H * I // 2 + 2 * (H * G_i * 2)
     ids = p.topk_ids.ravel()
@@ -285,6 +285,11 @@ def main():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of the forward, copy MIB MiB device-to-device 5 times "
                          "(the reference kernel for scaling HBM byte counters)")
+    ap.add_argument("--group-size", type=int, default=64, choices=[32, 64, 128],
+                    help="quantisation group size of the synthetic weights")
+    ap.add_argument("--intermediate", type=int, default=0, metavar="I",
+                    help="override the workload's intermediate size (e.g. 768 at group "
+                         "size 128, which does not divide 704)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -315,12 +320,19 @@ def main():
               flush=True)
         return
 
-    p = ms.make_config(args.workload, seed=0)
+    c = ms.CONFIGS[args.workload]
+    I = args.intermediate or c["I"]
+    custom = args.group_size != ms.GROUP_SIZE or I != c["I"]
+    if custom:
+        p = ms.make_problem(c["E"], c["H"], I, c["T"], c["k"], seed=0, router=c["router"],
+                            gs=args.group_size, name=args.workload)
+    else:
+        p = ms.make_config(args.workload, seed=0)
     A = p.T * p.k
     counts = np.bincount(p.topk_ids.ravel(), minlength=p.E)
     touched = int(np.count_nonzero(counts))
     log(f"workload {args.workload}: E={p.E} H={p.H} I={p.I} T={p.T} k={p.k} A={A} "
-        f"touched={touched}")
+        f"gs={p.gs} touched={touched}")
 
     dev = torch.device("cuda", 0)
 
@@ -333,7 +345,7 @@ def main():
                 t(p.b_down, np.int16)]
 
     sets = [upload() for _ in range(max(1, args.copies))]
-    prob = bgq.problem(p.T, p.k, p.E, p.H, p.I, 0)
+    prob = bgq.problem(p.T, p.k, p.E, p.H, p.I, 0, group_size=p.gs)
     ws = torch.empty(bgq.workspace_bytes(prob), dtype=torch.uint8, device=dev)
     out = torch.empty((p.T, p.H), dtype=torch.bfloat16, device=dev)
     stream = torch.cuda.current_stream()
@@ -382,7 +394,8 @@ def main():
     dominant = max((s for s in kernels if s not in not_launched), key=lambda s: mean_us[s])
     roof = roofline_entry(work[dominant], mean_us[dominant] * 1e-6)
     roof["kernel"] = dominant
-    roof["traffic"] = load_traffic(dominant, args.workload)
+    # counter summaries are committed for the named workloads only
+    roof["traffic"] = None if custom else load_traffic(dominant, args.workload)
 
     fwd_s = statistics.median(fwd_us) * 1e-6
     forward = dict(
@@ -423,7 +436,7 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": args.workload, "E": p.E, "H": p.H, "I": p.I, "T": p.T,
-                   "k": p.k, "assignments": A, "group_size": 64, "bits": 4,
+                   "k": p.k, "assignments": A, "group_size": p.gs, "bits": 4,
                    "router": ms.CONFIGS[args.workload]["router"], "seed": 0,
                    "touched_experts": touched, "input_copies": len(sets), **split},
         "roofline": roof,

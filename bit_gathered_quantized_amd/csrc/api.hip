@@ -17,13 +17,18 @@ bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 // Shape checks shared by the forward's size queries and the forward itself.
 moe_status check_problem(const moe_problem* p) {
     if (!p) return MOE_ERR_NULL;
-    if (p->bits != 4 || p->group_size != moe::kGroup) return MOE_ERR_UNSUPPORTED;
+    if (p->bits != 4) return MOE_ERR_UNSUPPORTED;
+    if (p->group_size != 32 && p->group_size != 64 && p->group_size != 128)
+        return MOE_ERR_UNSUPPORTED;
     if (p->flags & ~(MOE_F_FP32_OUT | MOE_F_FP32_INTERMEDIATE | MOE_F_SWIGLU))
         return MOE_ERR_UNSUPPORTED;
     if (p->T < 0 || p->k < 1 || p->E < 1 || p->H < 1 || p->I < 1) return MOE_ERR_SHAPE;
     if (p->E > MOE_MAX_EXPERTS) return MOE_ERR_UNSUPPORTED;
     if (p->k > p->E) return MOE_ERR_SHAPE;
-    if (p->H % moe::kGroup || p->I % moe::kGroup) return MOE_ERR_SHAPE;
+    // The kernels step through K in 64-column halves of 128-column chunks;
+    // a group never straddles two of those steps.
+    if (p->H % 64 || p->I % 64) return MOE_ERR_SHAPE;
+    if (p->H % p->group_size || p->I % p->group_size) return MOE_ERR_SHAPE;
     if (p->H > moe::kMaxDim || p->I > moe::kMaxDim) return MOE_ERR_UNSUPPORTED;
     const int64_t A = static_cast<int64_t>(p->T) * p->k;
     if (A > INT32_MAX / 2) return MOE_ERR_SHAPE;
@@ -46,7 +51,7 @@ moe_ws_layout make_layout(const moe_problem* p) {
         return at;
     };
     const size_t hbytes = (p->flags & MOE_F_FP32_INTERMEDIATE) ? 4 : 2;
-    const size_t G = p->H / moe::kGroup;
+    const size_t G = p->H / p->group_size;
     l.counts = take(sizeof(int32_t) * p->E);
     l.offsets = take(sizeof(int32_t) * (p->E + 1));
     l.perm = take(sizeof(int32_t) * A);
@@ -123,6 +128,7 @@ moe_status forward_impl(const moe_problem* p, const void* x, const int32_t* ids,
     r.x = static_cast<const uint16_t*>(x);
     r.T = p->T;
     r.H = p->H;
+    r.gs = p->group_size;
     r.xp = reinterpret_cast<uint16_t*>(base + l.x_perm);
     r.xs = reinterpret_cast<float*>(base + l.x_sums);
 
@@ -132,6 +138,7 @@ moe_status forward_impl(const moe_problem* p, const void* x, const int32_t* ids,
     f.E = p->E;
     f.H = p->H;
     f.I = p->I;
+    f.gs = p->group_size;
     f.max_tiles = l.max_tiles;
     f.max_skinny = l.max_skinny;
     f.skinny_only = skinny_only ? 1 : 0;
@@ -214,6 +221,7 @@ moe_status moe_sort_build_tiles(const int32_t* topk_ids, int32_t T, int32_t k, i
     r.hist = nullptr;
     r.num_tiles = num_tiles;
     r.x = nullptr;
+    r.gs = 0;
     r.T = T;
     r.H = 0;
     r.xp = nullptr;

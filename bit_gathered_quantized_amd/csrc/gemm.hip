@@ -55,7 +55,6 @@ constexpr int kThreads = 256;
 // and weight chunks in flight
 constexpr int kSkinnyGateUpRing = 2;
 constexpr int kSkinnyDownBlocks = 2, kSkinnyDownRing = 2;
-constexpr int kMaxG = kMaxDim / kGroup;    // groups per row the LDS tables hold
 
 // A buffer resource over n bytes at p (p the same in every lane): a 16-byte
 // load through it at a byte offset at or past n returns zeros and reads no
@@ -98,12 +97,39 @@ __device__ __forceinline__ int4 load_skinny_tile(const FfnArgs& a, int ncb, int&
     return ti < n ? t : int4{-1, 0, 0, 0};
 }
 
+// ------------------------------------------------------------ group geometry
+// A chunk is 128 columns of K: four MFMA slices of 32 columns (one weight word
+// per lane and slice).  The K loop scales products in chains of kChain
+// columns: a chain's slices are chained from zero on the MFMA, then acc += s P
+// with the scale of the chain's group.  A group of 32 or 64 columns is one
+// chain; a group of 128 columns is two chains of 64 with the same scale (one
+// chain of four slices would need twice the decoded weights in registers at
+// once).  K may end in a half chunk of 64 columns (not with GS = 128, where H
+// and I are multiples of 128).
+template <int GS>
+struct Geo {
+    static_assert(GS == 32 || GS == 64 || GS == 128, "group size");
+    static constexpr int kChain = GS < 64 ? GS : 64;    // columns per scaled chain
+    static constexpr int kSlices = kChain / 32;         // MFMA slices per chain
+    static constexpr int kChains = 128 / kChain;        // chains per chunk
+    static constexpr int kShift = GS == 128 ? 1 : 0;    // chain index >> kShift = group
+    static constexpr int kMaxG = kMaxDim / GS;          // groups per row, at most
+    static constexpr int kSteps = (kMaxG + 31) / 32;    // bias-contraction MFMA steps
+    // The chunk word (0..15) that lane group q feeds to slice s.  The four words
+    // of a slice (q = 0..3) lie in one chain.  64-column chains: words 2q and
+    // 2q + 1 of each chain; 32: word 4 s + q.
+    static __device__ __forceinline__ constexpr int word(int s, int q) {
+        return kChain == 64 ? 8 * (s >> 1) + 2 * q + (s & 1) : 4 * s + q;
+    }
+};
+
 // --------------------------------------------------------------- bias term
 // Operand of the bias contraction for one lane: 8 consecutive groups per MFMA
 // step (group 32 st + 8 q + j in element j), split into bf16 hi and lo.
+template <int NS>
 struct BiasOp {
-    u32x4 hi[kMaxBiasSteps];
-    u32x4 lo[kMaxBiasSteps];
+    u32x4 hi[NS];
+    u32x4 lo[NS];
 };
 
 __device__ __forceinline__ void pack_split(const float (&v)[8], u32x4& hi, u32x4& lo) {
@@ -118,10 +144,11 @@ __device__ __forceinline__ void pack_split(const float (&v)[8], u32x4& hi, u32x4
 // Column operand: c[g] = b[g] - 16 s[g] of one weight row, from its rows of
 // the scale and bias tables.  Groups past G repeat the last group: the row
 // operand is zero there, so those (finite) products add nothing.
-__device__ __forceinline__ void bias_from_table(BiasOp& o, const uint16_t* ts, const uint16_t* tb,
+template <int NS>
+__device__ __forceinline__ void bias_from_table(BiasOp<NS>& o, const uint16_t* ts, const uint16_t* tb,
                                                 int G, int q, int steps, bool active) {
 #pragma unroll
-    for (int st = 0; st < kMaxBiasSteps; ++st) {
+    for (int st = 0; st < NS; ++st) {
         if (st < steps) {
             float v[8];
 #pragma unroll
@@ -135,40 +162,53 @@ __device__ __forceinline__ void bias_from_table(BiasOp& o, const uint16_t* ts, c
     }
 }
 
-// Group sum g of h from its four 16-column block sums (h_sums row X16):
-// ((b0 + b1) + b2) + b3, the one order every path uses.
+// Group sum g of h from its GS / 16 block sums of 16 columns (h_sums row
+// X16), added in block order ((b0 + b1) + b2) + ..., the one order every path
+// uses.
+template <int GS>
 __device__ __forceinline__ float group_of_blocks(const float* X16, int g) {
-    const f32x4 b = *reinterpret_cast<const f32x4*>(X16 + 4 * g);
-    return ((b[0] + b[1]) + b[2]) + b[3];
+    if constexpr (GS == 32) {
+        const f32x2 b = *reinterpret_cast<const f32x2*>(X16 + 2 * g);
+        return b[0] + b[1];
+    } else if constexpr (GS == 64) {
+        const f32x4 b = *reinterpret_cast<const f32x4*>(X16 + 4 * g);
+        return ((b[0] + b[1]) + b[2]) + b[3];
+    } else {
+        const f32x4 b = *reinterpret_cast<const f32x4*>(X16 + 8 * g);
+        const f32x4 c = *reinterpret_cast<const f32x4*>(X16 + 8 * g + 4);
+        return ((((((b[0] + b[1]) + b[2]) + b[3]) + c[0]) + c[1]) + c[2]) + c[3];
+    }
 }
 
-// The group sums of one activation row as the bias operand.
+// The group sums of one activation row as the bias operand (NS steps).
+template <int NS>
 struct RowSums {
-    float v[kMaxBiasSteps][8];
+    float v[NS][8];
 
     __device__ __forceinline__ void load(const float* X, int G, int q) {
 #pragma unroll
-        for (int st = 0; st < kMaxBiasSteps; ++st)
+        for (int st = 0; st < NS; ++st)
 #pragma unroll
             for (int j = 0; j < 8; ++j) v[st][j] = X[min(32 * st + 8 * q + j, G - 1)];
     }
-    // from the 16-column block sums of the row (4 G floats); steps past the
-    // ones used are left unread
+    // from the 16-column block sums of the row (G * GS / 16 floats); steps past
+    // the ones used are left unread
+    template <int GS>
     __device__ __forceinline__ void load_blocks(const float* X16, int G, int q, int steps) {
 #pragma unroll
-        for (int st = 0; st < kMaxBiasSteps; ++st) {
+        for (int st = 0; st < NS; ++st) {
             if (st < steps) {
 #pragma unroll
-                for (int j = 0; j < 8; ++j) v[st][j] = group_of_blocks(X16, min(32 * st + 8 * q + j, G - 1));
+                for (int j = 0; j < 8; ++j) v[st][j] = group_of_blocks<GS>(X16, min(32 * st + 8 * q + j, G - 1));
             } else {
 #pragma unroll
                 for (int j = 0; j < 8; ++j) v[st][j] = 0.f;
             }
         }
     }
-    __device__ __forceinline__ void pack(BiasOp& o, int G, int q, int steps) const {
+    __device__ __forceinline__ void pack(BiasOp<NS>& o, int G, int q, int steps) const {
 #pragma unroll
-        for (int st = 0; st < kMaxBiasSteps; ++st) {
+        for (int st = 0; st < NS; ++st) {
             if (st < steps) {
                 float w[8];
 #pragma unroll
@@ -180,10 +220,11 @@ struct RowSums {
 };
 
 // sum_g c[n, g] X[m, g] for one 16x16 block: hi*hi + hi*lo + lo*hi per step.
-__device__ __forceinline__ f32x4 bias_mfma(const BiasOp& A, const BiasOp& B, int steps) {
+template <int NS>
+__device__ __forceinline__ f32x4 bias_mfma(const BiasOp<NS>& A, const BiasOp<NS>& B, int steps) {
     f32x4 r = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int st = 0; st < kMaxBiasSteps; ++st) {
+    for (int st = 0; st < NS; ++st) {
         if (st < steps) {
             r = mfma16(A.hi[st], B.hi[st], r);
             r = mfma16(A.hi[st], B.lo[st], r);
@@ -193,53 +234,47 @@ __device__ __forceinline__ f32x4 bias_mfma(const BiasOp& A, const BiasOp& B, int
     return r;
 }
 
-// One 64-column group of one 16x16 block: two MFMA steps, then the scale.
-// Every path goes through exactly this sequence.
-__device__ __forceinline__ f32x4 group_step(f32x4 acc, u32x4 a0, u32x4 a1, u32x4 b0, u32x4 b1,
+// P of one group for one 16x16 block: the group's NSL slices chained from
+// zero, in slice order (with P = 2 each slice's activation is hi + lo: the hi
+// part first).  Then acc += s P.  Every path goes through exactly this.
+template <int NSL, int P = 1>
+__device__ __forceinline__ f32x4 group_step(f32x4 acc, const u32x4 (&x)[NSL][P], const u32x4 (&b)[NSL],
                                             float s16) {
     f32x4 p = {0.f, 0.f, 0.f, 0.f};
-    p = mfma16(a0, b0, p);
-    p = mfma16(a1, b1, p);
 #pragma unroll
-    for (int v = 0; v < 4; ++v) acc[v] = fmaf(s16, p[v], acc[v]);
-    return acc;
-}
-// Same with the activation split into hi + lo parts (fp32 h, down matmul).
-__device__ __forceinline__ f32x4 group_step2(f32x4 acc, u32x4 a0h, u32x4 a0l, u32x4 a1h,
-                                             u32x4 a1l, u32x4 b0, u32x4 b1, float s16) {
-    f32x4 p = {0.f, 0.f, 0.f, 0.f};
-    p = mfma16(a0h, b0, p);
-    p = mfma16(a0l, b0, p);
-    p = mfma16(a1h, b1, p);
-    p = mfma16(a1l, b1, p);
+    for (int sl = 0; sl < NSL; ++sl)
+#pragma unroll
+        for (int pp = 0; pp < P; ++pp) p = mfma16(x[sl][pp], b[sl], p);
 #pragma unroll
     for (int v = 0; v < 4; ++v) acc[v] = fmaf(s16, p[v], acc[v]);
     return acc;
 }
 
-// Both groups of one chunk for NB weight blocks: the MFMA chains of all
-// (block, group) pairs are issued together, then each block takes its two
-// scaled products in group order -- group_step's arithmetic, pair by pair.
-template <int NB>
+// The groups of one chunk (NSL = 4 slices, or 2 for a half chunk) for NB
+// weight blocks: the MFMA chains of all (block, group) pairs are issued
+// together, slice by slice, then each block takes its scaled products in group
+// order -- group_step's arithmetic, pair by pair.  x[s]: slice s's activation
+// operand; wv[b][s]: block b's weight word for slice s.
+template <int GS, int NB, int NSL>
 __device__ __forceinline__ void chunk_steps(f32x4 (&acc)[NB], const u32x4 (&x)[4], const u32x4 (&wv)[NB],
-                                            const float (&s16)[NB][2], CodeConsts kc) {
-    f32x4 p[NB][2];
+                                            const float (&s16)[NB][Geo<GS>::kChains], CodeConsts kc) {
+    constexpr int MPG = Geo<GS>::kSlices, NG = NSL / MPG;
+    static_assert(NSL % MPG == 0, "a chunk holds whole groups");
+    f32x4 p[NB][NG];
 #pragma unroll
-    for (int gi = 0; gi < 2; ++gi)
+    for (int m = 0; m < MPG; ++m)
 #pragma unroll
-        for (int b = 0; b < NB; ++b)
-            p[b][gi] = mfma16(x[2 * gi], codes_as_bf16(wv[b][2 * gi], kc), f32x4{0.f, 0.f, 0.f, 0.f});
+        for (int j = 0; j < NG; ++j)
 #pragma unroll
-    for (int gi = 0; gi < 2; ++gi)
-#pragma unroll
-        for (int b = 0; b < NB; ++b)
-            p[b][gi] = mfma16(x[2 * gi + 1], codes_as_bf16(wv[b][2 * gi + 1], kc), p[b][gi]);
+            for (int b = 0; b < NB; ++b)
+                p[b][j] = mfma16(x[j * MPG + m], codes_as_bf16(wv[b][j * MPG + m], kc),
+                                 m == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : p[b][j]);
 #pragma unroll
     for (int b = 0; b < NB; ++b)
 #pragma unroll
-        for (int gi = 0; gi < 2; ++gi)
+        for (int j = 0; j < NG; ++j)
 #pragma unroll
-            for (int v = 0; v < 4; ++v) acc[b][v] = fmaf(s16[b][gi], p[b][gi][v], acc[b][v]);
+            for (int v = 0; v < 4; ++v) acc[b][v] = fmaf(s16[b][j], p[b][j][v], acc[b][v]);
 }
 
 // A bf16 scale as the factor of P.
@@ -285,7 +320,7 @@ __device__ __forceinline__ float store_h(const FfnArgs& a, size_t A, int srow, i
 // row.  LDS entry (row, q, g) = words 2q, 2q+1 of group g of the chunk, at
 // row * 16 + 4 * (q ^ ((row >> 2) & 3)) + 2 g  (u32 units); the XOR keeps the
 // 16 rows of a fragment read on distinct banks.
-template <int NCB>
+template <int NCB, int GS = 64>
 struct WaveW {
     uint32_t* lds;   // NCB * 16 rows x 16 u32
     Rsrc blk[NCB];   // block cb: its 16 weight rows
@@ -317,9 +352,24 @@ struct WaveW {
             *reinterpret_cast<u32x2*>(row + 4 * ((qa + 1) ^ sw) + 2 * g) = u32x2{v[cb][2], v[cb][3]};
         }
     }
-    // [g0 word 2q, g0 word 2q+1, g1 word 2q, g1 word 2q+1] of row 16 cb + lr
+    // The words lane (lr, q) feeds to slices 0..3 (Geo<GS>::word) of row
+    // 16 cb + lr; for GS = 64 that is [g0 word 2q, g0 word 2q+1, g1 word 2q,
+    // g1 word 2q+1], one 16-byte read.
     __device__ __forceinline__ u32x4 get(int cb, int lr, int q) const {
-        return *reinterpret_cast<const u32x4*>(lds + (16 * cb + lr) * 16 + 4 * (q ^ ((lr >> 2) & 3)));
+        const uint32_t* row = lds + (16 * cb + lr) * 16;
+        const int sw = (lr >> 2) & 3;
+        if constexpr (Geo<GS>::kChain == 64) {
+            return *reinterpret_cast<const u32x4*>(row + 4 * (q ^ sw));
+        } else {
+            // word w sits at 4 ((w & 7) >> 1 ^ sw) + 2 (w >> 3) + (w & 1)
+            u32x4 r;
+#pragma unroll
+            for (int sl = 0; sl < 4; ++sl) {
+                const int w = Geo<GS>::word(sl, q);
+                r[sl] = row[4 * (((w & 7) >> 1) ^ sw) + 2 * (w >> 3) + (w & 1)];
+            }
+            return r;
+        }
     }
 };
 
@@ -329,9 +379,9 @@ struct WaveW {
 // loads per lane and table cover G <= 64.  The loads are issued early and the
 // stores made later, so their latency overlaps the first weight loads.
 // kBias = false: scales only (the wide paths read biases from HBM at the end).
-template <int NCB, bool kBias = true>
+template <int NCB, bool kBias = true, int NP = 2>
 struct Tables {
-    u32x4 vs[NCB][2], vb[NCB][kBias ? 2 : 1];
+    u32x4 vs[NCB][NP], vb[NCB][kBias ? NP : 1];  // NP pieces per lane cover G <= 32 NP
 
     __device__ __forceinline__ void load(const uint16_t* s, const uint16_t* b,
                                          const size_t (&row0)[NCB], int G) {
@@ -341,11 +391,11 @@ struct Tables {
         for (int cb = 0; cb < NCB; ++cb) {
             const Rsrc rs = make_rsrc(s + row0[cb] * G, n);
 #pragma unroll
-            for (int j = 0; j < 2; ++j) vs[cb][j] = load16(rs, 16u * (lane + 64 * j), 0);
+            for (int j = 0; j < NP; ++j) vs[cb][j] = load16(rs, 16u * (lane + 64 * j), 0);
             if constexpr (kBias) {
                 const Rsrc rb = make_rsrc(b + row0[cb] * G, n);
 #pragma unroll
-                for (int j = 0; j < 2; ++j) vb[cb][j] = load16(rb, 16u * (lane + 64 * j), 0);
+                for (int j = 0; j < NP; ++j) vb[cb][j] = load16(rb, 16u * (lane + 64 * j), 0);
             }
         }
     }
@@ -354,7 +404,7 @@ struct Tables {
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
+            for (int j = 0; j < NP; ++j) {
                 const int idx = lane + 64 * j;
                 if (idx < np) {
                     *reinterpret_cast<u32x4*>(ts + cb * 16 * G + 8 * idx) = vs[cb][j];
@@ -367,11 +417,11 @@ struct Tables {
 
 // =========================================================== skinny paths
 // One wave's LDS: NB 16-row weight blocks.
-template <int NB>
+template <int NB, int MAXG>
 struct alignas(16) SkinnySmem {
     uint32_t w[NB * 16 * 16];      // weight transposition buffer
-    uint16_t ts[NB * 16 * kMaxG];  // scales of the wave's weight rows
-    uint16_t tb[NB * 16 * kMaxG];  // biases
+    uint16_t ts[NB * 16 * MAXG];   // scales of the wave's weight rows
+    uint16_t tb[NB * 16 * MAXG];   // biases
     int32_t dst[kBmSmall];         // down: destination slot of each row
     float wt[kBmSmall];            // down: its routing weight
 };
@@ -381,16 +431,16 @@ struct alignas(16) SkinnySmem {
 // n0 .. n0 + 15) and block up (rows I + n0 ..), and writes their 16-column
 // block sums of h.
 // RING chunks of weights are in flight.
-template <bool kF32H, int RING>
-__global__ __launch_bounds__(64, 3) void moe_gateup_skinny(FfnArgs a) {
-    constexpr int NB = 2;
-    __shared__ SkinnySmem<NB> sm;
+template <bool kF32H, int RING, int GS>
+__global__ __launch_bounds__(64, GS == 32 ? 2 : 3) void moe_gateup_skinny(FfnArgs a) {
+    constexpr int NB = 2, NS = Geo<GS>::kSteps, GPC = Geo<GS>::kChains, SH = Geo<GS>::kShift;
+    __shared__ SkinnySmem<NB, Geo<GS>::kMaxG> sm;
     int cb;
     const int4 tile = load_skinny_tile(a, a.I / 16, cb);
     if (tile.x < 0) return;
     const int e = tile.x, row_begin = tile.y, rows = tile.z;
     const int lane = threadIdx.x & 63, q = lane >> 4, lr = lane & 15;
-    const int H = a.H, I = a.I, G = H / kGroup;
+    const int H = a.H, I = a.I, G = H / GS;
     const size_t A = static_cast<size_t>(a.T) * a.k;
     const int hcol0 = cb * 16;
 
@@ -400,9 +450,9 @@ __global__ __launch_bounds__(64, 3) void moe_gateup_skinny(FfnArgs a) {
     row0[1] = row0[0] + I;
 #pragma unroll
     for (int b = 0; b < NB; ++b) blk[b] = a.w_gu + row0[b] * (H / 8);
-    Tables<NB> tab;
+    Tables<NB, true, Geo<GS>::kMaxG / 32> tab;
     tab.load(a.s_gu, a.b_gu, row0, G);
-    WaveW<NB> ww;
+    WaveW<NB, GS> ww;
     ww.init(sm.w, blk, H / 8);
     u32x4 rv[RING][NB];
 #pragma unroll
@@ -412,14 +462,18 @@ __global__ __launch_bounds__(64, 3) void moe_gateup_skinny(FfnArgs a) {
     const int tok = a.perm[row_begin + min(lr, rows - 1)] / a.k;
     const uint32_t* xa = reinterpret_cast<const uint32_t*>(a.xp) + static_cast<size_t>(tok) * (H / 2);
     u32x4 ra[2][4];
-    // this lane's pieces of group g start at xq + 32 g (g the same in every lane)
-    const uint32_t* const xq = xa + 8 * q;
+    // slice s of chunk c: the activation piece of chunk word Geo<GS>::word(s, q),
+    // in 64-column half 2 c + s / 2 (the same in every lane; past K the last
+    // half is read again and never used)
+    constexpr bool kC64 = Geo<GS>::kChain == 64;
+    const uint32_t* const xq = xa + (kC64 ? 8 : 4) * q;
     auto load_a = [&](int c, int buf) {
 #pragma unroll
-        for (int gi = 0; gi < 2; ++gi) {
-            const uint32_t* const xg = xq + static_cast<uint32_t>(32 * min(2 * c + gi, G - 1));
+        for (int hf = 0; hf < 2; ++hf) {
+            const uint32_t* const xg = xq + static_cast<uint32_t>(32 * min(2 * c + hf, H / 64 - 1));
 #pragma unroll
-            for (int s = 0; s < 2; ++s) ra[buf][2 * gi + s] = *reinterpret_cast<const u32x4*>(xg + 4 * s);
+            for (int s = 0; s < 2; ++s)
+                ra[buf][2 * hf + s] = *reinterpret_cast<const u32x4*>(xg + (kC64 ? 4 : 16) * s);
         }
     };
     load_a(0, 0);
@@ -427,18 +481,18 @@ __global__ __launch_bounds__(64, 3) void moe_gateup_skinny(FfnArgs a) {
     // as the tables are in place and added after the groups (the same
     // arithmetic as forming it there), so no load waits at the end
     const int steps = (G + 31) / 32;
-    RowSums xsum;
+    RowSums<NS> xsum;
     xsum.load(a.xs + static_cast<size_t>(tok) * G, G, q);
 
     tab.store(sm.ts, sm.tb, G);
     __builtin_amdgcn_wave_barrier();
     f32x4 bterm[NB];
     {
-        BiasOp X;
+        BiasOp<NS> X;
         xsum.pack(X, G, q, steps);
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
-            BiasOp C;
+            BiasOp<NS> C;
             bias_from_table(C, sm.ts + (16 * b + lr) * G, sm.tb + (16 * b + lr) * G, G, q, steps, true);
             bterm[b] = bias_mfma(X, C, steps);
         }
@@ -447,10 +501,10 @@ __global__ __launch_bounds__(64, 3) void moe_gateup_skinny(FfnArgs a) {
     f32x4 acc[NB];
 #pragma unroll
     for (int b = 0; b < NB; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const int nfull = G / 2, nch = (G + 1) / 2;
+    const int nfull = H / 128, nch = (H + 127) / 128;
     const CodeConsts kc = code_consts(a.zero);
     // chunk c: its weights go through LDS, the slot reloads with chunk c + RING
-    // at once, then the MFMAs run (an odd G ends with a one-group chunk)
+    // at once, then the MFMAs run (K may end in a half chunk of 64 columns)
     auto compute = [&](int slot, int abuf, int c, bool reload, bool full) {
         chunk_fence();
         ww.put(rv[slot]);
@@ -459,18 +513,16 @@ __global__ __launch_bounds__(64, 3) void moe_gateup_skinny(FfnArgs a) {
         u32x4 wv[NB];
 #pragma unroll
         for (int b = 0; b < NB; ++b) wv[b] = ww.get(b, lr, q);
+        float s16[NB][GPC];
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+            for (int j = 0; j < GPC; ++j)
+                s16[b][j] = scale16(sm.ts[(16 * b + lr) * G + min((GPC * c + j) >> SH, G - 1)]);
         if (full) {
-            float s16[NB][2];
-#pragma unroll
-            for (int b = 0; b < NB; ++b)
-#pragma unroll
-                for (int gi = 0; gi < 2; ++gi) s16[b][gi] = scale16(sm.ts[(16 * b + lr) * G + 2 * c + gi]);
-            chunk_steps<NB>(acc, ra[abuf], wv, s16, kc);
-        } else {
-#pragma unroll
-            for (int b = 0; b < NB; ++b)
-                acc[b] = group_step(acc[b], ra[abuf][0], ra[abuf][1], codes_as_bf16(wv[b][0], kc),
-                                    codes_as_bf16(wv[b][1], kc), scale16(sm.ts[(16 * b + lr) * G + 2 * c]));
+            chunk_steps<GS, NB, 4>(acc, ra[abuf], wv, s16, kc);
+        } else if constexpr (GS != 128) {
+            chunk_steps<GS, NB, 2>(acc, ra[abuf], wv, s16, kc);
         }
         __builtin_amdgcn_wave_barrier();
     };
@@ -511,16 +563,18 @@ __global__ __launch_bounds__(64, 3) void moe_gateup_skinny(FfnArgs a) {
 // down, tiles of <= 16 rows.  Grid: skinny tiles x H / (16 NB) column
 // blocks; one wave per workgroup owns output columns 16 NB cb + [0, 16 NB),
 // NB 16-row weight blocks.
-template <bool kF32H, int NB, int RING>
-__global__ __launch_bounds__(64, kF32H ? 2 : 3) void moe_down_skinny(FfnArgs a) {
-    constexpr int P = kF32H ? 2 : 1;
-    __shared__ SkinnySmem<NB> sm;
+template <bool kF32H, int NB, int RING, int GS>
+__global__ __launch_bounds__(64, kF32H || GS == 32 ? 2 : 3) void moe_down_skinny(FfnArgs a) {
+    constexpr int P = kF32H ? 2 : 1, NS = Geo<GS>::kSteps, GPC = Geo<GS>::kChains, MPG = Geo<GS>::kSlices;
+    constexpr int SH = Geo<GS>::kShift;
+    constexpr bool kC64 = Geo<GS>::kChain == 64;
+    __shared__ SkinnySmem<NB, Geo<GS>::kMaxG> sm;
     int cb;
     const int4 tile = load_skinny_tile(a, a.H / (16 * NB), cb);
     if (tile.x < 0) return;
     const int e = tile.x, row_begin = tile.y, rows = tile.z;
     const int lane = threadIdx.x & 63, q = lane >> 4, lr = lane & 15;
-    const int H = a.H, I = a.I, G = I / kGroup;
+    const int H = a.H, I = a.I, G = I / GS;
     const size_t A = static_cast<size_t>(a.T) * a.k;
     const int cbase = cb * 16 * NB;
     const int nb = min(NB, (H - cbase) / 16);  // blocks inside H (H is a multiple of 64)
@@ -532,9 +586,9 @@ __global__ __launch_bounds__(64, kF32H ? 2 : 3) void moe_down_skinny(FfnArgs a) 
         row0[b] = static_cast<size_t>(e) * H + cbase + 16 * min(b, nb - 1);
         blk[b] = a.w_d + row0[b] * (I / 8);
     }
-    Tables<NB> tab;
+    Tables<NB, true, Geo<GS>::kMaxG / 32> tab;
     tab.load(a.s_d, a.b_d, row0, G);
-    WaveW<NB> ww;
+    WaveW<NB, GS> ww;
     ww.init(sm.w, blk, I / 8);
     u32x4 rv[RING][NB];
 #pragma unroll
@@ -552,26 +606,27 @@ __global__ __launch_bounds__(64, kF32H ? 2 : 3) void moe_down_skinny(FfnArgs a) 
     const uint32_t* ha = reinterpret_cast<const uint32_t*>(a.h) + static_cast<size_t>(arow) * (I / 2);
     const size_t part = A * (I / 2);  // offset of the lo half, u32
     u32x4 ra[2][4][P];
-    // this lane's pieces of group g start at hq[pp] + 32 g (g the same in every lane)
+    // slice s of chunk c, as in the gate|up kernel (64-column half 2 c + s / 2)
     const uint32_t* hq[P];
 #pragma unroll
-    for (int pp = 0; pp < P; ++pp) hq[pp] = ha + pp * part + 8 * q;
+    for (int pp = 0; pp < P; ++pp) hq[pp] = ha + pp * part + (kC64 ? 8 : 4) * q;
     auto load_a = [&](int c, int buf) {
 #pragma unroll
-        for (int gi = 0; gi < 2; ++gi) {
-            const uint32_t goff = 32 * min(2 * c + gi, G - 1);
+        for (int hf = 0; hf < 2; ++hf) {
+            const uint32_t goff = 32 * min(2 * c + hf, I / 64 - 1);
 #pragma unroll
             for (int s = 0; s < 2; ++s)
 #pragma unroll
                 for (int pp = 0; pp < P; ++pp)
-                    ra[buf][2 * gi + s][pp] = *reinterpret_cast<const u32x4*>(hq[pp] + goff + 4 * s);
+                    ra[buf][2 * hf + s][pp] =
+                        *reinterpret_cast<const u32x4*>(hq[pp] + goff + (kC64 ? 4 : 16) * s);
         }
     };
     load_a(0, 0);
     // the bias term early, as in the gate|up kernel
     const int steps = (G + 31) / 32;
-    RowSums hsum;
-    hsum.load_blocks(a.hs + static_cast<size_t>(arow) * (I / 16), G, q, steps);
+    RowSums<NS> hsum;
+    hsum.template load_blocks<GS>(a.hs + static_cast<size_t>(arow) * (I / 16), G, q, steps);
 
     uint16_t* const ts = sm.ts;
     uint16_t* const tb = sm.tb;
@@ -579,11 +634,11 @@ __global__ __launch_bounds__(64, kF32H ? 2 : 3) void moe_down_skinny(FfnArgs a) 
     __builtin_amdgcn_wave_barrier();
     f32x4 bterm[NB];
     {
-        BiasOp X;
+        BiasOp<NS> X;
         hsum.pack(X, G, q, steps);
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
-            BiasOp C;
+            BiasOp<NS> C;
             bias_from_table(C, ts + (16 * b + lr) * G, tb + (16 * b + lr) * G, G, q, steps, true);
             bterm[b] = bias_mfma(X, C, steps);
         }
@@ -592,10 +647,10 @@ __global__ __launch_bounds__(64, kF32H ? 2 : 3) void moe_down_skinny(FfnArgs a) 
     f32x4 acc[NB];
 #pragma unroll
     for (int b = 0; b < NB; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const int nfull = G / 2, nch = (G + 1) / 2;
+    const int nfull = I / 128, nch = (I + 127) / 128;
     const CodeConsts kc = code_consts(a.zero);
     // chunk c: its weights go through LDS, the slot reloads with chunk c + RING
-    // at once, then the MFMAs run (an odd G ends with a one-group chunk)
+    // at once, then the MFMAs run (K may end in a half chunk of 64 columns)
     auto compute = [&](int slot, int abuf, int c, bool reload, bool full) {
         chunk_fence();
         ww.put(rv[slot]);
@@ -604,34 +659,37 @@ __global__ __launch_bounds__(64, kF32H ? 2 : 3) void moe_down_skinny(FfnArgs a) 
         u32x4 wv[NB];
 #pragma unroll
         for (int b = 0; b < NB; ++b) wv[b] = ww.get(b, lr, q);
+        float s16[NB][GPC];
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+            for (int j = 0; j < GPC; ++j)
+                s16[b][j] = scale16(ts[(16 * b + lr) * G + min((GPC * c + j) >> SH, G - 1)]);
         if constexpr (!kF32H) {
+            u32x4 x[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) x[j] = ra[abuf][j][0];
             if (full) {
-                float s16[NB][2];
-                u32x4 x[4];
-#pragma unroll
-                for (int j = 0; j < 4; ++j) x[j] = ra[abuf][j][0];
-#pragma unroll
-                for (int b = 0; b < NB; ++b)
-#pragma unroll
-                    for (int gi = 0; gi < 2; ++gi) s16[b][gi] = scale16(ts[(16 * b + lr) * G + 2 * c + gi]);
-                chunk_steps<NB>(acc, x, wv, s16, kc);
-            } else {
-#pragma unroll
-                for (int b = 0; b < NB; ++b)
-                    acc[b] = group_step(acc[b], ra[abuf][0][0], ra[abuf][1][0], codes_as_bf16(wv[b][0], kc),
-                                        codes_as_bf16(wv[b][1], kc), scale16(ts[(16 * b + lr) * G + 2 * c]));
+                chunk_steps<GS, NB, 4>(acc, x, wv, s16, kc);
+            } else if constexpr (GS != 128) {
+                chunk_steps<GS, NB, 2>(acc, x, wv, s16, kc);
             }
         } else {
+            // groups in order, each with its hi and lo activation slices
 #pragma unroll
-            for (int gi = 0; gi < 2; ++gi) {
-                const int g = 2 * c + gi;
-                if (gi == 0 || full) {
-                    const u32x4(&x)[4][P] = ra[abuf];
+            for (int j = 0; j < GPC; ++j) {
+                if (j * MPG < 2 || full) {
 #pragma unroll
                     for (int b = 0; b < NB; ++b) {
-                        const u32x4 b0 = codes_as_bf16(wv[b][2 * gi], kc), b1 = codes_as_bf16(wv[b][2 * gi + 1], kc);
-                        acc[b] = group_step2(acc[b], x[2 * gi][0], x[2 * gi][P - 1], x[2 * gi + 1][0],
-                                             x[2 * gi + 1][P - 1], b0, b1, scale16(ts[(16 * b + lr) * G + g]));
+                        u32x4 bw[MPG];
+                        u32x4 xs2[MPG][P];
+#pragma unroll
+                        for (int m = 0; m < MPG; ++m) {
+                            bw[m] = codes_as_bf16(wv[b][j * MPG + m], kc);
+#pragma unroll
+                            for (int pp = 0; pp < P; ++pp) xs2[m][pp] = ra[abuf][j * MPG + m][pp];
+                        }
+                        acc[b] = group_step<MPG, P>(acc[b], xs2, bw, s16[b][j]);
                     }
                 }
             }
@@ -698,9 +756,9 @@ struct alignas(16) WideSmem {
 // read raw as 16-byte pieces (lane l holds pieces l and l + 64 of each block)
 // while the last chunk is multiplied, and turned into operand order through
 // the wave's LDS buffer once the K loop is done.
-template <int CB>
+template <int CB, int NP>
 struct BiasRows {
-    u32x4 v[CB][2];
+    u32x4 v[CB][NP];  // NP pieces per lane cover G <= 32 NP
 
     // blk[cb]: the block's first bias (the same in every lane)
     __device__ __forceinline__ void load(const uint16_t* const (&blk)[CB], int G) {
@@ -709,27 +767,26 @@ struct BiasRows {
         for (int cb = 0; cb < CB; ++cb) {
             const Rsrc r = make_rsrc(blk[cb], 32u * G);  // pieces past the block read zeros
 #pragma unroll
-            for (int j = 0; j < 2; ++j) v[cb][j] = load16(r, 16u * (lane + 64 * j), 0);
+            for (int j = 0; j < NP; ++j) v[cb][j] = load16(r, 16u * (lane + 64 * j), 0);
         }
     }
     // block cb to buf as 16 rows of G (pieces past the block are not stored)
     __device__ __forceinline__ void store(uint16_t* buf, int cb, int G) const {
         const int lane = threadIdx.x & 63;
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < NP; ++j)
             if (lane + 64 * j < 2 * G) *reinterpret_cast<u32x4*>(buf + 8 * (lane + 64 * j)) = v[cb][j];
     }
 };
 // row stride (floats) of the group sums staged in a[] after the K loop: 16
-// rows of a fragment read fall on distinct banks, and 8-group reads up to
-// group 63 stay inside a row
-constexpr int kXStride = kMaxG + 4;
-static_assert(kXStride <= kAStride, "group sums must fit the activation buffer");
+// rows of a fragment read fall on distinct banks, and 8-group reads up to the
+// last group the tables hold stay inside a row
+template <int GS>
+constexpr int kXStride = Geo<GS>::kMaxG + 4;
 // One row-block count per kernel (a tile's unused row blocks are skipped at
 // run time): a kernel that branches to several instantiations is allocated
 // for all of them at once and overflows into accumulation registers.
 constexpr int kWideRowBlocks = kBmBig / 16, kWideRowBlocksF32 = kBmBigF32 / 16;
-constexpr int kWideMaxGSmall = 48;
 
 // Thread t copies piece t % 16 of rows t / 16 + 16 i.  Rows past the tile
 // read a real row and groups past G the last group: those values are never
@@ -739,11 +796,13 @@ struct Stager {
     static constexpr int kPasses = RB;
     u32x4 v[kPasses][P];
 
+    // chunk c of rows src[i]; nh = K / 64 halves of 64 columns (a half past K
+    // reads the last one again, never used)
     __device__ __forceinline__ void load(const uint32_t* const (&src)[kPasses], size_t part, int c,
-                                         int G) {
+                                         int nh) {
         const int pc = threadIdx.x & 15;
-        const int g = min(2 * c + (pc >> 3), G - 1);
-        const int piece = 8 * g + (pc & 7);
+        const int hf = min(2 * c + (pc >> 3), nh - 1);
+        const int piece = 8 * hf + (pc & 7);
 #pragma unroll
         for (int i = 0; i < kPasses; ++i)
 #pragma unroll
@@ -770,16 +829,16 @@ __device__ __forceinline__ u32x4 lds_frag(const WideSmem<RB, P, NBUF, MAXG>& sm,
 // Shared K loop of the wide paths: acc[rb][cb] over all groups for the four
 // 16-row weight blocks blk[cb] of this wave (row length K), activations staged
 // from src (P parts, `part` apart); row blocks rb >= nrb are skipped.
-template <int RB, int P, int NBUF, int MAXG, class Last>
+template <int GS, int RB, int P, int NBUF, int MAXG, class Last>
 __device__ __forceinline__ void wide_kloop(WideSmem<RB, P, NBUF, MAXG>& sm, Stager<RB, P>& st,
                                            const uint32_t* const (&src)[RB], size_t part,
                                            const uint32_t* const (&blk)[4], int K, bool active,
                                            int nrb, CodeConsts kc, f32x4 (&acc)[RB][4], Last&& last) {
-    constexpr int CB = 4;
+    constexpr int CB = 4, GPC = Geo<GS>::kChains, MPG = Geo<GS>::kSlices, SH = Geo<GS>::kShift;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, q = lane >> 4, lr = lane & 15;
-    const int G = K / kGroup;
-    const int nch = (G + 1) / 2;
-    WaveW<CB> ww;
+    const int G = K / GS, nh = K / 64;
+    const int nch = (K + 127) / 128;
+    WaveW<CB, GS> ww;
     ww.init(sm.w[wave], blk, K / 8);
     // chunk c + 1's weights arrive in registers while chunk c is multiplied and
     // go to the wave's LDS buffer after it (chunk c's reads are done by then)
@@ -798,42 +857,38 @@ __device__ __forceinline__ void wide_kloop(WideSmem<RB, P, NBUF, MAXG>& sm, Stag
         for (int cb = 0; cb < CB; ++cb) wq[cb] = ww.get(cb, lr, q);
         // the next chunk's loads; during the last chunk, the epilogue's
         if constexpr (!kLast) {
-            st.load(src, part, c + 1, G);
+            st.load(src, part, c + 1, nh);
             ww.load(c + 1, wn);
         } else {
             last();
         }
         if (active) {
 #pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                const int g = 2 * c + i;
-                if (g < G) {
-                    u32x4 b0[CB], b1[CB];
+            for (int j = 0; j < GPC; ++j) {
+                const int ch = GPC * c + j;  // chain; its group is ch >> SH
+                if (ch < K / Geo<GS>::kChain) {
+                    const int g = ch >> SH;
+                    u32x4 bw[CB][MPG];
                     float s16[CB];
 #pragma unroll
                     for (int cb = 0; cb < CB; ++cb) {
-                        b0[cb] = codes_as_bf16(wq[cb][2 * i], kc);
-                        b1[cb] = codes_as_bf16(wq[cb][2 * i + 1], kc);
+#pragma unroll
+                        for (int m = 0; m < MPG; ++m) bw[cb][m] = codes_as_bf16(wq[cb][j * MPG + m], kc);
                         s16[cb] = scale16(sm.ts[wave][(16 * cb + lr) * G + g]);
                     }
 #pragma unroll
                     for (int rb = 0; rb < RB; ++rb) {
                         if (rb >= nrb) break;  // row blocks past the tile
                         const int row = 16 * rb + lr;
-                        const u32x4 a0 = lds_frag(sm, buf, 0, row, 8 * i + 2 * q);
-                        const u32x4 a1 = lds_frag(sm, buf, 0, row, 8 * i + 2 * q + 1);
-                        if constexpr (P == 2) {
-                            const u32x4 a0l = lds_frag(sm, buf, 1, row, 8 * i + 2 * q);
-                            const u32x4 a1l = lds_frag(sm, buf, 1, row, 8 * i + 2 * q + 1);
+                        u32x4 xa[MPG][P];
 #pragma unroll
-                            for (int cb = 0; cb < CB; ++cb)
-                                acc[rb][cb] = group_step2(acc[rb][cb], a0, a0l, a1, a1l, b0[cb],
-                                                          b1[cb], s16[cb]);
-                        } else {
+                        for (int m = 0; m < MPG; ++m)
 #pragma unroll
-                            for (int cb = 0; cb < CB; ++cb)
-                                acc[rb][cb] = group_step(acc[rb][cb], a0, a1, b0[cb], b1[cb], s16[cb]);
-                        }
+                            for (int pp = 0; pp < P; ++pp)
+                                xa[m][pp] = lds_frag(sm, buf, pp, row, Geo<GS>::word(j * MPG + m, q));
+#pragma unroll
+                        for (int cb = 0; cb < CB; ++cb)
+                            acc[rb][cb] = group_step<MPG, P>(acc[rb][cb], xa, bw[cb], s16[cb]);
                     }
                 }
             }
@@ -856,33 +911,33 @@ __device__ __forceinline__ void wide_kloop(WideSmem<RB, P, NBUF, MAXG>& sm, Stag
 // The bias term of the wide paths, added once after the K loop.  The group
 // sums of the staged rows go through LDS (the activation buffers are free by
 // then): thread t copies groups t % 16 + 16 j of rows t / 16 + 16 i, from row
-// pointers xrow[i] (G floats each, or with kBlocks 4 G block sums of h).
-// br: the wave's bias rows, prefetched during the last chunk.
-template <int RB, int P, int NBUF, int MAXG, bool kBlocks>
+// pointers xrow[i] (G floats each, or with kBlocks the GS / 16 block sums of
+// h per group).  br: the wave's bias rows, prefetched during the last chunk.
+template <int GS, int RB, int P, int NBUF, int MAXG, bool kBlocks>
 __device__ __forceinline__ void wide_bias(WideSmem<RB, P, NBUF, MAXG>& sm,
-                                          const float* const (&xrow)[RB], const BiasRows<4>& br,
+                                          const float* const (&xrow)[RB],
+                                          const BiasRows<4, Geo<GS>::kMaxG / 32>& br,
                                           int G, bool active, int nrb, f32x4 (&acc)[RB][4]) {
-    constexpr int CB = 4;
+    constexpr int CB = 4, NS = Geo<GS>::kSteps, XS = kXStride<GS>;
+    static_assert(sizeof(float) * RB * 16 * XS <= sizeof(sm.a), "group sums must fit the activation buffer");
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, q = lane >> 4, lr = lane & 15;
     float* xl = reinterpret_cast<float*>(&sm.a[0][0][0]);
     const int pc = threadIdx.x & 15, r0 = threadIdx.x >> 4;
 #pragma unroll
     for (int i = 0; i < RB; ++i)
 #pragma unroll
-        for (int j = 0; j < kMaxG / 16; ++j) {
+        for (int j = 0; j < Geo<GS>::kMaxG / 16; ++j) {
             const int g = pc + 16 * j;
-            if (g < G) xl[(r0 + 16 * i) * kXStride + g] = kBlocks ? group_of_blocks(xrow[i], g) : xrow[i][g];
+            if (g < G) xl[(r0 + 16 * i) * XS + g] = kBlocks ? group_of_blocks<GS>(xrow[i], g) : xrow[i][g];
         }
     __syncthreads();
     const int steps = (G + 31) / 32;
-    // row operands once per row block (8 consecutive groups per step; reads
+    // the row operand of row block rb (8 consecutive groups per step; reads
     // past G stay inside the row stride and are replaced by 0)
-    BiasOp X[RB];
+    auto row_op = [&](int rb, BiasOp<NS>& X) {
+        const float* xr = xl + (16 * rb + lr) * XS;
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-        const float* xr = xl + (16 * rb + lr) * kXStride;
-#pragma unroll
-        for (int st = 0; st < kMaxBiasSteps; ++st) {
+        for (int st = 0; st < NS; ++st) {
             if (st < steps) {
                 const f32x4 v0 = *reinterpret_cast<const f32x4*>(xr + 32 * st + 8 * q);
                 const f32x4 v1 = *reinterpret_cast<const f32x4*>(xr + 32 * st + 8 * q + 4);
@@ -892,9 +947,17 @@ __device__ __forceinline__ void wide_bias(WideSmem<RB, P, NBUF, MAXG>& sm,
                     const float x = j < 4 ? v0[j] : v1[j - 4];
                     v[j] = 32 * st + 8 * q + j < G ? x : 0.f;
                 }
-                pack_split(v, X[rb].hi[st], X[rb].lo[st]);
+                pack_split(v, X.hi[st], X.lo[st]);
             }
         }
+    };
+    // up to two steps: the row operands once per row block; more (group size
+    // 32): rebuilt per weight block, which keeps the registers low
+    constexpr bool kKeepX = NS <= 2;
+    BiasOp<NS> X[kKeepX ? RB : 1];
+    if constexpr (kKeepX) {
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) row_op(rb, X[rb]);
     }
     const uint16_t* ts = sm.ts[wave];
     uint16_t* const wb = reinterpret_cast<uint16_t*>(sm.w[wave]);
@@ -902,13 +965,18 @@ __device__ __forceinline__ void wide_bias(WideSmem<RB, P, NBUF, MAXG>& sm,
     for (int cb = 0; cb < CB; ++cb) {
         br.store(wb, cb, G);
         __builtin_amdgcn_wave_barrier();
-        BiasOp C;
+        BiasOp<NS> C;
         bias_from_table(C, ts + (16 * cb + lr) * G, wb + lr * G, G, q, steps, active);
         __builtin_amdgcn_wave_barrier();
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
             if (rb >= nrb) break;  // row blocks past the tile
-            acc[rb][cb] += bias_mfma(X[rb], C, steps);
+            if constexpr (kKeepX) {
+                acc[rb][cb] += bias_mfma(X[rb], C, steps);
+            } else {
+                row_op(rb, X[0]);
+                acc[rb][cb] += bias_mfma(X[0], C, steps);
+            }
         }
         __builtin_amdgcn_sched_barrier(0);  // one weight block at a time: registers stay low
     }
@@ -918,13 +986,13 @@ __device__ __forceinline__ void wide_bias(WideSmem<RB, P, NBUF, MAXG>& sm,
 // n0 + 32 w + [0, 32): weight blocks 0/1 = gate columns +0/+16, blocks 2/3 =
 // the matching up columns.  Waves {0,1} cover 64-column group 2*by of h,
 // waves {2,3} group 2*by + 1.
-template <int RB, int MAXG, bool kF32H>
+template <int GS, int RB, int MAXG, bool kF32H>
 __device__ __forceinline__ void gateup_wide(const FfnArgs& a, WideSmem<RB, 1, 2, MAXG>& sm, int e,
                                             int row_begin, int rows, int by) {
     constexpr int P = 1, NBUF = 2, CB = 4;
     const int tid = threadIdx.x, lane = tid & 63, q = lane >> 4, lr = lane & 15;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: weight rows are per wave
-    const int H = a.H, I = a.I, G = H / kGroup;
+    const int H = a.H, I = a.I, G = H / GS;
     const size_t A = static_cast<size_t>(a.T) * a.k;
     const int n0 = by * 128;
     const bool active = n0 + 32 * wave < I;
@@ -937,7 +1005,7 @@ __device__ __forceinline__ void gateup_wide(const FfnArgs& a, WideSmem<RB, 1, 2,
         row0[cb] = static_cast<size_t>(e) * 2 * I + hbase + 16 * (cb & 1) + (cb >> 1) * I;
         blk[cb] = a.w_gu + row0[cb] * (H / 8);
     }
-    Tables<CB, false> tab;
+    Tables<CB, false, (MAXG + 31) / 32> tab;
     tab.load(a.s_gu, a.b_gu, row0, G);
 
     int tok[RB];
@@ -949,7 +1017,7 @@ __device__ __forceinline__ void gateup_wide(const FfnArgs& a, WideSmem<RB, 1, 2,
         src[i] = reinterpret_cast<const uint32_t*>(a.xp) + static_cast<size_t>(tok[i]) * (H / 2);
     }
     Stager<RB, P> st;
-    st.load(src, 0, 0, G);
+    st.load(src, 0, 0, H / 64);
     tab.store(sm.ts[wave], nullptr, G);
     st.store(sm, 0);
 
@@ -962,14 +1030,14 @@ __device__ __forceinline__ void gateup_wide(const FfnArgs& a, WideSmem<RB, 1, 2,
     const uint16_t* bblk[CB];
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) bblk[cb] = a.b_gu + row0[cb] * G;
-    BiasRows<CB> br;
-    wide_kloop<RB, P, NBUF, MAXG>(sm, st, src, 0, blk, H, active, (rows + 15) / 16, code_consts(a.zero), acc,
+    BiasRows<CB, Geo<GS>::kMaxG / 32> br;
+    wide_kloop<GS, RB, P, NBUF, MAXG>(sm, st, src, 0, blk, H, active, (rows + 15) / 16, code_consts(a.zero), acc,
                                   [&] { br.load(bblk, G); });
 
     const float* xrow[RB];
 #pragma unroll
     for (int i = 0; i < RB; ++i) xrow[i] = a.xs + static_cast<size_t>(tok[i]) * G;
-    wide_bias<RB, P, NBUF, MAXG, false>(sm, xrow, br, G, active, (rows + 15) / 16, acc);
+    wide_bias<GS, RB, P, NBUF, MAXG, false>(sm, xrow, br, G, active, (rows + 15) / 16, acc);
 
     // GeGLU epilogue and the 16-column block sums of h
 #pragma unroll
@@ -992,14 +1060,14 @@ __device__ __forceinline__ void gateup_wide(const FfnArgs& a, WideSmem<RB, 1, 2,
 
 // down wide, column block `by` of 256 output columns (ceil(H / 256) blocks).  Wave w owns output columns
 // n0 + 64 w + [0, 64): four 16-row weight blocks.
-template <int RB, int MAXG, bool kF32H>
+template <int GS, int RB, int MAXG, bool kF32H>
 __device__ __forceinline__ void down_wide(const FfnArgs& a,
                                           WideSmem<RB, kF32H ? 2 : 1, kF32H ? 1 : 2, MAXG>& sm,
                                           int e, int row_begin, int rows, int by) {
     constexpr int P = kF32H ? 2 : 1, NBUF = kF32H ? 1 : 2, CB = 4;
     const int tid = threadIdx.x, lane = tid & 63, q = lane >> 4, lr = lane & 15;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: weight rows are per wave
-    const int H = a.H, I = a.I, G = I / kGroup;
+    const int H = a.H, I = a.I, G = I / GS;
     const size_t A = static_cast<size_t>(a.T) * a.k;
     const int n0 = by * 256;
     const bool active = n0 + 64 * wave < H;  // H is a multiple of 64
@@ -1012,7 +1080,7 @@ __device__ __forceinline__ void down_wide(const FfnArgs& a,
         row0[cb] = static_cast<size_t>(e) * H + cbase + 16 * cb;
         blk[cb] = a.w_d + row0[cb] * (I / 8);
     }
-    Tables<CB, false> tab;
+    Tables<CB, false, (MAXG + 31) / 32> tab;
     tab.load(a.s_d, a.b_d, row0, G);
 
     int hrow[RB];
@@ -1032,7 +1100,7 @@ __device__ __forceinline__ void down_wide(const FfnArgs& a,
     }
     const size_t part = A * (I / 2);
     Stager<RB, P> st;
-    st.load(src, part, 0, G);
+    st.load(src, part, 0, I / 64);
     tab.store(sm.ts[wave], nullptr, G);
     st.store(sm, 0);
 
@@ -1045,14 +1113,14 @@ __device__ __forceinline__ void down_wide(const FfnArgs& a,
     const uint16_t* bblk[CB];
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) bblk[cb] = a.b_d + row0[cb] * G;
-    BiasRows<CB> br;
-    wide_kloop<RB, P, NBUF, MAXG>(sm, st, src, part, blk, I, active, (rows + 15) / 16, code_consts(a.zero), acc,
+    BiasRows<CB, Geo<GS>::kMaxG / 32> br;
+    wide_kloop<GS, RB, P, NBUF, MAXG>(sm, st, src, part, blk, I, active, (rows + 15) / 16, code_consts(a.zero), acc,
                                   [&] { br.load(bblk, G); });
 
     const float* xrow[RB];
 #pragma unroll
     for (int i = 0; i < RB; ++i) xrow[i] = a.hs + static_cast<size_t>(hrow[i]) * (I / 16);
-    wide_bias<RB, P, NBUF, MAXG, true>(sm, xrow, br, G, active, (rows + 15) / 16, acc);
+    wide_bias<GS, RB, P, NBUF, MAXG, true>(sm, xrow, br, G, active, (rows + 15) / 16, acc);
 
     if (!active) return;
     // weighted unsort (destinations and weights read before the K loop)
@@ -1093,24 +1161,32 @@ __device__ __forceinline__ bool wide_work(const FfnArgs& a, int ncol, int& tile,
     return true;
 }
 
+// Two workgroups share a CU when their LDS fits in half of it.
+template <class Smem, bool kF32H, int GS>
+constexpr int kWideWgsPerCu = sizeof(Smem) <= 80 * 1024 ? 2 : 1;
 template <bool kF32H, int MAXG>
-__global__ __launch_bounds__(kThreads, MAXG <= kWideMaxGSmall ? 2 : 1) void moe_gateup_wide(FfnArgs a) {
+using GateupWideSmem = WideSmem<kF32H ? kWideRowBlocksF32 : kWideRowBlocks, 1, 2, MAXG>;
+template <bool kF32H, int MAXG>
+using DownWideSmem = WideSmem<kF32H ? kWideRowBlocksF32 : kWideRowBlocks, kF32H ? 2 : 1, kF32H ? 1 : 2, MAXG>;
+
+template <bool kF32H, int MAXG, int GS>
+__global__ __launch_bounds__(kThreads, (kWideWgsPerCu<GateupWideSmem<kF32H, MAXG>, kF32H, GS>)) void moe_gateup_wide(FfnArgs a) {
     constexpr int RB = kF32H ? kWideRowBlocksF32 : kWideRowBlocks;
     __shared__ WideSmem<RB, 1, 2, MAXG> sm;
     int ti, by;
     if (!wide_work(a, (a.I + 127) / 128, ti, by)) return;
     const int4 tile = reinterpret_cast<const int4*>(a.tiles)[ti];
-    gateup_wide<RB, MAXG, kF32H>(a, sm, tile.x, tile.y, tile.z, by);
+    gateup_wide<GS, RB, MAXG, kF32H>(a, sm, tile.x, tile.y, tile.z, by);
 }
 
-template <bool kF32H, int MAXG>
-__global__ __launch_bounds__(kThreads, MAXG <= kWideMaxGSmall ? 2 : 1) void moe_down_wide(FfnArgs a) {
+template <bool kF32H, int MAXG, int GS>
+__global__ __launch_bounds__(kThreads, (kWideWgsPerCu<DownWideSmem<kF32H, MAXG>, kF32H, GS>)) void moe_down_wide(FfnArgs a) {
     constexpr int RB = kF32H ? kWideRowBlocksF32 : kWideRowBlocks;
     __shared__ WideSmem<RB, kF32H ? 2 : 1, kF32H ? 1 : 2, MAXG> sm;
     int ti, by;
     if (!wide_work(a, (a.H + 255) / 256, ti, by)) return;
     const int4 tile = reinterpret_cast<const int4*>(a.tiles)[ti];
-    down_wide<RB, MAXG, kF32H>(a, sm, tile.x, tile.y, tile.z, by);
+    down_wide<GS, RB, MAXG, kF32H>(a, sm, tile.x, tile.y, tile.z, by);
 }
 
 }  // namespace
@@ -1138,47 +1214,78 @@ static hipError_t skip_launch(hipStream_t stream, const KTiming& t) {
     return hipSuccess;
 }
 
-hipError_t launch_gateup_skinny(const FfnArgs& a, hipStream_t stream, const KTiming& t) {
+// The kernels take the group size as a template parameter; a.gs picks it.
+template <int GS>
+static hipError_t gateup_skinny_gs(const FfnArgs& a, hipStream_t stream, const KTiming& t) {
     constexpr int RING = kSkinnyGateUpRing;
     const dim3 grid(skinny_grid(a) * (a.I / 16));
     if (a.flags & MOE_F_FP32_INTERMEDIATE)
-        return launch_kernel(moe_gateup_skinny<true, RING>, grid, dim3(64), stream, t, a);
-    return launch_kernel(moe_gateup_skinny<false, RING>, grid, dim3(64), stream, t, a);
+        return launch_kernel(moe_gateup_skinny<true, RING, GS>, grid, dim3(64), stream, t, a);
+    return launch_kernel(moe_gateup_skinny<false, RING, GS>, grid, dim3(64), stream, t, a);
 }
 
-hipError_t launch_gateup_wide(const FfnArgs& a, hipStream_t stream, const KTiming& t) {
+// MAXG: groups per row the scale tables hold.  Rows of at most 3/4 of the
+// largest group count take the smaller tables (two workgroups per CU at group
+// size 64).
+template <int GS>
+static hipError_t gateup_wide_gs(const FfnArgs& a, hipStream_t stream, const KTiming& t) {
     const int n = wide_grid(a);
     if (n == 0) return skip_launch(stream, t);
     const int items = n * ((a.I + 127) / 128);
     const dim3 grid((items + kXcds - 1) / kXcds * kXcds);
-    const bool f32 = a.flags & MOE_F_FP32_INTERMEDIATE, small = a.H / kGroup <= kWideMaxGSmall;
+    constexpr int kBig = Geo<GS>::kMaxG, kSmall = 3 * kBig / 4;
+    const bool f32 = a.flags & MOE_F_FP32_INTERMEDIATE, small = a.H / GS <= kSmall;
     if (f32)
-        return small ? launch_kernel(moe_gateup_wide<true, kWideMaxGSmall>, grid, dim3(kThreads), stream, t, a)
-                     : launch_kernel(moe_gateup_wide<true, kMaxG>, grid, dim3(kThreads), stream, t, a);
-    return small ? launch_kernel(moe_gateup_wide<false, kWideMaxGSmall>, grid, dim3(kThreads), stream, t, a)
-                 : launch_kernel(moe_gateup_wide<false, kMaxG>, grid, dim3(kThreads), stream, t, a);
+        return small ? launch_kernel(moe_gateup_wide<true, kSmall, GS>, grid, dim3(kThreads), stream, t, a)
+                     : launch_kernel(moe_gateup_wide<true, kBig, GS>, grid, dim3(kThreads), stream, t, a);
+    return small ? launch_kernel(moe_gateup_wide<false, kSmall, GS>, grid, dim3(kThreads), stream, t, a)
+                 : launch_kernel(moe_gateup_wide<false, kBig, GS>, grid, dim3(kThreads), stream, t, a);
 }
 
-hipError_t launch_down_skinny(const FfnArgs& a, hipStream_t stream, const KTiming& t) {
+template <int GS>
+static hipError_t down_skinny_gs(const FfnArgs& a, hipStream_t stream, const KTiming& t) {
     constexpr int NB = kSkinnyDownBlocks, RING = kSkinnyDownRing;
-    static_assert(kGroup % (16 * NB) == 0, "H (a multiple of 64) must split into whole column blocks");
+    static_assert(64 % (16 * NB) == 0, "H (a multiple of 64) must split into whole column blocks");
     const dim3 grid(skinny_grid(a) * (a.H / (16 * NB)));
     if (a.flags & MOE_F_FP32_INTERMEDIATE)
-        return launch_kernel(moe_down_skinny<true, NB, RING>, grid, dim3(64), stream, t, a);
-    return launch_kernel(moe_down_skinny<false, NB, RING>, grid, dim3(64), stream, t, a);
+        return launch_kernel(moe_down_skinny<true, NB, RING, GS>, grid, dim3(64), stream, t, a);
+    return launch_kernel(moe_down_skinny<false, NB, RING, GS>, grid, dim3(64), stream, t, a);
 }
 
-hipError_t launch_down_wide(const FfnArgs& a, hipStream_t stream, const KTiming& t) {
+template <int GS>
+static hipError_t down_wide_gs(const FfnArgs& a, hipStream_t stream, const KTiming& t) {
     const int n = wide_grid(a);
     if (n == 0) return skip_launch(stream, t);
     const int items = n * ((a.H + 255) / 256);
     const dim3 grid((items + kXcds - 1) / kXcds * kXcds);
-    const bool f32 = a.flags & MOE_F_FP32_INTERMEDIATE, small = a.I / kGroup <= kWideMaxGSmall;
+    constexpr int kBig = Geo<GS>::kMaxG, kSmall = 3 * kBig / 4;
+    const bool f32 = a.flags & MOE_F_FP32_INTERMEDIATE, small = a.I / GS <= kSmall;
     if (f32)
-        return small ? launch_kernel(moe_down_wide<true, kWideMaxGSmall>, grid, dim3(kThreads), stream, t, a)
-                     : launch_kernel(moe_down_wide<true, kMaxG>, grid, dim3(kThreads), stream, t, a);
-    return small ? launch_kernel(moe_down_wide<false, kWideMaxGSmall>, grid, dim3(kThreads), stream, t, a)
-                 : launch_kernel(moe_down_wide<false, kMaxG>, grid, dim3(kThreads), stream, t, a);
+        return small ? launch_kernel(moe_down_wide<true, kSmall, GS>, grid, dim3(kThreads), stream, t, a)
+                     : launch_kernel(moe_down_wide<true, kBig, GS>, grid, dim3(kThreads), stream, t, a);
+    return small ? launch_kernel(moe_down_wide<false, kSmall, GS>, grid, dim3(kThreads), stream, t, a)
+                 : launch_kernel(moe_down_wide<false, kBig, GS>, grid, dim3(kThreads), stream, t, a);
 }
+
+#define MOE_BY_GROUP_SIZE(fn)                                  \
+    switch (a.gs) {                                            \
+        case 32: return fn<32>(a, stream, t);                  \
+        case 128: return fn<128>(a, stream, t);                \
+        default: return fn<64>(a, stream, t);                  \
+    }
+
+hipError_t launch_gateup_skinny(const FfnArgs& a, hipStream_t stream, const KTiming& t) {
+    MOE_BY_GROUP_SIZE(gateup_skinny_gs)
+}
+hipError_t launch_gateup_wide(const FfnArgs& a, hipStream_t stream, const KTiming& t) {
+    MOE_BY_GROUP_SIZE(gateup_wide_gs)
+}
+hipError_t launch_down_skinny(const FfnArgs& a, hipStream_t stream, const KTiming& t) {
+    MOE_BY_GROUP_SIZE(down_skinny_gs)
+}
+hipError_t launch_down_wide(const FfnArgs& a, hipStream_t stream, const KTiming& t) {
+    MOE_BY_GROUP_SIZE(down_wide_gs)
+}
+#undef MOE_BY_GROUP_SIZE
 
 }  // namespace moe

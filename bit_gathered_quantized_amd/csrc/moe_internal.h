@@ -16,7 +16,6 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kGroup = 64;      // quantisation group (columns per scale/bias)
 constexpr int kRouteThreads = 1024;
 constexpr int kRouteWaves = kRouteThreads / 64;
 
@@ -29,9 +28,9 @@ constexpr int kRouteWaves = kRouteThreads / 64;
 constexpr int kBmBig = 64;
 constexpr int kBmBigF32 = 32;  // with MOE_F_FP32_INTERMEDIATE
 constexpr int kBmSmall = 16;
-// Largest H and I the bias contraction handles (32 groups per MFMA step).
-constexpr int kMaxBiasSteps = 2;
-constexpr int kMaxDim = kMaxBiasSteps * 32 * kGroup;
+// Largest H and I the kernels take (the scale and bias tables in LDS and the
+// bias contraction are sized for it).
+constexpr int kMaxDim = 4096;
 
 // ---------------------------------------------------------- bf16 helpers
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
@@ -176,8 +175,9 @@ struct RouteArgs {
     // activation preparation (forward only; x == nullptr skips it)
     const uint16_t* x;  // [T, H] bf16
     int32_t T, H;
+    int32_t gs;         // quantisation group size: 32, 64 or 128
     uint16_t* xp;       // [T, H] bf16, pieces reordered by permute8
-    float* xs;          // [T, H/64] group sums
+    float* xs;          // [T, H/gs] group sums
 };
 hipError_t launch_route(const RouteArgs& a, hipStream_t stream, const KTiming& t = {});
 constexpr int kRouteSegment = kRouteThreads;  // assignments per counting workgroup
@@ -187,14 +187,15 @@ size_t route_lds_bytes(int E);
 
 struct FfnArgs {
     int32_t T, k, E, H, I, max_tiles;
+    int32_t gs;           // quantisation group size: 32, 64 or 128
     int32_t max_skinny;   // capacity of tiles_skinny
     int32_t skinny_only;  // 1: every tile is skinny, the wide launches are skipped
     uint32_t flags;
     uint32_t zero;       // always 0 (see CodeConsts)
     const uint16_t* x;
     const uint16_t* xp;  // [T, H] x with pieces reordered by permute8
-    const float* xs;     // [T, H/64] group sums of x
-    float* hs;           // [A, I/64] group sums of h (as the down matmul sees it)
+    const float* xs;     // [T, H/gs] group sums of x
+    float* hs;           // [A, I/16] sums of h over 16-column blocks (as the down matmul sees it)
     const int32_t* ids;
     const float* topk_w;
     const uint32_t* w_gu;

@@ -111,11 +111,13 @@ __device__ void wave_exclusive_scan(const int32_t* in, int32_t* out, int n) {
 
 // Activation preparation, run by workgroups 1.. of the same launch: x in MFMA
 // operand order (each 8-column piece reordered by permute8) and the fp32 sum
-// of each (token, 64-column group), which the matmuls use for the bias term.
-// Thread p handles piece p of the [T, H/8] piece grid; the 8 pieces of a group
-// are 8 consecutive lanes.
+// of each (token, quantisation group), which the matmuls use for the bias
+// term.  Thread p handles piece p of the [T, H/8] piece grid; the gs/8 pieces
+// of a group are that many consecutive lanes (gs divides H, so a group never
+// straddles two rows).
 __device__ void prepare_x(const RouteArgs& a, int block) {
     const int pieces_per_row = a.H / 8;
+    const int lanes = a.gs / 8;  // 4, 8 or 16
     const int64_t p = static_cast<int64_t>(block) * kRouteThreads + threadIdx.x;
     const int64_t total = static_cast<int64_t>(a.T) * pieces_per_row;
     const bool ok = p < total;
@@ -124,10 +126,11 @@ __device__ void prepare_x(const RouteArgs& a, int block) {
     float s = sum8_bf16(v);
     s += __shfl_xor(s, 1);
     s += __shfl_xor(s, 2);
-    s += __shfl_xor(s, 4);
+    if (lanes >= 8) s += __shfl_xor(s, 4);
+    if (lanes >= 16) s += __shfl_xor(s, 8);
     if (!ok) return;
     reinterpret_cast<u32x4*>(a.xp)[p] = permute8(v);
-    if ((p & 7) == 0) a.xs[p / 8] = s;
+    if ((p & (lanes - 1)) == 0) a.xs[p / lanes] = s;
 }
 
 // Key of flat assignment a (its expert id, or E for an out-of-range id).

@@ -17,16 +17,17 @@
  *
  * with gelu_tanh(v) = 0.5 v (1 + tanh(sqrt(2/pi) (v + 0.044715 v^3))).
  *
- * Weights are affine 4-bit, group size 64, in the layout of the Layr-Labs/mlx
- * PR #4 page ("What": packed gate/up [128, 1408, 352] and down [128, 2816, 88]
- * uint32 for 128 experts, hidden 2816, intermediate 704):
+ * Weights are affine 4-bit in groups of gs = group_size columns (64 on the
+ * pages; 32 and 128 are the other common choices), in the layout of the
+ * Layr-Labs/mlx PR #4 page ("What": packed gate/up [128, 1408, 352] and down
+ * [128, 2816, 88] uint32 for 128 experts, hidden 2816, intermediate 704):
  *
  *   w_gateup uint32 [E, 2I, H/8]  rows [0, I) gate, [I, 2I) up; K contiguous
- *   s_gateup bf16   [E, 2I, H/64] b_gateup bf16 [E, 2I, H/64]
- *   w_down   uint32 [E, H, I/8]   s_down bf16 [E, H, I/64]  b_down bf16 [E, H, I/64]
+ *   s_gateup bf16   [E, 2I, H/gs] b_gateup bf16 [E, 2I, H/gs]
+ *   w_down   uint32 [E, H, I/8]   s_down bf16 [E, H, I/gs]  b_down bf16 [E, H, I/gs]
  *
  * Element c of a row is the 4-bit code q at bits 4*(c%8) of word c/8 (low
- * nibble first) and dequantises to  W = S[c/64] * q + B[c/64]  in fp32.
+ * nibble first) and dequantises to  W = S[c/gs] * q + B[c/gs]  in fp32.
  *
  * Conventions for every entry point:
  *  - All array pointers are DEVICE pointers owned by the caller; the library
@@ -52,7 +53,7 @@ enum {
     MOE_OK = 0,
     MOE_ERR_NULL = -1,        /* a required pointer is NULL                    */
     MOE_ERR_SHAPE = -2,       /* a size is negative, inconsistent or overflows */
-    MOE_ERR_UNSUPPORTED = -3, /* bits != 4, group_size != 64, E too large, ... */
+    MOE_ERR_UNSUPPORTED = -3, /* bits != 4, group_size not 32/64/128, E too large, ... */
     MOE_ERR_ALIGN = -4,       /* a pointer is not aligned as required          */
     MOE_ERR_WORKSPACE = -5,   /* workspace missing or too small                */
     MOE_ERR_HIP = -6          /* the HIP runtime rejected a launch             */
@@ -74,9 +75,9 @@ typedef struct {
     int32_t T;          /* tokens, >= 0                                  */
     int32_t k;          /* experts per token, 1 <= k <= E                */
     int32_t E;          /* experts, 1 <= E <= MOE_MAX_EXPERTS            */
-    int32_t H;          /* hidden size, multiple of 64, <= 4096          */
-    int32_t I;          /* intermediate size, multiple of 64, <= 4096    */
-    int32_t group_size; /* must be 64                                    */
+    int32_t H;          /* hidden size, multiple of 64 and of group_size, <= 4096 */
+    int32_t I;          /* intermediate size, same rules as H            */
+    int32_t group_size; /* 32, 64 or 128 columns per scale and bias      */
     int32_t bits;       /* must be 4                                     */
     uint32_t flags;     /* MOE_F_* below                                 */
 } moe_problem;
@@ -169,13 +170,14 @@ typedef struct {
                          permutation; the route launch then sorted by
                          itself); [5..7] unused                           */
     size_t x_perm;    /* bf16 [T, H]: x in operand order                  */
-    size_t x_sums;    /* fp32 [T, H/64]: sum of x over each 64-column group */
+    size_t x_sums;    /* fp32 [T, H/gs]: sum of x over each group      */
     size_t h;         /* GeGLU output in sorted order, operand order:
                          bf16 [A, I]; with MOE_F_FP32_INTERMEDIATE two bf16
                          arrays [2, A, I], h = hi + lo                    */
     size_t h_sums;    /* fp32 [A, I/16]: sum of h (hi + lo) over each
                          16-column block (in column order); the sum of a
-                         64-column group is ((b0 + b1) + b2) + b3        */
+                         group adds its blocks left to right, e.g.
+                         ((b0 + b1) + b2) + b3 at gs = 64                */
     size_t y;         /* fp32 [A, H] flat order a = t*k + j, already
                          multiplied by topk_weights; rows of assignments
                          with an out-of-range id are not written          */

@@ -63,8 +63,10 @@ def test_workspace_layout_and_sizes():
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(bits=8), -3), (dict(group_size=32), -3), (dict(E=2000), -3), (dict(flags=8), -3),
-    (dict(flags=16), -3),
+    (dict(bits=8), -3), (dict(group_size=16), -3), (dict(group_size=256), -3),
+    (dict(group_size=48), -3), (dict(E=2000), -3), (dict(flags=8), -3), (dict(flags=16), -3),
+    (dict(group_size=128, H=192), -2), (dict(group_size=128, I=320), -2),
+    (dict(group_size=32, H=96), -2),
     (dict(H=100), -2), (dict(I=96), -2), (dict(H=8192), -3), (dict(I=4160), -3), (dict(k=0), -2), (dict(k=9, E=8), -2), (dict(T=-1), -2),
 ])
 def test_bad_problem(kw, status):

@@ -234,16 +234,21 @@ def test_symmetric_down_codes_cancel():
     assert np.abs(out).max() <= 5e-4 * rms
 
 
+@pytest.mark.parametrize("gs", [64, 32, 128])
 @pytest.mark.parametrize("fp32", [False, True])
-def test_prepared_activations_and_h_sums(fp32):
+def test_prepared_activations_and_h_sums(fp32, gs):
     """The route launch's x in operand order and group sums, and the gate|up
     kernels' 16-column block sums of h, against their definitions."""
-    p = ms.make_config("prefill4k")
+    if gs == 64:
+        p = ms.make_config("prefill4k")
+    else:
+        p = ms.make_problem(32, 1024, 256, 300, 4, seed=gs, gs=gs, name=f"sums-gs{gs}")
+    log(f"prepared sums: {p.name} gs={gs} fp32={fp32}")
     out, ws, lay = run_forward(p, fp32=fp32)
     xp = ws_view(ws, lay.x_perm, p.T * p.H, np.uint16).reshape(p.T, p.H)
     np.testing.assert_array_equal(from_operand_order(xp), p.x)
-    xs = ws_view(ws, lay.x_sums, p.T * p.H // 64, np.float32).reshape(p.T, -1)
-    ref = ms.bf16_bits_to_f32(p.x).astype(np.float64).reshape(p.T, -1, 64).sum(-1)
+    xs = ws_view(ws, lay.x_sums, p.T * p.H // gs, np.float32).reshape(p.T, -1)
+    ref = ms.bf16_bits_to_f32(p.x).astype(np.float64).reshape(p.T, -1, gs).sum(-1)
     assert np.abs(xs - ref).max() <= 1e-5 * np.abs(ref).max()
     A = p.T * p.k
     h = ws_h(ws, lay, p, fp32)
@@ -252,7 +257,7 @@ def test_prepared_activations_and_h_sums(fp32):
     assert np.abs(hs - href).max() <= 1e-5 * np.abs(href).max()
 
 
-def _expert0_rows(n_extra):
+def _expert0_rows(n_extra, gs=64):
     """20 tokens, 10 of them routed to expert 0 (slot 0); n_extra more tokens
     also go to expert 0, which moves its rows from the skinny path (10 rows)
     to the wide path (10 + n_extra rows)."""
@@ -263,16 +268,17 @@ def _expert0_rows(n_extra):
     ids[10:20, 0] = ids[10:20, 1] % (E - 1) + 1
     ids[10:20, 1] = np.where(ids[10:20, 0] == ids[10:20, 1], 0, ids[10:20, 1])
     ids[10:20, 1] = np.where(ids[10:20, 1] == 0, 3, ids[10:20, 1])
-    p = ms.make_problem(E, 256, 128, T, k, seed=12, topk_ids=ids, name=f"e0+{n_extra}")
+    p = ms.make_problem(E, 256, 128, T, k, seed=12, topk_ids=ids, gs=gs, name=f"e0+{n_extra}")
     return p
 
 
+@pytest.mark.parametrize("gs", [64, 32, 128])
 @pytest.mark.parametrize("fp32", [False, True])
-def test_rows_bitwise_independent_of_tile_path(oracle_lib, fp32):
+def test_rows_bitwise_independent_of_tile_path(oracle_lib, fp32, gs):
     """The same token's output is bit-identical whether its expert's rows run
     as one skinny tile (10 rows) or in wide tiles (10 + 30 rows)."""
-    a = _expert0_rows(0)
-    b = _expert0_rows(30)
+    a = _expert0_rows(0, gs)
+    b = _expert0_rows(30, gs)
     b.x[:20] = a.x
     b.topk_weights[:20] = a.topk_weights
     for f in ("w_gateup", "s_gateup", "b_gateup", "w_down", "s_down", "b_down"):
@@ -330,3 +336,66 @@ def test_swiglu_full(oracle_lib, name, fp32):
 def test_swiglu_prefill_sampled(oracle_lib, name):
     p = ms.make_config(name)
     compare(oracle_lib, p, False, tokens=sample_tokens(p), swiglu=True)
+
+
+# ------------------------------------------------------------- group sizes
+# Groups of 32 and 128 columns (one scale and bias per group): the same
+# kernels with the group loop, the scale tables and the bias contraction
+# sized for the group.  At 128 I = 704 is not a whole number of groups, so
+# the production-like cases take I = 768 there.
+@pytest.mark.parametrize("gs", [32, 128])
+@pytest.mark.parametrize("fp32", [False, True])
+def test_group_size_tiny_full(oracle_lib, gs, fp32):
+    compare(oracle_lib, ms.make_problem(8, 256, 128, 64, 2, seed=gs, gs=gs, name=f"tiny-gs{gs}"), fp32)
+
+
+@pytest.mark.parametrize("gs,I", [(32, 704), (128, 768)])
+@pytest.mark.parametrize("fp32", [False, True])
+def test_group_size_decode_full(oracle_lib, gs, I, fp32):
+    compare(oracle_lib, ms.make_problem(128, 2816, I, 8, 8, seed=gs, gs=gs, name=f"decode-gs{gs}"), fp32)
+
+
+@pytest.mark.parametrize("gs,I", [(32, 704), (128, 768)])
+@pytest.mark.parametrize("fp32", [False, True])
+def test_group_size_prefill_sampled(oracle_lib, gs, I, fp32):
+    p = ms.make_problem(128, 2816, I, 512, 8, seed=gs, gs=gs, name=f"prefill4k-gs{gs}")
+    compare(oracle_lib, p, fp32, tokens=sample_tokens(p, n=16))
+
+
+@pytest.mark.parametrize("gs,shape", [
+    (32, (4, 192, 64, 5, 2)),      # 6 and 2 groups: a half chunk on both matmuls
+    (32, (3, 320, 192, 40, 3)),    # 10 and 6 groups, wide and skinny tiles
+    (32, (8, 256, 128, 200, 2)),   # full and tail wide tiles
+    (32, (2, 4096, 256, 40, 1)),   # 128 groups per gate|up row: the largest tables
+    (32, (2, 256, 4096, 40, 1)),   # 128 groups per down row
+    (128, (3, 384, 128, 40, 3)),   # 3 and 1 groups
+    (128, (8, 256, 128, 200, 2)),  # full and tail wide tiles
+    (128, (2, 4096, 256, 40, 1)),  # 32 groups per gate|up row: the largest tables
+    (128, (2, 256, 4096, 40, 1)),  # 32 groups per down row
+])
+@pytest.mark.parametrize("fp32", [False, True])
+def test_group_size_shapes_full(oracle_lib, gs, shape, fp32):
+    E, H, I, T, k = shape
+    compare(oracle_lib, ms.make_problem(E, H, I, T, k, seed=H + T + gs, gs=gs, name=f"shape-gs{gs}"), fp32)
+
+
+@pytest.mark.parametrize("gs", [32, 128])
+def test_group_size_swiglu(oracle_lib, gs):
+    compare(oracle_lib, ms.make_problem(8, 256, 128, 64, 2, seed=gs + 1, gs=gs, name=f"tiny-gs{gs}"),
+            False, swiglu=True)
+
+
+def test_group_size_32_large_batch_repeatable(oracle_lib):
+    """16384 assignments at group size 32, where the bf16 wide kernels run one
+    workgroup per CU (their scale tables fill the LDS) and hold part of their
+    state in accumulation registers: sampled parity, and repeated runs
+    bit-identical."""
+    c = ms.CONFIGS["prefill16k"]
+    p = ms.make_problem(c["E"], c["H"], c["I"], c["T"], c["k"], seed=0, router=c["router"], gs=32,
+                        name="prefill16k-gs32")
+    first = compare(oracle_lib, p, False, tokens=sample_tokens(p, n=12))
+    d = dev_arrays(p)
+    for _ in range(2):
+        again, _, _ = run_forward(p, d=d)
+        np.testing.assert_array_equal(again, first)
+

@@ -291,6 +291,17 @@ def test_fuzz_shapes_match_brute_force(oracle_lib, shape):
     assert rel_err(r["out"], brute_force_out(p)) < 1e-12
 
 
+@pytest.mark.parametrize("gs,shape", [(32, (3, 96, 64, 6, 2)), (32, (2, 64, 160, 4, 2)),
+                                      (128, (3, 256, 128, 5, 2)), (128, (2, 128, 384, 3, 1))])
+def test_group_sizes_match_brute_force(oracle_lib, gs, shape):
+    """Groups of 32 and 128 columns: one scale and bias per gs columns."""
+    E, H, I, T, k = shape
+    p = ms.make_problem(E, H, I, T, k, seed=gs + T, gs=gs)
+    assert p.s_gateup.shape[-1] == H // gs and p.s_down.shape[-1] == I // gs
+    r = oracle_lib.ffn_tokens(p)
+    assert rel_err(r["out"], brute_force_out(p)) < 1e-12
+
+
 def test_invalid_ids_contribute_zero(oracle_lib):
     p = ms.make_problem(E=4, H=64, I=64, T=4, k=2, seed=8)
     ref = brute_force_out(p)

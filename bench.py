@@ -47,13 +47,14 @@ def algorithmic_work(p):
     E, H, I, T, k = p.E, p.H, p.I, p.T, p.k
     A = T * k
     G_h, G_i = H // p.gs, I // p.gs
-    gu_expert = 2 * I * H // 2 + 2 * (2 * I * G_h * 2)      # codes + scales + biases
-    d_expert = H * I // 2 + 2 * (H * G_i * 2)
+    cb = p.bits / 8                                           # code bytes per weight
+    gu_expert = int(2 * I * H * cb) + 2 * (2 * I * G_h * 2)   # codes + scales + biases
+    d_expert = int(H * I * cb) + 2 * (H * G_i * 2)
     ids = p.topk_ids.ravel()
     counts = np.bincount(ids, minlength=E)
     # experts of <= 16 rows run as one skinny tile, larger ones in wide
     # tiles; batches of <= 16 tokens run every expert on the skinny path
-    skinny_max = A if T <= BM_SMALL else BM_SMALL
+    skinny_max = A if T <= BM_SMALL or p.bits == 8 else BM_SMALL
     skinny_rows = np.where(counts <= skinny_max, counts, 0)
     wide_rows = counts - skinny_rows
     in_skinny = np.isin(ids, np.nonzero((counts > 0) & (counts <= skinny_max))[0])
@@ -287,6 +288,8 @@ def main():
                          "(the reference kernel for scaling HBM byte counters)")
     ap.add_argument("--group-size", type=int, default=64, choices=[32, 64, 128],
                     help="quantisation group size of the synthetic weights")
+    ap.add_argument("--bits", type=int, default=4, choices=[4, 8],
+                    help="code width of the synthetic weights (8: skinny kernels only)")
     ap.add_argument("--intermediate", type=int, default=0, metavar="I",
                     help="override the workload's intermediate size (e.g. 768 at group "
                          "size 128, which does not divide 704)")
@@ -322,10 +325,10 @@ def main():
 
     c = ms.CONFIGS[args.workload]
     I = args.intermediate or c["I"]
-    custom = args.group_size != ms.GROUP_SIZE or I != c["I"]
+    custom = args.group_size != ms.GROUP_SIZE or I != c["I"] or args.bits != 4
     if custom:
         p = ms.make_problem(c["E"], c["H"], I, c["T"], c["k"], seed=0, router=c["router"],
-                            gs=args.group_size, name=args.workload)
+                            gs=args.group_size, bits=args.bits, name=args.workload)
     else:
         p = ms.make_config(args.workload, seed=0)
     A = p.T * p.k
@@ -345,7 +348,7 @@ def main():
                 t(p.b_down, np.int16)]
 
     sets = [upload() for _ in range(max(1, args.copies))]
-    prob = bgq.problem(p.T, p.k, p.E, p.H, p.I, 0, group_size=p.gs)
+    prob = bgq.problem(p.T, p.k, p.E, p.H, p.I, 0, group_size=p.gs, bits=p.bits)
     ws = torch.empty(bgq.workspace_bytes(prob), dtype=torch.uint8, device=dev)
     out = torch.empty((p.T, p.H), dtype=torch.bfloat16, device=dev)
     stream = torch.cuda.current_stream()
@@ -390,7 +393,7 @@ def main():
     work, fwd_work, split = algorithmic_work(p)
     # at most 16 tokens the library launches no wide kernel: their event pair
     # brackets nothing
-    not_launched = {"moe_gateup_wide", "moe_down_wide"} if p.T <= BM_SMALL else set()
+    not_launched = {"moe_gateup_wide", "moe_down_wide"} if p.T <= BM_SMALL or p.bits == 8 else set()
     dominant = max((s for s in kernels if s not in not_launched), key=lambda s: mean_us[s])
     roof = roofline_entry(work[dominant], mean_us[dominant] * 1e-6)
     roof["kernel"] = dominant
@@ -436,7 +439,7 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": args.workload, "E": p.E, "H": p.H, "I": p.I, "T": p.T,
-                   "k": p.k, "assignments": A, "group_size": p.gs, "bits": 4,
+                   "k": p.k, "assignments": A, "group_size": p.gs, "bits": p.bits,
                    "router": ms.CONFIGS[args.workload]["router"], "seed": 0,
                    "touched_experts": touched, "input_copies": len(sets), **split},
         "roofline": roof,

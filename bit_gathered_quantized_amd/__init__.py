@@ -201,9 +201,10 @@ def expert_ffn_forward(x, topk_ids, topk_weights, w_gateup, s_gateup, b_gateup,
                        fp32_intermediate: bool = False, swiglu: bool = False, out=None,
                        workspace=None, stream=None, events=None, sorted_order=None):
     """Expert FFN forward.  Shapes: x [T, H] (2-byte), topk_ids int32 [T, k],
-    topk_weights fp32 [T, k], w_gateup 4-byte [E, 2I, H/8], s/b_gateup 2-byte
-    [E, 2I, H/gs], w_down 4-byte [E, H, I/8], s/b_down 2-byte [E, H, I/gs]; the
-    group size gs (32, 64 or 128) is read off the scale shapes.
+    topk_weights fp32 [T, k], w_gateup 4-byte [E, 2I, H*bits/32], s/b_gateup
+    2-byte [E, 2I, H/gs], w_down 4-byte [E, H, I*bits/32], s/b_down 2-byte
+    [E, H, I/gs]; the code width (4 or 8 bits) is read off the weight shapes
+    and the group size gs (32, 64 or 128) off the scale shapes.
     Returns out [T, H] (bf16, or fp32 with fp32_out); swiglu selects
     h = silu(g) * u instead of gelu_tanh(g) * u.  With sorted_order (int32
     [T*k], slot -> flat assignment, sorted by expert) the pre-sorted entry is
@@ -216,11 +217,17 @@ def expert_ffn_forward(x, topk_ids, topk_weights, w_gateup, s_gateup, b_gateup,
     I = I2 // 2
     flags = ((MOE_F_FP32_OUT if fp32_out else 0) | (MOE_F_FP32_INTERMEDIATE if fp32_intermediate else 0)
              | (MOE_F_SWIGLU if swiglu else 0))
+    if w_gateup.shape[-1] * 8 == H:
+        bits = 4
+    elif w_gateup.shape[-1] * 4 == H:
+        bits = 8
+    else:
+        raise ValueError(f"w_gateup has {w_gateup.shape[-1]} words per row: neither 4-bit nor 8-bit codes of H={H}")
     ng = s_gateup.shape[-1]
     if ng < 1 or H % ng:
         raise ValueError(f"s_gateup has {ng} groups per row, which does not divide H={H}")
     gs = H // ng
-    p = problem(T, k, E, H, I, flags, group_size=gs)
+    p = problem(T, k, E, H, I, flags, group_size=gs, bits=bits)
     if topk_ids.dtype != torch.int32 or topk_weights.dtype != torch.float32:
         raise ValueError("topk_ids must be int32 and topk_weights float32")
     G = ng
@@ -228,10 +235,10 @@ def expert_ffn_forward(x, topk_ids, topk_weights, w_gateup, s_gateup, b_gateup,
         _dev_ptr(x, "x", 2, (T, H)),
         _dev_ptr(topk_ids, "topk_ids", 4, (T, k)),
         _dev_ptr(topk_weights, "topk_weights", 4, (T, k)),
-        _dev_ptr(w_gateup, "w_gateup", 4, (E, 2 * I, H // 8)),
+        _dev_ptr(w_gateup, "w_gateup", 4, (E, 2 * I, H * bits // 32)),
         _dev_ptr(s_gateup, "s_gateup", 2, (E, 2 * I, G)),
         _dev_ptr(b_gateup, "b_gateup", 2, (E, 2 * I, G)),
-        _dev_ptr(w_down, "w_down", 4, (E, H, I // 8)),
+        _dev_ptr(w_down, "w_down", 4, (E, H, I * bits // 32)),
         _dev_ptr(s_down, "s_down", 2, (E, H, I // gs)),
         _dev_ptr(b_down, "b_down", 2, (E, H, I // gs)),
     ]

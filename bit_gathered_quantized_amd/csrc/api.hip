@@ -17,7 +17,7 @@ bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 // Shape checks shared by the forward's size queries and the forward itself.
 moe_status check_problem(const moe_problem* p) {
     if (!p) return MOE_ERR_NULL;
-    if (p->bits != 4) return MOE_ERR_UNSUPPORTED;
+    if (p->bits != 4 && p->bits != 8) return MOE_ERR_UNSUPPORTED;
     if (p->group_size != 32 && p->group_size != 64 && p->group_size != 128)
         return MOE_ERR_UNSUPPORTED;
     if (p->flags & ~(MOE_F_FP32_OUT | MOE_F_FP32_INTERMEDIATE | MOE_F_SWIGLU))
@@ -112,8 +112,9 @@ moe_status forward_impl(const moe_problem* p, const void* x, const int32_t* ids,
     r.max_skinny = l.max_skinny;
     // At most bm_small tokens: no expert has more rows unless a token repeats
     // an id, so every expert takes the skinny path (in tiles of bm_small) and
-    // the wide launches are left out.
-    const bool skinny_only = p->T <= l.bm_small;
+    // the wide launches are left out.  8-bit codes have skinny kernels only:
+    // every batch is routed that way.
+    const bool skinny_only = p->T <= l.bm_small || p->bits == 8;
     r.skinny_max_rows = skinny_only ? INT32_MAX : l.bm_small;
     r.counts = reinterpret_cast<int32_t*>(base + l.counts);
     r.offsets = reinterpret_cast<int32_t*>(base + l.offsets);
@@ -139,6 +140,7 @@ moe_status forward_impl(const moe_problem* p, const void* x, const int32_t* ids,
     f.H = p->H;
     f.I = p->I;
     f.gs = p->group_size;
+    f.bits = p->bits;
     f.max_tiles = l.max_tiles;
     f.max_skinny = l.max_skinny;
     f.skinny_only = skinny_only ? 1 : 0;

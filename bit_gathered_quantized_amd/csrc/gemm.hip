@@ -141,10 +141,11 @@ __device__ __forceinline__ void pack_split(const float (&v)[8], u32x4& hi, u32x4
     }
 }
 
-// Column operand: c[g] = b[g] - 16 s[g] of one weight row, from its rows of
-// the scale and bias tables.  Groups past G repeat the last group: the row
-// operand is zero there, so those (finite) products add nothing.
-template <int NS>
+// Column operand: c[g] = b[g] - OFF s[g] of one weight row (OFF the code
+// offset), from its rows of the scale and bias tables.  Groups past G repeat
+// the last group: the row operand is zero there, so those (finite) products
+// add nothing.
+template <int NS, int OFF = 16>
 __device__ __forceinline__ void bias_from_table(BiasOp<NS>& o, const uint16_t* ts, const uint16_t* tb,
                                                 int G, int q, int steps, bool active) {
 #pragma unroll
@@ -154,7 +155,7 @@ __device__ __forceinline__ void bias_from_table(BiasOp<NS>& o, const uint16_t* t
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 const int gc = min(32 * st + 8 * q + j, G - 1);
-                const float c = fmaf(-kCodeOffset, bf16_to_f32(ts[gc]), bf16_to_f32(tb[gc]));
+                const float c = fmaf(-static_cast<float>(OFF), bf16_to_f32(ts[gc]), bf16_to_f32(tb[gc]));
                 v[j] = active ? c : 0.f;
             }
             pack_split(v, o.hi[st], o.lo[st]);
@@ -250,13 +251,28 @@ __device__ __forceinline__ f32x4 group_step(f32x4 acc, const u32x4 (&x)[NSL][P],
     return acc;
 }
 
+// A lane's weight words for the four slices of a chunk: one per slice for
+// 4-bit codes, two (words 2 s and 2 s + 1) for 8-bit codes.
+template <int BITS>
+using WLane = std::conditional_t<BITS == 4, u32x4, u32x8>;
+
+// Slice s's weight operand from the lane's words.
+template <int BITS>
+__device__ __forceinline__ u32x4 slice_operand(const WLane<BITS>& w, int s, CodeConsts kc) {
+    if constexpr (BITS == 4) {
+        return codes_as_bf16(w[s], kc);
+    } else {
+        return bytes_as_bf16(w[2 * s], w[2 * s + 1]);
+    }
+}
+
 // The groups of one chunk (NSL = 4 slices, or 2 for a half chunk) for NB
 // weight blocks: the MFMA chains of all (block, group) pairs are issued
 // together, slice by slice, then each block takes its scaled products in group
 // order -- group_step's arithmetic, pair by pair.  x[s]: slice s's activation
-// operand; wv[b][s]: block b's weight word for slice s.
-template <int GS, int NB, int NSL>
-__device__ __forceinline__ void chunk_steps(f32x4 (&acc)[NB], const u32x4 (&x)[4], const u32x4 (&wv)[NB],
+// operand; wv[b]: block b's weight words.
+template <int GS, int NB, int NSL, int BITS = 4>
+__device__ __forceinline__ void chunk_steps(f32x4 (&acc)[NB], const u32x4 (&x)[4], const WLane<BITS> (&wv)[NB],
                                             const float (&s16)[NB][Geo<GS>::kChains], CodeConsts kc) {
     constexpr int MPG = Geo<GS>::kSlices, NG = NSL / MPG;
     static_assert(NSL % MPG == 0, "a chunk holds whole groups");
@@ -267,7 +283,7 @@ __device__ __forceinline__ void chunk_steps(f32x4 (&acc)[NB], const u32x4 (&x)[4
         for (int j = 0; j < NG; ++j)
 #pragma unroll
             for (int b = 0; b < NB; ++b)
-                p[b][j] = mfma16(x[j * MPG + m], codes_as_bf16(wv[b][j * MPG + m], kc),
+                p[b][j] = mfma16(x[j * MPG + m], slice_operand<BITS>(wv[b], j * MPG + m, kc),
                                  m == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : p[b][j]);
 #pragma unroll
     for (int b = 0; b < NB; ++b)
@@ -316,13 +332,17 @@ __device__ __forceinline__ float store_h(const FfnArgs& a, size_t A, int srow, i
 // (4 lanes per row: a quad reads one line) and the chunk is turned into
 // operand order through a small LDS buffer private to the wave (no barrier).
 //
-// A wave owns NCB blocks of 16 weight rows; a chunk is 2 groups = 64 bytes per
-// row.  LDS entry (row, q, g) = words 2q, 2q+1 of group g of the chunk, at
-// row * 16 + 4 * (q ^ ((row >> 2) & 3)) + 2 g  (u32 units); the XOR keeps the
-// 16 rows of a fragment read on distinct banks.
-template <int NCB, int GS = 64>
+// A wave owns NCB blocks of 16 weight rows.  With 4-bit codes a chunk is 64
+// bytes per row: 16 words w = 8 g + 2 q + p (g the 64-column half, p = 0, 1),
+// word w at u32 offset 4 * (q ^ ((row >> 2) & 3)) + 2 g + p of a 16-u32 LDS
+// row; the XOR keeps the 16 rows of a fragment read on distinct banks.  With
+// 8-bit codes a chunk is 128 bytes per row, and the pair of words holding the
+// columns of 4-bit word w sits where w would, in 8-byte units of a 32-u32 row.
+template <int NCB, int GS = 64, int BITS = 4>
 struct WaveW {
-    uint32_t* lds;   // NCB * 16 rows x 16 u32
+    static constexpr int kParts = BITS / 4;       // 16-byte loads per lane and block
+    static constexpr int kRowU32 = 16 * kParts;   // u32 per LDS row
+    uint32_t* lds;   // NCB * 16 rows x kRowU32 u32
     Rsrc blk[NCB];   // block cb: its 16 weight rows
     uint32_t voff;   // this lane's load row and piece, bytes
 
@@ -335,38 +355,67 @@ struct WaveW {
         for (int cb = 0; cb < NCB; ++cb) blk[cb] = make_rsrc(blk_ptr[cb], 64u * row_words);
         voff = 4u * ((lane >> 2) * row_words + 4 * (lane & 3));
     }
-    // Chunk c.  Pieces past a row's end (the second group of the last chunk of
-    // an odd group count, chunks past the last) read the next row or, past the
+    // Chunk c (part h at 64 h bytes).  Pieces past a row's end (the second half
+    // of a half chunk, chunks past the last) read the next row or, past the
     // block, zeros; they are never used.
-    __device__ __forceinline__ void load(int c, u32x4 (&v)[NCB]) const {
+    __device__ __forceinline__ void load(int c, u32x4 (&v)[NCB][kParts]) const {
 #pragma unroll
-        for (int cb = 0; cb < NCB; ++cb) v[cb] = load16(blk[cb], voff, 64u * c);
+        for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+            for (int h = 0; h < kParts; ++h) v[cb][h] = load16(blk[cb], voff, 64u * (kParts * c + h));
     }
-    __device__ __forceinline__ void put(const u32x4 (&v)[NCB]) const {
+    __device__ __forceinline__ void put(const u32x4 (&v)[NCB][kParts]) const {
         const int lane = threadIdx.x & 63;
-        const int j = lane & 3, g = j >> 1, qa = 2 * (j & 1), sw = (lane >> 4) & 3;
+        const int j = lane & 3, sw = (lane >> 4) & 3;
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb) {
-            uint32_t* row = lds + (16 * cb + (lane >> 2)) * 16;
-            *reinterpret_cast<u32x2*>(row + 4 * (qa ^ sw) + 2 * g) = u32x2{v[cb][0], v[cb][1]};
-            *reinterpret_cast<u32x2*>(row + 4 * ((qa + 1) ^ sw) + 2 * g) = u32x2{v[cb][2], v[cb][3]};
+            uint32_t* row = lds + (16 * cb + (lane >> 2)) * kRowU32;
+            if constexpr (BITS == 4) {
+                const int g = j >> 1, qa = 2 * (j & 1);
+                *reinterpret_cast<u32x2*>(row + 4 * (qa ^ sw) + 2 * g) = u32x2{v[cb][0][0], v[cb][0][1]};
+                *reinterpret_cast<u32x2*>(row + 4 * ((qa + 1) ^ sw) + 2 * g) = u32x2{v[cb][0][2], v[cb][0][3]};
+            } else {
+                // part h: words 4 j .. 4 j + 3 of half h = the pairs of 4-bit
+                // words 8 h + 2 j and 8 h + 2 j + 1
+#pragma unroll
+                for (int h = 0; h < 2; ++h) *reinterpret_cast<u32x4*>(row + 8 * (j ^ sw) + 4 * h) = v[cb][h];
+            }
         }
     }
     // The words lane (lr, q) feeds to slices 0..3 (Geo<GS>::word) of row
-    // 16 cb + lr; for GS = 64 that is [g0 word 2q, g0 word 2q+1, g1 word 2q,
-    // g1 word 2q+1], one 16-byte read.
-    __device__ __forceinline__ u32x4 get(int cb, int lr, int q) const {
-        const uint32_t* row = lds + (16 * cb + lr) * 16;
+    // 16 cb + lr; for 64-column chains one contiguous read ([g0 word 2q,
+    // g0 word 2q+1, g1 word 2q, g1 word 2q+1], pairs of words for 8-bit codes).
+    __device__ __forceinline__ WLane<BITS> get(int cb, int lr, int q) const {
+        const uint32_t* row = lds + (16 * cb + lr) * kRowU32;
         const int sw = (lr >> 2) & 3;
-        if constexpr (Geo<GS>::kChain == 64) {
-            return *reinterpret_cast<const u32x4*>(row + 4 * (q ^ sw));
-        } else {
-            // word w sits at 4 ((w & 7) >> 1 ^ sw) + 2 (w >> 3) + (w & 1)
-            u32x4 r;
+        if constexpr (BITS == 4) {
+            if constexpr (Geo<GS>::kChain == 64) {
+                return *reinterpret_cast<const u32x4*>(row + 4 * (q ^ sw));
+            } else {
+                // word w sits at 4 ((w & 7) >> 1 ^ sw) + 2 (w >> 3) + (w & 1)
+                u32x4 r;
 #pragma unroll
-            for (int sl = 0; sl < 4; ++sl) {
-                const int w = Geo<GS>::word(sl, q);
-                r[sl] = row[4 * (((w & 7) >> 1) ^ sw) + 2 * (w >> 3) + (w & 1)];
+                for (int sl = 0; sl < 4; ++sl) {
+                    const int w = Geo<GS>::word(sl, q);
+                    r[sl] = row[4 * (((w & 7) >> 1) ^ sw) + 2 * (w >> 3) + (w & 1)];
+                }
+                return r;
+            }
+        } else {
+            u32x8 r;
+            if constexpr (Geo<GS>::kChain == 64) {
+                const u32x4 lo = *reinterpret_cast<const u32x4*>(row + 8 * (q ^ sw));
+                const u32x4 hi = *reinterpret_cast<const u32x4*>(row + 8 * (q ^ sw) + 4);
+                r = u32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            } else {
+#pragma unroll
+                for (int sl = 0; sl < 4; ++sl) {
+                    const int w = Geo<GS>::word(sl, q);
+                    const u32x2 pr = *reinterpret_cast<const u32x2*>(
+                        row + 2 * (4 * (((w & 7) >> 1) ^ sw) + 2 * (w >> 3) + (w & 1)));
+                    r[2 * sl] = pr[0];
+                    r[2 * sl + 1] = pr[1];
+                }
             }
             return r;
         }
@@ -417,9 +466,9 @@ struct Tables {
 
 // =========================================================== skinny paths
 // One wave's LDS: NB 16-row weight blocks.
-template <int NB, int MAXG>
+template <int NB, int MAXG, int BITS>
 struct alignas(16) SkinnySmem {
-    uint32_t w[NB * 16 * 16];      // weight transposition buffer
+    uint32_t w[NB * 16 * 4 * BITS];  // weight transposition buffer (16 or 32 u32 per row)
     uint16_t ts[NB * 16 * MAXG];   // scales of the wave's weight rows
     uint16_t tb[NB * 16 * MAXG];   // biases
     int32_t dst[kBmSmall];         // down: destination slot of each row
@@ -431,10 +480,10 @@ struct alignas(16) SkinnySmem {
 // n0 .. n0 + 15) and block up (rows I + n0 ..), and writes their 16-column
 // block sums of h.
 // RING chunks of weights are in flight.
-template <bool kF32H, int RING, int GS>
-__global__ __launch_bounds__(64, GS == 32 ? 2 : 3) void moe_gateup_skinny(FfnArgs a) {
+template <bool kF32H, int RING, int GS, int BITS>
+__global__ __launch_bounds__(64, GS == 32 || BITS == 8 ? 2 : 3) void moe_gateup_skinny(FfnArgs a) {
     constexpr int NB = 2, NS = Geo<GS>::kSteps, GPC = Geo<GS>::kChains, SH = Geo<GS>::kShift;
-    __shared__ SkinnySmem<NB, Geo<GS>::kMaxG> sm;
+    __shared__ SkinnySmem<NB, Geo<GS>::kMaxG, BITS> sm;
     int cb;
     const int4 tile = load_skinny_tile(a, a.I / 16, cb);
     if (tile.x < 0) return;
@@ -449,12 +498,12 @@ __global__ __launch_bounds__(64, GS == 32 ? 2 : 3) void moe_gateup_skinny(FfnArg
     row0[0] = static_cast<size_t>(e) * 2 * I + hcol0;
     row0[1] = row0[0] + I;
 #pragma unroll
-    for (int b = 0; b < NB; ++b) blk[b] = a.w_gu + row0[b] * (H / 8);
+    for (int b = 0; b < NB; ++b) blk[b] = a.w_gu + row0[b] * (H / 32 * BITS);
     Tables<NB, true, Geo<GS>::kMaxG / 32> tab;
     tab.load(a.s_gu, a.b_gu, row0, G);
-    WaveW<NB, GS> ww;
-    ww.init(sm.w, blk, H / 8);
-    u32x4 rv[RING][NB];
+    WaveW<NB, GS, BITS> ww;
+    ww.init(sm.w, blk, H / 32 * BITS);
+    u32x4 rv[RING][NB][BITS / 4];
 #pragma unroll
     for (int i = 0; i < RING; ++i) ww.load(i, rv[i]);
 
@@ -493,7 +542,8 @@ __global__ __launch_bounds__(64, GS == 32 ? 2 : 3) void moe_gateup_skinny(FfnArg
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
             BiasOp<NS> C;
-            bias_from_table(C, sm.ts + (16 * b + lr) * G, sm.tb + (16 * b + lr) * G, G, q, steps, true);
+            bias_from_table<NS, kCodeOffset<BITS>>(C, sm.ts + (16 * b + lr) * G, sm.tb + (16 * b + lr) * G, G, q,
+                                                   steps, true);
             bterm[b] = bias_mfma(X, C, steps);
         }
     }
@@ -510,7 +560,7 @@ __global__ __launch_bounds__(64, GS == 32 ? 2 : 3) void moe_gateup_skinny(FfnArg
         ww.put(rv[slot]);
         if (reload) ww.load(c + RING, rv[slot]);
         __builtin_amdgcn_wave_barrier();
-        u32x4 wv[NB];
+        WLane<BITS> wv[NB];
 #pragma unroll
         for (int b = 0; b < NB; ++b) wv[b] = ww.get(b, lr, q);
         float s16[NB][GPC];
@@ -520,9 +570,9 @@ __global__ __launch_bounds__(64, GS == 32 ? 2 : 3) void moe_gateup_skinny(FfnArg
             for (int j = 0; j < GPC; ++j)
                 s16[b][j] = scale16(sm.ts[(16 * b + lr) * G + min((GPC * c + j) >> SH, G - 1)]);
         if (full) {
-            chunk_steps<GS, NB, 4>(acc, ra[abuf], wv, s16, kc);
+            chunk_steps<GS, NB, 4, BITS>(acc, ra[abuf], wv, s16, kc);
         } else if constexpr (GS != 128) {
-            chunk_steps<GS, NB, 2>(acc, ra[abuf], wv, s16, kc);
+            chunk_steps<GS, NB, 2, BITS>(acc, ra[abuf], wv, s16, kc);
         }
         __builtin_amdgcn_wave_barrier();
     };
@@ -563,12 +613,12 @@ __global__ __launch_bounds__(64, GS == 32 ? 2 : 3) void moe_gateup_skinny(FfnArg
 // down, tiles of <= 16 rows.  Grid: skinny tiles x H / (16 NB) column
 // blocks; one wave per workgroup owns output columns 16 NB cb + [0, 16 NB),
 // NB 16-row weight blocks.
-template <bool kF32H, int NB, int RING, int GS>
-__global__ __launch_bounds__(64, kF32H || GS == 32 ? 2 : 3) void moe_down_skinny(FfnArgs a) {
+template <bool kF32H, int NB, int RING, int GS, int BITS>
+__global__ __launch_bounds__(64, kF32H || GS == 32 || BITS == 8 ? 2 : 3) void moe_down_skinny(FfnArgs a) {
     constexpr int P = kF32H ? 2 : 1, NS = Geo<GS>::kSteps, GPC = Geo<GS>::kChains, MPG = Geo<GS>::kSlices;
     constexpr int SH = Geo<GS>::kShift;
     constexpr bool kC64 = Geo<GS>::kChain == 64;
-    __shared__ SkinnySmem<NB, Geo<GS>::kMaxG> sm;
+    __shared__ SkinnySmem<NB, Geo<GS>::kMaxG, BITS> sm;
     int cb;
     const int4 tile = load_skinny_tile(a, a.H / (16 * NB), cb);
     if (tile.x < 0) return;
@@ -584,13 +634,13 @@ __global__ __launch_bounds__(64, kF32H || GS == 32 ? 2 : 3) void moe_down_skinny
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
         row0[b] = static_cast<size_t>(e) * H + cbase + 16 * min(b, nb - 1);
-        blk[b] = a.w_d + row0[b] * (I / 8);
+        blk[b] = a.w_d + row0[b] * (I / 32 * BITS);
     }
     Tables<NB, true, Geo<GS>::kMaxG / 32> tab;
     tab.load(a.s_d, a.b_d, row0, G);
-    WaveW<NB, GS> ww;
-    ww.init(sm.w, blk, I / 8);
-    u32x4 rv[RING][NB];
+    WaveW<NB, GS, BITS> ww;
+    ww.init(sm.w, blk, I / 32 * BITS);
+    u32x4 rv[RING][NB][BITS / 4];
 #pragma unroll
     for (int i = 0; i < RING; ++i) ww.load(i, rv[i]);
 
@@ -639,7 +689,8 @@ __global__ __launch_bounds__(64, kF32H || GS == 32 ? 2 : 3) void moe_down_skinny
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
             BiasOp<NS> C;
-            bias_from_table(C, ts + (16 * b + lr) * G, tb + (16 * b + lr) * G, G, q, steps, true);
+            bias_from_table<NS, kCodeOffset<BITS>>(C, ts + (16 * b + lr) * G, tb + (16 * b + lr) * G, G, q, steps,
+                                                   true);
             bterm[b] = bias_mfma(X, C, steps);
         }
     }
@@ -656,7 +707,7 @@ __global__ __launch_bounds__(64, kF32H || GS == 32 ? 2 : 3) void moe_down_skinny
         ww.put(rv[slot]);
         if (reload) ww.load(c + RING, rv[slot]);
         __builtin_amdgcn_wave_barrier();
-        u32x4 wv[NB];
+        WLane<BITS> wv[NB];
 #pragma unroll
         for (int b = 0; b < NB; ++b) wv[b] = ww.get(b, lr, q);
         float s16[NB][GPC];
@@ -670,9 +721,9 @@ __global__ __launch_bounds__(64, kF32H || GS == 32 ? 2 : 3) void moe_down_skinny
 #pragma unroll
             for (int j = 0; j < 4; ++j) x[j] = ra[abuf][j][0];
             if (full) {
-                chunk_steps<GS, NB, 4>(acc, x, wv, s16, kc);
+                chunk_steps<GS, NB, 4, BITS>(acc, x, wv, s16, kc);
             } else if constexpr (GS != 128) {
-                chunk_steps<GS, NB, 2>(acc, x, wv, s16, kc);
+                chunk_steps<GS, NB, 2, BITS>(acc, x, wv, s16, kc);
             }
         } else {
             // groups in order, each with its hi and lo activation slices
@@ -685,7 +736,7 @@ __global__ __launch_bounds__(64, kF32H || GS == 32 ? 2 : 3) void moe_down_skinny
                         u32x4 xs2[MPG][P];
 #pragma unroll
                         for (int m = 0; m < MPG; ++m) {
-                            bw[m] = codes_as_bf16(wv[b][j * MPG + m], kc);
+                            bw[m] = slice_operand<BITS>(wv[b], j * MPG + m, kc);
 #pragma unroll
                             for (int pp = 0; pp < P; ++pp) xs2[m][pp] = ra[abuf][j * MPG + m][pp];
                         }
@@ -842,7 +893,7 @@ __device__ __forceinline__ void wide_kloop(WideSmem<RB, P, NBUF, MAXG>& sm, Stag
     ww.init(sm.w[wave], blk, K / 8);
     // chunk c + 1's weights arrive in registers while chunk c is multiplied and
     // go to the wave's LDS buffer after it (chunk c's reads are done by then)
-    u32x4 wn[CB];
+    u32x4 wn[CB][1];
     ww.load(0, wn);
     ww.put(wn);
     __syncthreads();  // stage 0 and the scale tables are in place
@@ -1214,14 +1265,15 @@ static hipError_t skip_launch(hipStream_t stream, const KTiming& t) {
     return hipSuccess;
 }
 
-// The kernels take the group size as a template parameter; a.gs picks it.
-template <int GS>
+// The kernels take the group size and the code width as template
+// parameters; a.gs and a.bits pick them.
+template <int GS, int BITS>
 static hipError_t gateup_skinny_gs(const FfnArgs& a, hipStream_t stream, const KTiming& t) {
     constexpr int RING = kSkinnyGateUpRing;
     const dim3 grid(skinny_grid(a) * (a.I / 16));
     if (a.flags & MOE_F_FP32_INTERMEDIATE)
-        return launch_kernel(moe_gateup_skinny<true, RING, GS>, grid, dim3(64), stream, t, a);
-    return launch_kernel(moe_gateup_skinny<false, RING, GS>, grid, dim3(64), stream, t, a);
+        return launch_kernel(moe_gateup_skinny<true, RING, GS, BITS>, grid, dim3(64), stream, t, a);
+    return launch_kernel(moe_gateup_skinny<false, RING, GS, BITS>, grid, dim3(64), stream, t, a);
 }
 
 // MAXG: groups per row the scale tables hold.  Rows of at most 3/4 of the
@@ -1242,14 +1294,14 @@ static hipError_t gateup_wide_gs(const FfnArgs& a, hipStream_t stream, const KTi
                  : launch_kernel(moe_gateup_wide<false, kBig, GS>, grid, dim3(kThreads), stream, t, a);
 }
 
-template <int GS>
+template <int GS, int BITS>
 static hipError_t down_skinny_gs(const FfnArgs& a, hipStream_t stream, const KTiming& t) {
     constexpr int NB = kSkinnyDownBlocks, RING = kSkinnyDownRing;
     static_assert(64 % (16 * NB) == 0, "H (a multiple of 64) must split into whole column blocks");
     const dim3 grid(skinny_grid(a) * (a.H / (16 * NB)));
     if (a.flags & MOE_F_FP32_INTERMEDIATE)
-        return launch_kernel(moe_down_skinny<true, NB, RING, GS>, grid, dim3(64), stream, t, a);
-    return launch_kernel(moe_down_skinny<false, NB, RING, GS>, grid, dim3(64), stream, t, a);
+        return launch_kernel(moe_down_skinny<true, NB, RING, GS, BITS>, grid, dim3(64), stream, t, a);
+    return launch_kernel(moe_down_skinny<false, NB, RING, GS, BITS>, grid, dim3(64), stream, t, a);
 }
 
 template <int GS>
@@ -1267,23 +1319,29 @@ static hipError_t down_wide_gs(const FfnArgs& a, hipStream_t stream, const KTimi
                  : launch_kernel(moe_down_wide<false, kBig, GS>, grid, dim3(kThreads), stream, t, a);
 }
 
-#define MOE_BY_GROUP_SIZE(fn)                                  \
+#define MOE_BY_GROUP_SIZE(fn, ...)                             \
     switch (a.gs) {                                            \
-        case 32: return fn<32>(a, stream, t);                  \
-        case 128: return fn<128>(a, stream, t);                \
-        default: return fn<64>(a, stream, t);                  \
+        case 32: return fn<32 __VA_ARGS__>(a, stream, t);      \
+        case 128: return fn<128 __VA_ARGS__>(a, stream, t);    \
+        default: return fn<64 __VA_ARGS__>(a, stream, t);      \
     }
 
 hipError_t launch_gateup_skinny(const FfnArgs& a, hipStream_t stream, const KTiming& t) {
-    MOE_BY_GROUP_SIZE(gateup_skinny_gs)
-}
-hipError_t launch_gateup_wide(const FfnArgs& a, hipStream_t stream, const KTiming& t) {
-    MOE_BY_GROUP_SIZE(gateup_wide_gs)
+    if (a.bits == 8) MOE_BY_GROUP_SIZE(gateup_skinny_gs, , 8)
+    MOE_BY_GROUP_SIZE(gateup_skinny_gs, , 4)
 }
 hipError_t launch_down_skinny(const FfnArgs& a, hipStream_t stream, const KTiming& t) {
-    MOE_BY_GROUP_SIZE(down_skinny_gs)
+    if (a.bits == 8) MOE_BY_GROUP_SIZE(down_skinny_gs, , 8)
+    MOE_BY_GROUP_SIZE(down_skinny_gs, , 4)
+}
+// The wide kernels take 4-bit codes only; 8-bit problems run every expert as
+// skinny tiles (skinny_only) and never reach them.
+hipError_t launch_gateup_wide(const FfnArgs& a, hipStream_t stream, const KTiming& t) {
+    if (a.bits != 4) return a.skinny_only ? skip_launch(stream, t) : hipErrorInvalidValue;
+    MOE_BY_GROUP_SIZE(gateup_wide_gs)
 }
 hipError_t launch_down_wide(const FfnArgs& a, hipStream_t stream, const KTiming& t) {
+    if (a.bits != 4) return a.skinny_only ? skip_launch(stream, t) : hipErrorInvalidValue;
     MOE_BY_GROUP_SIZE(down_wide_gs)
 }
 #undef MOE_BY_GROUP_SIZE

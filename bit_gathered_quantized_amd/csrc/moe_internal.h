@@ -15,6 +15,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kRouteThreads = 1024;
 constexpr int kRouteWaves = kRouteThreads / 64;
@@ -83,7 +84,21 @@ __device__ __forceinline__ u32x4 codes_as_bf16(uint32_t w, CodeConsts k) {
     r[3] = ((w >> 9) & k.mask) | k.one;  // q3, q7
     return r;
 }
-constexpr float kCodeOffset = 16.0f;  // the 16 of 16 + q
+// 8-bit codes: the bf16 mantissa cannot take q under a fixed exponent, so
+// each byte is converted (exactly: q <= 255 has 8 significant bits) and the
+// operand is q itself, offset 0.  w0 holds columns 0..3 of the 8-column piece,
+// w1 columns 4..7; element pairs come out in the permute8 order [q0, q4, q1,
+// q5, q2, q6, q3, q7], as for the 4-bit codes.
+__device__ __forceinline__ u32x4 bytes_as_bf16(uint32_t w0, uint32_t w1) {
+    u32x4 r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        r[i] = pack_bf16x2(static_cast<float>((w0 >> (8 * i)) & 0xFFu), static_cast<float>((w1 >> (8 * i)) & 0xFFu));
+    return r;
+}
+// The code offset of the exact operand: 16 + q for 4-bit codes, q for 8-bit.
+template <int BITS>
+constexpr int kCodeOffset = BITS == 4 ? 16 : 0;
 
 // Position of column c (0..7) of an 8-column piece after permute8.
 __device__ __forceinline__ int permuted_pos(int c) { return ((c & 3) << 1) | (c >> 2); }
@@ -188,6 +203,7 @@ size_t route_lds_bytes(int E);
 struct FfnArgs {
     int32_t T, k, E, H, I, max_tiles;
     int32_t gs;           // quantisation group size: 32, 64 or 128
+    int32_t bits;         // code width: 4 or 8 (8: skinny kernels only)
     int32_t max_skinny;   // capacity of tiles_skinny
     int32_t skinny_only;  // 1: every tile is skinny, the wide launches are skipped
     uint32_t flags;

@@ -28,6 +28,8 @@
  *
  * Element c of a row is the 4-bit code q at bits 4*(c%8) of word c/8 (low
  * nibble first) and dequantises to  W = S[c/gs] * q + B[c/gs]  in fp32.
+ * With bits = 8 the same format holds 8-bit codes: H/4 (I/4) words per row,
+ * code c at bits 8*(c%4) of word c/4 (low byte first).
  *
  * Conventions for every entry point:
  *  - All array pointers are DEVICE pointers owned by the caller; the library
@@ -53,7 +55,7 @@ enum {
     MOE_OK = 0,
     MOE_ERR_NULL = -1,        /* a required pointer is NULL                    */
     MOE_ERR_SHAPE = -2,       /* a size is negative, inconsistent or overflows */
-    MOE_ERR_UNSUPPORTED = -3, /* bits != 4, group_size not 32/64/128, E too large, ... */
+    MOE_ERR_UNSUPPORTED = -3, /* bits not 4/8, group_size not 32/64/128, E too large, ... */
     MOE_ERR_ALIGN = -4,       /* a pointer is not aligned as required          */
     MOE_ERR_WORKSPACE = -5,   /* workspace missing or too small                */
     MOE_ERR_HIP = -6          /* the HIP runtime rejected a launch             */
@@ -78,7 +80,8 @@ typedef struct {
     int32_t H;          /* hidden size, multiple of 64 and of group_size, <= 4096 */
     int32_t I;          /* intermediate size, same rules as H            */
     int32_t group_size; /* 32, 64 or 128 columns per scale and bias      */
-    int32_t bits;       /* must be 4                                     */
+    int32_t bits;       /* 4 or 8 (8: every expert runs as tiles of at most
+                           16 rows; the wide tiles are 4-bit only)      */
     uint32_t flags;     /* MOE_F_* below                                 */
 } moe_problem;
 

@@ -12,9 +12,10 @@ Layr-Labs/mlx PR #4 page, section "What"):
   topk_ids     int32             [T, k]   expert id of each routed copy
   topk_weights float32           [T, k]   routing weight of each copy
   w_gateup     uint32            [E, 2I, H/8]   rows [0,I) gate, [I,2I) up
+                                                (H/4 with 8-bit codes)
   s_gateup     bf16 bits  uint16 [E, 2I, H/gs]
   b_gateup     bf16 bits  uint16 [E, 2I, H/gs]
-  w_down       uint32            [E, H, I/8]
+  w_down       uint32            [E, H, I/8]    (I/4 with 8-bit codes)
   s_down       bf16 bits  uint16 [E, H, I/gs]
   b_down       bf16 bits  uint16 [E, H, I/gs]
 
@@ -105,13 +106,14 @@ class Problem:
     s_down: np.ndarray
     b_down: np.ndarray
     logits: Optional[np.ndarray] = field(default=None, repr=False)
+    bits: int = 4
 
     @property
     def A(self) -> int:
         return self.T * self.k
 
     def shapes(self) -> dict:
-        return dict(E=self.E, H=self.H, I=self.I, T=self.T, k=self.k, gs=self.gs)
+        return dict(E=self.E, H=self.H, I=self.I, T=self.T, k=self.k, gs=self.gs, bits=self.bits)
 
 
 def route_topk(logits: np.ndarray, k: int):
@@ -149,20 +151,26 @@ def _router_logits(rng: np.random.Generator, router: str, T: int, E: int) -> np.
     raise ValueError(f"unknown router {router!r}")
 
 
-def _scales(rng: np.random.Generator, shape):
-    s = f32_to_bf16_bits(np.abs(rng.normal(0.0, SCALE_STD, size=shape)).astype(np.float32))
-    b = f32_to_bf16_bits(bf16_bits_to_f32(s) * np.float32(-8.0))
+def _scales(rng: np.random.Generator, shape, bits: int = 4):
+    """Scales |N(0, std)| and biases -2^(bits-1) * scale (centred codes); 8-bit
+    scales are 16x smaller so that the weights keep the 4-bit spread."""
+    std = SCALE_STD if bits == 4 else SCALE_STD / 16
+    s = f32_to_bf16_bits(np.abs(rng.normal(0.0, std, size=shape)).astype(np.float32))
+    b = f32_to_bf16_bits(bf16_bits_to_f32(s) * np.float32(-(2 ** (bits - 1))))
     return s, b
 
 
 def make_problem(E: int, H: int, I: int, T: int, k: int, seed: int = 0,
                  router: str = "normal", gs: int = GROUP_SIZE, name: str = "custom",
                  topk_ids: Optional[np.ndarray] = None,
-                 topk_weights: Optional[np.ndarray] = None) -> Problem:
+                 topk_weights: Optional[np.ndarray] = None, bits: int = 4) -> Problem:
     """Draw one problem.  ``topk_ids``/``topk_weights`` override the router draw
-    (the logits are still drawn so the rest of the stream is unchanged)."""
+    (the logits are still drawn so the rest of the stream is unchanged).
+    ``bits``: 4 (8 codes per uint32 word) or 8 (4 codes per word)."""
     if H % 8 or I % 8 or H % gs or I % gs:
         raise ValueError("H and I must be multiples of 8 and of the group size")
+    if bits not in (4, 8):
+        raise ValueError("bits must be 4 or 8")
     rng = np.random.default_rng(seed)
     logits = _router_logits(rng, router, T, E)
     if k <= E:
@@ -175,13 +183,14 @@ def make_problem(E: int, H: int, I: int, T: int, k: int, seed: int = 0,
     if topk_weights is not None:
         w = np.ascontiguousarray(topk_weights, dtype=np.float32).reshape(T, k)
     x = f32_to_bf16_bits(rng.standard_normal((T, H), dtype=np.float32))
-    w_gu = rng.integers(0, 2**32, size=(E, 2 * I, H // 8), dtype=np.uint32)
-    s_gu, b_gu = _scales(rng, (E, 2 * I, H // gs))
-    w_d = rng.integers(0, 2**32, size=(E, H, I // 8), dtype=np.uint32)
-    s_d, b_d = _scales(rng, (E, H, I // gs))
+    w_gu = rng.integers(0, 2**32, size=(E, 2 * I, H * bits // 32), dtype=np.uint32)
+    s_gu, b_gu = _scales(rng, (E, 2 * I, H // gs), bits)
+    w_d = rng.integers(0, 2**32, size=(E, H, I * bits // 32), dtype=np.uint32)
+    s_d, b_d = _scales(rng, (E, H, I // gs), bits)
     return Problem(name=name, seed=seed, E=E, H=H, I=I, T=T, k=k, gs=gs, x=x,
                    topk_ids=ids, topk_weights=w, w_gateup=w_gu, s_gateup=s_gu,
-                   b_gateup=b_gu, w_down=w_d, s_down=s_d, b_down=b_d, logits=logits)
+                   b_gateup=b_gu, w_down=w_d, s_down=s_d, b_down=b_d, logits=logits,
+                   bits=bits)
 
 
 def make_config(name: str, seed: int = 0) -> Problem:

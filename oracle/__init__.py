@@ -50,7 +50,7 @@ def _load():
         lib.oracle_route.restype = ctypes.c_int
         lib.oracle_tiles.argtypes = [P, P, i32, i32, i32, P, i64, P]
         lib.oracle_tiles.restype = ctypes.c_int
-        lib.oracle_weight.argtypes = [P, P, P, i64, i64, i32, i64, i64, i64]
+        lib.oracle_weight.argtypes = [P, P, P, i64, i64, i32, i32, i64, i64, i64]
         lib.oracle_weight.restype = dbl
         lib.oracle_gelu_tanh.argtypes = [dbl]
         lib.oracle_gelu_tanh.restype = dbl
@@ -58,7 +58,7 @@ def _load():
         lib.oracle_silu.restype = dbl
         lib.oracle_router_topk.argtypes = [P, i32, i32, i32, P, P]
         lib.oracle_router_topk.restype = ctypes.c_int
-        lib.oracle_ffn_tokens.argtypes = [i32] * 6 + [P] * 9 + [P, i32, i32, P, P, P]
+        lib.oracle_ffn_tokens.argtypes = [i32] * 7 + [P] * 9 + [P, i32, i32, P, P, P]
         lib.oracle_ffn_tokens.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -141,10 +141,12 @@ def forward_tiles(counts: np.ndarray, offsets: np.ndarray, bm_big: int, bm_small
     return (np.array(wide, np.int32).reshape(-1, 4), np.array(short, np.int32).reshape(-1, 4))
 
 
-def weight(P: np.ndarray, S: np.ndarray, B: np.ndarray, gs: int, e: int, n: int, c: int) -> float:
-    """One dequantised weight W[e, n, c] of a packed [E, rows, K/8] matrix."""
+def weight(P: np.ndarray, S: np.ndarray, B: np.ndarray, gs: int, e: int, n: int, c: int,
+           bits: int = 4) -> float:
+    """One dequantised weight W[e, n, c] of a packed [E, rows, K * bits / 32] matrix."""
     E, rows, kw = P.shape
-    return float(_load().oracle_weight(_ptr(P), _ptr(S), _ptr(B), rows, kw * 8, gs, e, n, c))
+    return float(_load().oracle_weight(_ptr(P), _ptr(S), _ptr(B), rows, kw * 32 // bits, gs, bits,
+                                       e, n, c))
 
 
 def gelu_tanh(v: float) -> float:
@@ -189,7 +191,7 @@ def ffn_tokens(p, tokens=None, want_h: bool = True, want_y: bool = True,
                                               p.s_gateup, p.b_gateup, p.w_down, p.s_down,
                                               p.b_down)]
     assert arrs[1].dtype == np.int32 and arrs[2].dtype == np.float32
-    rc = _load().oracle_ffn_tokens(p.T, p.k, p.E, p.H, p.I, p.gs, *[_ptr(a) for a in arrs],
+    rc = _load().oracle_ffn_tokens(p.T, p.k, p.E, p.H, p.I, p.gs, p.bits, *[_ptr(a) for a in arrs],
                                    _ptr(tokens), n, ACTIVATIONS[act], _ptr(h), _ptr(y),
                                    _ptr(out))
     if rc != 0:

@@ -21,7 +21,9 @@
  *           element c (low nibble first in each uint32 word): the affine
  *           4-bit, group-size-64 format of the PR #4 page ("What"), with the
  *           scale and bias widened before use (mlx-node PR #168 page: the
- *           sidecars are promoted to f32 "either way").
+ *           sidecars are promoted to f32 "either way").  Group sizes 32 and
+ *           128 and 8-bit codes (4 per word, low byte first) are the same
+ *           affine format at other geometries; the pages use only 4-bit, 64.
  *   gate|up g = x . W_gu[e, n, :], u = x . W_gu[e, I+n, :]  (PR #168 page:
  *           one packed "MLP gate|up" projection split in two halves).
  *   GeGLU   h = gelu_tanh(g) * u, with
@@ -142,22 +144,24 @@ int oracle_tiles(const int32_t* counts, const int32_t* offsets, int32_t E,
 
 /* ------------------------------------------------------------- weights */
 
-/* The 4-bit code of column c in one packed row (8 codes per word, low nibble
- * first). */
-static int32_t code_at(const uint32_t* packed_row, int64_t c) {
-    uint32_t word = packed_row[c / 8];
-    return (int32_t)((word >> (4 * (c % 8))) & 15u);
+/* The code of column c in one packed row: bits = 4, 8 codes per word, low
+ * nibble first; bits = 8, 4 codes per word, low byte first. */
+static int32_t code_at(const uint32_t* packed_row, int64_t c, int32_t bits) {
+    const int64_t per_word = 32 / bits;
+    const uint32_t word = packed_row[c / per_word];
+    const uint32_t mask = (1u << bits) - 1u;
+    return (int32_t)((word >> (bits * (c % per_word))) & mask);
 }
 
-/* Dequantised weight W[e, n, c] of a [E, rows, K] matrix. */
+/* Dequantised weight W[e, n, c] of a [E, rows, K] matrix of bits-wide codes. */
 double oracle_weight(const uint32_t* P, const uint16_t* S, const uint16_t* B,
-                     int64_t rows, int64_t K, int32_t gs, int64_t e, int64_t n,
-                     int64_t c) {
+                     int64_t rows, int64_t K, int32_t gs, int32_t bits, int64_t e,
+                     int64_t n, int64_t c) {
     const int64_t row = e * rows + n;
     const int64_t groups = K / gs;
     double s = bf16_value(S[row * groups + c / gs]);
     double b = bf16_value(B[row * groups + c / gs]);
-    return s * (double)code_at(P + row * (K / 8), c) + b;
+    return s * (double)code_at(P + row * (K * bits / 32), c, bits) + b;
 }
 
 double oracle_gelu_tanh(double v) {
@@ -169,11 +173,11 @@ double oracle_silu(double v) { return v / (1.0 + exp(-v)); }
 
 /* dot(W[e, n, :], v) over K columns, v in double. */
 static double row_dot(const uint32_t* P, const uint16_t* S, const uint16_t* B,
-                      int64_t rows, int64_t K, int32_t gs, int64_t e, int64_t n,
-                      const double* v) {
+                      int64_t rows, int64_t K, int32_t gs, int32_t bits, int64_t e,
+                      int64_t n, const double* v) {
     double acc = 0.0;
     for (int64_t c = 0; c < K; ++c)
-        acc += oracle_weight(P, S, B, rows, K, gs, e, n, c) * v[c];
+        acc += oracle_weight(P, S, B, rows, K, gs, bits, e, n, c) * v[c];
     return acc;
 }
 
@@ -189,7 +193,7 @@ static double row_dot(const uint32_t* P, const uint16_t* S, const uint16_t* B,
  * Rows of an assignment with an out-of-range expert id are zero.
  */
 int oracle_ffn_tokens(int32_t T, int32_t k, int32_t E, int32_t H, int32_t I,
-                      int32_t gs, const uint16_t* x, const int32_t* ids,
+                      int32_t gs, int32_t bits, const uint16_t* x, const int32_t* ids,
                       const float* w, const uint32_t* w_gu, const uint16_t* s_gu,
                       const uint16_t* b_gu, const uint32_t* w_d,
                       const uint16_t* s_d, const uint16_t* b_d,
@@ -197,7 +201,8 @@ int oracle_ffn_tokens(int32_t T, int32_t k, int32_t E, int32_t H, int32_t I,
                       double* y, double* out) {
     if (act != 0 && act != 1) return ORACLE_ERR_ARG;
     if (T < 0 || k <= 0 || E <= 0 || H <= 0 || I <= 0 || gs <= 0 || H % gs ||
-        I % gs || H % 8 || I % 8 || ntok < 0 || (ntok > 0 && !tokens))
+        I % gs || H % 8 || I % 8 || (bits != 4 && bits != 8) || ntok < 0 ||
+        (ntok > 0 && !tokens))
         return ORACLE_ERR_ARG;
     for (int32_t i = 0; i < ntok; ++i)
         if (tokens[i] < 0 || tokens[i] >= T) return ORACLE_ERR_ARG;
@@ -223,12 +228,12 @@ int oracle_ffn_tokens(int32_t T, int32_t k, int32_t E, int32_t H, int32_t I,
         for (int64_t c = 0; c < H; ++c) xv[c] = bf16_value(x[t * H + c]);
         if (e >= 0 && e < E) {
             for (int64_t n = 0; n < I; ++n) {
-                double g = row_dot(w_gu, s_gu, b_gu, 2 * (int64_t)I, H, gs, e, n, xv);
-                double u = row_dot(w_gu, s_gu, b_gu, 2 * (int64_t)I, H, gs, e, I + n, xv);
+                double g = row_dot(w_gu, s_gu, b_gu, 2 * (int64_t)I, H, gs, bits, e, n, xv);
+                double u = row_dot(w_gu, s_gu, b_gu, 2 * (int64_t)I, H, gs, bits, e, I + n, xv);
                 hv[n] = (act ? oracle_silu(g) : oracle_gelu_tanh(g)) * u;
             }
             for (int64_t m = 0; m < H; ++m)
-                yy[r * H + m] = row_dot(w_d, s_d, b_d, H, I, gs, e, m, hv);
+                yy[r * H + m] = row_dot(w_d, s_d, b_d, H, I, gs, bits, e, m, hv);
         } else {
             for (int64_t n = 0; n < I; ++n) hv[n] = 0.0;
         }

@@ -50,7 +50,7 @@ def run_forward(p, fp32=False, d=None, workspace=None, swiglu=False):
         d = dev_arrays(p)
     flags = (bgq.MOE_F_FP32_OUT | bgq.MOE_F_FP32_INTERMEDIATE) if fp32 else 0
     flags |= bgq.MOE_F_SWIGLU if swiglu else 0
-    prob = bgq.problem(p.T, p.k, p.E, p.H, p.I, flags, group_size=p.gs)
+    prob = bgq.problem(p.T, p.k, p.E, p.H, p.I, flags, group_size=p.gs, bits=p.bits)
     lay = bgq.workspace_layout(prob)
     if workspace is None:
         workspace = torch.zeros(max(lay.total, 256), dtype=torch.uint8, device="cuda")

@@ -63,7 +63,7 @@ def test_workspace_layout_and_sizes():
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(bits=8), -3), (dict(group_size=16), -3), (dict(group_size=256), -3),
+    (dict(bits=2), -3), (dict(bits=16), -3), (dict(bits=3), -3), (dict(group_size=16), -3), (dict(group_size=256), -3),
     (dict(group_size=48), -3), (dict(E=2000), -3), (dict(flags=8), -3), (dict(flags=16), -3),
     (dict(group_size=128, H=192), -2), (dict(group_size=128, I=320), -2),
     (dict(group_size=32, H=96), -2),

@@ -257,7 +257,7 @@ def test_prepared_activations_and_h_sums(fp32, gs):
     assert np.abs(hs - href).max() <= 1e-5 * np.abs(href).max()
 
 
-def _expert0_rows(n_extra, gs=64):
+def _expert0_rows(n_extra, gs=64, bits=4):
     """20 tokens, 10 of them routed to expert 0 (slot 0); n_extra more tokens
     also go to expert 0, which moves its rows from the skinny path (10 rows)
     to the wide path (10 + n_extra rows)."""
@@ -268,17 +268,18 @@ def _expert0_rows(n_extra, gs=64):
     ids[10:20, 0] = ids[10:20, 1] % (E - 1) + 1
     ids[10:20, 1] = np.where(ids[10:20, 0] == ids[10:20, 1], 0, ids[10:20, 1])
     ids[10:20, 1] = np.where(ids[10:20, 1] == 0, 3, ids[10:20, 1])
-    p = ms.make_problem(E, 256, 128, T, k, seed=12, topk_ids=ids, gs=gs, name=f"e0+{n_extra}")
+    p = ms.make_problem(E, 256, 128, T, k, seed=12, topk_ids=ids, gs=gs, bits=bits, name=f"e0+{n_extra}")
     return p
 
 
-@pytest.mark.parametrize("gs", [64, 32, 128])
+@pytest.mark.parametrize("gs,bits", [(64, 4), (32, 4), (128, 4), (64, 8)])
 @pytest.mark.parametrize("fp32", [False, True])
-def test_rows_bitwise_independent_of_tile_path(oracle_lib, fp32, gs):
+def test_rows_bitwise_independent_of_tile_path(oracle_lib, fp32, gs, bits):
     """The same token's output is bit-identical whether its expert's rows run
-    as one skinny tile (10 rows) or in wide tiles (10 + 30 rows)."""
-    a = _expert0_rows(0, gs)
-    b = _expert0_rows(30, gs)
+    as one skinny tile (10 rows) or in wide tiles (10 + 30 rows; with 8-bit
+    codes, in three 16-row skinny tiles)."""
+    a = _expert0_rows(0, gs, bits)
+    b = _expert0_rows(30, gs, bits)
     b.x[:20] = a.x
     b.topk_weights[:20] = a.topk_weights
     for f in ("w_gateup", "s_gateup", "b_gateup", "w_down", "s_down", "b_down"):
@@ -398,4 +399,43 @@ def test_group_size_32_large_batch_repeatable(oracle_lib):
     for _ in range(2):
         again, _, _ = run_forward(p, d=d)
         np.testing.assert_array_equal(again, first)
+
+
+# ------------------------------------------------------------- 8-bit codes
+# Four codes per word, low byte first; every expert runs as 16-row tiles of
+# the skinny kernels, whatever the batch.
+@pytest.mark.parametrize("gs", [64, 32, 128])
+@pytest.mark.parametrize("fp32", [False, True])
+def test_8bit_tiny_full(oracle_lib, gs, fp32):
+    compare(oracle_lib, ms.make_problem(8, 256, 128, 64, 2, seed=gs + 2, gs=gs, bits=8,
+                                        name=f"tiny-8bit-gs{gs}"), fp32)
+
+
+@pytest.mark.parametrize("fp32", [False, True])
+def test_8bit_decode_full(oracle_lib, fp32):
+    compare(oracle_lib, ms.make_problem(128, 2816, 704, 8, 8, seed=3, bits=8, name="decode-8bit"), fp32)
+
+
+@pytest.mark.parametrize("fp32", [False, True])
+def test_8bit_prefill_sampled(oracle_lib, fp32):
+    p = ms.make_problem(128, 2816, 704, 512, 8, seed=3, bits=8, name="prefill4k-8bit")
+    compare(oracle_lib, p, fp32, tokens=sample_tokens(p, n=16))
+
+
+@pytest.mark.parametrize("gs,shape", [
+    (64, (4, 192, 64, 5, 2)),      # half chunks on both matmuls
+    (64, (3, 320, 192, 40, 3)),    # 5 and 3 groups
+    (32, (8, 256, 128, 200, 2)),   # experts of ~50 rows: several 16-row tiles each
+    (64, (2, 4096, 256, 40, 1)),   # 64 groups per gate|up row
+    (128, (2, 256, 4096, 40, 1)),  # 32 groups per down row
+])
+@pytest.mark.parametrize("fp32", [False, True])
+def test_8bit_shapes_full(oracle_lib, gs, shape, fp32):
+    E, H, I, T, k = shape
+    compare(oracle_lib, ms.make_problem(E, H, I, T, k, seed=H + T + 8, gs=gs, bits=8, name=f"shape-8bit-gs{gs}"),
+            fp32)
+
+
+def test_8bit_swiglu(oracle_lib):
+    compare(oracle_lib, ms.make_problem(8, 256, 128, 64, 2, seed=9, bits=8, name="tiny-8bit"), False, swiglu=True)
 

@@ -28,8 +28,15 @@ def unpack_codes(P: np.ndarray) -> np.ndarray:
     return q.astype(np.float64)
 
 
-def dense_weights(P, S, B, gs):
-    q = unpack_codes(P)
+def unpack_bytes(P: np.ndarray) -> np.ndarray:
+    """8-bit codes: the words' bytes in memory order (little-endian: low byte
+    first), through numpy's byte view rather than shifts."""
+    b = np.ascontiguousarray(P).astype("<u4").view(np.uint8)
+    return b.reshape(*P.shape[:-1], P.shape[-1] * 4).astype(np.float64)
+
+
+def dense_weights(P, S, B, gs, bits=4):
+    q = unpack_codes(P) if bits == 4 else unpack_bytes(P)
     s = np.repeat(ms.bf16_bits_to_f32(S).astype(np.float64), gs, axis=-1)
     b = np.repeat(ms.bf16_bits_to_f32(B).astype(np.float64), gs, axis=-1)
     return s * q + b
@@ -47,8 +54,8 @@ def brute_force_out(p, act="gelu") -> np.ndarray:
     """Dense, unrouted recomputation: every token through every expert, then
     out[t] = sum_e C[t, e] * FFN_e(x_t) with C[t, e] = sum_j [ids[t,j] == e] w[t,j]."""
     x = ms.bf16_bits_to_f32(p.x).astype(np.float64)
-    Wgu = dense_weights(p.w_gateup, p.s_gateup, p.b_gateup, p.gs)
-    Wd = dense_weights(p.w_down, p.s_down, p.b_down, p.gs)
+    Wgu = dense_weights(p.w_gateup, p.s_gateup, p.b_gateup, p.gs, p.bits)
+    Wd = dense_weights(p.w_down, p.s_down, p.b_down, p.gs, p.bits)
     C = np.zeros((p.T, p.E))
     for j in range(p.k):
         valid = (p.topk_ids[:, j] >= 0) & (p.topk_ids[:, j] < p.E)
@@ -198,6 +205,41 @@ def test_dequant_matches_independent_unpack(oracle_lib):
     for _ in range(200):
         e, n, c = rng.integers(0, 3), rng.integers(0, 128), rng.integers(0, 128)
         assert oracle_lib.weight(p.w_gateup, p.s_gateup, p.b_gateup, p.gs, e, n, c) == W[e, n, c]
+
+
+def test_8bit_byte_order(oracle_lib):
+    """Hand-made words: 8-bit code c sits in byte c % 4 of word c / 4, low
+    byte first; scale 1 and bias 0 give the code itself."""
+    P = np.array([[[0x04030201, 0xFF00807F]]], np.uint32)
+    S = np.full((1, 1, 1), 0x3F80, np.uint16)   # bf16 1.0
+    B = np.zeros((1, 1, 1), np.uint16)
+    want = [1, 2, 3, 4, 0x7F, 0x80, 0x00, 0xFF]
+    got = [oracle_lib.weight(P, S, B, 8, 0, 0, c, bits=8) for c in range(8)]
+    assert got == want
+
+
+@pytest.mark.parametrize("gs,shape", [(64, (3, 128, 64, 6, 2)), (32, (2, 96, 64, 4, 2)),
+                                      (128, (3, 256, 128, 5, 2))])
+def test_8bit_matches_brute_force(oracle_lib, gs, shape):
+    E, H, I, T, k = shape
+    p = ms.make_problem(E, H, I, T, k, seed=gs + T + 1, gs=gs, bits=8)
+    assert p.w_gateup.shape[-1] == H // 4 and p.w_down.shape[-1] == I // 4
+    r = oracle_lib.ffn_tokens(p)
+    ref = brute_force_out(p)
+    assert rel_err(r["out"], ref) < 1e-12
+    # the generator's 8-bit weights keep the 4-bit spread
+    W = dense_weights(p.w_gateup, p.s_gateup, p.b_gateup, gs, 8)
+    W4 = dense_weights(*[getattr(ms.make_problem(E, H, I, T, k, seed=1, gs=gs), f)
+                         for f in ("w_gateup", "s_gateup", "b_gateup")], gs)
+    assert 0.5 < W.std() / W4.std() < 2
+
+
+def test_8bit_symmetric_code_gives_zero_output(oracle_lib):
+    """q = 128 everywhere with B = -128 S dequantises to exactly zero."""
+    p = ms.make_problem(E=4, H=128, I=64, T=6, k=2, seed=5, bits=8)
+    p.w_gateup[:] = 0x80808080
+    r = oracle_lib.ffn_tokens(p)
+    assert np.all(r["h"] == 0) and np.all(r["out"] == 0)
 
 
 def test_symmetric_code_gives_zero_output(oracle_lib):

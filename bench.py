@@ -54,7 +54,8 @@ def algorithmic_work(p):
     counts = np.bincount(ids, minlength=E)
     # experts of <= 16 rows run as one skinny tile, larger ones in wide
     # tiles; batches of <= 16 tokens run every expert on the skinny path
-    skinny_max = A if T <= BM_SMALL or p.bits == 8 else BM_SMALL
+    skinny_max = A if T <= BM_SMALL else BM_SMALL
+    bm_big = 32 if p.bits == 8 else BM_BIG  # the forward's wide tile height
     skinny_rows = np.where(counts <= skinny_max, counts, 0)
     wide_rows = counts - skinny_rows
     in_skinny = np.isin(ids, np.nonzero((counts > 0) & (counts <= skinny_max))[0])
@@ -88,12 +89,12 @@ def algorithmic_work(p):
                 r = min(BM_SMALL, c - r0)
                 hist["skinny 1-4" if r <= 4 else "skinny 5-8" if r <= 8 else "skinny 9-16"] += 1
             continue
-        n = -(-c // BM_BIG)
+        n = -(-c // bm_big)
         for j in range(n):
             r = c // n + (1 if j < c % n else 0)
             hist["wide 17-32" if r <= 32 else "wide 33-48" if r <= 48 else "wide 49-64"] += 1
     split = dict(skinny_rows=rs, wide_rows=rw, experts_with_skinny_tile=es,
-                 wide_tiles=int(np.sum((wide_rows + BM_BIG - 1) // BM_BIG)), tile_rows=hist)
+                 wide_tiles=int(np.sum((wide_rows + bm_big - 1) // bm_big)), tile_rows=hist)
     return work, fwd, split
 
 
@@ -289,7 +290,7 @@ def main():
     ap.add_argument("--group-size", type=int, default=64, choices=[32, 64, 128],
                     help="quantisation group size of the synthetic weights")
     ap.add_argument("--bits", type=int, default=4, choices=[4, 8],
-                    help="code width of the synthetic weights (8: skinny kernels only)")
+                    help="code width of the synthetic weights")
     ap.add_argument("--intermediate", type=int, default=0, metavar="I",
                     help="override the workload's intermediate size (e.g. 768 at group "
                          "size 128, which does not divide 704)")
@@ -393,7 +394,7 @@ def main():
     work, fwd_work, split = algorithmic_work(p)
     # at most 16 tokens the library launches no wide kernel: their event pair
     # brackets nothing
-    not_launched = {"moe_gateup_wide", "moe_down_wide"} if p.T <= BM_SMALL or p.bits == 8 else set()
+    not_launched = {"moe_gateup_wide", "moe_down_wide"} if p.T <= BM_SMALL else set()
     dominant = max((s for s in kernels if s not in not_launched), key=lambda s: mean_us[s])
     roof = roofline_entry(work[dominant], mean_us[dominant] * 1e-6)
     roof["kernel"] = dominant

@@ -38,9 +38,10 @@ moe_status check_problem(const moe_problem* p) {
 moe_ws_layout make_layout(const moe_problem* p) {
     moe_ws_layout l = {};
     const int64_t A = static_cast<int64_t>(p->T) * p->k;
-    // With an fp32 h the down matmul carries two activation parts; it runs
-    // on tiles of at most 64 rows (at most 4 row blocks per wave).
-    l.bm_big = (p->flags & MOE_F_FP32_INTERMEDIATE) ? moe::kBmBigF32 : moe::kBmBig;
+    // Wide tiles of at most 64 rows (4 row blocks per wave), or 32 with an
+    // fp32 h (the down matmul carries two activation parts) or 8-bit codes
+    // (twice the weight words in flight).
+    l.bm_big = (p->flags & MOE_F_FP32_INTERMEDIATE) || p->bits == 8 ? moe::kBmBigF32 : moe::kBmBig;
     l.bm_small = moe::kBmSmall;
     l.max_tiles = moe_max_tiles(A, p->E, l.bm_big);
     l.max_skinny = moe_max_tiles(A, p->E, l.bm_small);
@@ -112,9 +113,8 @@ moe_status forward_impl(const moe_problem* p, const void* x, const int32_t* ids,
     r.max_skinny = l.max_skinny;
     // At most bm_small tokens: no expert has more rows unless a token repeats
     // an id, so every expert takes the skinny path (in tiles of bm_small) and
-    // the wide launches are left out.  8-bit codes have skinny kernels only:
-    // every batch is routed that way.
-    const bool skinny_only = p->T <= l.bm_small || p->bits == 8;
+    // the wide launches are left out.
+    const bool skinny_only = p->T <= l.bm_small;
     r.skinny_max_rows = skinny_only ? INT32_MAX : l.bm_small;
     r.counts = reinterpret_cast<int32_t*>(base + l.counts);
     r.offsets = reinterpret_cast<int32_t*>(base + l.offsets);

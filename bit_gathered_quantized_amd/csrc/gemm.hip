@@ -499,6 +499,11 @@ __global__ __launch_bounds__(64, GS == 32 || BITS == 8 ? 2 : 3) void moe_gateup_
     row0[1] = row0[0] + I;
 #pragma unroll
     for (int b = 0; b < NB; ++b) blk[b] = a.w_gu + row0[b] * (H / 32 * BITS);
+    // the row's token first: loads retire in issue order, so the activation
+    // loads that depend on it can go out while the tables and weights are
+    // still in flight (padding lanes, row >= rows, read row 0: their outputs
+    // are never stored)
+    const int tok = a.perm[row_begin + min(lr, rows - 1)] / a.k;
     Tables<NB, true, Geo<GS>::kMaxG / 32> tab;
     tab.load(a.s_gu, a.b_gu, row0, G);
     WaveW<NB, GS, BITS> ww;
@@ -507,8 +512,6 @@ __global__ __launch_bounds__(64, GS == 32 || BITS == 8 ? 2 : 3) void moe_gateup_
 #pragma unroll
     for (int i = 0; i < RING; ++i) ww.load(i, rv[i]);
 
-    // padding lanes (row >= rows) read row 0: their outputs are never stored
-    const int tok = a.perm[row_begin + min(lr, rows - 1)] / a.k;
     const uint32_t* xa = reinterpret_cast<const uint32_t*>(a.xp) + static_cast<size_t>(tok) * (H / 2);
     u32x4 ra[2][4];
     // slice s of chunk c: the activation piece of chunk word Geo<GS>::word(s, q),
@@ -793,10 +796,10 @@ constexpr int kAStride = 2 * 32 + 4;  // u32 per staged activation row
 
 // MAXG bounds the group count the scale tables hold: 48 keeps a workgroup's
 // LDS under 80 KB, so that two workgroups share a CU.
-template <int RB, int P, int NBUF, int MAXG>
+template <int RB, int P, int NBUF, int MAXG, int BITS = 4>
 struct alignas(16) WideSmem {
     uint32_t a[NBUF][P][RB * 16 * kAStride];  // after the K loop: group sums of the rows
-    uint32_t w[4][64 * 16];     // per-wave weight transposition buffer; after the K loop
+    uint32_t w[4][64 * 4 * BITS];  // per-wave weight transposition buffer; after the K loop
                                 // the wave's bias rows, one block at a time
     uint16_t ts[4][64 * MAXG];  // per-wave scales of its 64 weight rows
     int32_t dst[RB * 16];       // down: destination slot of each row
@@ -860,8 +863,8 @@ struct Stager {
             for (int pp = 0; pp < P; ++pp)
                 v[i][pp] = *reinterpret_cast<const u32x4*>(src[i] + pp * part + 4 * piece);
     }
-    template <int NBUF, int MAXG>
-    __device__ __forceinline__ void store(WideSmem<RB, P, NBUF, MAXG>& sm, int buf) const {
+    template <int NBUF, int MAXG, int BITS>
+    __device__ __forceinline__ void store(WideSmem<RB, P, NBUF, MAXG, BITS>& sm, int buf) const {
         const int pc = threadIdx.x & 15, r0 = threadIdx.x >> 4;
 #pragma unroll
         for (int i = 0; i < kPasses; ++i)
@@ -871,8 +874,8 @@ struct Stager {
     }
 };
 
-template <int RB, int P, int NBUF, int MAXG>
-__device__ __forceinline__ u32x4 lds_frag(const WideSmem<RB, P, NBUF, MAXG>& sm, int buf, int pp, int row,
+template <int RB, int P, int NBUF, int MAXG, int BITS>
+__device__ __forceinline__ u32x4 lds_frag(const WideSmem<RB, P, NBUF, MAXG, BITS>& sm, int buf, int pp, int row,
                                           int piece) {
     return *reinterpret_cast<const u32x4*>(&sm.a[buf][pp][row * kAStride + 4 * piece]);
 }
@@ -880,8 +883,8 @@ __device__ __forceinline__ u32x4 lds_frag(const WideSmem<RB, P, NBUF, MAXG>& sm,
 // Shared K loop of the wide paths: acc[rb][cb] over all groups for the four
 // 16-row weight blocks blk[cb] of this wave (row length K), activations staged
 // from src (P parts, `part` apart); row blocks rb >= nrb are skipped.
-template <int GS, int RB, int P, int NBUF, int MAXG, class Last>
-__device__ __forceinline__ void wide_kloop(WideSmem<RB, P, NBUF, MAXG>& sm, Stager<RB, P>& st,
+template <int GS, int RB, int P, int NBUF, int MAXG, int BITS, class Last>
+__device__ __forceinline__ void wide_kloop(WideSmem<RB, P, NBUF, MAXG, BITS>& sm, Stager<RB, P>& st,
                                            const uint32_t* const (&src)[RB], size_t part,
                                            const uint32_t* const (&blk)[4], int K, bool active,
                                            int nrb, CodeConsts kc, f32x4 (&acc)[RB][4], Last&& last) {
@@ -889,11 +892,11 @@ __device__ __forceinline__ void wide_kloop(WideSmem<RB, P, NBUF, MAXG>& sm, Stag
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, q = lane >> 4, lr = lane & 15;
     const int G = K / GS, nh = K / 64;
     const int nch = (K + 127) / 128;
-    WaveW<CB, GS> ww;
-    ww.init(sm.w[wave], blk, K / 8);
+    WaveW<CB, GS, BITS> ww;
+    ww.init(sm.w[wave], blk, K / 32 * BITS);
     // chunk c + 1's weights arrive in registers while chunk c is multiplied and
     // go to the wave's LDS buffer after it (chunk c's reads are done by then)
-    u32x4 wn[CB][1];
+    u32x4 wn[CB][BITS / 4];
     ww.load(0, wn);
     ww.put(wn);
     __syncthreads();  // stage 0 and the scale tables are in place
@@ -903,7 +906,7 @@ __device__ __forceinline__ void wide_kloop(WideSmem<RB, P, NBUF, MAXG>& sm, Stag
     auto chunk = [&](int c, auto last_tag) {
         constexpr bool kLast = decltype(last_tag)::value;
         const int buf = NBUF == 2 ? (c & 1) : 0;
-        u32x4 wq[CB];
+        WLane<BITS> wq[CB];
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb) wq[cb] = ww.get(cb, lr, q);
         // the next chunk's loads; during the last chunk, the epilogue's
@@ -924,7 +927,7 @@ __device__ __forceinline__ void wide_kloop(WideSmem<RB, P, NBUF, MAXG>& sm, Stag
 #pragma unroll
                     for (int cb = 0; cb < CB; ++cb) {
 #pragma unroll
-                        for (int m = 0; m < MPG; ++m) bw[cb][m] = codes_as_bf16(wq[cb][j * MPG + m], kc);
+                        for (int m = 0; m < MPG; ++m) bw[cb][m] = slice_operand<BITS>(wq[cb], j * MPG + m, kc);
                         s16[cb] = scale16(sm.ts[wave][(16 * cb + lr) * G + g]);
                     }
 #pragma unroll
@@ -964,8 +967,8 @@ __device__ __forceinline__ void wide_kloop(WideSmem<RB, P, NBUF, MAXG>& sm, Stag
 // then): thread t copies groups t % 16 + 16 j of rows t / 16 + 16 i, from row
 // pointers xrow[i] (G floats each, or with kBlocks the GS / 16 block sums of
 // h per group).  br: the wave's bias rows, prefetched during the last chunk.
-template <int GS, int RB, int P, int NBUF, int MAXG, bool kBlocks>
-__device__ __forceinline__ void wide_bias(WideSmem<RB, P, NBUF, MAXG>& sm,
+template <int GS, int RB, int P, int NBUF, int MAXG, int BITS, bool kBlocks>
+__device__ __forceinline__ void wide_bias(WideSmem<RB, P, NBUF, MAXG, BITS>& sm,
                                           const float* const (&xrow)[RB],
                                           const BiasRows<4, Geo<GS>::kMaxG / 32>& br,
                                           int G, bool active, int nrb, f32x4 (&acc)[RB][4]) {
@@ -1017,7 +1020,7 @@ __device__ __forceinline__ void wide_bias(WideSmem<RB, P, NBUF, MAXG>& sm,
         br.store(wb, cb, G);
         __builtin_amdgcn_wave_barrier();
         BiasOp<NS> C;
-        bias_from_table(C, ts + (16 * cb + lr) * G, wb + lr * G, G, q, steps, active);
+        bias_from_table<NS, kCodeOffset<BITS>>(C, ts + (16 * cb + lr) * G, wb + lr * G, G, q, steps, active);
         __builtin_amdgcn_wave_barrier();
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
@@ -1037,8 +1040,8 @@ __device__ __forceinline__ void wide_bias(WideSmem<RB, P, NBUF, MAXG>& sm,
 // n0 + 32 w + [0, 32): weight blocks 0/1 = gate columns +0/+16, blocks 2/3 =
 // the matching up columns.  Waves {0,1} cover 64-column group 2*by of h,
 // waves {2,3} group 2*by + 1.
-template <int GS, int RB, int MAXG, bool kF32H>
-__device__ __forceinline__ void gateup_wide(const FfnArgs& a, WideSmem<RB, 1, 2, MAXG>& sm, int e,
+template <int GS, int RB, int MAXG, bool kF32H, int BITS>
+__device__ __forceinline__ void gateup_wide(const FfnArgs& a, WideSmem<RB, 1, 2, MAXG, BITS>& sm, int e,
                                             int row_begin, int rows, int by) {
     constexpr int P = 1, NBUF = 2, CB = 4;
     const int tid = threadIdx.x, lane = tid & 63, q = lane >> 4, lr = lane & 15;
@@ -1054,7 +1057,7 @@ __device__ __forceinline__ void gateup_wide(const FfnArgs& a, WideSmem<RB, 1, 2,
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
         row0[cb] = static_cast<size_t>(e) * 2 * I + hbase + 16 * (cb & 1) + (cb >> 1) * I;
-        blk[cb] = a.w_gu + row0[cb] * (H / 8);
+        blk[cb] = a.w_gu + row0[cb] * (H / 32 * BITS);
     }
     Tables<CB, false, (MAXG + 31) / 32> tab;
     tab.load(a.s_gu, a.b_gu, row0, G);
@@ -1082,13 +1085,13 @@ __device__ __forceinline__ void gateup_wide(const FfnArgs& a, WideSmem<RB, 1, 2,
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) bblk[cb] = a.b_gu + row0[cb] * G;
     BiasRows<CB, Geo<GS>::kMaxG / 32> br;
-    wide_kloop<GS, RB, P, NBUF, MAXG>(sm, st, src, 0, blk, H, active, (rows + 15) / 16, code_consts(a.zero), acc,
+    wide_kloop<GS, RB, P, NBUF, MAXG, BITS>(sm, st, src, 0, blk, H, active, (rows + 15) / 16, code_consts(a.zero), acc,
                                   [&] { br.load(bblk, G); });
 
     const float* xrow[RB];
 #pragma unroll
     for (int i = 0; i < RB; ++i) xrow[i] = a.xs + static_cast<size_t>(tok[i]) * G;
-    wide_bias<GS, RB, P, NBUF, MAXG, false>(sm, xrow, br, G, active, (rows + 15) / 16, acc);
+    wide_bias<GS, RB, P, NBUF, MAXG, BITS, false>(sm, xrow, br, G, active, (rows + 15) / 16, acc);
 
     // GeGLU epilogue and the 16-column block sums of h
 #pragma unroll
@@ -1111,9 +1114,9 @@ __device__ __forceinline__ void gateup_wide(const FfnArgs& a, WideSmem<RB, 1, 2,
 
 // down wide, column block `by` of 256 output columns (ceil(H / 256) blocks).  Wave w owns output columns
 // n0 + 64 w + [0, 64): four 16-row weight blocks.
-template <int GS, int RB, int MAXG, bool kF32H>
+template <int GS, int RB, int MAXG, bool kF32H, int BITS>
 __device__ __forceinline__ void down_wide(const FfnArgs& a,
-                                          WideSmem<RB, kF32H ? 2 : 1, kF32H ? 1 : 2, MAXG>& sm,
+                                          WideSmem<RB, kF32H ? 2 : 1, kF32H ? 1 : 2, MAXG, BITS>& sm,
                                           int e, int row_begin, int rows, int by) {
     constexpr int P = kF32H ? 2 : 1, NBUF = kF32H ? 1 : 2, CB = 4;
     const int tid = threadIdx.x, lane = tid & 63, q = lane >> 4, lr = lane & 15;
@@ -1129,7 +1132,7 @@ __device__ __forceinline__ void down_wide(const FfnArgs& a,
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
         row0[cb] = static_cast<size_t>(e) * H + cbase + 16 * cb;
-        blk[cb] = a.w_d + row0[cb] * (I / 8);
+        blk[cb] = a.w_d + row0[cb] * (I / 32 * BITS);
     }
     Tables<CB, false, (MAXG + 31) / 32> tab;
     tab.load(a.s_d, a.b_d, row0, G);
@@ -1165,13 +1168,13 @@ __device__ __forceinline__ void down_wide(const FfnArgs& a,
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) bblk[cb] = a.b_d + row0[cb] * G;
     BiasRows<CB, Geo<GS>::kMaxG / 32> br;
-    wide_kloop<GS, RB, P, NBUF, MAXG>(sm, st, src, part, blk, I, active, (rows + 15) / 16, code_consts(a.zero), acc,
+    wide_kloop<GS, RB, P, NBUF, MAXG, BITS>(sm, st, src, part, blk, I, active, (rows + 15) / 16, code_consts(a.zero), acc,
                                   [&] { br.load(bblk, G); });
 
     const float* xrow[RB];
 #pragma unroll
     for (int i = 0; i < RB; ++i) xrow[i] = a.hs + static_cast<size_t>(hrow[i]) * (I / 16);
-    wide_bias<GS, RB, P, NBUF, MAXG, true>(sm, xrow, br, G, active, (rows + 15) / 16, acc);
+    wide_bias<GS, RB, P, NBUF, MAXG, BITS, true>(sm, xrow, br, G, active, (rows + 15) / 16, acc);
 
     if (!active) return;
     // weighted unsort (destinations and weights read before the K loop)
@@ -1213,31 +1216,35 @@ __device__ __forceinline__ bool wide_work(const FfnArgs& a, int ncol, int& tile,
 }
 
 // Two workgroups share a CU when their LDS fits in half of it.
-template <class Smem, bool kF32H, int GS>
+template <class Smem>
 constexpr int kWideWgsPerCu = sizeof(Smem) <= 80 * 1024 ? 2 : 1;
-template <bool kF32H, int MAXG>
-using GateupWideSmem = WideSmem<kF32H ? kWideRowBlocksF32 : kWideRowBlocks, 1, 2, MAXG>;
-template <bool kF32H, int MAXG>
-using DownWideSmem = WideSmem<kF32H ? kWideRowBlocksF32 : kWideRowBlocks, kF32H ? 2 : 1, kF32H ? 1 : 2, MAXG>;
+// Row blocks per wave: 4 (64-row tiles), or 2 (32-row tiles) with an fp32 h
+// or 8-bit codes, whose extra operand registers would not fit beside four.
+template <bool kF32H, int BITS>
+constexpr int kWideRB = kF32H || BITS == 8 ? kWideRowBlocksF32 : kWideRowBlocks;
+template <bool kF32H, int MAXG, int BITS>
+using GateupWideSmem = WideSmem<kWideRB<kF32H, BITS>, 1, 2, MAXG, BITS>;
+template <bool kF32H, int MAXG, int BITS>
+using DownWideSmem = WideSmem<kWideRB<kF32H, BITS>, kF32H ? 2 : 1, kF32H ? 1 : 2, MAXG, BITS>;
 
-template <bool kF32H, int MAXG, int GS>
-__global__ __launch_bounds__(kThreads, (kWideWgsPerCu<GateupWideSmem<kF32H, MAXG>, kF32H, GS>)) void moe_gateup_wide(FfnArgs a) {
-    constexpr int RB = kF32H ? kWideRowBlocksF32 : kWideRowBlocks;
-    __shared__ WideSmem<RB, 1, 2, MAXG> sm;
+template <bool kF32H, int MAXG, int GS, int BITS>
+__global__ __launch_bounds__(kThreads, (kWideWgsPerCu<GateupWideSmem<kF32H, MAXG, BITS>>)) void moe_gateup_wide(
+    FfnArgs a) {
+    __shared__ GateupWideSmem<kF32H, MAXG, BITS> sm;
     int ti, by;
     if (!wide_work(a, (a.I + 127) / 128, ti, by)) return;
     const int4 tile = reinterpret_cast<const int4*>(a.tiles)[ti];
-    gateup_wide<GS, RB, MAXG, kF32H>(a, sm, tile.x, tile.y, tile.z, by);
+    gateup_wide<GS, kWideRB<kF32H, BITS>, MAXG, kF32H, BITS>(a, sm, tile.x, tile.y, tile.z, by);
 }
 
-template <bool kF32H, int MAXG, int GS>
-__global__ __launch_bounds__(kThreads, (kWideWgsPerCu<DownWideSmem<kF32H, MAXG>, kF32H, GS>)) void moe_down_wide(FfnArgs a) {
-    constexpr int RB = kF32H ? kWideRowBlocksF32 : kWideRowBlocks;
-    __shared__ WideSmem<RB, kF32H ? 2 : 1, kF32H ? 1 : 2, MAXG> sm;
+template <bool kF32H, int MAXG, int GS, int BITS>
+__global__ __launch_bounds__(kThreads, (kWideWgsPerCu<DownWideSmem<kF32H, MAXG, BITS>>)) void moe_down_wide(
+    FfnArgs a) {
+    __shared__ DownWideSmem<kF32H, MAXG, BITS> sm;
     int ti, by;
     if (!wide_work(a, (a.H + 255) / 256, ti, by)) return;
     const int4 tile = reinterpret_cast<const int4*>(a.tiles)[ti];
-    down_wide<GS, RB, MAXG, kF32H>(a, sm, tile.x, tile.y, tile.z, by);
+    down_wide<GS, kWideRB<kF32H, BITS>, MAXG, kF32H, BITS>(a, sm, tile.x, tile.y, tile.z, by);
 }
 
 }  // namespace
@@ -1279,7 +1286,7 @@ static hipError_t gateup_skinny_gs(const FfnArgs& a, hipStream_t stream, const K
 // MAXG: groups per row the scale tables hold.  Rows of at most 3/4 of the
 // largest group count take the smaller tables (two workgroups per CU at group
 // size 64).
-template <int GS>
+template <int GS, int BITS>
 static hipError_t gateup_wide_gs(const FfnArgs& a, hipStream_t stream, const KTiming& t) {
     const int n = wide_grid(a);
     if (n == 0) return skip_launch(stream, t);
@@ -1288,10 +1295,10 @@ static hipError_t gateup_wide_gs(const FfnArgs& a, hipStream_t stream, const KTi
     constexpr int kBig = Geo<GS>::kMaxG, kSmall = 3 * kBig / 4;
     const bool f32 = a.flags & MOE_F_FP32_INTERMEDIATE, small = a.H / GS <= kSmall;
     if (f32)
-        return small ? launch_kernel(moe_gateup_wide<true, kSmall, GS>, grid, dim3(kThreads), stream, t, a)
-                     : launch_kernel(moe_gateup_wide<true, kBig, GS>, grid, dim3(kThreads), stream, t, a);
-    return small ? launch_kernel(moe_gateup_wide<false, kSmall, GS>, grid, dim3(kThreads), stream, t, a)
-                 : launch_kernel(moe_gateup_wide<false, kBig, GS>, grid, dim3(kThreads), stream, t, a);
+        return small ? launch_kernel(moe_gateup_wide<true, kSmall, GS, BITS>, grid, dim3(kThreads), stream, t, a)
+                     : launch_kernel(moe_gateup_wide<true, kBig, GS, BITS>, grid, dim3(kThreads), stream, t, a);
+    return small ? launch_kernel(moe_gateup_wide<false, kSmall, GS, BITS>, grid, dim3(kThreads), stream, t, a)
+                 : launch_kernel(moe_gateup_wide<false, kBig, GS, BITS>, grid, dim3(kThreads), stream, t, a);
 }
 
 template <int GS, int BITS>
@@ -1304,7 +1311,7 @@ static hipError_t down_skinny_gs(const FfnArgs& a, hipStream_t stream, const KTi
     return launch_kernel(moe_down_skinny<false, NB, RING, GS, BITS>, grid, dim3(64), stream, t, a);
 }
 
-template <int GS>
+template <int GS, int BITS>
 static hipError_t down_wide_gs(const FfnArgs& a, hipStream_t stream, const KTiming& t) {
     const int n = wide_grid(a);
     if (n == 0) return skip_launch(stream, t);
@@ -1313,10 +1320,10 @@ static hipError_t down_wide_gs(const FfnArgs& a, hipStream_t stream, const KTimi
     constexpr int kBig = Geo<GS>::kMaxG, kSmall = 3 * kBig / 4;
     const bool f32 = a.flags & MOE_F_FP32_INTERMEDIATE, small = a.I / GS <= kSmall;
     if (f32)
-        return small ? launch_kernel(moe_down_wide<true, kSmall, GS>, grid, dim3(kThreads), stream, t, a)
-                     : launch_kernel(moe_down_wide<true, kBig, GS>, grid, dim3(kThreads), stream, t, a);
-    return small ? launch_kernel(moe_down_wide<false, kSmall, GS>, grid, dim3(kThreads), stream, t, a)
-                 : launch_kernel(moe_down_wide<false, kBig, GS>, grid, dim3(kThreads), stream, t, a);
+        return small ? launch_kernel(moe_down_wide<true, kSmall, GS, BITS>, grid, dim3(kThreads), stream, t, a)
+                     : launch_kernel(moe_down_wide<true, kBig, GS, BITS>, grid, dim3(kThreads), stream, t, a);
+    return small ? launch_kernel(moe_down_wide<false, kSmall, GS, BITS>, grid, dim3(kThreads), stream, t, a)
+                 : launch_kernel(moe_down_wide<false, kBig, GS, BITS>, grid, dim3(kThreads), stream, t, a);
 }
 
 #define MOE_BY_GROUP_SIZE(fn, ...)                             \
@@ -1334,15 +1341,13 @@ hipError_t launch_down_skinny(const FfnArgs& a, hipStream_t stream, const KTimin
     if (a.bits == 8) MOE_BY_GROUP_SIZE(down_skinny_gs, , 8)
     MOE_BY_GROUP_SIZE(down_skinny_gs, , 4)
 }
-// The wide kernels take 4-bit codes only; 8-bit problems run every expert as
-// skinny tiles (skinny_only) and never reach them.
 hipError_t launch_gateup_wide(const FfnArgs& a, hipStream_t stream, const KTiming& t) {
-    if (a.bits != 4) return a.skinny_only ? skip_launch(stream, t) : hipErrorInvalidValue;
-    MOE_BY_GROUP_SIZE(gateup_wide_gs)
+    if (a.bits == 8) MOE_BY_GROUP_SIZE(gateup_wide_gs, , 8)
+    MOE_BY_GROUP_SIZE(gateup_wide_gs, , 4)
 }
 hipError_t launch_down_wide(const FfnArgs& a, hipStream_t stream, const KTiming& t) {
-    if (a.bits != 4) return a.skinny_only ? skip_launch(stream, t) : hipErrorInvalidValue;
-    MOE_BY_GROUP_SIZE(down_wide_gs)
+    if (a.bits == 8) MOE_BY_GROUP_SIZE(down_wide_gs, , 8)
+    MOE_BY_GROUP_SIZE(down_wide_gs, , 4)
 }
 #undef MOE_BY_GROUP_SIZE
 

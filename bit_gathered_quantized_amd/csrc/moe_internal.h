@@ -27,7 +27,7 @@ constexpr int kRouteWaves = kRouteThreads / 64;
 // keeps the wide kernels within 256 vector registers (32 rows with fp32
 // intermediates).
 constexpr int kBmBig = 64;
-constexpr int kBmBigF32 = 32;  // with MOE_F_FP32_INTERMEDIATE
+constexpr int kBmBigF32 = 32;  // with MOE_F_FP32_INTERMEDIATE or 8-bit codes
 constexpr int kBmSmall = 16;
 // Largest H and I the kernels take (the scale and bias tables in LDS and the
 // bias contraction are sized for it).

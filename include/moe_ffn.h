@@ -80,8 +80,7 @@ typedef struct {
     int32_t H;          /* hidden size, multiple of 64 and of group_size, <= 4096 */
     int32_t I;          /* intermediate size, same rules as H            */
     int32_t group_size; /* 32, 64 or 128 columns per scale and bias      */
-    int32_t bits;       /* 4 or 8 (8: every expert runs as tiles of at most
-                           16 rows; the wide tiles are 4-bit only)      */
+    int32_t bits;       /* 4 or 8 (8: wide tiles of at most 32 rows)     */
     uint32_t flags;     /* MOE_F_* below                                 */
 } moe_problem;
 

@@ -276,8 +276,8 @@ def _expert0_rows(n_extra, gs=64, bits=4):
 @pytest.mark.parametrize("fp32", [False, True])
 def test_rows_bitwise_independent_of_tile_path(oracle_lib, fp32, gs, bits):
     """The same token's output is bit-identical whether its expert's rows run
-    as one skinny tile (10 rows) or in wide tiles (10 + 30 rows; with 8-bit
-    codes, in three 16-row skinny tiles)."""
+    as one skinny tile (10 rows) or in wide tiles (10 + 30 rows: one 40-row
+    tile, or with 8-bit codes two 20-row tiles)."""
     a = _expert0_rows(0, gs, bits)
     b = _expert0_rows(30, gs, bits)
     b.x[:20] = a.x
@@ -402,8 +402,7 @@ def test_group_size_32_large_batch_repeatable(oracle_lib):
 
 
 # ------------------------------------------------------------- 8-bit codes
-# Four codes per word, low byte first; every expert runs as 16-row tiles of
-# the skinny kernels, whatever the batch.
+# Four codes per word, low byte first; wide tiles of at most 32 rows.
 @pytest.mark.parametrize("gs", [64, 32, 128])
 @pytest.mark.parametrize("fp32", [False, True])
 def test_8bit_tiny_full(oracle_lib, gs, fp32):
@@ -425,7 +424,7 @@ def test_8bit_prefill_sampled(oracle_lib, fp32):
 @pytest.mark.parametrize("gs,shape", [
     (64, (4, 192, 64, 5, 2)),      # half chunks on both matmuls
     (64, (3, 320, 192, 40, 3)),    # 5 and 3 groups
-    (32, (8, 256, 128, 200, 2)),   # experts of ~50 rows: several 16-row tiles each
+    (32, (8, 256, 128, 200, 2)),   # experts of ~50 rows: two wide tiles each
     (64, (2, 4096, 256, 40, 1)),   # 64 groups per gate|up row
     (128, (2, 256, 4096, 40, 1)),  # 32 groups per down row
 ])
@@ -438,4 +437,15 @@ def test_8bit_shapes_full(oracle_lib, gs, shape, fp32):
 
 def test_8bit_swiglu(oracle_lib):
     compare(oracle_lib, ms.make_problem(8, 256, 128, 64, 2, seed=9, bits=8, name="tiny-8bit"), False, swiglu=True)
+
+
+def test_8bit_large_batch_sampled(oracle_lib):
+    """16384 assignments (Zipf router) with 8-bit codes: sampled parity, and a
+    repeated run bit-identical."""
+    c = ms.CONFIGS["prefill16k"]
+    p = ms.make_problem(c["E"], c["H"], c["I"], c["T"], c["k"], seed=0, router=c["router"], bits=8,
+                        name="prefill16k-8bit")
+    first = compare(oracle_lib, p, False, tokens=sample_tokens(p, n=12))
+    again, _, _ = run_forward(p)
+    np.testing.assert_array_equal(again, first)
 

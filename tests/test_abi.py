@@ -166,3 +166,14 @@ def test_presorted_host_checks():
                                                   out, ws, need, None)
     assert call(None) == -1
     assert call(P(0x10002)) == -4
+
+
+@pytest.mark.parametrize("gs,bits", [(32, 4), (64, 4), (128, 4), (32, 8), (64, 8), (128, 8)])
+def test_layout_other_geometries(gs, bits):
+    """Group sums take H/gs floats per token; 8-bit codes use 32-row wide tiles."""
+    T, k, E, H, I = 300, 4, 16, 1024, 256
+    lay = bgq.workspace_layout(bgq.problem(T, k, E, H, I, 0, group_size=gs, bits=bits))
+    assert lay.h - lay.x_sums >= T * (H // gs) * 4
+    assert lay.bm_big == (32 if bits == 8 else 64) and lay.bm_small == 16
+    assert lay.max_tiles == bgq.max_tiles(T * k, E, lay.bm_big)
+

@@ -449,3 +449,18 @@ def test_8bit_large_batch_sampled(oracle_lib):
     again, _, _ = run_forward(p)
     np.testing.assert_array_equal(again, first)
 
+
+@pytest.mark.parametrize("gs,bits", [(32, 4), (128, 8), (64, 8)])
+def test_other_geometries_invalid_ids_and_empty(oracle_lib, gs, bits):
+    """Out-of-range ids contribute zero and T = 0 is a no-op at the other
+    group sizes and code widths too."""
+    p = ms.make_problem(8, 256, 128, 64, 2, seed=gs + bits, gs=gs, bits=bits, name=f"tiny-gs{gs}-b{bits}")
+    p.topk_ids[3, 0] = p.E
+    p.topk_ids[10, 1] = -1
+    p.topk_ids[11, :] = 99
+    compare(oracle_lib, p, False)
+    compare(oracle_lib, p, True)
+    e = ms.make_problem(4, 256, 128, 0, 2, seed=0, gs=gs, bits=bits, name="empty")
+    out, _, _ = run_forward(e)
+    assert out.shape == (0, 256)
+

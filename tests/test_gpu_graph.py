@@ -14,11 +14,16 @@ from gpu_util import dev_arrays, log
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("name,swiglu", [("decode", False), ("prefill4k", True)])
+@pytest.mark.parametrize("name,swiglu", [("decode", False), ("prefill4k", True),
+                                         ("prefill4k-8bit-gs128", False)])
 def test_graph_replays_match_eager(name, swiglu):
-    p = ms.make_config(name)
+    if name == "prefill4k-8bit-gs128":
+        p = ms.make_problem(128, 2816, 768, 512, 8, seed=0, gs=128, bits=8, name=name)
+    else:
+        p = ms.make_config(name)
     d = dev_arrays(p)
-    prob = bgq.problem(p.T, p.k, p.E, p.H, p.I, bgq.MOE_F_SWIGLU if swiglu else 0)
+    prob = bgq.problem(p.T, p.k, p.E, p.H, p.I, bgq.MOE_F_SWIGLU if swiglu else 0, group_size=p.gs,
+                       bits=p.bits)
     ws = torch.zeros(bgq.workspace_bytes(prob), dtype=torch.uint8, device="cuda")
     out = torch.empty((p.T, p.H), dtype=torch.bfloat16, device="cuda")
     args = [d[n] for n in ("x", "ids", "w", "w_gu", "s_gu", "b_gu", "w_d", "s_d", "b_d")]

@@ -15,7 +15,7 @@ pytestmark = pytest.mark.gpu
 
 
 def _run(p, d, order=None):
-    prob = bgq.problem(p.T, p.k, p.E, p.H, p.I, 0)
+    prob = bgq.problem(p.T, p.k, p.E, p.H, p.I, 0, group_size=p.gs, bits=p.bits)
     ws = torch.zeros(bgq.workspace_bytes(prob), dtype=torch.uint8, device="cuda")
     so = None if order is None else torch.from_numpy(np.ascontiguousarray(order, np.int32)).cuda()
     out = bgq.expert_ffn_forward(d["x"], d["ids"], d["w"], d["w_gu"], d["s_gu"], d["b_gu"],
@@ -40,9 +40,15 @@ def _sorted_orders(p, oracle_lib):
     return stable, shuffled
 
 
-@pytest.mark.parametrize("name", ["decode", "prefill16k"])
+def _problem(name):
+    if name == "prefill4k-8bit-gs32":
+        return ms.make_problem(128, 2816, 704, 512, 8, seed=0, gs=32, bits=8, name=name)
+    return ms.make_config(name)
+
+
+@pytest.mark.parametrize("name", ["decode", "prefill16k", "prefill4k-8bit-gs32"])
 def test_presorted_orders_used_and_bitwise_equal(oracle_lib, name):
-    p = ms.make_config(name)
+    p = _problem(name)
     d = dev_arrays(p)
     ref, _, _ = _run(p, d)
     stable, shuffled = _sorted_orders(p, oracle_lib)

@@ -1,4 +1,4 @@
-"""Python binding of libmoeffn, the routed 4-bit MoE expert FFN for MI355X.
+"""Python binding of libmoeffn, the routed 4-bit (or 8-bit) MoE expert FFN for MI355X.
 
 Argument marshalling only: every step of the computation runs in the HIP
 kernels of ``libmoeffn.so``.  PyTorch supplies device memory and the stream.

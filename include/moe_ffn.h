@@ -1,5 +1,5 @@
 /*
- * moe_ffn.h -- C ABI of libmoeffn, the routed 4-bit MoE expert FFN for AMD
+ * moe_ffn.h -- C ABI of libmoeffn, the routed 4-bit (or 8-bit) MoE expert FFN for AMD
  * MI355X (gfx950).
  *
  * The operation (switch-GLU expert FFN with a tanh-GELU product):
@@ -203,9 +203,10 @@ typedef struct {
 moe_status moe_ffn_workspace_layout(const moe_problem* p, moe_ws_layout* layout);
 
 /*
- * Full expert FFN forward: route/sort/tile, gathered 4-bit gate|up matmul with
- * the fused GeGLU product, gathered 4-bit down matmul with the weighted
- * unsort, and the combine back to tokens.
+ * Full expert FFN forward: route/sort/tile, gathered quantised gate|up matmul
+ * with the fused GeGLU product, gathered quantised down matmul with the
+ * weighted unsort, and the combine back to tokens (codes of p->bits bits in
+ * groups of p->group_size columns).
  *
  *   x            bf16 [T, H]        16-byte aligned
  *   topk_ids     int32 [T, k]

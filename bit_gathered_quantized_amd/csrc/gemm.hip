@@ -1,4 +1,4 @@
-// Gathered 4-bit quantised matmuls over expert tiles.
+// Gathered 4-bit (or 8-bit) quantised matmuls over expert tiles.
 //
 //   gate|up  h[s, n] = act(x[tok(s)] . Wg[e, n]) * (x[tok(s)] . Wu[e, n]),
 //            act = gelu_tanh (GeGLU), or silu with MOE_F_SWIGLU (SwiGLU)
@@ -11,9 +11,10 @@
 // standing").  Design for gfx950:
 //
 //  * Every product runs on v_mfma_f32_16x16x32_bf16.  The weight operand is
-//    the 4-bit code itself, exactly (codes_as_bf16: 16 + q), decoded in
-//    registers.  Per 64-column group the fp32 accumulator takes s * P (one
-//    FMA per output per group); the rest, sum_g (b - 16 s) X, is itself a
+//    the code itself, exactly (codes_as_bf16: 16 + q for 4-bit codes,
+//    bytes_as_bf16: q for 8-bit ones), decoded in registers.  Per group (a
+//    chain of 32 or 64 columns) the fp32 accumulator takes s * P (one FMA per
+//    output per chain); the rest, sum_g (b - 16 s) X, is itself a
 //    small contraction over groups, run on MFMAs once per tile after the
 //    groups, with both factors split into bf16 hi + lo.  Rounding dequantised
 //    weights to bf16 instead would cost the accuracy the fp32 path needs.
@@ -424,8 +425,8 @@ struct WaveW {
 
 // Scale and bias rows of NCB blocks of 16 weight rows, copied raw into a
 // wave's LDS tables (entry (row, g) at row * G + g).  A block's 16 rows are
-// contiguous, 32 G bytes, so they move as 16-byte pieces in row order: two
-// loads per lane and table cover G <= 64.  The loads are issued early and the
+// contiguous, 32 G bytes, so they move as 16-byte pieces in row order: NP
+// loads per lane and table cover G <= 32 NP.  The loads are issued early and the
 // stores made later, so their latency overlaps the first weight loads.
 // kBias = false: scales only (the wide paths read biases from HBM at the end).
 template <int NCB, bool kBias = true, int NP = 2>
@@ -581,7 +582,7 @@ __global__ __launch_bounds__(64, GS == 32 || BITS == 8 ? 2 : 3) void moe_gateup_
     };
     // the loop runs full chunks only, U per trip (a multiple of the ring and
     // of the two activation buffers); the rest (at most U chunks, the last one
-    // a single group when G is odd) follows
+    // possibly a half chunk of 64 columns) follows
     constexpr int U = RING % 2 == 0 ? RING : 2 * RING;
     int c0 = 0;
     for (; c0 + U <= nfull; c0 += U) {
@@ -787,8 +788,8 @@ __global__ __launch_bounds__(64, kF32H || GS == 32 || BITS == 8 ? 2 : 3) void mo
 }
 
 // ============================================================= wide paths
-// Tiles of 17..96 rows (17..64 with an fp32 h); RB = 16-row blocks.
-// The activation tile (RB*16 rows) is staged in LDS in chunks of 2 groups
+// Tiles of 17..64 rows (17..32 with an fp32 h or 8-bit codes); RB = 16-row
+// blocks.  The activation tile (RB*16 rows) is staged in LDS in chunks of 128 columns
 // (NBUF buffers); an LDS row is 16 pieces of 16 bytes plus 16 bytes of
 // padding, so the 16 rows of a fragment read fall on distinct banks.  Each
 // wave owns 4 blocks of 16 weight rows, moved through its own LDS buffer.
@@ -1038,8 +1039,8 @@ __device__ __forceinline__ void wide_bias(WideSmem<RB, P, NBUF, MAXG, BITS>& sm,
 
 // gate|up wide, column block `by` of 128 h columns (ceil(I / 128) blocks).  Wave w owns h columns
 // n0 + 32 w + [0, 32): weight blocks 0/1 = gate columns +0/+16, blocks 2/3 =
-// the matching up columns.  Waves {0,1} cover 64-column group 2*by of h,
-// waves {2,3} group 2*by + 1.
+// the matching up columns.  Waves {0,1} cover h columns 128 by + [0, 64),
+// waves {2,3} the next 64.
 template <int GS, int RB, int MAXG, bool kF32H, int BITS>
 __device__ __forceinline__ void gateup_wide(const FfnArgs& a, WideSmem<RB, 1, 2, MAXG, BITS>& sm, int e,
                                             int row_begin, int rows, int by) {

@@ -435,8 +435,20 @@ def test_8bit_shapes_full(oracle_lib, gs, shape, fp32):
             fp32)
 
 
-def test_8bit_swiglu(oracle_lib):
-    compare(oracle_lib, ms.make_problem(8, 256, 128, 64, 2, seed=9, bits=8, name="tiny-8bit"), False, swiglu=True)
+@pytest.mark.parametrize("fp32", [False, True])
+def test_8bit_swiglu(oracle_lib, fp32):
+    compare(oracle_lib, ms.make_problem(8, 256, 128, 64, 2, seed=9, bits=8, name="tiny-8bit"), fp32, swiglu=True)
+
+
+@pytest.mark.parametrize("gs,I", [(32, 704), (128, 768)])
+@pytest.mark.parametrize("fp32", [False, True])
+def test_8bit_other_group_sizes_production_shape(oracle_lib, gs, I, fp32):
+    """8-bit codes at group sizes 32 and 128: decode in full, 4096 assignments
+    sampled."""
+    compare(oracle_lib, ms.make_problem(128, 2816, I, 8, 8, seed=gs + 5, gs=gs, bits=8,
+                                        name=f"decode-8bit-gs{gs}"), fp32)
+    p = ms.make_problem(128, 2816, I, 512, 8, seed=gs + 6, gs=gs, bits=8, name=f"prefill4k-8bit-gs{gs}")
+    compare(oracle_lib, p, fp32, tokens=sample_tokens(p, n=12))
 
 
 def test_8bit_large_batch_sampled(oracle_lib):

@@ -270,6 +270,50 @@ def extra_legs(args, p, sets, prob, ws, out, stream):
     sec = timed_loop(lambda i: graphs[i % len(graphs)].replay(), steps)
     res["graph_forward"] = dict(ms_per_step=round(sec * 1e3, 5),
                                 assignments_per_s=round(A / sec, 1))
+    if args.bits == 4 and args.group_size == 64 and not args.intermediate:
+        res["other_geometries"] = geometry_legs(args, p, steps, stream)
+    return res
+
+
+def geometry_legs(args, p, steps, stream):
+    """The same tokens and routing with weights of the other geometries: 8-bit
+    codes, and 4-bit codes in groups of 32 and 128 columns (I rounded up to a
+    multiple of 128 there).  Two copies of the weights are rotated."""
+    import numpy as np
+    import torch
+
+    import bit_gathered_quantized_amd as bgq
+    import moe_synth as ms
+
+    c = ms.CONFIGS[args.workload]
+    A = p.T * p.k
+    res = {}
+    for bits, gs in ((8, 64), (4, 32), (4, 128)):
+        I = -(-p.I // gs) * gs
+        q = ms.make_problem(p.E, p.H, I, p.T, p.k, seed=0, router=c["router"], gs=gs, bits=bits,
+                            name=args.workload)
+        assert np.array_equal(q.topk_ids, p.topk_ids)
+
+        def t(a, dt):
+            return torch.from_numpy(np.ascontiguousarray(a).view(dt)).cuda()
+        sets = []
+        for _ in range(2):
+            sets.append([t(q.x, np.int16).view(torch.bfloat16), t(q.topk_ids, np.int32),
+                         t(q.topk_weights, np.float32), t(q.w_gateup, np.int32), t(q.s_gateup, np.int16),
+                         t(q.b_gateup, np.int16), t(q.w_down, np.int32), t(q.s_down, np.int16),
+                         t(q.b_down, np.int16)])
+        prob = bgq.problem(q.T, q.k, q.E, q.H, q.I, 0, group_size=gs, bits=bits)
+        ws = torch.empty(bgq.workspace_bytes(prob), dtype=torch.uint8, device="cuda")
+        out = torch.empty((q.T, q.H), dtype=torch.bfloat16, device="cuda")
+
+        def step(i):
+            bgq.expert_ffn_forward(*sets[i % 2], out=out, workspace=ws, stream=stream)
+        for i in range(3):
+            step(i)
+        sec = timed_loop(step, steps)
+        res[f"bits{bits}_gs{gs}"] = dict(I=I, ms_per_step=round(sec * 1e3, 5),
+                                         assignments_per_s=round(A / sec, 1))
+        del sets, ws, out
     return res
 
 

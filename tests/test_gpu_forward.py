@@ -300,12 +300,19 @@ def test_rows_bitwise_independent_of_tile_path(oracle_lib, fp32, gs, bits):
 
 
 @pytest.mark.parametrize("name,fp32", [("prefill16k", False), ("prefill4k", True),
-                                        ("decode", False), ("tiny", False)])
+                                        ("decode", False), ("tiny", False), ("prefill16k-8bit", False)])
 def test_forward_tile_lists(oracle_lib, name, fp32):
     """The forward routes into two lists, each in expert order: experts of
-    more than 16 rows cut into near-equal tiles, and experts of 1..16 rows.
-    Bit-exact against the oracle's plain statement of that rule."""
-    p = ms.make_config(name)
+    more than 16 rows cut into near-equal tiles (of at most 64 rows, or 32 with
+    an fp32 h or 8-bit codes), and experts of 1..16 rows.  Bit-exact against the
+    oracle's plain statement of that rule."""
+    if name == "prefill16k-8bit":
+        c = ms.CONFIGS["prefill16k"]
+        p = ms.make_problem(c["E"], c["H"], c["I"], c["T"], c["k"], seed=0, router=c["router"], bits=8,
+                            name=name)
+        assert lay_bm_big(p) == 32
+    else:
+        p = ms.make_config(name)
     _, ws, lay = run_forward(p, fp32=fp32)
     counts, offsets, _, _, _ = oracle_lib.route(p.topk_ids, p.E)
     rw, rs = oracle_lib.forward_tiles(counts, offsets, lay.bm_big, lay.bm_small,
@@ -475,4 +482,8 @@ def test_other_geometries_invalid_ids_and_empty(oracle_lib, gs, bits):
     e = ms.make_problem(4, 256, 128, 0, 2, seed=0, gs=gs, bits=bits, name="empty")
     out, _, _ = run_forward(e)
     assert out.shape == (0, 256)
+
+
+def lay_bm_big(p):
+    return bgq.workspace_layout(bgq.problem(p.T, p.k, p.E, p.H, p.I, 0, group_size=p.gs, bits=p.bits)).bm_big
 

@@ -19,7 +19,7 @@ ARCH = "gfx950"
 
 # -packed-fp32-ops: hipcc must not form packed fp32 instructions on its own.
 HIPCC_FLAGS = [
-    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     "-Wall", "-Wextra", "-fno-fast-math",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     # MFMA results straight into VGPRs: the per-group scale FMA reads them
@@ -44,10 +44,7 @@ def source_digest() -> str:
     return h.hexdigest()[:16]
 
 
-def build(verbose: bool = False) -> str:
-    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-    tmp = LIB_PATH + ".tmp"
-    cmd = [hipcc, *HIPCC_FLAGS, f"-I{INCLUDE}", f"-I{CSRC}", *sources(), "-o", tmp]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -57,6 +54,25 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
     if err.strip() and verbose:
         print(err, file=sys.stderr)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source to an object (in parallel), then link the shared
+    library.  Objects go to a temporary folder; only the .so stays in-tree."""
+    import tempfile
+    from concurrent.futures import ThreadPoolExecutor
+    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+    tmp = LIB_PATH + ".tmp"
+    with tempfile.TemporaryDirectory(prefix="moeffn_build_") as d:
+        objs, cmds = [], []
+        for src in sources():
+            obj = os.path.join(d, os.path.basename(src) + ".o")
+            objs.append(obj)
+            cmds.append([hipcc, *HIPCC_FLAGS, "-c", f"-I{INCLUDE}", f"-I{CSRC}", src, "-o", obj])
+        jobs = max(1, min(len(cmds), os.cpu_count() or 1, 16))
+        with ThreadPoolExecutor(jobs) as ex:
+            list(ex.map(lambda c: _run(c, verbose), cmds))
+        _run([hipcc, *HIPCC_FLAGS, "-shared", *objs, "-o", tmp], verbose)
     os.replace(tmp, LIB_PATH)
     return LIB_PATH
 

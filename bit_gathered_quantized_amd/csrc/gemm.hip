@@ -25,7 +25,7 @@
 //    rows (16-byte coalesced loads, turned into operand order through a
 //    small LDS buffer) with RING chunks of loads in flight, and issues the
 //    MFMA chains of a chunk's groups and blocks together.
-//  * Wide path, tiles of 17..64 rows (prefill): the activation tile is
+//  * Wide path, tiles of up to 64 rows (prefill): the activation tile is
 //    staged in LDS, double-buffered; each wave owns 4 column blocks and all
 //    row blocks, so a decoded weight word feeds every row block and an LDS
 //    activation fragment feeds 4 MFMAs; weights go through a per-wave LDS
@@ -42,8 +42,8 @@
 //  * Each path reads its own tile list (experts of more than 16 rows, cut
 //    into near-equal tiles; experts of 1..16 rows).  Grids are sized from
 //    bounds the host knows (at most one skinny tile per expert, at most
-//    A / 17 wide tiles) and workgroups past the list's device-side count exit
-//    at once: the host never reads it back.
+//    max_tiles wide tiles) and workgroups past the list's device-side count
+//    exit at once: the host never reads it back.
 #include "moe_internal.h"
 
 #include <type_traits>
@@ -788,8 +788,8 @@ __global__ __launch_bounds__(64, kF32H || GS == 32 || BITS == 8 ? 2 : 3) void mo
 }
 
 // ============================================================= wide paths
-// Tiles of 17..64 rows (17..32 with an fp32 h or 8-bit codes); RB = 16-row
-// blocks.  The activation tile (RB*16 rows) is staged in LDS in chunks of 128 columns
+// Tiles of at most 64 rows (32 with an fp32 h or 8-bit codes; 16 or more, as
+// an expert of 33 rows gives 17 + 16 at 32); RB = 16-row blocks.  The activation tile (RB*16 rows) is staged in LDS in chunks of 128 columns
 // (NBUF buffers); an LDS row is 16 pieces of 16 bytes plus 16 bytes of
 // padding, so the 16 rows of a fragment read fall on distinct banks.  Each
 // wave owns 4 blocks of 16 weight rows, moved through its own LDS buffer.
@@ -1250,17 +1250,19 @@ __global__ __launch_bounds__(kThreads, (kWideWgsPerCu<DownWideSmem<kF32H, MAXG, 
 
 }  // namespace
 
-// Grid widths: a skinny tile is a whole expert of <= 16 rows (at most one per
-// expert, at least one row), or with skinny_only a piece of <= 16 rows of
-// one (at most one short piece per expert); a wide tile has more than
-// kBmSmall rows.
+// Grid widths, from bounds that hold for every routing.  A skinny tile is a
+// whole expert of <= 16 rows (at most one per expert), or with skinny_only a
+// piece of <= 16 rows of one (ceil(c / 16) <= floor(c / 16) + 1 pieces for an
+// expert of c rows).  The wide list holds ceil(c / bm_big) tiles per expert of
+// more than 16 rows, at most floor(A / bm_big) + min(E, A) = max_tiles in all
+// (a sum of floors never exceeds the floor of the sum).  The height of a wide
+// tile is no bound: with bm_big = 32 an expert of 33 rows gives tiles of 17
+// and 16 rows.
 static int skinny_grid(const FfnArgs& a) {
     const int A = a.T * a.k;
     return min(a.max_skinny, min(a.E, A) + (a.skinny_only ? A / kBmSmall : 0));
 }
-static int wide_grid(const FfnArgs& a) {
-    return a.skinny_only ? 0 : min(a.max_tiles, a.T * a.k / (kBmSmall + 1));
-}
+static int wide_grid(const FfnArgs& a) { return a.skinny_only ? 0 : a.max_tiles; }
 
 // No tile can be wide: nothing to launch, but the timing events still mark
 // the (empty) interval.

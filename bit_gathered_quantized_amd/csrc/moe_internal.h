@@ -22,8 +22,9 @@ constexpr int kRouteWaves = kRouteThreads / 64;
 
 // Tile heights used by the forward's own routing: an expert of at most 16
 // rows is one skinny tile; a larger one is cut into ceil(rows / 64) wide
-// tiles of near-equal height (17..64 rows each), so no expert leaves a short
-// tail that reads its weights once more.  64 rows = 4 row blocks per wave
+// tiles of near-equal height (17..64 rows each; with 32, 16..32: an expert of
+// 33 rows gives 17 + 16), so no expert leaves a short tail that reads its
+// weights once more.  64 rows = 4 row blocks per wave
 // keeps the wide kernels within 256 vector registers (32 rows with fp32
 // intermediates).
 constexpr int kBmBig = 64;

@@ -31,7 +31,8 @@ Recipe (one numpy ``default_rng(seed)`` per problem, draws in this order):
   3. gate|up words, then gate|up scales bf16(|N(0, 0.02)|);
   4. down words, then down scales bf16(|N(0, 0.02)|);
   biases are -8 * scale (exact in bf16), so every dequantised weight is
-  scale * (q - 8).
+  scale * (q - 8); or, with bias="independent", bf16(N(0, 0.05)) drawn right
+  after each scale array (the general affine format).
 
 Routing: softmax over all E experts in float32, the k largest logits (ties to
 the lower expert id, per-token order by descending logit), weights divided by
@@ -107,6 +108,7 @@ class Problem:
     b_down: np.ndarray
     logits: Optional[np.ndarray] = field(default=None, repr=False)
     bits: int = 4
+    bias: str = "centred"
 
     @property
     def A(self) -> int:
@@ -151,22 +153,34 @@ def _router_logits(rng: np.random.Generator, router: str, T: int, E: int) -> np.
     raise ValueError(f"unknown router {router!r}")
 
 
-def _scales(rng: np.random.Generator, shape, bits: int = 4):
-    """Scales |N(0, std)| and biases -2^(bits-1) * scale (centred codes); 8-bit
-    scales are 16x smaller so that the weights keep the 4-bit spread."""
+BIAS_STD = 0.05
+
+
+def _scales(rng: np.random.Generator, shape, bits: int = 4, bias: str = "centred"):
+    """Scales |N(0, std)|; 8-bit scales are 16x smaller so that the weights
+    keep the 4-bit spread.  Biases: "centred" -2^(bits-1) * scale (exact), or
+    "independent" bf16(N(0, 0.05)) drawn right after the scales, unrelated to
+    them (the general affine format: any bias with any scale)."""
     std = SCALE_STD if bits == 4 else SCALE_STD / 16
     s = f32_to_bf16_bits(np.abs(rng.normal(0.0, std, size=shape)).astype(np.float32))
-    b = f32_to_bf16_bits(bf16_bits_to_f32(s) * np.float32(-(2 ** (bits - 1))))
+    if bias == "centred":
+        b = f32_to_bf16_bits(bf16_bits_to_f32(s) * np.float32(-(2 ** (bits - 1))))
+    elif bias == "independent":
+        b = f32_to_bf16_bits(rng.normal(0.0, BIAS_STD, size=shape).astype(np.float32))
+    else:
+        raise ValueError(f"unknown bias mode {bias!r}")
     return s, b
 
 
 def make_problem(E: int, H: int, I: int, T: int, k: int, seed: int = 0,
                  router: str = "normal", gs: int = GROUP_SIZE, name: str = "custom",
                  topk_ids: Optional[np.ndarray] = None,
-                 topk_weights: Optional[np.ndarray] = None, bits: int = 4) -> Problem:
+                 topk_weights: Optional[np.ndarray] = None, bits: int = 4,
+                 bias: str = "centred") -> Problem:
     """Draw one problem.  ``topk_ids``/``topk_weights`` override the router draw
     (the logits are still drawn so the rest of the stream is unchanged).
-    ``bits``: 4 (8 codes per uint32 word) or 8 (4 codes per word)."""
+    ``bits``: 4 (8 codes per uint32 word) or 8 (4 codes per word).
+    ``bias``: "centred" (-2^(bits-1) * scale) or "independent" (see _scales)."""
     if H % 8 or I % 8 or H % gs or I % gs:
         raise ValueError("H and I must be multiples of 8 and of the group size")
     if bits not in (4, 8):
@@ -184,13 +198,13 @@ def make_problem(E: int, H: int, I: int, T: int, k: int, seed: int = 0,
         w = np.ascontiguousarray(topk_weights, dtype=np.float32).reshape(T, k)
     x = f32_to_bf16_bits(rng.standard_normal((T, H), dtype=np.float32))
     w_gu = rng.integers(0, 2**32, size=(E, 2 * I, H * bits // 32), dtype=np.uint32)
-    s_gu, b_gu = _scales(rng, (E, 2 * I, H // gs), bits)
+    s_gu, b_gu = _scales(rng, (E, 2 * I, H // gs), bits, bias)
     w_d = rng.integers(0, 2**32, size=(E, H, I * bits // 32), dtype=np.uint32)
-    s_d, b_d = _scales(rng, (E, H, I // gs), bits)
+    s_d, b_d = _scales(rng, (E, H, I // gs), bits, bias)
     return Problem(name=name, seed=seed, E=E, H=H, I=I, T=T, k=k, gs=gs, x=x,
                    topk_ids=ids, topk_weights=w, w_gateup=w_gu, s_gateup=s_gu,
                    b_gateup=b_gu, w_down=w_d, s_down=s_d, b_down=b_d, logits=logits,
-                   bits=bits)
+                   bits=bits, bias=bias)
 
 
 def make_config(name: str, seed: int = 0) -> Problem:

@@ -60,6 +60,10 @@ def _load():
         lib.oracle_router_topk.restype = ctypes.c_int
         lib.oracle_ffn_tokens.argtypes = [i32] * 7 + [P] * 9 + [P, i32, i32, P, P, P]
         lib.oracle_ffn_tokens.restype = ctypes.c_int
+        lib.oracle_ffn_all.argtypes = [i32] * 7 + [P] * 9 + [i32, P, P, P]
+        lib.oracle_ffn_all.restype = ctypes.c_int
+        lib.oracle_down_rows.argtypes = [i32] * 5 + [P] * 4 + [i64] + [P] * 3
+        lib.oracle_down_rows.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -197,3 +201,46 @@ def ffn_tokens(p, tokens=None, want_h: bool = True, want_y: bool = True,
     if rc != 0:
         raise ValueError(f"oracle_ffn_tokens failed ({rc})")
     return dict(h=h, y=y, out=out, tokens=tokens)
+
+
+def ffn_all(p, want_h: bool = True, want_y: bool = True, act: str = "gelu"):
+    """Expert FFN for every assignment of problem ``p``, organised by expert
+    (each expert dequantised once): the same sums in the same order as
+    :func:`ffn_tokens`, hence the same bits, fast enough for a whole 16384-
+    assignment batch.
+
+    Returns dict with h [T*k, I] and y [T*k, H] (unweighted) in flat order
+    a = t*k + j, and out [T, H].
+    """
+    A = p.T * p.k
+    h = np.zeros((A, p.I)) if want_h else None
+    y = np.zeros((A, p.H)) if want_y else None
+    out = np.zeros((p.T, p.H))
+    arrs = [np.ascontiguousarray(a) for a in (p.x, p.topk_ids, p.topk_weights, p.w_gateup,
+                                              p.s_gateup, p.b_gateup, p.w_down, p.s_down,
+                                              p.b_down)]
+    assert arrs[1].dtype == np.int32 and arrs[2].dtype == np.float32
+    rc = _load().oracle_ffn_all(p.T, p.k, p.E, p.H, p.I, p.gs, p.bits, *[_ptr(a) for a in arrs],
+                                ACTIVATIONS[act], _ptr(h), _ptr(y), _ptr(out))
+    if rc != 0:
+        raise ValueError(f"oracle_ffn_all failed ({rc})")
+    return dict(h=h, y=y, out=out)
+
+
+def down_rows(p, experts: np.ndarray, h: np.ndarray, want_abs: bool = True):
+    """The down projection of problem ``p``'s weights for rows with a given h:
+    y[r] = W_d[experts[r]] . h[r] (unweighted, fp64, ascending-n sums), and
+    yabs[r] = sum_n |W_d[experts[r], :, n] h[r, n]|.  Returns (y, yabs)."""
+    experts = np.ascontiguousarray(experts, dtype=np.int32).ravel()
+    h = np.ascontiguousarray(h, dtype=np.float64)
+    n = experts.size
+    assert h.shape == (n, p.I)
+    y = np.zeros((max(n, 1), p.H))
+    ya = np.zeros((max(n, 1), p.H)) if want_abs else None
+    rc = _load().oracle_down_rows(p.E, p.H, p.I, p.gs, p.bits, _ptr(np.ascontiguousarray(p.w_down)),
+                                  _ptr(np.ascontiguousarray(p.s_down)),
+                                  _ptr(np.ascontiguousarray(p.b_down)), _ptr(experts), n, _ptr(h),
+                                  _ptr(y), _ptr(ya))
+    if rc != 0:
+        raise ValueError(f"oracle_down_rows failed ({rc})")
+    return y[:n], (ya[:n] if ya is not None else None)

@@ -39,6 +39,10 @@
  *           "Already on main": weightedExpertSum; PR #4 "Measured standing":
  *           the direct weighted unsort back to token order).
  *
+ * oracle_ffn_all computes the same sums for a whole batch, expert by expert
+ * (each expert's matrices dequantised once), in the same order, so its
+ * results are the same bits as oracle_ffn_tokens'.
+ *
  * Expert ids outside [0, E) are not routed: they are counted, placed after all
  * valid rows in the sorted order (ascending a), get no tile, and contribute
  * zero to the combine.
@@ -261,6 +265,156 @@ int oracle_ffn_tokens(int32_t T, int32_t k, int32_t E, int32_t H, int32_t I,
         }
     }
     free(yy);
+    return ORACLE_OK;
+}
+
+/*
+ * The same expert FFN for every assignment of the batch, organised by expert
+ * so that a large batch finishes in seconds: each expert's matrices are
+ * dequantised once (W = S * q + B, the values oracle_weight gives), then
+ * every dot product is the same plain sum over the columns in ascending
+ * order as in oracle_ffn_tokens, so the results are bit-identical to it.
+ * Only the loop order differs: for each expert, output neuron n runs over
+ * all of the expert's assignments (ascending a) while row n of the matrix is
+ * at hand.
+ *   h   [T*k, I]  flat order a = t*k + j (NULL to skip)
+ *   y   [T*k, H]  unweighted expert output, flat order (NULL to skip)
+ *   out [T, H]    sum_j w[t, j] * y[t*k+j] (NULL to skip)
+ * Rows of an assignment with an out-of-range expert id are zero.
+ */
+int oracle_ffn_all(int32_t T, int32_t k, int32_t E, int32_t H, int32_t I, int32_t gs,
+                   int32_t bits, const uint16_t* x, const int32_t* ids, const float* w,
+                   const uint32_t* w_gu, const uint16_t* s_gu, const uint16_t* b_gu,
+                   const uint32_t* w_d, const uint16_t* s_d, const uint16_t* b_d,
+                   int32_t act, double* h, double* y, double* out) {
+    if (act != 0 && act != 1) return ORACLE_ERR_ARG;
+    if (T < 0 || k <= 0 || E <= 0 || H <= 0 || I <= 0 || gs <= 0 || H % gs ||
+        I % gs || H % 8 || I % 8 || (bits != 4 && bits != 8))
+        return ORACLE_ERR_ARG;
+    const int64_t A = (int64_t)T * k;
+    const size_t nA = (size_t)(A > 0 ? A : 1);
+    double* xv = (double*)malloc(sizeof(double) * (size_t)(T > 0 ? T : 1) * (size_t)H);
+    double* hh = (double*)calloc(nA * (size_t)I, sizeof(double));
+    double* yy = (double*)calloc(nA * (size_t)H, sizeof(double));
+    double* wgu = (double*)malloc(sizeof(double) * 2 * (size_t)I * (size_t)H);
+    double* wd = (double*)malloc(sizeof(double) * (size_t)H * (size_t)I);
+    int64_t* rows = (int64_t*)malloc(sizeof(int64_t) * nA);
+    if (!xv || !hh || !yy || !wgu || !wd || !rows) {
+        free(xv); free(hh); free(yy); free(wgu); free(wd); free(rows);
+        return ORACLE_ERR_ALLOC;
+    }
+    for (int64_t i = 0; i < (int64_t)T * H; ++i) xv[i] = bf16_value(x[i]);
+    for (int32_t e = 0; e < E; ++e) {
+        int64_t n_rows = 0;
+        for (int64_t a = 0; a < A; ++a)
+            if (ids[a] == e) rows[n_rows++] = a;
+        if (n_rows == 0) continue;
+#pragma omp parallel for schedule(static)
+        for (int64_t n = 0; n < 2 * (int64_t)I; ++n)
+            for (int64_t c = 0; c < H; ++c)
+                wgu[n * H + c] = oracle_weight(w_gu, s_gu, b_gu, 2 * (int64_t)I, H, gs, bits, e, n, c);
+#pragma omp parallel for schedule(static)
+        for (int64_t m = 0; m < H; ++m)
+            for (int64_t c = 0; c < I; ++c)
+                wd[m * I + c] = oracle_weight(w_d, s_d, b_d, H, I, gs, bits, e, m, c);
+#pragma omp parallel for schedule(dynamic, 8)
+        for (int64_t n = 0; n < I; ++n) {
+            const double* wg = wgu + n * H;
+            const double* wu = wgu + (I + n) * H;
+            for (int64_t r = 0; r < n_rows; ++r) {
+                const int64_t a = rows[r];
+                const double* xr = xv + (a / k) * H;
+                double g = 0.0, u = 0.0;
+                for (int64_t c = 0; c < H; ++c) g += wg[c] * xr[c];
+                for (int64_t c = 0; c < H; ++c) u += wu[c] * xr[c];
+                hh[a * I + n] = (act ? oracle_silu(g) : oracle_gelu_tanh(g)) * u;
+            }
+        }
+#pragma omp parallel for schedule(dynamic, 16)
+        for (int64_t m = 0; m < H; ++m) {
+            const double* wm = wd + m * I;
+            for (int64_t r = 0; r < n_rows; ++r) {
+                const int64_t a = rows[r];
+                const double* hr = hh + a * I;
+                double acc = 0.0;
+                for (int64_t c = 0; c < I; ++c) acc += wm[c] * hr[c];
+                yy[a * H + m] = acc;
+            }
+        }
+    }
+    if (out) {
+#pragma omp parallel for schedule(static)
+        for (int64_t t = 0; t < T; ++t) {
+            for (int64_t m = 0; m < H; ++m) {
+                double acc = 0.0;
+                for (int64_t j = 0; j < k; ++j) {
+                    const int32_t e = ids[t * k + j];
+                    if (e < 0 || e >= E) continue;
+                    acc += (double)w[t * k + j] * yy[(t * k + j) * H + m];
+                }
+                out[t * H + m] = acc;
+            }
+        }
+    }
+    if (h) memcpy(h, hh, sizeof(double) * (size_t)A * (size_t)I);
+    if (y) memcpy(y, yy, sizeof(double) * (size_t)A * (size_t)H);
+    free(xv); free(hh); free(yy); free(wgu); free(wd); free(rows);
+    return ORACLE_OK;
+}
+
+/*
+ * The down projection alone, for rows whose h is given: row r (expert
+ * experts[r]) gets y[r, m] = sum_n W_d[e, m, n] * h[r, n], summed over n in
+ * ascending order, and yabs[r, m] = sum_n |W_d[e, m, n] * h[r, n]| (the sum of
+ * the terms' magnitudes, which bounds the rounding error of any fp32
+ * evaluation of the same sum; NULL to skip).  Rows of an out-of-range expert
+ * are zero.
+ */
+int oracle_down_rows(int32_t E, int32_t H, int32_t I, int32_t gs, int32_t bits,
+                     const uint32_t* w_d, const uint16_t* s_d, const uint16_t* b_d,
+                     const int32_t* experts, int64_t n_rows, const double* h, double* y,
+                     double* yabs) {
+    if (E <= 0 || H <= 0 || I <= 0 || gs <= 0 || I % gs || I % 8 || n_rows < 0 ||
+        (bits != 4 && bits != 8) || (n_rows > 0 && (!experts || !h || !y)))
+        return ORACLE_ERR_ARG;
+    double* wd = (double*)malloc(sizeof(double) * (size_t)H * (size_t)I);
+    int64_t* rows = (int64_t*)malloc(sizeof(int64_t) * (size_t)(n_rows > 0 ? n_rows : 1));
+    if (!wd || !rows) {
+        free(wd);
+        free(rows);
+        return ORACLE_ERR_ALLOC;
+    }
+    for (int64_t i = 0; i < n_rows * H; ++i) {
+        y[i] = 0.0;
+        if (yabs) yabs[i] = 0.0;
+    }
+    for (int32_t e = 0; e < E; ++e) {
+        int64_t cnt = 0;
+        for (int64_t r = 0; r < n_rows; ++r)
+            if (experts[r] == e) rows[cnt++] = r;
+        if (cnt == 0) continue;
+#pragma omp parallel for schedule(static)
+        for (int64_t m = 0; m < H; ++m)
+            for (int64_t c = 0; c < I; ++c)
+                wd[m * I + c] = oracle_weight(w_d, s_d, b_d, H, I, gs, bits, e, m, c);
+#pragma omp parallel for schedule(dynamic, 16)
+        for (int64_t m = 0; m < H; ++m) {
+            const double* wm = wd + m * I;
+            for (int64_t i = 0; i < cnt; ++i) {
+                const int64_t r = rows[i];
+                const double* hr = h + r * I;
+                double acc = 0.0, mag = 0.0;
+                for (int64_t c = 0; c < I; ++c) {
+                    acc += wm[c] * hr[c];
+                    mag += fabs(wm[c] * hr[c]);
+                }
+                y[r * H + m] = acc;
+                if (yabs) yabs[r * H + m] = mag;
+            }
+        }
+    }
+    free(wd);
+    free(rows);
     return ORACLE_OK;
 }
 

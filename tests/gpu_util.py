@@ -96,10 +96,65 @@ def ws_h(ws, lay, p, fp32):
 
 def ws_y_rows(ws, lay, p, rows):
     """Rows (flat assignment indices) of the weighted y buffer."""
+    rows = np.asarray(rows, dtype=np.int64)
+    A = p.T * p.k
+    if rows.size > A // 4:
+        return ws_view(ws, lay.y, A * p.H, np.float32).reshape(A, p.H)[rows].astype(np.float64)
     out = np.zeros((len(rows), p.H))
     for i, a in enumerate(rows):
         out[i] = ws_view(ws, lay.y + int(a) * p.H * 4, p.H, np.float32)
     return out
+
+
+def dense_codes(P: np.ndarray, bits: int) -> np.ndarray:
+    """Codes of packed words, through numpy's little-endian byte view."""
+    b = np.ascontiguousarray(P).astype("<u4").view(np.uint8)
+    if bits == 8:
+        return b.reshape(*P.shape[:-1], P.shape[-1] * 4)
+    return np.stack([b & 0x0F, b >> 4], axis=-1).reshape(*P.shape[:-1], P.shape[-1] * 8)
+
+
+def bias_magnitude(p, experts, h):
+    """sum_g (|B[m, g]| + off |S[m, g]|) sum_{n in g} |h[n]| per row and output
+    column, with off = 16 for 4-bit codes and 0 for 8-bit ones: the size of
+    the bias contraction the down kernels evaluate, sum_g (B - off S) X_g, with
+    both factors split into bf16 hi + lo."""
+    off = 16.0 if p.bits == 4 else 0.0
+    G = p.I // p.gs
+    out = np.zeros((len(experts), p.H))
+    xa = np.abs(h).reshape(len(experts), G, p.gs).sum(-1)
+    for e in np.unique(experts):
+        if e < 0 or e >= p.E:
+            continue
+        sel = experts == e
+        c = (np.abs(ms.bf16_bits_to_f32(p.b_down[e]).astype(np.float64))
+             + off * np.abs(ms.bf16_bits_to_f32(p.s_down[e]).astype(np.float64)))
+        out[sel] = xa[sel] @ c.T
+    return out
+
+
+# Worst-case relative rounding of the kernels' fp32 sums against the sum of
+# the terms' magnitudes: n * 2^-24 for n <= 1024 terms is below 2^-14, and
+# the bias contraction's bf16 hi + lo factors are each within 2^-17.
+Y_MODEL_REL = 2.0 ** -14
+
+
+def check_y_model(oracle_lib, p, rows, h_gpu, y_gpu, what="y"):
+    """Per-element check of the weighted down output of the given flat rows
+    against the oracle's down projection of the kernel's own h (bf16, or
+    bf16 hi + lo in fp32 mode): |y_gpu - w y_model| <= 2^-14 w (sum_n |W h| +
+    bias magnitude).  Returns (w * y_model, bound) for the valid rows."""
+    ids = p.topk_ids.ravel()[rows]
+    valid = (ids >= 0) & (ids < p.E)
+    w = p.topk_weights.ravel()[rows].astype(np.float64)[:, None]
+    ym, ya = oracle_lib.down_rows(p, np.where(valid, ids, p.E), h_gpu)
+    bound = Y_MODEL_REL * w * (ya + bias_magnitude(p, ids, h_gpu))
+    model = w * ym
+    err = np.abs(y_gpu - model)[valid]
+    worst = float(np.max(err / np.maximum(bound[valid], 1e-300))) if err.size else 0.0
+    log(f"  {what}: per element |y - model| / bound max = {worst:.3g}")
+    assert np.all(err <= bound[valid]), f"{what}: per-element model bound exceeded ({worst})"
+    return model, bound
 
 
 def half_ulp_bf16(v: np.ndarray) -> np.ndarray:

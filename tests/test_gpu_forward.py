@@ -13,40 +13,87 @@ import torch
 
 import bit_gathered_quantized_amd as bgq
 import moe_synth as ms
-from gpu_util import (assert_bf16_close, assert_fp32_close, bf16_excess, dev_arrays,
-                      from_operand_order, log, run_forward, sample_tokens, ws_h, ws_view,
-                      ws_y_rows)
+from gpu_util import (assert_bf16_close, assert_fp32_close, bf16_excess, check_y_model,
+                      dev_arrays, from_operand_order, half_ulp_bf16, log, run_forward,
+                      ws_h, ws_view, ws_y_rows)
 
 pytestmark = pytest.mark.gpu
 
 
-def compare(oracle_lib, p, fp32, tokens=None, swiglu=False):
-    log(f"forward: {p.name} E={p.E} H={p.H} I={p.I} T={p.T} k={p.k} fp32={fp32} "
-        f"swiglu={swiglu} tokens={'all' if tokens is None else len(tokens)}")
-    out, ws, lay = run_forward(p, fp32=fp32, swiglu=swiglu)
-    toks = np.arange(p.T, dtype=np.int32) if tokens is None else tokens
-    ref = oracle_lib.ffn_tokens(p, toks, act="silu" if swiglu else "gelu")
+def production_shape(p):
+    """The five named workloads and every problem of their 128-expert
+    geometry.  There the bf16 rule (2e-2 rms after the half-ulp allowance)
+    holds for the method itself; on small made-up shapes with few slots per
+    token the rounding of h to bf16 alone can reach it (the exact output of
+    the bf16-h model, computed on the CPU, gives the same excess as the
+    kernels), so there the per-element model bound is the gate."""
+    return p.name in ms.CONFIGS or (p.E == 128 and p.H == 2816)
+
+
+def compare(oracle_lib, p, fp32, tokens=None, swiglu=False, run=None):
+    """Run the forward (or `run(p, fp32, swiglu)`, which returns the same
+    (out, ws, layout) triple) and check it against the oracle:
+
+      h    per element: bf16 mode, the half-ulp rounding of the stored bf16
+           value only (excess <= 1e-3 rms); fp32 mode, L2 1e-3;
+      y    per element against the oracle's down projection of the kernel's
+           own h (check_y_model's derived bound), and in fp32 mode L2 1e-3
+           against the oracle's y;
+      out  the bf16 rule (bf16 mode, at the production geometry) or L2 1e-3
+           (fp32 mode) against the oracle, and per element against the
+           combine of the model y (within the y bounds plus the output's
+           own rounding).
+
+    tokens=None compares every token (the oracle's whole-batch entry)."""
+    log(f"forward: {p.name} E={p.E} H={p.H} I={p.I} T={p.T} k={p.k} gs={p.gs} bits={p.bits} "
+        f"bias={p.bias} fp32={fp32} swiglu={swiglu} tokens={'all' if tokens is None else len(tokens)}")
+    if run is None:
+        out, ws, lay = run_forward(p, fp32=fp32, swiglu=swiglu)
+    else:
+        out, ws, lay = run(p, fp32, swiglu)
+    act = "silu" if swiglu else "gelu"
+    if tokens is None:
+        toks = np.arange(p.T, dtype=np.int32)
+        ref = oracle_lib.ffn_all(p, act=act)
+    else:
+        toks = tokens
+        ref = oracle_lib.ffn_tokens(p, toks, act=act)
     rows = (toks[:, None] * p.k + np.arange(p.k)[None, :]).ravel()
     valid = ((p.topk_ids.ravel()[rows] >= 0) & (p.topk_ids.ravel()[rows] < p.E))
     # h: sorted order -> flat order through inv_perm
     A = p.T * p.k
     inv = ws_view(ws, lay.inv_perm, A, np.int32)
     h = ws_h(ws, lay, p, fp32)[inv[rows]]
+    h = np.where(valid[:, None], h, 0.0)
     # y: weighted, flat order
-    y = ws_y_rows(ws, lay, p, rows[valid])
+    y = ws_y_rows(ws, lay, p, rows)
+    ymodel, ybound = check_y_model(oracle_lib, p, rows, h, y)
     yref = (ref["y"] * p.topk_weights.ravel()[rows][:, None])[valid]
     o = out[toks]
     if fp32:
         assert_fp32_close(h[valid], ref["h"][valid], "h")
-        assert_fp32_close(y, yref, "y")
+        assert_fp32_close(y[valid], yref, "y")
         assert_fp32_close(o, ref["out"], "out")
+        own = 2.0 ** -23 * np.abs(o)
     else:
         # h is the bf16 rounding of an fp32 value: only the half-ulp remains
-        assert bf16_excess(h[valid], ref["h"][valid]) <= 1e-3
-        # y is fp32 but built from the bf16 h, whose rounding (2^-9 relative
-        # per element) gives ~1.6e-3 L2-relative; the bar is 2.5x that
-        assert_fp32_close(y, yref, "y (from bf16 h)", tol=4e-3)
-        assert_bf16_close(o, ref["out"], "out")
+        ex = bf16_excess(h[valid], ref["h"][valid])
+        log(f"  h: bf16 excess/rms={ex:.3g}")
+        assert ex <= 1e-3
+        if production_shape(p):
+            assert_bf16_close(o, ref["out"], "out")
+        else:
+            log(f"  out: bf16 excess/rms={bf16_excess(o, ref['out']):.4g} (bar not applied: "
+                f"not the production geometry; the model bound below is)")
+        own = half_ulp_bf16(np.maximum(np.abs(o), 1e-30))
+    # out against the combine of the model y (invalid slots contribute 0)
+    ym = np.where(valid[:, None], ymodel, 0.0).reshape(len(toks), p.k, p.H)
+    yb = np.where(valid[:, None], ybound, 0.0).reshape(len(toks), p.k, p.H)
+    omodel = ym.sum(1)
+    obound = yb.sum(1) + 2.0 ** -22 * np.abs(ym).sum(1) + own + 2.0 * half_ulp_bf16(omodel) * (not fp32)
+    oerr = np.abs(o - omodel)
+    log(f"  out: per element |out - model| / bound max = {float(np.max(oerr / np.maximum(obound, 1e-300))):.3g}")
+    assert np.all(oerr <= obound), "out: per-element model bound exceeded"
     return out
 
 
@@ -86,7 +133,7 @@ def test_forward_route_invalid_ids_large(oracle_lib):
     rng = np.random.default_rng(17)
     ids = rng.integers(-2, E + 3, size=(T, k)).astype(np.int32)
     p = ms.make_problem(E, 256, 128, T, k, seed=19, topk_ids=ids, name="invalid-large")
-    compare(oracle_lib, p, False, tokens=sample_tokens(p, n=40))
+    compare(oracle_lib, p, False)
     _, ws, lay = run_forward(p)
     counts, offsets, operm, oinv, obad = oracle_lib.route(p.topk_ids, p.E)
     nt = ws_view(ws, lay.num_tiles, 4, np.int32)
@@ -144,25 +191,37 @@ def test_small_batch_matches_large(oracle_lib, fp32):
     np.testing.assert_array_equal(ob[:8], oa)
 
 
-# Two GPU memory faults, causes not found by reading the code (every kernel's
-# index arithmetic checks out on the CPU for these workloads), so these cases
-# stay off the GPU until a cause is shown:
-#  * fp32 mode at prefill8k faulted with wide tiles of more than 64 rows; that
-#    path is switched off (fp32 mode now routes 64-row tiles);
-#  * bf16 prefill8k faulted under an experimental loop structure that has been
-#    taken out again (the kernels are back to the version that passed it).
-_FAULTED = pytest.mark.skip(reason="GPU memory fault on this case, cause not yet found")
+# Round-one record: two GPU memory faults at 8192 assignments (prefill8k),
+# fp32 mode in moe_down_wide under a since-removed 128-row tile path and bf16
+# mode under a since-removed loop structure.  No cause has been shown, so
+# these two cases stay off the GPU (skipped).  16384 assignments in fp32 mode
+# never faulted; it runs.
+_FAULTED = pytest.mark.skip(reason="GPU memory fault on this workload in an earlier build; "
+                                   "cause not shown, case kept off the GPU")
 
 
 @pytest.mark.parametrize("name,fp32", [
-    ("prefill4k", False), pytest.param("prefill8k", False, marks=_FAULTED),
-    ("prefill16k", False), ("prefill4k", True),
+    ("prefill4k", False), ("prefill4k", True),
+    pytest.param("prefill8k", False, marks=_FAULTED),
     pytest.param("prefill8k", True, marks=_FAULTED),
-    pytest.param("prefill16k", True, marks=_FAULTED),
+    ("prefill16k", False), ("prefill16k", True),
 ])
-def test_prefill_sampled(oracle_lib, name, fp32):
-    p = ms.make_config(name)
-    compare(oracle_lib, p, fp32, tokens=sample_tokens(p, n=20))
+def test_prefill_all_tokens(oracle_lib, name, fp32):
+    """Every token of the prefill workloads against the oracle's whole-batch
+    entry, in the launch configuration the benchmark times."""
+    compare(oracle_lib, ms.make_config(name), fp32)
+
+
+@pytest.mark.parametrize("name,bits", [("decode", 4), ("decode", 8), ("prefill4k", 4), ("prefill4k", 8)])
+@pytest.mark.parametrize("fp32", [False, True])
+def test_independent_biases(oracle_lib, name, bits, fp32):
+    """Biases drawn independently of the scales (bf16(N(0, 0.05))): the affine
+    term b must enter on its own, not through the scale.  Skinny path
+    (decode) and wide path (4096 assignments), 4- and 8-bit codes."""
+    c = ms.CONFIGS[name]
+    p = ms.make_problem(c["E"], c["H"], c["I"], c["T"], c["k"], seed=41, router=c["router"], bits=bits,
+                        bias="independent", name=f"{name}-indep")
+    compare(oracle_lib, p, fp32)
 
 
 @pytest.mark.parametrize("shape", [
@@ -343,7 +402,7 @@ def test_swiglu_full(oracle_lib, name, fp32):
 @pytest.mark.parametrize("name", ["prefill4k", "prefill16k"])
 def test_swiglu_prefill_sampled(oracle_lib, name):
     p = ms.make_config(name)
-    compare(oracle_lib, p, False, tokens=sample_tokens(p), swiglu=True)
+    compare(oracle_lib, p, False, swiglu=True)
 
 
 # ------------------------------------------------------------- group sizes
@@ -367,7 +426,7 @@ def test_group_size_decode_full(oracle_lib, gs, I, fp32):
 @pytest.mark.parametrize("fp32", [False, True])
 def test_group_size_prefill_sampled(oracle_lib, gs, I, fp32):
     p = ms.make_problem(128, 2816, I, 512, 8, seed=gs, gs=gs, name=f"prefill4k-gs{gs}")
-    compare(oracle_lib, p, fp32, tokens=sample_tokens(p, n=16))
+    compare(oracle_lib, p, fp32)
 
 
 @pytest.mark.parametrize("gs,shape", [
@@ -401,7 +460,7 @@ def test_group_size_32_large_batch_repeatable(oracle_lib):
     c = ms.CONFIGS["prefill16k"]
     p = ms.make_problem(c["E"], c["H"], c["I"], c["T"], c["k"], seed=0, router=c["router"], gs=32,
                         name="prefill16k-gs32")
-    first = compare(oracle_lib, p, False, tokens=sample_tokens(p, n=12))
+    first = compare(oracle_lib, p, False)
     d = dev_arrays(p)
     for _ in range(2):
         again, _, _ = run_forward(p, d=d)
@@ -425,7 +484,7 @@ def test_8bit_decode_full(oracle_lib, fp32):
 @pytest.mark.parametrize("fp32", [False, True])
 def test_8bit_prefill_sampled(oracle_lib, fp32):
     p = ms.make_problem(128, 2816, 704, 512, 8, seed=3, bits=8, name="prefill4k-8bit")
-    compare(oracle_lib, p, fp32, tokens=sample_tokens(p, n=16))
+    compare(oracle_lib, p, fp32)
 
 
 @pytest.mark.parametrize("gs,shape", [
@@ -455,7 +514,7 @@ def test_8bit_other_group_sizes_production_shape(oracle_lib, gs, I, fp32):
     compare(oracle_lib, ms.make_problem(128, 2816, I, 8, 8, seed=gs + 5, gs=gs, bits=8,
                                         name=f"decode-8bit-gs{gs}"), fp32)
     p = ms.make_problem(128, 2816, I, 512, 8, seed=gs + 6, gs=gs, bits=8, name=f"prefill4k-8bit-gs{gs}")
-    compare(oracle_lib, p, fp32, tokens=sample_tokens(p, n=12))
+    compare(oracle_lib, p, fp32)
 
 
 def test_8bit_large_batch_sampled(oracle_lib):
@@ -464,7 +523,7 @@ def test_8bit_large_batch_sampled(oracle_lib):
     c = ms.CONFIGS["prefill16k"]
     p = ms.make_problem(c["E"], c["H"], c["I"], c["T"], c["k"], seed=0, router=c["router"], bits=8,
                         name="prefill16k-8bit")
-    first = compare(oracle_lib, p, False, tokens=sample_tokens(p, n=12))
+    first = compare(oracle_lib, p, False)
     again, _, _ = run_forward(p)
     np.testing.assert_array_equal(again, first)
 
@@ -487,3 +546,20 @@ def test_other_geometries_invalid_ids_and_empty(oracle_lib, gs, bits):
 def lay_bm_big(p):
     return bgq.workspace_layout(bgq.problem(p.T, p.k, p.E, p.H, p.I, 0, group_size=p.gs, bits=p.bits)).bm_big
 
+
+
+@pytest.mark.parametrize("fp32,bits", [(True, 4), (True, 8), (False, 8)])
+def test_every_expert_33_rows(oracle_lib, fp32, bits):
+    """Every expert holds exactly 33 rows.  With 32-row wide tiles (fp32 h or
+    8-bit codes) each is cut into tiles of 17 and 16 rows, so the wide list
+    holds more than A / 17 tiles: every one of them must be launched (all
+    tokens compared)."""
+    E, T, k = 16, 33 * 8, 2
+    ids = (np.arange(T * k, dtype=np.int32) % E).reshape(T, k)
+    p = ms.make_problem(E, 256, 128, T, k, seed=34, topk_ids=ids, bits=bits, name="e33")
+    _, ws, lay = run_forward(p, fp32=fp32)
+    nt = ws_view(ws, lay.num_tiles, 4, np.int32)
+    expect = 2 * E if lay.bm_big == 32 else E
+    log(f"  bm_big={lay.bm_big}: {nt[2]} wide tiles (A / 17 = {T * k // 17})")
+    assert nt[2] == expect and (lay.bm_big == 64 or nt[2] > T * k // 17)
+    compare(oracle_lib, p, fp32)

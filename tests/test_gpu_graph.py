@@ -1,7 +1,7 @@
 """The forward captured in a HIP graph (the analogue of a whole-forward
 compile): every replay, with new inputs copied into the captured buffers and
-eager work and synchronisations between replays, equals the eager forward
-bit for bit.  The forward records no memset, allocates nothing and never
+eager work and synchronisations between replays, matches the oracle on those
+inputs and equals the eager forward bit for bit.  The forward records no memset, allocates nothing and never
 synchronises, so it captures as six kernel nodes."""
 import numpy as np
 import pytest
@@ -9,14 +9,17 @@ import torch
 
 import bit_gathered_quantized_amd as bgq
 import moe_synth as ms
+import dataclasses
+
 from gpu_util import dev_arrays, log
+from test_gpu_forward import compare
 
 pytestmark = pytest.mark.gpu
 
 
 @pytest.mark.parametrize("name,swiglu", [("decode", False), ("prefill4k", True),
                                          ("prefill4k-8bit-gs128", False)])
-def test_graph_replays_match_eager(name, swiglu):
+def test_graph_replays_match_eager(oracle_lib, name, swiglu):
     if name == "prefill4k-8bit-gs128":
         p = ms.make_problem(128, 2816, 768, 512, 8, seed=0, gs=128, bits=8, name=name)
     else:
@@ -54,6 +57,10 @@ def test_graph_replays_match_eager(name, swiglu):
         g.replay()
         torch.cuda.synchronize()
         got = out.clone()
+        q = dataclasses.replace(p, x=x, topk_ids=ids, topk_weights=w, name=f"{name}-replay{rep}")
+        lay = bgq.workspace_layout(prob)
+        compare(oracle_lib, q, False, swiglu=swiglu,
+                run=lambda *_: (got.float().cpu().numpy().astype(np.float64), ws, lay))
         _ = (d["x"].float() * 2).sum()  # unrelated eager work between replays
         fwd()
         torch.cuda.synchronize()

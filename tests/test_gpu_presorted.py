@@ -10,6 +10,7 @@ import torch
 import bit_gathered_quantized_amd as bgq
 import moe_synth as ms
 from gpu_util import dev_arrays, log, ws_view
+from test_gpu_forward import compare
 
 pytestmark = pytest.mark.gpu
 
@@ -81,3 +82,29 @@ def test_presorted_bad_orders_fall_back(oracle_lib):
         assert status == want
         np.testing.assert_array_equal(perm, stable)  # the device sorted by itself
         assert torch.equal(out, ref)
+
+
+@pytest.mark.parametrize("name", ["decode", "prefill4k", "prefill16k"])
+@pytest.mark.parametrize("fp32", [False, True])
+def test_presorted_against_oracle(oracle_lib, name, fp32):
+    """The pre-sorted entry, given a sorted order with each expert's rows
+    shuffled, against the oracle (every token, intermediates included)."""
+    p = ms.make_config(name)
+    _, shuffled = _sorted_orders(p, oracle_lib)
+    d = dev_arrays(p)
+    flags = (bgq.MOE_F_FP32_OUT | bgq.MOE_F_FP32_INTERMEDIATE) if fp32 else 0
+    prob = bgq.problem(p.T, p.k, p.E, p.H, p.I, flags, group_size=p.gs, bits=p.bits)
+    lay = bgq.workspace_layout(prob)
+
+    def run(p_, fp32_, swiglu_):
+        ws = torch.zeros(lay.total, dtype=torch.uint8, device="cuda")
+        so = torch.from_numpy(shuffled).cuda()
+        out = bgq.expert_ffn_forward(d["x"], d["ids"], d["w"], d["w_gu"], d["s_gu"], d["b_gu"],
+                                     d["w_d"], d["s_d"], d["b_d"], fp32_out=fp32_,
+                                     fp32_intermediate=fp32_, workspace=ws, sorted_order=so)
+        torch.cuda.synchronize()
+        assert int(ws_view(ws, lay.num_tiles, 8, np.int32)[4]) == 0
+        np.testing.assert_array_equal(ws_view(ws, lay.perm, p.T * p.k, np.int32), shuffled)
+        return out.float().cpu().numpy().astype(np.float64), ws, lay
+
+    compare(oracle_lib, p, fp32, run=run)

@@ -8,7 +8,8 @@ import torch
 
 import bit_gathered_quantized_amd as bgq
 import moe_synth as ms
-from gpu_util import log, run_forward
+from gpu_util import log
+from test_gpu_forward import compare
 
 pytestmark = pytest.mark.gpu
 
@@ -55,7 +56,4 @@ def test_router_feeds_forward(oracle_lib):
     np.testing.assert_array_equal(ids.cpu().numpy(), gid)
     p.topk_ids = ids.cpu().numpy()
     p.topk_weights = w.cpu().numpy()
-    out, _, _ = run_forward(p)
-    ref = oracle_lib.ffn_tokens(p, want_h=False, want_y=False)["out"]
-    rms = np.sqrt(np.mean(ref ** 2))
-    assert np.abs(out - ref).max() <= 0.03 * rms
+    compare(oracle_lib, p, False)

@@ -459,3 +459,61 @@ def test_forward_tiles_invariants(oracle_lib, seed):
             # consecutive, covering the expert's rows exactly
             assert w[0, 1] == offsets[e] and np.all(w[1:, 1] == w[:-1, 1] + w[:-1, 2])
             assert w[:, 2].sum() == c
+
+
+# ------------------------------------------------- whole-batch entry point
+@pytest.mark.parametrize("case", ["tiny", "invalid", "silu", "gs32-8bit", "gs128-indep"])
+def test_ffn_all_same_bits_as_per_token_path(oracle_lib, case):
+    """The expert-major whole-batch entry computes the same sums in the same
+    order as the per-token path: identical bits for h, y and out."""
+    act = "gelu"
+    if case == "tiny":
+        p = ms.make_config("tiny")
+    elif case == "invalid":
+        p = ms.make_problem(6, 128, 64, 30, 3, seed=4, name="inv")
+        p.topk_ids[2, 1] = -1
+        p.topk_ids[7, :] = 6
+    elif case == "silu":
+        p = ms.make_problem(5, 192, 128, 20, 2, seed=5, name="silu")
+        act = "silu"
+    elif case == "gs32-8bit":
+        p = ms.make_problem(4, 128, 64, 16, 2, seed=6, gs=32, bits=8, name="g32b8")
+    else:
+        p = ms.make_problem(4, 256, 128, 16, 2, seed=7, gs=128, bias="independent", name="g128")
+    a = oracle_lib.ffn_tokens(p, act=act)
+    b = oracle_lib.ffn_all(p, act=act)
+    for key in ("h", "y", "out"):
+        np.testing.assert_array_equal(a[key], b[key])
+
+
+@pytest.mark.parametrize("bits,gs", [(4, 64), (8, 32)])
+def test_independent_biases_match_brute_force(oracle_lib, bits, gs):
+    """Biases drawn independently of the scales (the general affine format):
+    the whole-batch entry against the dense, unrouted recomputation."""
+    p = ms.make_problem(6, 256, 128, 24, 3, seed=8 + bits, gs=gs, bits=bits, bias="independent",
+                        name="indep")
+    s = ms.bf16_bits_to_f32(p.s_gateup).astype(np.float64)
+    b = ms.bf16_bits_to_f32(p.b_gateup).astype(np.float64)
+    assert np.mean(b + 2 ** (bits - 1) * s == 0) < 0.01  # not the centred draw
+    ref = brute_force_out(p)
+    got = oracle_lib.ffn_all(p)["out"]
+    assert np.abs(got - ref).max() <= 1e-10 * np.abs(ref).max()
+
+
+def test_down_rows_same_bits_as_whole_forward(oracle_lib):
+    """The down projection for a given h reproduces the whole forward's y
+    bit for bit when handed the forward's own h; its magnitude sum bounds |y|
+    and equals it for a one-column matrix of non-negative terms."""
+    p = ms.make_problem(6, 128, 64, 30, 3, seed=12, name="down")
+    p.topk_ids[4, 2] = -3
+    r = oracle_lib.ffn_all(p)
+    y, ya = oracle_lib.down_rows(p, p.topk_ids.ravel(), r["h"])
+    np.testing.assert_array_equal(y, r["y"])
+    assert np.all(ya >= np.abs(y))
+    assert not np.any(y[4 * 3 + 2]) and not np.any(ya[4 * 3 + 2])
+    q = ms.make_problem(1, 64, 64, 1, 1, seed=1, name="one")
+    q.s_down[:] = ms.f32_to_bf16_bits(np.array([1.0], np.float32))
+    q.b_down[:] = 0
+    h = np.full((1, 64), 0.5)
+    y, ya = oracle_lib.down_rows(q, np.zeros(1, np.int32), h)
+    np.testing.assert_array_equal(y, ya)

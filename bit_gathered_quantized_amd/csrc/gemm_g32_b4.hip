@@ -1,0 +1,6 @@
+// The quantised matmul kernels for groups of 32 columns and 4-bit codes.
+#include "gemm_kernels.h"
+
+namespace moe {
+MOE_GEMM_INSTANCE(32, 4)
+}  // namespace moe

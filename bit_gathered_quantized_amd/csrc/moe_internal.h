@@ -229,6 +229,15 @@ struct FfnArgs {
     float* y;
     void* out;
 };
+// The four quantised matmul launches; each (group size, code width) pair is
+// instantiated in a translation unit of its own.
+enum class GemmOp { kGateupSkinny, kGateupWide, kDownSkinny, kDownWide };
+hipError_t launch_gemm_g32_b4(GemmOp op, const FfnArgs& a, hipStream_t stream, const KTiming& t);
+hipError_t launch_gemm_g32_b8(GemmOp op, const FfnArgs& a, hipStream_t stream, const KTiming& t);
+hipError_t launch_gemm_g64_b4(GemmOp op, const FfnArgs& a, hipStream_t stream, const KTiming& t);
+hipError_t launch_gemm_g64_b8(GemmOp op, const FfnArgs& a, hipStream_t stream, const KTiming& t);
+hipError_t launch_gemm_g128_b4(GemmOp op, const FfnArgs& a, hipStream_t stream, const KTiming& t);
+hipError_t launch_gemm_g128_b8(GemmOp op, const FfnArgs& a, hipStream_t stream, const KTiming& t);
 hipError_t launch_gateup_skinny(const FfnArgs& a, hipStream_t stream, const KTiming& t = {});
 hipError_t launch_gateup_wide(const FfnArgs& a, hipStream_t stream, const KTiming& t = {});
 hipError_t launch_down_skinny(const FfnArgs& a, hipStream_t stream, const KTiming& t = {});

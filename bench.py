@@ -75,6 +75,7 @@ def algorithmic_work(p):
         "moe_down_wide": dict(bytes=ew * d_expert + rw * I * 2 + rw * H * 4, flops=rw * 2 * H * I),
         "moe_combine": dict(bytes=A * H * 4 + T * H * 2 + A * 4, flops=A * H),
     }
+
     touched = int(np.count_nonzero(counts))
     fwd = dict(bytes=touched * (gu_expert + d_expert) + T * H * 2 + A * 8 + T * H * 2,
                flops=A * 6 * H * I)
@@ -323,11 +324,15 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="decode",
+    ap.add_argument("--workload", default="prefill16k",
                     choices=["tiny", "decode", "prefill4k", "prefill8k", "prefill16k"])
     ap.add_argument("--copies", type=int, default=4, help="input copies rotated across steps")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the router, SwiGLU, pre-sorted, graph and geometry legs")
+    ap.add_argument("--no-legs", action="store_true",
+                    help="time only --workload (not the other workloads as well)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of the forward, copy MIB MiB device-to-device 5 times "
                          "(the reference kernel for scaling HBM byte counters)")
@@ -368,18 +373,75 @@ def main():
               flush=True)
         return
 
-    c = ms.CONFIGS[args.workload]
-    I = args.intermediate or c["I"]
-    custom = args.group_size != ms.GROUP_SIZE or I != c["I"] or args.bits != 4
+    result, ctx = measure_workload(args, args.workload, args.steps, args.warmup, args.group_size,
+                                   args.bits, args.intermediate, args.cpu_seconds,
+                                   not args.no_cpu_baseline)
+    p, sets, prob, ws, out, stream = ctx
+    result = {
+        "metric": METRIC,
+        "value": result.pop("value"),
+        "unit": "assignments/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": result.pop("ms_per_step"),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        **result,
+    }
+    result["extras"] = None if args.no_extras else extra_legs(args, p, sets, prob, ws, out, stream)
+    del sets, ws, out
+    # the other workloads on the same GPU, each with its own roofline, parity
+    # and CPU baseline (the headline is the largest one)
+    legs = {}
+    if not args.no_legs and not result["config"].get("custom"):
+        for name, steps in LEG_STEPS.items():
+            if name == args.workload:
+                continue
+            if name in NOT_RUN:
+                legs[name] = dict(measured=False, reason=NOT_RUN[name])
+                continue
+            leg, _ = measure_workload(args, name, steps, max(5, steps // 10), ms.GROUP_SIZE, 4, 0,
+                                      args.cpu_seconds / 2, not args.no_cpu_baseline)
+            legs[name] = leg
+    result["workloads"] = legs
+    print(json.dumps(result), flush=True)
+
+
+# Timed steps of the other workloads carried in the same JSON line.
+LEG_STEPS = {"decode": 200, "prefill4k": 50, "prefill8k": 30}
+# Workloads kept off the GPU, with the reason.
+NOT_RUN = {"prefill8k": "a GPU memory fault on this workload in an earlier build of the kernels; "
+                        "its cause has not been shown, so the workload is kept off the GPU"}
+
+
+def measure_workload(args, name, steps, warmup, gs, bits, inter, cpu_seconds, want_cpu):
+    """One workload: timed forward, per-kernel events, roofline of the dominant
+    kernel, the whole forward's fraction of its roofline, and (want_cpu) the
+    oracle's rate on a bounded sample with a parity check of the GPU output.
+    Returns (result fields, (problem, input sets, problem struct, workspace,
+    out, stream))."""
+    import numpy as np
+    import torch
+
+    import bit_gathered_quantized_amd as bgq
+    import moe_synth as ms
+
+    c = ms.CONFIGS[name]
+    I = inter or c["I"]
+    custom = gs != ms.GROUP_SIZE or I != c["I"] or bits != 4
     if custom:
         p = ms.make_problem(c["E"], c["H"], I, c["T"], c["k"], seed=0, router=c["router"],
-                            gs=args.group_size, bits=args.bits, name=args.workload)
+                            gs=gs, bits=bits, name=name)
     else:
-        p = ms.make_config(args.workload, seed=0)
+        p = ms.make_config(name, seed=0)
     A = p.T * p.k
     counts = np.bincount(p.topk_ids.ravel(), minlength=p.E)
     touched = int(np.count_nonzero(counts))
-    log(f"workload {args.workload}: E={p.E} H={p.H} I={p.I} T={p.T} k={p.k} A={A} "
+    log(f"workload {name}: E={p.E} H={p.H} I={p.I} T={p.T} k={p.k} A={A} "
         f"gs={p.gs} touched={touched}")
 
     dev = torch.device("cuda", 0)
@@ -402,22 +464,22 @@ def main():
         bgq.expert_ffn_forward(*sets[i % len(sets)], out=out, workspace=ws, stream=stream,
                                events=events)
 
-    for i in range(args.warmup):
+    for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
 
     # timed loop: whole forward, host clock
     t0 = time.perf_counter()
-    for i in range(args.steps):
+    for i in range(steps):
         step(i)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    ms_per_step = elapsed / args.steps * 1e3
-    log(f"timed loop: {args.steps} steps, {ms_per_step * 1e3:.1f} us/step")
+    ms_per_step = elapsed / steps * 1e3
+    log(f"timed loop: {steps} steps, {ms_per_step * 1e3:.1f} us/step")
 
     # instrumented loop: per-kernel durations from events on the same stream
     kernels = bgq.KERNELS
-    n_ev = min(args.steps, 100)
+    n_ev = min(steps, 100)
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(bgq.N_EVENTS)]
            for _ in range(n_ev)]
     for row in evs:
@@ -443,9 +505,10 @@ def main():
     roof = roofline_entry(work[dominant], mean_us[dominant] * 1e-6)
     roof["kernel"] = dominant
     # counter summaries are committed for the named workloads only
-    roof["traffic"] = None if custom else load_traffic(dominant, args.workload)
+    roof["traffic"] = None if custom else load_traffic(dominant, name)
 
     fwd_s = statistics.median(fwd_us) * 1e-6
+    fwd_roof = roofline_entry(fwd_work, ms_per_step * 1e-3)
     forward = dict(
         event_us_median=round(statistics.median(fwd_us), 2),
         event_us_p10=round(float(np.percentile(fwd_us, 10)), 2),
@@ -456,8 +519,12 @@ def main():
         algorithmic_flops=int(fwd_work["flops"]),
         bound=bound_of(fwd_work),
         frac=roofline_entry(fwd_work, fwd_s)["frac"],
-        wall_frac=roofline_entry(fwd_work, ms_per_step * 1e-3)["frac"],
+        wall_frac=fwd_roof["frac"],
     )
+    # the whole forward beside the dominant kernel: the fraction of its own
+    # roofline (bytes or flops of the forward over the timed loop's time)
+    roof["forward_frac"] = fwd_roof["frac"]
+    roof["forward_bound"] = fwd_roof["bound"]
     kstats = {}
     for s in kernels:
         w = work[s]
@@ -471,38 +538,26 @@ def main():
         kstats[s] = entry
 
     result = {
-        "metric": METRIC,
         "value": round(A / (ms_per_step * 1e-3), 1),
-        "unit": "assignments/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 5),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic",
-        "config": {"workload": args.workload, "E": p.E, "H": p.H, "I": p.I, "T": p.T,
+        "steps": steps,
+        "config": {"workload": name, "E": p.E, "H": p.H, "I": p.I, "T": p.T,
                    "k": p.k, "assignments": A, "group_size": p.gs, "bits": p.bits,
-                   "router": ms.CONFIGS[args.workload]["router"], "seed": 0,
-                   "touched_experts": touched, "input_copies": len(sets), **split},
+                   "router": ms.CONFIGS[name]["router"], "seed": 0,
+                   "touched_experts": touched, "input_copies": len(sets), **split,
+                   **({"custom": True} if custom else {})},
         "roofline": roof,
         "forward": forward,
         "kernels": kstats,
     }
-
-    result["extras"] = extra_legs(args, p, sets, prob, ws, out, stream)
-
-    if not args.no_cpu_baseline:
+    if want_cpu:
         gpu_out = out.float().cpu().numpy().astype(np.float64)
-        base, parity = cpu_baseline_leg(p, gpu_out, args.cpu_seconds)
+        base, parity = cpu_baseline_leg(p, gpu_out, cpu_seconds)
         result["cpu_baseline"] = base
         result["parity"] = parity
     else:
         result["cpu_baseline"] = None
-
-    print(json.dumps(result), flush=True)
+    return result, (p, sets, prob, ws, out, stream)
 
 
 if __name__ == "__main__":

@@ -554,9 +554,9 @@ def test_every_expert_33_rows(oracle_lib, fp32, bits):
     8-bit codes) each is cut into tiles of 17 and 16 rows, so the wide list
     holds more than A / 17 tiles: every one of them must be launched (all
     tokens compared)."""
-    E, T, k = 16, 33 * 8, 2
+    E, T, k = 128, 528, 8
     ids = (np.arange(T * k, dtype=np.int32) % E).reshape(T, k)
-    p = ms.make_problem(E, 256, 128, T, k, seed=34, topk_ids=ids, bits=bits, name="e33")
+    p = ms.make_problem(E, 2816, 704, T, k, seed=34, topk_ids=ids, bits=bits, name="e33")
     _, ws, lay = run_forward(p, fp32=fp32)
     nt = ws_view(ws, lay.num_tiles, 4, np.int32)
     expect = 2 * E if lay.bm_big == 32 else E

@@ -33,8 +33,10 @@ EXPORTED_SYMBOLS = (
     "moe_max_tiles", "moe_sort_build_tiles", "moe_ffn_workspace_bytes",
     "moe_ffn_workspace_layout", "moe_expert_ffn_forward",
     "moe_expert_ffn_forward_timed", "moe_expert_ffn_forward_presorted", "moe_router_topk",
-    "moe_status_string",
+    "moe_status_string", "moe_expert_ffn_forward_noalloc",
 )
+MOE_ERR_SCRATCH = -7
+NOALLOC_SCRATCH_BYTES = 32 << 20
 
 
 class MoeError(RuntimeError):
@@ -84,6 +86,8 @@ def lib():
         L.moe_expert_ffn_forward_timed.restype = i32
         L.moe_expert_ffn_forward_presorted.argtypes = fwd[:4] + [P] + fwd[4:]
         L.moe_expert_ffn_forward_presorted.restype = i32
+        L.moe_expert_ffn_forward_noalloc.argtypes = [ctypes.POINTER(MoeProblem)] + [P] * 10 + [P]
+        L.moe_expert_ffn_forward_noalloc.restype = i32
         L.moe_status_string.argtypes = [i32]
         L.moe_status_string.restype = ctypes.c_char_p
         L.moe_router_topk.argtypes = [P, i32, i32, i32, P, P, P]
@@ -199,7 +203,8 @@ def sort_build_tiles(topk_ids, E: int, bm_big: int = 32, bm_small: int = 16, str
 def expert_ffn_forward(x, topk_ids, topk_weights, w_gateup, s_gateup, b_gateup,
                        w_down, s_down, b_down, *, fp32_out: bool = False,
                        fp32_intermediate: bool = False, swiglu: bool = False, out=None,
-                       workspace=None, stream=None, events=None, sorted_order=None):
+                       workspace=None, stream=None, events=None, sorted_order=None,
+                       no_alloc: bool = False):
     """Expert FFN forward.  Shapes: x [T, H] (2-byte), topk_ids int32 [T, k],
     topk_weights fp32 [T, k], w_gateup 4-byte [E, 2I, H*bits/32], s/b_gateup
     2-byte [E, 2I, H/gs], w_down 4-byte [E, H, I*bits/32], s/b_down 2-byte
@@ -209,7 +214,10 @@ def expert_ffn_forward(x, topk_ids, topk_weights, w_gateup, s_gateup, b_gateup,
     h = silu(g) * u instead of gelu_tanh(g) * u.  With sorted_order (int32
     [T*k], slot -> flat assignment, sorted by expert) the pre-sorted entry is
     used.  `workspace` is a uint8
-    device tensor of at least workspace_bytes() bytes (allocated if None)."""
+    device tensor of at least workspace_bytes() bytes (allocated if None).
+    With no_alloc the allocation-free entry point runs on the library's
+    built-in scratch array instead (no workspace; `out` must then be given
+    for the call itself to allocate nothing)."""
     torch = _torch()
     T, H = x.shape
     k = topk_ids.shape[1]
@@ -245,6 +253,13 @@ def expert_ffn_forward(x, topk_ids, topk_weights, w_gateup, s_gateup, b_gateup,
     if out is None:
         out = torch.empty((T, H), dtype=torch.float32 if fp32_out else torch.bfloat16, device=x.device)
     optr = _dev_ptr(out, "out", 4 if fp32_out else 2, (T, H))
+    if no_alloc:
+        if workspace is not None or events is not None or sorted_order is not None:
+            raise ValueError("no_alloc takes no workspace, events or sorted_order")
+        st = lib().moe_expert_ffn_forward_noalloc(ctypes.byref(p), *ptrs, optr,
+                                                  ctypes.c_void_p(_stream(stream)))
+        _check(st, "moe_expert_ffn_forward_noalloc")
+        return out
     need = workspace_bytes(p)
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=x.device)

@@ -4,9 +4,42 @@
 #include <limits.h>
 #include <stddef.h>
 
+#include <mutex>
+
 #include "moe_internal.h"
 
+// The built-in workspace of moe_expert_ffn_forward_noalloc: one copy per
+// GPU, alive until the process ends.  Host code never passes `scratch`
+// itself to a kernel or a copy (in host code it is a stand-in, not a device
+// address): it takes the device address from hipGetSymbolAddress, once per
+// device, with that device current.
+static __device__ __align__(256) unsigned char scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
 namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch array (looked up on the
+// first call on that device), or nullptr with *err set.
+void* scratch_for_current_device(hipError_t* err) {
+    int dev = 0;
+    *err = hipGetDevice(&dev);
+    if (*err != hipSuccess) return nullptr;
+    if (dev < 0 || dev >= kMaxDevices) {
+        *err = hipErrorInvalidDevice;
+        return nullptr;
+    }
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void* ptr = nullptr;
+        *err = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (*err != hipSuccess) return nullptr;
+        g_scratch_ptr[dev] = ptr;
+    }
+    return g_scratch_ptr[dev];
+}
 
 constexpr size_t kAlign = 256;
 
@@ -254,6 +287,23 @@ moe_status moe_expert_ffn_forward(const moe_problem* p, const void* x, const int
                         s_down, b_down, out, ws, ws_bytes, stream, nullptr, nullptr, false);
 }
 
+moe_status moe_expert_ffn_forward_noalloc(const moe_problem* p, const void* x,
+                                          const int32_t* topk_ids, const float* topk_weights,
+                                          const uint32_t* w_gateup, const void* s_gateup,
+                                          const void* b_gateup, const uint32_t* w_down,
+                                          const void* s_down, const void* b_down, void* out,
+                                          void* stream) {
+    const moe_status st = check_problem(p);
+    if (st != MOE_OK) return st;
+    if (p->T == 0) return MOE_OK;
+    if (make_layout(p).total > MOE_NOALLOC_SCRATCH_BYTES) return MOE_ERR_SCRATCH;
+    hipError_t err = hipSuccess;
+    void* ws = scratch_for_current_device(&err);
+    if (ws == nullptr) return MOE_ERR_HIP;
+    return forward_impl(p, x, topk_ids, topk_weights, w_gateup, s_gateup, b_gateup, w_down, s_down,
+                        b_down, out, ws, MOE_NOALLOC_SCRATCH_BYTES, stream, nullptr, nullptr, false);
+}
+
 moe_status moe_expert_ffn_forward_presorted(const moe_problem* p, const void* x,
                                             const int32_t* topk_ids, const float* topk_weights,
                                             const int32_t* sorted_order,
@@ -299,6 +349,8 @@ const char* moe_status_string(moe_status s) {
         case MOE_ERR_ALIGN: return "a pointer is misaligned";
         case MOE_ERR_WORKSPACE: return "workspace or tile buffer missing or too small";
         case MOE_ERR_HIP: return "HIP runtime error while enqueueing work";
+        case MOE_ERR_SCRATCH:
+            return "problem needs more workspace than the built-in scratch buffer of the allocation-free entry point holds";
         default: return "unknown status";
     }
 }

@@ -37,8 +37,9 @@
  *    (a hipStream_t; NULL is the default stream) and is stream-ordered.
  *  - Entry points never throw and never abort.  Host-checkable errors are
  *    returned before anything is enqueued.
- *  - The library keeps no mutable global state; concurrent calls on distinct
- *    buffers are safe.
+ *  - Apart from the scratch arrays of moe_expert_ffn_forward_noalloc (one per
+ *    GPU, see there), the library keeps no mutable global state; concurrent
+ *    calls on distinct buffers are safe.
  */
 #ifndef MOE_FFN_H
 #define MOE_FFN_H
@@ -58,7 +59,8 @@ enum {
     MOE_ERR_UNSUPPORTED = -3, /* bits not 4/8, group_size not 32/64/128, E too large, ... */
     MOE_ERR_ALIGN = -4,       /* a pointer is not aligned as required          */
     MOE_ERR_WORKSPACE = -5,   /* workspace missing or too small                */
-    MOE_ERR_HIP = -6          /* the HIP runtime rejected a launch             */
+    MOE_ERR_HIP = -6,         /* the HIP runtime rejected a launch             */
+    MOE_ERR_SCRATCH = -7      /* too large for moe_expert_ffn_forward_noalloc  */
 };
 
 /* One tile of sorted rows of a single expert: rows
@@ -253,6 +255,32 @@ moe_status moe_expert_ffn_forward_presorted(const moe_problem* p, const void* x,
                                             const void* b_gateup, const uint32_t* w_down,
                                             const void* s_down, const void* b_down, void* out,
                                             void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * moe_expert_ffn_forward without a workspace argument, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation).  It calls no hipMalloc, hipFree
+ * or allocating routine: its workspace is a scratch array built into the
+ * library, MOE_NOALLOC_SCRATCH_BYTES per GPU, which each GPU the library
+ * runs on holds until the process ends (its device address is looked up
+ * once per device, on the first call there).
+ *
+ * Arguments as moe_expert_ffn_forward, minus ws and ws_bytes.  Problems whose
+ * workspace (moe_ffn_workspace_bytes) exceeds MOE_NOALLOC_SCRATCH_BYTES
+ * return MOE_ERR_SCRATCH before anything is enqueued (at hidden 2816 and
+ * intermediate 704 the limit is about 2400 assignments, e.g. 300 tokens at
+ * top-8).  Every call on a
+ * GPU shares that GPU's scratch array: calls that overlap on one GPU (other
+ * streams, other threads) race and must be ordered by the caller.  Nothing in
+ * the scratch array needs clearing between calls.
+ */
+#define MOE_NOALLOC_SCRATCH_BYTES (32u << 20)
+moe_status moe_expert_ffn_forward_noalloc(const moe_problem* p, const void* x,
+                                          const int32_t* topk_ids, const float* topk_weights,
+                                          const uint32_t* w_gateup, const void* s_gateup,
+                                          const void* b_gateup, const uint32_t* w_down,
+                                          const void* s_down, const void* b_down, void* out,
+                                          void* stream);
 
 /* Same as moe_expert_ffn_forward, with per-kernel timing: events[2i] and
  * events[2i+1] (hipEvent_t, created by the caller) are recorded at the start

@@ -301,12 +301,21 @@ __device__ __forceinline__ void chunk_steps(f32x4 (&acc)[NB], const u32x4 (&x)[4
 // A bf16 scale as the factor of P.
 __device__ __forceinline__ float scale16(uint16_t t) { return bf16_to_f32(t); }
 
-// Sum over the 16 lanes of a 16-lane row (the same value in every lane).
+// v from another lane of the same 16-lane row, by a DPP control (no LDS).
+template <int CTRL>
+__device__ __forceinline__ float dpp_row(float v) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+// Sum over the 16 lanes of a 16-lane row (the same value in every lane): a
+// butterfly, lane i adding lane i ^ 1, i ^ 2, i ^ 4, i ^ 8 in turn.  The first
+// two are quad permutations; after them the value is the same across each
+// quad, so the half-row mirror (lane i of 8 -> 7 - i) reads lane i ^ 4's
+// value, and after that the row mirror (i -> 15 - i) reads lane i ^ 8's.
 __device__ __forceinline__ float sum16(float v) {
-    v += __shfl_xor(v, 1);
-    v += __shfl_xor(v, 2);
-    v += __shfl_xor(v, 4);
-    v += __shfl_xor(v, 8);
+    v += dpp_row<0xB1>(v);   // quad_perm [1, 0, 3, 2]
+    v += dpp_row<0x4E>(v);   // quad_perm [2, 3, 0, 1]
+    v += dpp_row<0x141>(v);  // row_half_mirror
+    v += dpp_row<0x140>(v);  // row_mirror
     return v;
 }
 

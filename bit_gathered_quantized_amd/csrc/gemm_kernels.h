@@ -147,21 +147,26 @@ __device__ __forceinline__ void pack_split(const float (&v)[8], u32x4& hi, u32x4
 }
 
 // Column operand: c[g] = b[g] - OFF s[g] of one weight row (OFF the code
-// offset), from its rows of the scale and bias tables.  Groups past G repeat
-// the last group: the row operand is zero there, so those (finite) products
-// add nothing.
+// offset), from its rows of the scale and bias tables.  Entries past G read
+// whatever follows the row in LDS (the next row, or the next member of the
+// shared-memory struct: at most 32 NS - 1 entries past the last row) at fixed
+// offsets from one address, and are replaced by 0, so no bits read there
+// reach the product.
 template <int NS, int OFF = 16>
 __device__ __forceinline__ void bias_from_table(BiasOp<NS>& o, const uint16_t* ts, const uint16_t* tb,
                                                 int G, int q, int steps, bool active) {
+    const uint16_t* const s8 = ts + 8 * q;
+    const uint16_t* const b8 = tb + 8 * q;
+    const int lim = active ? G - 8 * q : 0;  // entries j of step st valid while 32 st + j < lim
 #pragma unroll
     for (int st = 0; st < NS; ++st) {
         if (st < steps) {
             float v[8];
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
-                const int gc = min(32 * st + 8 * q + j, G - 1);
-                const float c = fmaf(-static_cast<float>(OFF), bf16_to_f32(ts[gc]), bf16_to_f32(tb[gc]));
-                v[j] = active ? c : 0.f;
+                const float c =
+                    fmaf(-static_cast<float>(OFF), bf16_to_f32(s8[32 * st + j]), bf16_to_f32(b8[32 * st + j]));
+                v[j] = 32 * st + j < lim ? c : 0.f;
             }
             pack_split(v, o.hi[st], o.lo[st]);
         }
@@ -302,9 +307,11 @@ __device__ __forceinline__ void chunk_steps(f32x4 (&acc)[NB], const u32x4 (&x)[4
 __device__ __forceinline__ float scale16(uint16_t t) { return bf16_to_f32(t); }
 
 // v from another lane of the same 16-lane row, by a DPP control (no LDS).
+// Every control used here reads inside the row; with bound_ctrl set the move
+// folds into the add that consumes it (one v_add_f32_dpp).
 template <int CTRL>
 __device__ __forceinline__ float dpp_row(float v) {
-    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
 }
 // Sum over the 16 lanes of a 16-lane row (the same value in every lane): a
 // butterfly, lane i adding lane i ^ 1, i ^ 2, i ^ 4, i ^ 8 in turn.  The first
@@ -319,24 +326,47 @@ __device__ __forceinline__ float sum16(float v) {
     return v;
 }
 
-// h for (sorted row srow, column hcol), stored once in operand order; returns
-// the value the down matmul will see (bf16 h, or hi + lo), 0 if not valid.
+// h of the rows [row_begin, row_begin + rows) of a tile, stored once in
+// operand order, and their 16-column block sums.  The stores go through
+// buffer resources over exactly those rows (none for a wave without columns),
+// so a store for a row past the tile falls outside and is dropped: no branch
+// per store, 32-bit offsets.
 template <bool kF32H>
-__device__ __forceinline__ float store_h(const FfnArgs& a, size_t A, int srow, int hcol, float g,
-                                         float u, bool valid) {
-    const float hv = ((a.flags & MOE_F_SWIGLU) ? silu(g) : gelu_tanh(g)) * u;
-    const size_t pos = static_cast<size_t>(srow) * a.I + (hcol & ~7) + permuted_pos(hcol & 7);
-    uint16_t* h = static_cast<uint16_t*>(a.h);
-    const uint16_t hi = f32_to_bf16(hv);
-    float seen = bf16_to_f32(hi);
-    if constexpr (kF32H) {
-        const uint16_t lo = f32_to_bf16(hv - seen);
-        seen += bf16_to_f32(lo);
-        if (valid) h[A * a.I + pos] = lo;
+struct HOut {
+    Rsrc hi, lo, sums;
+    int I;
+
+    __device__ __forceinline__ void init(const FfnArgs& a, size_t A, int row_begin, int rows, bool active) {
+        I = a.I;
+        const uint32_t n = active ? static_cast<uint32_t>(rows) : 0u;
+        uint16_t* const h = static_cast<uint16_t*>(a.h) + static_cast<size_t>(row_begin) * I;
+        hi = make_rsrc(h, n * I * 2u);
+        if constexpr (kF32H) lo = make_rsrc(h + A * I, n * I * 2u);
+        sums = make_rsrc(a.hs + static_cast<size_t>(row_begin) * (I / 16), n * (I / 16) * 4u);
     }
-    if (valid) h[pos] = hi;
-    return valid ? seen : 0.f;
-}
+    // h = act(g) * u for tile row r, column hcol (act = silu with kSilu, else
+    // gelu_tanh); returns the value the down matmul will see (bf16 h, or hi + lo)
+    template <bool kSilu>
+    __device__ __forceinline__ float put(int r, int hcol, float g, float u) const {
+        const float hv = (kSilu ? silu(g) : gelu_tanh(g)) * u;
+        const uint32_t off = 2u * static_cast<uint32_t>(r * I + (hcol & ~7) + permuted_pos(hcol & 7));
+        const uint16_t h16 = f32_to_bf16(hv);
+        float seen = bf16_to_f32(h16);
+        if constexpr (kF32H) {
+            const uint16_t l16 = f32_to_bf16(hv - seen);
+            seen += bf16_to_f32(l16);
+            __builtin_amdgcn_raw_buffer_store_b16(l16, lo, off, 0, 0);
+        }
+        __builtin_amdgcn_raw_buffer_store_b16(h16, hi, off, 0, 0);
+        return seen;
+    }
+    // the 16-column block sum of row r (its 16 lanes' values), block cb16
+    __device__ __forceinline__ void put_sum(int r, int cb16, float seen, int lr) const {
+        const float s = sum16(seen);
+        const uint32_t off = lr == 0 ? 4u * static_cast<uint32_t>(r * (I / 16) + cb16) : 0xFFFFFFF0u;
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(s), sums, off, 0, 0);
+    }
+};
 
 // ================================================== weights through LDS
 // The MFMA operand wants lane (lr, q) to hold words 2q, 2q+1 of weight row lr
@@ -618,13 +648,19 @@ __global__ __launch_bounds__(64, GS == 32 || BITS == 8 ? 2 : 3) void moe_gateup_
     for (int b = 0; b < NB; ++b) acc[b] += bterm[b];
 
     // GeGLU, h once, and the 16-column block sum of h per row
+    HOut<kF32H> ho;
+    ho.init(a, A, row_begin, rows, true);
+    auto epilogue = [&](auto silu_tag) {
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-        const int r = 4 * q + v;
-        const float seen = store_h<kF32H>(a, A, row_begin + r, hcol0 + lr, acc[0][v], acc[1][v], r < rows);
-        const float s = sum16(seen);
-        if (lr == 0 && r < rows) a.hs[static_cast<size_t>(row_begin + r) * (I / 16) + cb] = s;
-    }
+        for (int v = 0; v < 4; ++v) {
+            const int r = 4 * q + v;
+            ho.put_sum(r, cb, ho.template put<decltype(silu_tag)::value>(r, hcol0 + lr, acc[0][v], acc[1][v]), lr);
+        }
+    };
+    if (a.flags & MOE_F_SWIGLU)
+        epilogue(std::true_type{});
+    else
+        epilogue(std::false_type{});
 }
 
 // down, tiles of <= 16 rows.  Grid: skinny tiles x H / (16 NB) column
@@ -1108,22 +1144,29 @@ __device__ __forceinline__ void gateup_wide(const FfnArgs& a, WideSmem<RB, 1, 2,
     wide_bias<GS, RB, P, NBUF, MAXG, BITS, false>(sm, xrow, br, G, active, (rows + 15) / 16, acc);
 
     // GeGLU epilogue and the 16-column block sums of h
+    HOut<kF32H> ho;
+    ho.init(a, A, row_begin, rows, active);
+    auto epilogue = [&](auto silu_tag) {
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
+        for (int rb = 0; rb < RB; ++rb) {
+            if (rb >= (rows + 15) / 16) break;  // row blocks past the tile
 #pragma unroll
-        for (int half = 0; half < 2; ++half) {
-            const int hcol = hbase + 16 * half + lr;
+            for (int half = 0; half < 2; ++half) {
+                const int hcol = hbase + 16 * half + lr;
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const int r = 16 * rb + 4 * q + v;
-                const float seen = store_h<kF32H>(a, A, row_begin + r, hcol, acc[rb][half][v],
-                                                  acc[rb][2 + half][v], active && r < rows);
-                const float s = sum16(seen);
-                if (lr == 0 && active && r < rows)
-                    a.hs[static_cast<size_t>(row_begin + r) * (I / 16) + hbase / 16 + half] = s;
+                for (int v = 0; v < 4; ++v) {
+                    const int r = 16 * rb + 4 * q + v;
+                    const float seen = ho.template put<decltype(silu_tag)::value>(r, hcol, acc[rb][half][v],
+                                                                                  acc[rb][2 + half][v]);
+                    ho.put_sum(r, hbase / 16 + half, seen, lr);
+                }
             }
         }
-    }
+    };
+    if (a.flags & MOE_F_SWIGLU)
+        epilogue(std::true_type{});
+    else
+        epilogue(std::false_type{});
 }
 
 // down wide, column block `by` of 256 output columns (ceil(H / 256) blocks).  Wave w owns output columns

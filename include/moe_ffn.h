@@ -89,8 +89,13 @@ typedef struct {
 #define MOE_MAX_EXPERTS 1024
 /* out is fp32 [T, H] instead of bf16 */
 #define MOE_F_FP32_OUT 1u
-/* the GeGLU intermediate h is kept in fp32 instead of bf16 (the
- * fp32-accumulator path); combine with MOE_F_FP32_OUT for a full-fp32 result */
+/* the GeGLU intermediate h is kept to 16 significant bits (bf16 hi + lo)
+ * instead of bf16 (the fp32-accumulator path); combine with MOE_F_FP32_OUT
+ * for a full-fp32 result.  Without it h is bf16, the dtype of x (SwiftLM
+ * issue #236, "What #27 set out to do" (3): the switch-GLU intermediates stay
+ * in the original dtype).  The weighted down output y is fp32 either way: a
+ * bf16 y costs more than the bf16 output's error budget on a 16384-assignment
+ * batch. */
 #define MOE_F_FP32_INTERMEDIATE 2u
 /* SwiGLU instead of GeGLU: h = silu(g) * u with silu(v) = v / (1 + exp(-v))
  * (SwiftLM issue #236, "What #27 set out to do" (2) and "Already on main":
@@ -99,7 +104,10 @@ typedef struct {
 #define MOE_F_SWIGLU 4u
 
 /* Upper bound on the number of tiles for A assignments over E experts with
- * tile height bm_big: floor(A / bm_big) + min(E, A).  Returns -1 on bad input. */
+ * tile height bm_big: floor(A / bm_big) + min(E, A) (every expert's tiles
+ * are full bm_big-row tiles plus at most one shorter tile: the BM32 expert
+ * tiles with BM16 fallback rows of the Layr-Labs/mlx PR #4 page, "What").
+ * Sizes the tile arrays of moe_sort_build_tiles.  Returns -1 on bad input. */
 int32_t moe_max_tiles(int64_t A, int32_t E, int32_t bm_big);
 
 /*
@@ -121,7 +129,10 @@ int32_t moe_max_tiles(int64_t A, int32_t E, int32_t bm_big);
  *
  * Requires 1 <= bm_small <= bm_big, E <= MOE_MAX_EXPERTS and
  * max_tiles >= moe_max_tiles(T*k, E, bm_big).  T = 0 is valid (counts and
- * offsets are zeroed).  All outputs are bit-exact and deterministic.
+ * offsets are zeroed).  All outputs are bit-exact and deterministic.  It
+ * takes no workspace: one workgroup sorts in its LDS (per-key counts, scan
+ * and ranks never leave the chip), so the only device memory written is the
+ * caller's outputs above.
  */
 moe_status moe_sort_build_tiles(const int32_t* topk_ids, int32_t T, int32_t k,
                                 int32_t E, int32_t bm_big, int32_t bm_small,
@@ -150,7 +161,11 @@ moe_status moe_router_topk(const float* logits, int32_t T, int32_t E, int32_t k,
                            int32_t* topk_ids, float* topk_weights, void* stream);
 
 /* Bytes of device workspace moe_expert_ffn_forward needs for problem p
- * (0 on invalid p). */
+ * (0 on invalid p).  The pages' forward keeps its sorted indices, tile
+ * descriptors and switch-GLU intermediates in buffers of its own (Layr-Labs/
+ * mlx PR #4, "What"; SwiftLM issue #236, "What #27 set out to do" (3)); here
+ * they live in one caller-owned workspace, laid out by
+ * moe_ffn_workspace_layout. */
 size_t moe_ffn_workspace_bytes(const moe_problem* p);
 
 /* Byte offsets of the forward's intermediates inside its workspace, so that
@@ -183,8 +198,10 @@ typedef struct {
                          group adds its blocks left to right, e.g.
                          ((b0 + b1) + b2) + b3 at gs = 64                */
     size_t y;         /* fp32 [A, H] flat order a = t*k + j, already
-                         multiplied by topk_weights; rows of assignments
-                         with an out-of-range id are not written          */
+                         multiplied by topk_weights (the direct weighted
+                         unsort of the Layr-Labs/mlx PR #4 page,
+                         "Measured standing"); rows of assignments with an
+                         out-of-range id are not written                  */
     size_t total;     /* == moe_ffn_workspace_bytes(p)                    */
     int32_t max_tiles;
     int32_t bm_big;
@@ -208,7 +225,11 @@ moe_status moe_ffn_workspace_layout(const moe_problem* p, moe_ws_layout* layout)
  * Full expert FFN forward: route/sort/tile, gathered quantised gate|up matmul
  * with the fused GeGLU product, gathered quantised down matmul with the
  * weighted unsort, and the combine back to tokens (codes of p->bits bits in
- * groups of p->group_size columns).
+ * groups of p->group_size columns).  Defined by: the expert-tile gathered
+ * QMM over sorted indices (Layr-Labs/mlx PR #4, "What"), the GeGLU product
+ * activation(xGate) * xUp with the approximate GELU (SwiftLM issue #236,
+ * "Still missing"), the weighted unsort (PR #4, "Measured standing") and
+ * the weighted expert sum (issue #236, "Already on main").
  *
  *   x            bf16 [T, H]        16-byte aligned
  *   topk_ids     int32 [T, k]

@@ -191,11 +191,11 @@ def test_small_batch_matches_large(oracle_lib, fp32):
     np.testing.assert_array_equal(ob[:8], oa)
 
 
-# Round-one record: two GPU memory faults at 8192 assignments (prefill8k),
-# fp32 mode in moe_down_wide under a since-removed 128-row tile path and bf16
-# mode under a since-removed loop structure.  No cause has been shown, so
-# these two cases stay off the GPU (skipped).  16384 assignments in fp32 mode
-# never faulted; it runs.
+# Two GPU memory faults were recorded at 8192 assignments (prefill8k) with
+# earlier kernels: fp32 mode in moe_down_wide under a since-removed 128-row
+# tile path, and bf16 mode under a since-removed loop structure.  No cause
+# has been shown, so these two cases stay off the GPU (skipped).  16384
+# assignments in fp32 mode never faulted; it runs.
 _FAULTED = pytest.mark.skip(reason="GPU memory fault on this workload in an earlier build; "
                                    "cause not shown, case kept off the GPU")
 

@@ -191,6 +191,33 @@ __device__ __forceinline__ float group_of_blocks(const float* X16, int g) {
     }
 }
 
+// The GS / 16 block sums of one group, loaded now and added later in the
+// order of group_of_blocks.
+template <int GS>
+struct BlockSums {
+    float b[GS / 16];
+    __device__ __forceinline__ void load(const float* X16, int g) {
+        if constexpr (GS == 32) {
+            const f32x2 v = *reinterpret_cast<const f32x2*>(X16 + 2 * g);
+            b[0] = v[0];
+            b[1] = v[1];
+        } else {
+#pragma unroll
+            for (int h = 0; h < GS / 64; ++h) {
+                const f32x4 v = *reinterpret_cast<const f32x4*>(X16 + (GS / 16) * g + 4 * h);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) b[4 * h + i] = v[i];
+            }
+        }
+    }
+    __device__ __forceinline__ float sum() const {
+        float v = b[0];
+#pragma unroll
+        for (int i = 1; i < GS / 16; ++i) v += b[i];
+        return v;
+    }
+};
+
 // The group sums of one activation row as the bias operand (NS steps).
 template <int NS>
 struct RowSums {
@@ -856,6 +883,16 @@ struct alignas(16) WideSmem {
     float wt[RB * 16];          // down: its routing weight
 };
 
+// The down kernels' shared memory: the wide layout plus the group sums of
+// the tile's rows, read in the prologue when a row has at most kPreG groups
+// (704 columns at group size 32 or 64).  At 4 row blocks the bf16 layout then
+// fills exactly half of a CU's LDS, so two workgroups still share a CU.
+constexpr int kPreG = 22;
+template <int RB, bool kF32H, int MAXG, int BITS>
+struct alignas(16) DownSmem : WideSmem<RB, kF32H ? 2 : 1, kF32H ? 1 : 2, MAXG, BITS> {
+    float xg[RB * 16 * kPreG];
+};
+
 // Bias rows of a wave's four weight blocks (16 rows x G bf16 each, contiguous),
 // read raw as 16-byte pieces (lane l holds pieces l and l + 64 of each block)
 // while the last chunk is multiplied, and turned into operand order through
@@ -1012,28 +1049,35 @@ __device__ __forceinline__ void wide_kloop(WideSmem<RB, P, NBUF, MAXG, BITS>& sm
     chunk(nch - 1, std::true_type{});
 }
 
-// The bias term of the wide paths, added once after the K loop.  The group
-// sums of the staged rows go through LDS (the activation buffers are free by
-// then): thread t copies groups t % 16 + 16 j of rows t / 16 + 16 i, from row
-// pointers xrow[i] (G floats each, or with kBlocks the GS / 16 block sums of
-// h per group).  br: the wave's bias rows, prefetched during the last chunk.
-template <int GS, int RB, int P, int NBUF, int MAXG, int BITS, bool kBlocks>
-__device__ __forceinline__ void wide_bias(WideSmem<RB, P, NBUF, MAXG, BITS>& sm,
-                                          const float* const (&xrow)[RB],
-                                          const BiasRows<4, Geo<GS>::kMaxG / 32>& br,
-                                          int G, bool active, int nrb, f32x4 (&acc)[RB][4]) {
-    constexpr int CB = 4, NS = Geo<GS>::kSteps, XS = kXStride<GS>;
+// The group sums of the staged rows go to LDS for the bias term (the
+// activation buffers are free once the K loop is done): thread t writes
+// groups g = t % 16 + 16 j of rows t / 16 + 16 i, the value xsum(i, j, g)
+// (G <= MAXG).
+template <int GS, int RB, int P, int NBUF, int MAXG, int BITS, class XSum>
+__device__ __forceinline__ void stage_group_sums(WideSmem<RB, P, NBUF, MAXG, BITS>& sm, int G, XSum&& xsum) {
+    constexpr int XS = kXStride<GS>;
     static_assert(sizeof(float) * RB * 16 * XS <= sizeof(sm.a), "group sums must fit the activation buffer");
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, q = lane >> 4, lr = lane & 15;
     float* xl = reinterpret_cast<float*>(&sm.a[0][0][0]);
     const int pc = threadIdx.x & 15, r0 = threadIdx.x >> 4;
 #pragma unroll
     for (int i = 0; i < RB; ++i)
 #pragma unroll
-        for (int j = 0; j < Geo<GS>::kMaxG / 16; ++j) {
+        for (int j = 0; j < (MAXG + 15) / 16; ++j) {
             const int g = pc + 16 * j;
-            if (g < G) xl[(r0 + 16 * i) * XS + g] = kBlocks ? group_of_blocks<GS>(xrow[i], g) : xrow[i][g];
+            if (g < G) xl[(r0 + 16 * i) * XS + g] = xsum(i, j, g);
         }
+}
+
+// The bias term of the wide paths, added once after the K loop, from the
+// group sums stage_group_sums left in LDS.  br: the wave's bias rows,
+// prefetched during the last chunk.
+template <int GS, int RB, int P, int NBUF, int MAXG, int BITS>
+__device__ __forceinline__ void wide_bias(WideSmem<RB, P, NBUF, MAXG, BITS>& sm,
+                                          const BiasRows<4, Geo<GS>::kMaxG / 32>& br,
+                                          int G, bool active, int nrb, f32x4 (&acc)[RB][4]) {
+    constexpr int CB = 4, NS = Geo<GS>::kSteps, XS = kXStride<GS>;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, q = lane >> 4, lr = lane & 15;
+    const float* xl = reinterpret_cast<const float*>(&sm.a[0][0][0]);
     __syncthreads();
     const int steps = (G + 31) / 32;
     // the row operand of row block rb (8 consecutive groups per step; reads
@@ -1135,13 +1179,25 @@ __device__ __forceinline__ void gateup_wide(const FfnArgs& a, WideSmem<RB, 1, 2,
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) bblk[cb] = a.b_gu + row0[cb] * G;
     BiasRows<CB, Geo<GS>::kMaxG / 32> br;
-    wide_kloop<GS, RB, P, NBUF, MAXG, BITS>(sm, st, src, 0, blk, H, active, (rows + 15) / 16, code_consts(a.zero), acc,
-                                  [&] { br.load(bblk, G); });
-
-    const float* xrow[RB];
+    // the bias rows and the rows' group sums of x (thread t: groups t % 16 +
+    // 16 j of rows t / 16 + 16 i) are read during the last chunk
+    constexpr int XJ = (MAXG + 15) / 16;
+    float xv[RB][XJ];
+    auto last = [&] {
+        br.load(bblk, G);
+        const int pc = tid & 15;
 #pragma unroll
-    for (int i = 0; i < RB; ++i) xrow[i] = a.xs + static_cast<size_t>(tok[i]) * G;
-    wide_bias<GS, RB, P, NBUF, MAXG, BITS, false>(sm, xrow, br, G, active, (rows + 15) / 16, acc);
+        for (int i = 0; i < RB; ++i) {
+            const float* xrow = a.xs + static_cast<size_t>(tok[i]) * G;
+#pragma unroll
+            for (int j = 0; j < XJ; ++j) xv[i][j] = pc + 16 * j < G ? xrow[pc + 16 * j] : 0.f;
+        }
+    };
+    wide_kloop<GS, RB, P, NBUF, MAXG, BITS>(sm, st, src, 0, blk, H, active, (rows + 15) / 16, code_consts(a.zero), acc,
+                                            last);
+
+    stage_group_sums<GS>(sm, G, [&](int i, int j, int) { return xv[i][j]; });
+    wide_bias<GS>(sm, br, G, active, (rows + 15) / 16, acc);
 
     // GeGLU epilogue and the 16-column block sums of h
     HOut<kF32H> ho;
@@ -1172,9 +1228,8 @@ __device__ __forceinline__ void gateup_wide(const FfnArgs& a, WideSmem<RB, 1, 2,
 // down wide, column block `by` of 256 output columns (ceil(H / 256) blocks).  Wave w owns output columns
 // n0 + 64 w + [0, 64): four 16-row weight blocks.
 template <int GS, int RB, int MAXG, bool kF32H, int BITS>
-__device__ __forceinline__ void down_wide(const FfnArgs& a,
-                                          WideSmem<RB, kF32H ? 2 : 1, kF32H ? 1 : 2, MAXG, BITS>& sm,
-                                          int e, int row_begin, int rows, int by) {
+__device__ __forceinline__ void down_wide(const FfnArgs& a, DownSmem<RB, kF32H, MAXG, BITS>& sm, int e,
+                                          int row_begin, int rows, int by) {
     constexpr int P = kF32H ? 2 : 1, NBUF = kF32H ? 1 : 2, CB = 4;
     const int tid = threadIdx.x, lane = tid & 63, q = lane >> 4, lr = lane & 15;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: weight rows are per wave
@@ -1212,8 +1267,31 @@ __device__ __forceinline__ void down_wide(const FfnArgs& a,
     const size_t part = A * (I / 2);
     Stager<RB, P> st;
     st.load(src, part, 0, I / 64);
+    // rows of at most kPreG groups: their group sums (from the block sums of
+    // h, in the one order) are read now, with the first stage, and kept in
+    // LDS for the bias term, which then waits on no global load
+    const bool pre = G <= kPreG;
+    constexpr int PN = (RB * 16 * kPreG + kThreads - 1) / kThreads;
+    BlockSums<GS> pb[PN];
+    if (pre) {
+#pragma unroll
+        for (int n = 0; n < PN; ++n) {
+            const int idx = tid + kThreads * n;
+            if (idx < RB * 16 * G) {
+                const int r = idx / G;
+                pb[n].load(a.hs + static_cast<size_t>(row_begin + min(r, rows - 1)) * (I / 16), idx - r * G);
+            }
+        }
+    }
     tab.store(sm.ts[wave], nullptr, G);
     st.store(sm, 0);
+    if (pre) {
+#pragma unroll
+        for (int n = 0; n < PN; ++n) {
+            const int idx = tid + kThreads * n;
+            if (idx < RB * 16 * G) sm.xg[idx] = pb[n].sum();
+        }
+    }
 
     f32x4 acc[RB][CB];
 #pragma unroll
@@ -1228,10 +1306,13 @@ __device__ __forceinline__ void down_wide(const FfnArgs& a,
     wide_kloop<GS, RB, P, NBUF, MAXG, BITS>(sm, st, src, part, blk, I, active, (rows + 15) / 16, code_consts(a.zero), acc,
                                   [&] { br.load(bblk, G); });
 
-    const float* xrow[RB];
-#pragma unroll
-    for (int i = 0; i < RB; ++i) xrow[i] = a.hs + static_cast<size_t>(hrow[i]) * (I / 16);
-    wide_bias<GS, RB, P, NBUF, MAXG, BITS, true>(sm, xrow, br, G, active, (rows + 15) / 16, acc);
+    if (pre)
+        stage_group_sums<GS>(sm, G, [&](int i, int, int g) { return sm.xg[((tid >> 4) + 16 * i) * G + g]; });
+    else
+        stage_group_sums<GS>(sm, G, [&](int i, int, int g) {
+            return group_of_blocks<GS>(a.hs + static_cast<size_t>(hrow[i]) * (I / 16), g);
+        });
+    wide_bias<GS>(sm, br, G, active, (rows + 15) / 16, acc);
 
     if (!active) return;
     // weighted unsort (destinations and weights read before the K loop)
@@ -1282,7 +1363,7 @@ constexpr int kWideRB = kF32H || BITS == 8 ? kWideRowBlocksF32 : kWideRowBlocks;
 template <bool kF32H, int MAXG, int BITS>
 using GateupWideSmem = WideSmem<kWideRB<kF32H, BITS>, 1, 2, MAXG, BITS>;
 template <bool kF32H, int MAXG, int BITS>
-using DownWideSmem = WideSmem<kWideRB<kF32H, BITS>, kF32H ? 2 : 1, kF32H ? 1 : 2, MAXG, BITS>;
+using DownWideSmem = DownSmem<kWideRB<kF32H, BITS>, kF32H, MAXG, BITS>;
 
 template <bool kF32H, int MAXG, int GS, int BITS>
 __global__ __launch_bounds__(kThreads, (kWideWgsPerCu<GateupWideSmem<kF32H, MAXG, BITS>>)) void moe_gateup_wide(

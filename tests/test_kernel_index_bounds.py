@@ -31,6 +31,7 @@ K_ROUTE_WAVES = 16
 K_ROUTE_SEGMENT = 1024
 K_ROUTE_MULTI_MIN = 2048
 K_SKINNY_DOWN_BLOCKS = 2
+K_PRE_G = 22                      # down wide: group sums read in the prologue up to this many groups
 
 
 def max_groups(gs):
@@ -266,6 +267,15 @@ def check_wide(c, s, kind):
         c.within("down wide: destination read", np.where(tid[None, :] < RB * 16, dsrc, 0), s.A)
         c.within("down wide: h block sums", srow * (s.I // 16) + (GS // 16) * (G - 1) + GS // 16 - 1,
                  s.size["hs"])
+        if G <= K_PRE_G:
+            # the same sums read in the prologue into DownSmem::xg (entry
+            # idx = row * G + g of RB * 16 * kPreG), read back per staged row
+            idx = tid[:, None] + 256 * np.arange(-(-RB * 16 * K_PRE_G // 256))[None, :]
+            ok = idx < RB * 16 * G
+            c.within("down wide: prefetched sum row", np.where(ok, idx // G, 0), RB * 16)
+            c.within("down wide: prefetched sum entry", np.where(ok, idx, 0), RB * 16 * K_PRE_G)
+            c.within("down wide: prefetched sum read", ((tid >> 4)[:, None] + 16 * np.arange(RB)[None, :]) * G + G - 1,
+                     RB * 16 * K_PRE_G)
         rr = 16 * np.arange(RB)[:, None] + 4 * q[None, :]
         for v in range(4):
             rowv = rr + v

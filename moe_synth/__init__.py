@@ -176,11 +176,13 @@ def make_problem(E: int, H: int, I: int, T: int, k: int, seed: int = 0,
                  router: str = "normal", gs: int = GROUP_SIZE, name: str = "custom",
                  topk_ids: Optional[np.ndarray] = None,
                  topk_weights: Optional[np.ndarray] = None, bits: int = 4,
-                 bias: str = "centred") -> Problem:
+                 bias: str = "centred", routing_only: bool = False) -> Problem:
     """Draw one problem.  ``topk_ids``/``topk_weights`` override the router draw
     (the logits are still drawn so the rest of the stream is unchanged).
     ``bits``: 4 (8 codes per uint32 word) or 8 (4 codes per word).
-    ``bias``: "centred" (-2^(bits-1) * scale) or "independent" (see _scales)."""
+    ``bias``: "centred" (-2^(bits-1) * scale) or "independent" (see _scales).
+    ``routing_only``: stop after the router draw (x and the weights are left
+    None): the same ids and routing weights, for checks that need no data."""
     if H % 8 or I % 8 or H % gs or I % gs:
         raise ValueError("H and I must be multiples of 8 and of the group size")
     if bits not in (4, 8):
@@ -196,6 +198,11 @@ def make_problem(E: int, H: int, I: int, T: int, k: int, seed: int = 0,
         ids = np.ascontiguousarray(topk_ids, dtype=np.int32).reshape(T, k)
     if topk_weights is not None:
         w = np.ascontiguousarray(topk_weights, dtype=np.float32).reshape(T, k)
+    if routing_only:
+        return Problem(name=name, seed=seed, E=E, H=H, I=I, T=T, k=k, gs=gs, x=None,
+                       topk_ids=ids, topk_weights=w, w_gateup=None, s_gateup=None,
+                       b_gateup=None, w_down=None, s_down=None, b_down=None, logits=logits,
+                       bits=bits, bias=bias)
     x = f32_to_bf16_bits(rng.standard_normal((T, H), dtype=np.float32))
     w_gu = rng.integers(0, 2**32, size=(E, 2 * I, H * bits // 32), dtype=np.uint32)
     s_gu, b_gu = _scales(rng, (E, 2 * I, H // gs), bits, bias)
@@ -207,8 +214,8 @@ def make_problem(E: int, H: int, I: int, T: int, k: int, seed: int = 0,
                    bits=bits, bias=bias)
 
 
-def make_config(name: str, seed: int = 0) -> Problem:
+def make_config(name: str, seed: int = 0, routing_only: bool = False) -> Problem:
     """One of the five named workloads (see CONFIGS)."""
     c = CONFIGS[name]
     return make_problem(c["E"], c["H"], c["I"], c["T"], c["k"], seed=seed,
-                        router=c["router"], name=name)
+                        router=c["router"], name=name, routing_only=routing_only)

@@ -31,6 +31,7 @@ K_ROUTE_WAVES = 16
 K_ROUTE_SEGMENT = 1024
 K_ROUTE_MULTI_MIN = 2048
 K_SKINNY_DOWN_BLOCKS = 2
+EMU_BATCH = 256                   # items emulated at once
 K_PRE_G = 22                      # down wide: group sums read in the prologue up to this many groups
 
 
@@ -189,6 +190,15 @@ def check_wide(c, s, kind):
     ti, by, _ = wide_items(s, ncol)
     if ti.size == 0:
         return
+    # items in batches: small arrays keep the emulation's memory (and page
+    # faults) low
+    for b0 in range(0, ti.size, EMU_BATCH):
+        _wide_batch(c, s, kind, P, NBUF, RB, BITS, GS, K, N, G, MAXG, sm, ti[b0:b0 + EMU_BATCH],
+                    by[b0:b0 + EMU_BATCH])
+
+
+def _wide_batch(c, s, kind, P, NBUF, RB, BITS, GS, K, N, G, MAXG, sm, ti, by):
+    p = s.p
     e, rbeg, rows = (s.wide[ti, j].astype(np.int64)[:, None] for j in range(3))
     by = by.astype(np.int64)[:, None]
     tid, wave, lane, q, lr = thread_ids()
@@ -301,6 +311,12 @@ def check_skinny(c, s, kind):
     _, ti, cb, _ = skinny_items(s, ncb)
     if ti.size == 0:
         return
+    for b0 in range(0, ti.size, EMU_BATCH):
+        _skinny_batch(c, s, kind, GS, BITS, NB, ncb, K, N, G, ti[b0:b0 + EMU_BATCH], cb[b0:b0 + EMU_BATCH])
+
+
+def _skinny_batch(c, s, kind, GS, BITS, NB, ncb, K, N, G, ti, cb):
+    p = s.p
     e, rbeg, rows = (s.short[ti, j].astype(np.int64)[:, None] for j in range(3))
     cb = cb.astype(np.int64)[:, None]
     lane = np.arange(64)
@@ -413,14 +429,14 @@ def check_problem(oracle, p, fp32):
 def _problem(name, gs=64, bits=4, I=None):
     cfg = ms.CONFIGS[name]
     return ms.make_problem(cfg["E"], cfg["H"], I or cfg["I"], cfg["T"], cfg["k"], seed=0,
-                           router=cfg["router"], gs=gs, bits=bits, name=name)
+                           router=cfg["router"], gs=gs, bits=bits, name=name, routing_only=True)
 
 
 @pytest.mark.parametrize("name", ms.CONFIG_ORDER)
 @pytest.mark.parametrize("fp32", [False, True])
 def test_named_workloads(oracle_lib, name, fp32):
     """The five workloads (8192 assignments included), both modes."""
-    check_problem(oracle_lib, ms.make_config(name), fp32)
+    check_problem(oracle_lib, ms.make_config(name, routing_only=True), fp32)
 
 
 @pytest.mark.parametrize("gs,bits,I", [(32, 4, 704), (128, 4, 768), (64, 8, 704), (32, 8, 704),
@@ -437,7 +453,7 @@ def test_every_expert_33_rows(oracle_lib, fp32, bits):
     all covered by the grid."""
     E, T, k = 128, 528, 8
     ids = (np.arange(T * k, dtype=np.int32) % E).reshape(T, k)
-    p = ms.make_problem(E, 2816, 704, T, k, seed=34, topk_ids=ids, bits=bits, name="e33")
+    p = ms.make_problem(E, 2816, 704, T, k, seed=34, topk_ids=ids, bits=bits, name="e33", routing_only=True)
     s = check_problem(oracle_lib, p, fp32)
     assert len(s.wide) == (2 * E if s.bm_big == 32 else E)
     if s.bm_big == 32:
@@ -464,12 +480,12 @@ def test_wide_tile_count_bound_every_expert_size(oracle_lib, c_rows):
 
 
 def test_invalid_ids_and_tiny_batches(oracle_lib):
-    p = ms.make_config("tiny")
+    p = ms.make_config("tiny", routing_only=True)
     p.topk_ids[3, 0] = p.E
     p.topk_ids[10, 1] = -1
     check_problem(oracle_lib, p, False)
     for T in (1, 5, 16, 17):
-        q = ms.make_problem(128, 2816, 704, T, 8, seed=T, name=f"T{T}")
+        q = ms.make_problem(128, 2816, 704, T, 8, seed=T, name=f"T{T}", routing_only=True)
         check_problem(oracle_lib, q, False)
         check_problem(oracle_lib, q, True)
 
@@ -477,7 +493,7 @@ def test_invalid_ids_and_tiny_batches(oracle_lib):
 def test_checker_catches_a_planted_overrun(oracle_lib):
     """The emulation is not vacuous: the same formulas with a wide grid for
     half the tiles, or a y index one row too far, are reported."""
-    p = ms.make_config("prefill4k")
+    p = ms.make_config("prefill4k", routing_only=True)
     s = Setup(oracle_lib, p, False)
     c = Checker("planted grid")
     s.wide_grid = len(s.wide) // 2

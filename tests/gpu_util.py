@@ -133,6 +133,38 @@ def bias_magnitude(p, experts, h):
     return out
 
 
+def h_model_bound(p, rows):
+    """Per-element bound on |h_kernel - h_exact| before h's own rounding, for
+    the given flat rows (valid ids): the kernels' g and u carry the same
+    error model as y, |dg| <= 2^-14 (sum_k |x W_g| + sum_g (|B| + off |S|)
+    sum_{k in g} |x|) (likewise du), and with |act(g)| <= |g| and |act'| <=
+    1.13 (GELU and SiLU), |dh| <= 1.13 |u| dg + |g| du + 1.13 dg du.  The
+    bias contraction (hi + lo factors) dominates where its term is large
+    against g: few groups and cancelling offsets.  g and u come from numpy
+    here only to size the bound; the reference h is the oracle's."""
+    rows = np.asarray(rows, dtype=np.int64)
+    ids = p.topk_ids.ravel()[rows]
+    x = ms.bf16_bits_to_f32(p.x).astype(np.float64)[rows // p.k]
+    off = 16.0 if p.bits == 4 else 0.0
+    G = p.H // p.gs
+    bound = np.zeros((len(rows), p.I))
+    for e in np.unique(ids):
+        sel = ids == e
+        q = dense_codes(p.w_gateup[e], p.bits).astype(np.float64)           # [2I, H]
+        S = ms.bf16_bits_to_f32(p.s_gateup[e]).astype(np.float64)            # [2I, G]
+        B = ms.bf16_bits_to_f32(p.b_gateup[e]).astype(np.float64)
+        W = q * np.repeat(S, p.gs, axis=1) + np.repeat(B, p.gs, axis=1)
+        xs = x[sel]
+        gu = xs @ W.T
+        mag = np.abs(xs) @ np.abs(W).T
+        xg = np.abs(xs).reshape(len(xs), G, p.gs).sum(-1)
+        mag += xg @ (np.abs(B) + off * np.abs(S)).T
+        d = 2.0 ** -14 * mag
+        g, u, dg, du = gu[:, :p.I], gu[:, p.I:], d[:, :p.I], d[:, p.I:]
+        bound[sel] = 1.13 * np.abs(u) * dg + np.abs(g) * du + 1.13 * dg * du
+    return bound
+
+
 # Worst-case relative rounding of the kernels' fp32 sums against the sum of
 # the terms' magnitudes: n * 2^-24 for n <= 1024 terms is below 2^-14, and
 # the bias contraction's bf16 hi + lo factors are each within 2^-17.

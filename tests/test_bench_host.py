@@ -71,7 +71,7 @@ def test_committed_traffic_summaries():
     digest it was taken on; the benchmark reports its traffic only while that
     digest matches the sources."""
     from bit_gathered_quantized_amd.build import source_digest
-    for k, w in (("moe_gateup_skinny", "decode"), ("moe_gateup_wide", "prefill16k")):
+    for k, w in (("moe_gateup_skinny", "decode"), ("moe_gateup_wide", "prefill16k"), ("moe_gateup_wide", "prefill4k")):
         rec = json.load(open(os.path.join(ROOT, "profiles", f"{k}_{w}_traffic.json")))
         assert rec["kernel"] == k and rec["workload"] == w and rec["bytes_per_launch"] > 0
         assert len(rec["commands"]) == 2 and rec["fetch_scale"] > 0

@@ -179,12 +179,13 @@ __device__ __forceinline__ void write_tile(int32_t* t, int e, int row_begin, int
 }
 
 // Counts, offsets and the tile lists from the per-key totals (s_cnt) and
-// their exclusive scan (s_off), by the first NT threads: the whole block, or
-// wave 0 alone (NT = 64, no barriers).
+// their exclusive scan (s_off), by NT threads: the whole block, or one wave
+// (NT = 64, no barriers).
 template <int NT>
 __device__ void emit_tiles(const RouteArgs& a, int32_t* s_tab, const int32_t* s_cnt, const int32_t* s_off,
                            int32_t* s_toff, int32_t* s_soff, int32_t* s_wsum, int32_t order_status) {
-    const int tid = threadIdx.x, E = a.E, nkeys = E + 1;
+    static_assert((NT & (NT - 1)) == 0, "NT: a power of two");
+    const int tid = static_cast<int>(threadIdx.x) & (NT - 1), E = a.E, nkeys = E + 1;
     auto sync = [] {
         if constexpr (NT == 64) __builtin_amdgcn_wave_barrier(); else __syncthreads();
     };
@@ -283,24 +284,35 @@ __global__ __launch_bounds__(kRouteThreads) void moe_route_sort_tiles(RouteArgs 
     const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
 
     if (A <= 64 && a.presorted == nullptr) {
-        // one row of keys: wave 0 alone, a match-any gives each key's count
-        // (at its lowest lane) and each assignment's rank among equal keys
-        if (wave != 0) return;
-        for (int i = lane; i < nkeys; i += 64) s_cnt[i] = 0;
+        // one row of keys: a match-any gives each key's count (at its lowest
+        // lane) and each assignment's rank among equal keys.  Waves 0 and 1
+        // both count, in LDS of their own; wave 0 then scatters while wave 1
+        // writes counts, offsets and the tile lists.
+        if (wave > 1) return;
+        int32_t* const cnt = wave == 0 ? s_cnt : s_tab;
+        int32_t* const off = wave == 0 ? s_off : s_tab + nkeys;
+        for (int i = lane; i < nkeys; i += 64) cnt[i] = 0;
         const bool act = lane < A;
         const uint32_t key = act ? load_key(a, lane, A, E) : static_cast<uint32_t>(E);
         const uint64_t m = match_any(key, nbits, __ballot(act));
         __builtin_amdgcn_wave_barrier();
-        if (act && (m & below) == 0) s_cnt[key] = __popcll(m);
+        if (act && (m & below) == 0) cnt[key] = __popcll(m);
         __builtin_amdgcn_wave_barrier();
-        wave_exclusive_scan(s_cnt, s_off, nkeys);
+        wave_exclusive_scan(cnt, off, nkeys);
         __builtin_amdgcn_wave_barrier();
-        if (act) {
-            const int32_t slot = s_off[key] + __popcll(m & below);
-            a.perm[slot] = lane;
-            a.inv_perm[lane] = slot;
+        if (wave == 0) {
+            if (act) {
+                const int32_t slot = off[key] + __popcll(m & below);
+                a.perm[slot] = lane;
+                a.inv_perm[lane] = slot;
+            }
+        } else {
+            // wave 1's scratch follows its counts and offsets in s_tab
+            int32_t* const tab = off + nkeys + 1;  // [2 nkeys]
+            int32_t* const toff = tab + 2 * nkeys;  // [nkeys + 1]
+            int32_t* const soff = toff + nkeys + 1; // [nkeys + 1]
+            emit_tiles<64>(a, tab, cnt, off, toff, soff, s_wsum, 0);
         }
-        emit_tiles<64>(a, s_tab, s_cnt, s_off, s_toff, s_soff, s_wsum, 0);
         return;
     }
 
@@ -396,7 +408,7 @@ __global__ __launch_bounds__(kRouteThreads) void moe_route_sort_tiles(RouteArgs 
 // ride in the same launch.  moe_route_scatter: each workgroup forms the totals
 // and its own base per key from hist (sums in workgroup order, so the sort is
 // the same stable sort), ranks its rows with a wave match-any and scatters;
-// workgroup 0 also writes counts, offsets and the tile lists.
+// one more workgroup writes counts, offsets and the tile lists meanwhile.
 __global__ __launch_bounds__(kRouteThreads) void moe_route_count(RouteArgs a) {
     if (static_cast<int>(blockIdx.x) >= a.count_wgs) {
         prepare_x(a, blockIdx.x - a.count_wgs);
@@ -424,6 +436,20 @@ __global__ __launch_bounds__(kRouteThreads) void moe_route_scatter(RouteArgs a) 
     int32_t* const s_toff = s_off + nkeys + 1;              // [nkeys + 1]
     int32_t* const s_soff = s_toff + nkeys + 1;             // [nkeys + 1]
     int32_t* const s_wsum = s_soff + nkeys + 1;             // [waves + 1]
+    if (wg == a.count_wgs) {
+        // the last workgroup writes counts, offsets and the tile lists (from
+        // the same totals), while the others scatter
+        for (int k = tid; k < nkeys; k += kRouteThreads) {
+            int32_t tot = 0;
+#pragma unroll 16
+            for (int w = 0; w < a.count_wgs; ++w) tot += a.hist[static_cast<size_t>(w) * nkeys + k];
+            s_cnt[k] = tot;
+        }
+        __syncthreads();
+        block_exclusive_scan(s_cnt, s_off, nkeys, s_wsum);
+        emit_tiles<kRouteThreads>(a, s_tab, s_cnt, s_off, s_toff, s_soff, s_wsum, 0);
+        return;
+    }
     const int nbits = 32 - __clz(E);
     const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
     for (int i = tid; i < kRouteWaves * nkeys; i += kRouteThreads) s_tab[i] = 0;
@@ -462,7 +488,6 @@ __global__ __launch_bounds__(kRouteThreads) void moe_route_scatter(RouteArgs a) 
         a.perm[slot] = ai;
         a.inv_perm[ai] = slot;
     }
-    if (wg == 0) emit_tiles<kRouteThreads>(a, s_tab, s_cnt, s_off, s_toff, s_soff, s_wsum, 0);
 }
 
 }  // namespace
@@ -497,7 +522,7 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t stream, const KTiming& t
         hipLaunchKernelGGL(moe_route_count, dim3(a.count_wgs + prep), dim3(kRouteThreads), lds1, stream, a);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
-        hipLaunchKernelGGL(moe_route_scatter, dim3(a.count_wgs), dim3(kRouteThreads), lds, stream, a);
+        hipLaunchKernelGGL(moe_route_scatter, dim3(a.count_wgs + 1), dim3(kRouteThreads), lds, stream, a);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
         if (t.stop != nullptr) return hipEventRecord(t.stop, stream);

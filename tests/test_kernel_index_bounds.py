@@ -400,6 +400,13 @@ def check_route_and_combine(c, s):
     if count_wgs:
         ai = np.arange(count_wgs * K_ROUTE_SEGMENT)
         c.within("route: assignment read", ai[ai < s.A], s.A)
+        # the extra scatter workgroup sums hist [count_wgs][nkeys] for the tile lists
+        w, kk = np.meshgrid(np.arange(count_wgs), np.arange(nkeys), indexing="ij")
+        c.within("route: emitter hist read", w * nkeys + kk, count_wgs * nkeys)
+    if s.A <= 64:
+        # one row of keys: wave 1's counts, offsets and emit scratch inside s_tab
+        used = nkeys + (nkeys + 1) + 2 * nkeys + 2 * (nkeys + 1)
+        c.true("route: wave 1 scratch fits s_tab", used <= K_ROUTE_WAVES * nkeys)
     if len(s.wide):
         c.within("route: wide tile store", 4 * (min(len(s.wide), s.max_tiles) - 1) + 3, s.size["tiles"])
     if len(s.short):

@@ -888,8 +888,23 @@ struct alignas(16) WideSmem {
 // (704 columns at group size 32 or 64).  At 4 row blocks the bf16 layout then
 // fills exactly half of a CU's LDS, so two workgroups still share a CU.
 constexpr int kPreG = 22;
+// Down rows of at most kLdsBiasG groups also read their bias rows in the
+// prologue, into LDS beside the scales (the smaller tables leave room), so
+// that the bias term after the K loop waits on no global load.
+constexpr int kLdsBiasG = 16;
+// per-wave biases of its 64 weight rows (64 N per wave), or nothing
+template <int N>
+struct DownBiasTable {
+    uint16_t tb[4 * 64 * N];
+    __device__ __forceinline__ uint16_t* wave_tb(int wave) { return tb + wave * 64 * N; }
+};
+template <>
+struct DownBiasTable<0> {
+    __device__ __forceinline__ uint16_t* wave_tb(int) { return nullptr; }
+};
 template <int RB, bool kF32H, int MAXG, int BITS>
-struct alignas(16) DownSmem : WideSmem<RB, kF32H ? 2 : 1, kF32H ? 1 : 2, MAXG, BITS> {
+struct alignas(16) DownSmem : WideSmem<RB, kF32H ? 2 : 1, kF32H ? 1 : 2, MAXG, BITS>,
+                              DownBiasTable<MAXG <= kLdsBiasG ? MAXG : 0> {
     float xg[RB * 16 * kPreG];
 };
 
@@ -1069,11 +1084,11 @@ __device__ __forceinline__ void stage_group_sums(WideSmem<RB, P, NBUF, MAXG, BIT
 }
 
 // The bias term of the wide paths, added once after the K loop, from the
-// group sums stage_group_sums left in LDS.  br: the wave's bias rows,
-// prefetched during the last chunk.
-template <int GS, int RB, int P, int NBUF, int MAXG, int BITS>
-__device__ __forceinline__ void wide_bias(WideSmem<RB, P, NBUF, MAXG, BITS>& sm,
-                                          const BiasRows<4, Geo<GS>::kMaxG / 32>& br,
+// group sums stage_group_sums left in LDS.  rows(cb): the wave's bias rows of
+// weight block cb in LDS (16 rows of G): from the tables, or staged from the
+// registers that took them during the last chunk (wide_bias_rows).
+template <int GS, int RB, int P, int NBUF, int MAXG, int BITS, class Rows>
+__device__ __forceinline__ void wide_bias(WideSmem<RB, P, NBUF, MAXG, BITS>& sm, Rows&& rows,
                                           int G, bool active, int nrb, f32x4 (&acc)[RB][4]) {
     constexpr int CB = 4, NS = Geo<GS>::kSteps, XS = kXStride<GS>;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, q = lane >> 4, lr = lane & 15;
@@ -1108,13 +1123,11 @@ __device__ __forceinline__ void wide_bias(WideSmem<RB, P, NBUF, MAXG, BITS>& sm,
         for (int rb = 0; rb < RB; ++rb) row_op(rb, X[rb]);
     }
     const uint16_t* ts = sm.ts[wave];
-    uint16_t* const wb = reinterpret_cast<uint16_t*>(sm.w[wave]);
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
-        br.store(wb, cb, G);
-        __builtin_amdgcn_wave_barrier();
+        const uint16_t* const tb = rows(cb);
         BiasOp<NS> C;
-        bias_from_table<NS, kCodeOffset<BITS>>(C, ts + (16 * cb + lr) * G, wb + lr * G, G, q, steps, active);
+        bias_from_table<NS, kCodeOffset<BITS>>(C, ts + (16 * cb + lr) * G, tb + lr * G, G, q, steps, active);
         __builtin_amdgcn_wave_barrier();
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
@@ -1128,6 +1141,21 @@ __device__ __forceinline__ void wide_bias(WideSmem<RB, P, NBUF, MAXG, BITS>& sm,
         }
         __builtin_amdgcn_sched_barrier(0);  // one weight block at a time: registers stay low
     }
+}
+
+// Bias rows of block cb for wide_bias, from registers through the wave's
+// weight buffer (free after the K loop).
+template <int RB, int P, int NBUF, int MAXG, int BITS, int NP>
+__device__ __forceinline__ auto wide_bias_rows(WideSmem<RB, P, NBUF, MAXG, BITS>& sm, const BiasRows<4, NP>& br,
+                                               int G) {
+    uint16_t* const wb = reinterpret_cast<uint16_t*>(sm.w[threadIdx.x >> 6]);
+    return [&sm, &br, wb, G](int cb) -> const uint16_t* {
+        (void)sm;
+        __builtin_amdgcn_wave_barrier();  // the previous block's reads are done
+        br.store(wb, cb, G);
+        __builtin_amdgcn_wave_barrier();
+        return wb;
+    };
 }
 
 // gate|up wide, column block `by` of 128 h columns (ceil(I / 128) blocks).  Wave w owns h columns
@@ -1197,7 +1225,7 @@ __device__ __forceinline__ void gateup_wide(const FfnArgs& a, WideSmem<RB, 1, 2,
                                             last);
 
     stage_group_sums<GS>(sm, G, [&](int i, int j, int) { return xv[i][j]; });
-    wide_bias<GS>(sm, br, G, active, (rows + 15) / 16, acc);
+    wide_bias<GS>(sm, wide_bias_rows(sm, br, G), G, active, (rows + 15) / 16, acc);
 
     // GeGLU epilogue and the 16-column block sums of h
     HOut<kF32H> ho;
@@ -1246,7 +1274,8 @@ __device__ __forceinline__ void down_wide(const FfnArgs& a, DownSmem<RB, kF32H, 
         row0[cb] = static_cast<size_t>(e) * H + cbase + 16 * cb;
         blk[cb] = a.w_d + row0[cb] * (I / 32 * BITS);
     }
-    Tables<CB, false, (MAXG + 31) / 32> tab;
+    constexpr bool kLdsBias = MAXG <= kLdsBiasG;
+    Tables<CB, kLdsBias, (MAXG + 31) / 32> tab;
     tab.load(a.s_d, a.b_d, row0, G);
 
     int hrow[RB];
@@ -1283,7 +1312,8 @@ __device__ __forceinline__ void down_wide(const FfnArgs& a, DownSmem<RB, kF32H, 
             }
         }
     }
-    tab.store(sm.ts[wave], nullptr, G);
+    uint16_t* const tbw = sm.wave_tb(wave);
+    tab.store(sm.ts[wave], kLdsBias ? tbw : nullptr, G);
     st.store(sm, 0);
     if (pre) {
 #pragma unroll
@@ -1304,7 +1334,9 @@ __device__ __forceinline__ void down_wide(const FfnArgs& a, DownSmem<RB, kF32H, 
     for (int cb = 0; cb < CB; ++cb) bblk[cb] = a.b_d + row0[cb] * G;
     BiasRows<CB, Geo<GS>::kMaxG / 32> br;
     wide_kloop<GS, RB, P, NBUF, MAXG, BITS>(sm, st, src, part, blk, I, active, (rows + 15) / 16, code_consts(a.zero), acc,
-                                  [&] { br.load(bblk, G); });
+                                  [&] {
+                                      if constexpr (!kLdsBias) br.load(bblk, G);
+                                  });
 
     if (pre)
         stage_group_sums<GS>(sm, G, [&](int i, int, int g) { return sm.xg[((tid >> 4) + 16 * i) * G + g]; });
@@ -1312,7 +1344,11 @@ __device__ __forceinline__ void down_wide(const FfnArgs& a, DownSmem<RB, kF32H, 
         stage_group_sums<GS>(sm, G, [&](int i, int, int g) {
             return group_of_blocks<GS>(a.hs + static_cast<size_t>(hrow[i]) * (I / 16), g);
         });
-    wide_bias<GS>(sm, br, G, active, (rows + 15) / 16, acc);
+    if constexpr (kLdsBias)
+        wide_bias<GS>(sm, [&](int cb) -> const uint16_t* { return tbw + 16 * cb * G; }, G, active,
+                      (rows + 15) / 16, acc);
+    else
+        wide_bias<GS>(sm, wide_bias_rows(sm, br, G), G, active, (rows + 15) / 16, acc);
 
     if (!active) return;
     // weighted unsort (destinations and weights read before the K loop)
@@ -1457,8 +1493,14 @@ static hipError_t down_wide_gs(const FfnArgs& a, hipStream_t stream, const KTimi
     if (n == 0) return skip_launch(stream, t);
     const int items = n * ((a.H + 255) / 256);
     const dim3 grid((items + kXcds - 1) / kXcds * kXcds);
-    constexpr int kBig = Geo<GS>::kMaxG, kSmall = 3 * kBig / 4;
-    const bool f32 = a.flags & MOE_F_FP32_INTERMEDIATE, small = a.I / GS <= kSmall;
+    constexpr int kBig = Geo<GS>::kMaxG, kSmall = 3 * kBig / 4, kTiny = kLdsBiasG;
+    static_assert(kTiny < kSmall || GS == 128, "table sizes");
+    const bool f32 = a.flags & MOE_F_FP32_INTERMEDIATE;
+    const int G = a.I / GS;
+    if (G <= kTiny)
+        return f32 ? launch_kernel(moe_down_wide<true, kTiny, GS, BITS>, grid, dim3(kThreads), stream, t, a)
+                   : launch_kernel(moe_down_wide<false, kTiny, GS, BITS>, grid, dim3(kThreads), stream, t, a);
+    const bool small = G <= kSmall;
     if (f32)
         return small ? launch_kernel(moe_down_wide<true, kSmall, GS, BITS>, grid, dim3(kThreads), stream, t, a)
                      : launch_kernel(moe_down_wide<true, kBig, GS, BITS>, grid, dim3(kThreads), stream, t, a);

@@ -33,6 +33,7 @@ K_ROUTE_MULTI_MIN = 2048
 K_SKINNY_DOWN_BLOCKS = 2
 EMU_BATCH = 256                   # items emulated at once
 K_PRE_G = 22                      # down wide: group sums read in the prologue up to this many groups
+K_LDS_BIAS_G = 16                 # down wide: bias rows in LDS up to this many groups
 
 
 def max_groups(gs):
@@ -118,9 +119,11 @@ class Setup:
             h_u16=(2 if fp32 else 1) * self.A * p.I, hs=self.A * p.I // 16,
             y=self.A * p.H, out=p.T * p.H)
 
-    def maxg_wide(self, K):
+    def maxg_wide(self, K, kind="gateup"):
         big = max_groups(self.gs)
         small = 3 * big // 4
+        if kind == "down" and K // self.gs <= K_LDS_BIAS_G:
+            return K_LDS_BIAS_G
         return small if K // self.gs <= small else big
 
 
@@ -184,7 +187,7 @@ def check_wide(c, s, kind):
     K = s.H if kind == "gateup" else s.I    # K of the matmul
     N = 2 * s.I if kind == "gateup" else s.H  # weight rows per expert
     G = K // GS
-    MAXG = s.maxg_wide(K)
+    MAXG = s.maxg_wide(K, kind)
     sm = wide_smem_u32(RB, P, NBUF, MAXG, BITS)
     ncol = -(-s.I // 128) if kind == "gateup" else -(-s.H // 256)
     ti, by, _ = wide_items(s, ncol)
@@ -242,8 +245,15 @@ def _wide_batch(c, s, kind, P, NBUF, RB, BITS, GS, K, N, G, MAXG, sm, ti, by):
     # Stager::store and lds_frag: rows below RB * 16, pieces below 16
     c.true("wide: staged activation row stays in its buffer",
            (RB * 16 - 1) * K_ASTRIDE + 4 * 15 + 3 < sm["a_per_buf_part"])
-    # Tables::store into ts[wave]: entries cb * 16 G + 8 idx + 7, idx < 2 G
+    # Tables::store into ts[wave] (and, down with G <= kLdsBiasG, tb[wave] of
+    # the same size): entries cb * 16 G + 8 idx + 7, idx < 2 G
     c.true("wide: scale table fits", 3 * 16 * G + 8 * (2 * G - 1) + 7 < sm["ts_per_wave"])
+    if kind == "down" and G <= K_LDS_BIAS_G:
+        c.true("down wide: bias table fits", 3 * 16 * G + 8 * (2 * G - 1) + 7 < 64 * MAXG)
+        # bias_from_table reads 8 entries from (16 cb + lr) G + 8 q + 32 st of the
+        # wave's rows (masked past G): at most 32 entries past the last row,
+        # inside the struct (the next wave's rows, or the group sums after)
+        c.true("down wide: bias table reads", 63 * G + 8 * 3 + 32 * (-(-G // 32) - 1) + 7 < 64 * MAXG + 32)
     # WaveW put/get rows: 64 rows of 16 * (BITS / 4) u32
     c.true("wide: weight transpose buffer", 64 * 16 * (BITS // 4) <= sm["w_per_wave"])
     # BiasRows::store into the wave's weight buffer (as u16): 16 rows of G

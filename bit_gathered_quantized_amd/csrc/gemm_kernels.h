@@ -13,10 +13,11 @@
 // standing").  Design for gfx950:
 //
 //  * Every product runs on v_mfma_f32_16x16x32_bf16.  The weight operand is
-//    the code itself, exactly (codes_as_bf16: 16 + q for 4-bit codes,
+//    the code itself, exactly (codes_as_bf16: OFF + q for 4-bit codes, OFF =
+//    16 in the fp32 intermediate mode and 128 in the bf16 mode;
 //    bytes_as_bf16: q for 8-bit ones), decoded in registers.  Per group (a
 //    chain of 32 or 64 columns) the fp32 accumulator takes s * P (one FMA per
-//    output per chain); the rest, sum_g (b - 16 s) X, is itself a
+//    output per chain); the rest, sum_g (b - OFF s) X, is itself a
 //    small contraction over groups, run on MFMAs once per tile after the
 //    groups, with both factors split into bf16 hi + lo.  Rounding dequantised
 //    weights to bf16 instead would cost the accuracy the fp32 path needs.
@@ -294,8 +295,8 @@ template <int BITS>
 using WLane = std::conditional_t<BITS == 4, u32x4, u32x8>;
 
 // Slice s's weight operand from the lane's words.
-template <int BITS>
-__device__ __forceinline__ u32x4 slice_operand(const WLane<BITS>& w, int s, CodeConsts kc) {
+template <int BITS, int OFF>
+__device__ __forceinline__ u32x4 slice_operand(const WLane<BITS>& w, int s, CodeConsts<OFF> kc) {
     if constexpr (BITS == 4) {
         return codes_as_bf16(w[s], kc);
     } else {
@@ -308,9 +309,9 @@ __device__ __forceinline__ u32x4 slice_operand(const WLane<BITS>& w, int s, Code
 // together, slice by slice, then each block takes its scaled products in group
 // order -- group_step's arithmetic, pair by pair.  x[s]: slice s's activation
 // operand; wv[b]: block b's weight words.
-template <int GS, int NB, int NSL, int BITS = 4>
+template <int GS, int NB, int NSL, int BITS, int OFF>
 __device__ __forceinline__ void chunk_steps(f32x4 (&acc)[NB], const u32x4 (&x)[4], const WLane<BITS> (&wv)[NB],
-                                            const float (&s16)[NB][Geo<GS>::kChains], CodeConsts kc) {
+                                            const float (&s16)[NB][Geo<GS>::kChains], CodeConsts<OFF> kc) {
     constexpr int MPG = Geo<GS>::kSlices, NG = NSL / MPG;
     static_assert(NSL % MPG == 0, "a chunk holds whole groups");
     f32x4 p[NB][NG];
@@ -320,7 +321,7 @@ __device__ __forceinline__ void chunk_steps(f32x4 (&acc)[NB], const u32x4 (&x)[4
         for (int j = 0; j < NG; ++j)
 #pragma unroll
             for (int b = 0; b < NB; ++b)
-                p[b][j] = mfma16(x[j * MPG + m], slice_operand<BITS>(wv[b], j * MPG + m, kc),
+                p[b][j] = mfma16(x[j * MPG + m], slice_operand<BITS, OFF>(wv[b], j * MPG + m, kc),
                                  m == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : p[b][j]);
 #pragma unroll
     for (int b = 0; b < NB; ++b)
@@ -554,6 +555,7 @@ struct alignas(16) SkinnySmem {
 template <bool kF32H, int RING, int GS, int BITS>
 __global__ __launch_bounds__(64, GS == 32 || BITS == 8 ? 2 : 3) void moe_gateup_skinny(FfnArgs a) {
     constexpr int NB = 2, NS = Geo<GS>::kSteps, GPC = Geo<GS>::kChains, SH = Geo<GS>::kShift;
+    constexpr int OFF = kCodeOffset<BITS, kF32H>;
     __shared__ SkinnySmem<NB, Geo<GS>::kMaxG, BITS> sm;
     int cb;
     const int4 tile = load_skinny_tile(a, a.I / 16, cb);
@@ -616,7 +618,7 @@ __global__ __launch_bounds__(64, GS == 32 || BITS == 8 ? 2 : 3) void moe_gateup_
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
             BiasOp<NS> C;
-            bias_from_table<NS, kCodeOffset<BITS>>(C, sm.ts + (16 * b + lr) * G, sm.tb + (16 * b + lr) * G, G, q,
+            bias_from_table<NS, OFF>(C, sm.ts + (16 * b + lr) * G, sm.tb + (16 * b + lr) * G, G, q,
                                                    steps, true);
             bterm[b] = bias_mfma(X, C, steps);
         }
@@ -626,7 +628,7 @@ __global__ __launch_bounds__(64, GS == 32 || BITS == 8 ? 2 : 3) void moe_gateup_
 #pragma unroll
     for (int b = 0; b < NB; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
     const int nfull = H / 128, nch = (H + 127) / 128;
-    const CodeConsts kc = code_consts(a.zero);
+    const CodeConsts<OFF> kc = code_consts<OFF>(a.zero);
     // chunk c: its weights go through LDS, the slot reloads with chunk c + RING
     // at once, then the MFMAs run (K may end in a half chunk of 64 columns)
     auto compute = [&](int slot, int abuf, int c, bool reload, bool full) {
@@ -696,7 +698,7 @@ __global__ __launch_bounds__(64, GS == 32 || BITS == 8 ? 2 : 3) void moe_gateup_
 template <bool kF32H, int NB, int RING, int GS, int BITS>
 __global__ __launch_bounds__(64, kF32H || GS == 32 || BITS == 8 ? 2 : 3) void moe_down_skinny(FfnArgs a) {
     constexpr int P = kF32H ? 2 : 1, NS = Geo<GS>::kSteps, GPC = Geo<GS>::kChains, MPG = Geo<GS>::kSlices;
-    constexpr int SH = Geo<GS>::kShift;
+    constexpr int SH = Geo<GS>::kShift, OFF = kCodeOffset<BITS, kF32H>;
     constexpr bool kC64 = Geo<GS>::kChain == 64;
     __shared__ SkinnySmem<NB, Geo<GS>::kMaxG, BITS> sm;
     int cb;
@@ -769,7 +771,7 @@ __global__ __launch_bounds__(64, kF32H || GS == 32 || BITS == 8 ? 2 : 3) void mo
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
             BiasOp<NS> C;
-            bias_from_table<NS, kCodeOffset<BITS>>(C, ts + (16 * b + lr) * G, tb + (16 * b + lr) * G, G, q, steps,
+            bias_from_table<NS, OFF>(C, ts + (16 * b + lr) * G, tb + (16 * b + lr) * G, G, q, steps,
                                                    true);
             bterm[b] = bias_mfma(X, C, steps);
         }
@@ -779,7 +781,7 @@ __global__ __launch_bounds__(64, kF32H || GS == 32 || BITS == 8 ? 2 : 3) void mo
 #pragma unroll
     for (int b = 0; b < NB; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
     const int nfull = I / 128, nch = (I + 127) / 128;
-    const CodeConsts kc = code_consts(a.zero);
+    const CodeConsts<OFF> kc = code_consts<OFF>(a.zero);
     // chunk c: its weights go through LDS, the slot reloads with chunk c + RING
     // at once, then the MFMAs run (K may end in a half chunk of 64 columns)
     auto compute = [&](int slot, int abuf, int c, bool reload, bool full) {
@@ -816,7 +818,7 @@ __global__ __launch_bounds__(64, kF32H || GS == 32 || BITS == 8 ? 2 : 3) void mo
                         u32x4 xs2[MPG][P];
 #pragma unroll
                         for (int m = 0; m < MPG; ++m) {
-                            bw[m] = slice_operand<BITS>(wv[b], j * MPG + m, kc);
+                            bw[m] = slice_operand<BITS, OFF>(wv[b], j * MPG + m, kc);
 #pragma unroll
                             for (int pp = 0; pp < P; ++pp) xs2[m][pp] = ra[abuf][j * MPG + m][pp];
                         }
@@ -985,11 +987,11 @@ __device__ __forceinline__ u32x4 lds_frag(const WideSmem<RB, P, NBUF, MAXG, BITS
 // Shared K loop of the wide paths: acc[rb][cb] over all groups for the four
 // 16-row weight blocks blk[cb] of this wave (row length K), activations staged
 // from src (P parts, `part` apart); row blocks rb >= nrb are skipped.
-template <int GS, int RB, int P, int NBUF, int MAXG, int BITS, class Last>
+template <int GS, int RB, int P, int NBUF, int MAXG, int BITS, int OFF, class Last>
 __device__ __forceinline__ void wide_kloop(WideSmem<RB, P, NBUF, MAXG, BITS>& sm, Stager<RB, P>& st,
                                            const uint32_t* const (&src)[RB], size_t part,
                                            const uint32_t* const (&blk)[4], int K, bool active,
-                                           int nrb, CodeConsts kc, f32x4 (&acc)[RB][4], Last&& last) {
+                                           int nrb, CodeConsts<OFF> kc, f32x4 (&acc)[RB][4], Last&& last) {
     constexpr int CB = 4, GPC = Geo<GS>::kChains, MPG = Geo<GS>::kSlices, SH = Geo<GS>::kShift;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, q = lane >> 4, lr = lane & 15;
     const int G = K / GS, nh = K / 64;
@@ -1029,7 +1031,7 @@ __device__ __forceinline__ void wide_kloop(WideSmem<RB, P, NBUF, MAXG, BITS>& sm
 #pragma unroll
                     for (int cb = 0; cb < CB; ++cb) {
 #pragma unroll
-                        for (int m = 0; m < MPG; ++m) bw[cb][m] = slice_operand<BITS>(wq[cb], j * MPG + m, kc);
+                        for (int m = 0; m < MPG; ++m) bw[cb][m] = slice_operand<BITS, OFF>(wq[cb], j * MPG + m, kc);
                         s16[cb] = scale16(sm.ts[wave][(16 * cb + lr) * G + g]);
                     }
 #pragma unroll
@@ -1087,7 +1089,7 @@ __device__ __forceinline__ void stage_group_sums(WideSmem<RB, P, NBUF, MAXG, BIT
 // group sums stage_group_sums left in LDS.  rows(cb): the wave's bias rows of
 // weight block cb in LDS (16 rows of G): from the tables, or staged from the
 // registers that took them during the last chunk (wide_bias_rows).
-template <int GS, int RB, int P, int NBUF, int MAXG, int BITS, class Rows>
+template <int GS, int OFF, int RB, int P, int NBUF, int MAXG, int BITS, class Rows>
 __device__ __forceinline__ void wide_bias(WideSmem<RB, P, NBUF, MAXG, BITS>& sm, Rows&& rows,
                                           int G, bool active, int nrb, f32x4 (&acc)[RB][4]) {
     constexpr int CB = 4, NS = Geo<GS>::kSteps, XS = kXStride<GS>;
@@ -1127,7 +1129,7 @@ __device__ __forceinline__ void wide_bias(WideSmem<RB, P, NBUF, MAXG, BITS>& sm,
     for (int cb = 0; cb < CB; ++cb) {
         const uint16_t* const tb = rows(cb);
         BiasOp<NS> C;
-        bias_from_table<NS, kCodeOffset<BITS>>(C, ts + (16 * cb + lr) * G, tb + lr * G, G, q, steps, active);
+        bias_from_table<NS, OFF>(C, ts + (16 * cb + lr) * G, tb + lr * G, G, q, steps, active);
         __builtin_amdgcn_wave_barrier();
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
@@ -1221,11 +1223,11 @@ __device__ __forceinline__ void gateup_wide(const FfnArgs& a, WideSmem<RB, 1, 2,
             for (int j = 0; j < XJ; ++j) xv[i][j] = pc + 16 * j < G ? xrow[pc + 16 * j] : 0.f;
         }
     };
-    wide_kloop<GS, RB, P, NBUF, MAXG, BITS>(sm, st, src, 0, blk, H, active, (rows + 15) / 16, code_consts(a.zero), acc,
+    wide_kloop<GS, RB, P, NBUF, MAXG, BITS>(sm, st, src, 0, blk, H, active, (rows + 15) / 16, code_consts<kCodeOffset<BITS, kF32H>>(a.zero), acc,
                                             last);
 
     stage_group_sums<GS>(sm, G, [&](int i, int j, int) { return xv[i][j]; });
-    wide_bias<GS>(sm, wide_bias_rows(sm, br, G), G, active, (rows + 15) / 16, acc);
+    wide_bias<GS, kCodeOffset<BITS, kF32H>>(sm, wide_bias_rows(sm, br, G), G, active, (rows + 15) / 16, acc);
 
     // GeGLU epilogue and the 16-column block sums of h
     HOut<kF32H> ho;
@@ -1333,7 +1335,7 @@ __device__ __forceinline__ void down_wide(const FfnArgs& a, DownSmem<RB, kF32H, 
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) bblk[cb] = a.b_d + row0[cb] * G;
     BiasRows<CB, Geo<GS>::kMaxG / 32> br;
-    wide_kloop<GS, RB, P, NBUF, MAXG, BITS>(sm, st, src, part, blk, I, active, (rows + 15) / 16, code_consts(a.zero), acc,
+    wide_kloop<GS, RB, P, NBUF, MAXG, BITS>(sm, st, src, part, blk, I, active, (rows + 15) / 16, code_consts<kCodeOffset<BITS, kF32H>>(a.zero), acc,
                                   [&] {
                                       if constexpr (!kLdsBias) br.load(bblk, G);
                                   });
@@ -1345,10 +1347,10 @@ __device__ __forceinline__ void down_wide(const FfnArgs& a, DownSmem<RB, kF32H, 
             return group_of_blocks<GS>(a.hs + static_cast<size_t>(hrow[i]) * (I / 16), g);
         });
     if constexpr (kLdsBias)
-        wide_bias<GS>(sm, [&](int cb) -> const uint16_t* { return tbw + 16 * cb * G; }, G, active,
+        wide_bias<GS, kCodeOffset<BITS, kF32H>>(sm, [&](int cb) -> const uint16_t* { return tbw + 16 * cb * G; }, G, active,
                       (rows + 15) / 16, acc);
     else
-        wide_bias<GS>(sm, wide_bias_rows(sm, br, G), G, active, (rows + 15) / 16, acc);
+        wide_bias<GS, kCodeOffset<BITS, kF32H>>(sm, wide_bias_rows(sm, br, G), G, active, (rows + 15) / 16, acc);
 
     if (!active) return;
     // weighted unsort (destinations and weights read before the K loop)

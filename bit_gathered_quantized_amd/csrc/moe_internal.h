@@ -53,36 +53,51 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 }
 
 // ------------------------------------------------------------ dequant
-// The eight 4-bit codes of one weight word as eight bf16 values 16 + q:
-// q goes into the top four of the seven mantissa bits of 16.0, which bf16
-// holds exactly.  Element order in the MFMA operand is
-// [q0, q4, q1, q5, q2, q6, q3, q7]; the activation operand is stored in the
-// same order (permute8 below), so each code still meets its own column.
-// With P = sum_k x_k (16 + q_k) and X = sum_k x_k over a 64-column group,
-//   sum_k x_k (s q_k + b) = s P + (b - 16 s) X.
-// The offset 16 (rather than, say, 128 + q) keeps P close in size to the
-// part that carries information, so little is lost when X is taken out.
+// The eight 4-bit codes of one weight word as eight bf16 values OFF + q,
+// exactly: with OFF = 16, q goes into the top four of the seven mantissa
+// bits of 16.0; with OFF = 128, into the bottom four of 128.0, which needs no
+// shift for the first pair (7 instructions per word instead of 8).  Element
+// order in the MFMA operand is [q0, q4, q1, q5, q2, q6, q3, q7]; the
+// activation operand is stored in the same order (permute8 below), so each
+// code still meets its own column.  With P = sum_k x_k (OFF + q_k) and
+// X = sum_k x_k over a group,
+//   sum_k x_k (s q_k + b) = s P + (b - OFF s) X.
+// A small offset keeps P close in size to the part that carries information,
+// so little is lost when X is taken out: the fp32 intermediate mode uses 16;
+// the bf16 mode, whose h is rounded to 8 bits anyway, uses 128.
 //
 // The two constants sit in registers (CodeConsts, built from a zero the
 // compiler cannot see through): folded into literals, each AND-OR below would
 // take two VALU instructions, because gfx9 VOP3 forms such as v_and_or_b32
 // take no literal operand.
+template <int OFF>
 struct CodeConsts {
     uint32_t mask, one;
 };
 // The mask goes to a vector register (a per-lane select on a condition the
 // compiler cannot fold) and the other constant stays scalar: one VOP3
-// instruction may read only one scalar operand.
-__device__ __forceinline__ CodeConsts code_consts(uint32_t zero) {
-    const uint32_t mask = (threadIdx.x & zero) ? 0u : 0x00780078u;
-    return CodeConsts{mask, 0x41804180u | zero};
+// instruction may read only one scalar operand.  (OFF = 0, 8-bit codes: not
+// used.)
+template <int OFF>
+__device__ __forceinline__ CodeConsts<OFF> code_consts(uint32_t zero) {
+    static_assert(OFF == 0 || OFF == 16 || OFF == 128, "code offset");
+    const uint32_t mask = (threadIdx.x & zero) ? 0u : (OFF == 128 ? 0x000F000Fu : 0x00780078u);
+    return CodeConsts<OFF>{mask, (OFF == 128 ? 0x43004300u : 0x41804180u) | zero};
 }
-__device__ __forceinline__ u32x4 codes_as_bf16(uint32_t w, CodeConsts k) {
+template <int OFF>
+__device__ __forceinline__ u32x4 codes_as_bf16(uint32_t w, CodeConsts<OFF> k) {
     u32x4 r;
-    r[0] = ((w << 3) & k.mask) | k.one;  // q0, q4
-    r[1] = ((w >> 1) & k.mask) | k.one;  // q1, q5
-    r[2] = ((w >> 5) & k.mask) | k.one;  // q2, q6
-    r[3] = ((w >> 9) & k.mask) | k.one;  // q3, q7
+    if constexpr (OFF == 128) {
+        r[0] = (w & k.mask) | k.one;          // q0, q4
+        r[1] = ((w >> 4) & k.mask) | k.one;   // q1, q5
+        r[2] = ((w >> 8) & k.mask) | k.one;   // q2, q6
+        r[3] = ((w >> 12) & k.mask) | k.one;  // q3, q7
+    } else {
+        r[0] = ((w << 3) & k.mask) | k.one;  // q0, q4
+        r[1] = ((w >> 1) & k.mask) | k.one;  // q1, q5
+        r[2] = ((w >> 5) & k.mask) | k.one;  // q2, q6
+        r[3] = ((w >> 9) & k.mask) | k.one;  // q3, q7
+    }
     return r;
 }
 // 8-bit codes: the bf16 mantissa cannot take q under a fixed exponent, so
@@ -97,9 +112,10 @@ __device__ __forceinline__ u32x4 bytes_as_bf16(uint32_t w0, uint32_t w1) {
         r[i] = pack_bf16x2(static_cast<float>((w0 >> (8 * i)) & 0xFFu), static_cast<float>((w1 >> (8 * i)) & 0xFFu));
     return r;
 }
-// The code offset of the exact operand: 16 + q for 4-bit codes, q for 8-bit.
-template <int BITS>
-constexpr int kCodeOffset = BITS == 4 ? 16 : 0;
+// The code offset of the exact operand: 16 + q (fp32 intermediate mode) or
+// 128 + q (bf16 mode) for 4-bit codes, q for 8-bit.
+template <int BITS, bool kF32H>
+constexpr int kCodeOffset = BITS == 4 ? (kF32H ? 16 : 128) : 0;
 
 // Position of column c (0..7) of an 8-column piece after permute8.
 __device__ __forceinline__ int permuted_pos(int c) { return ((c & 3) << 1) | (c >> 2); }

@@ -114,12 +114,18 @@ def dense_codes(P: np.ndarray, bits: int) -> np.ndarray:
     return np.stack([b & 0x0F, b >> 4], axis=-1).reshape(*P.shape[:-1], P.shape[-1] * 8)
 
 
-def bias_magnitude(p, experts, h):
+def code_offset(p, fp32):
+    """The kernels' code offset: the 4-bit operand is off + q (16 in the fp32
+    intermediate mode, 128 in the bf16 mode), the 8-bit one q."""
+    return (16.0 if fp32 else 128.0) if p.bits == 4 else 0.0
+
+
+def bias_magnitude(p, experts, h, fp32):
     """sum_g (|B[m, g]| + off |S[m, g]|) sum_{n in g} |h[n]| per row and output
-    column, with off = 16 for 4-bit codes and 0 for 8-bit ones: the size of
-    the bias contraction the down kernels evaluate, sum_g (B - off S) X_g, with
-    both factors split into bf16 hi + lo."""
-    off = 16.0 if p.bits == 4 else 0.0
+    column (off: code_offset): the size of the bias contraction the down
+    kernels evaluate, sum_g (B - off S) X_g, with both factors split into
+    bf16 hi + lo."""
+    off = code_offset(p, fp32)
     G = p.I // p.gs
     out = np.zeros((len(experts), p.H))
     xa = np.abs(h).reshape(len(experts), G, p.gs).sum(-1)
@@ -133,7 +139,7 @@ def bias_magnitude(p, experts, h):
     return out
 
 
-def h_model_bound(p, rows):
+def h_model_bound(p, rows, fp32):
     """Per-element bound on |h_kernel - h_exact| before h's own rounding, for
     the given flat rows (valid ids): the kernels' g and u carry the same
     error model as y, |dg| <= 2^-14 (sum_k |x W_g| + sum_g (|B| + off |S|)
@@ -145,7 +151,7 @@ def h_model_bound(p, rows):
     rows = np.asarray(rows, dtype=np.int64)
     ids = p.topk_ids.ravel()[rows]
     x = ms.bf16_bits_to_f32(p.x).astype(np.float64)[rows // p.k]
-    off = 16.0 if p.bits == 4 else 0.0
+    off = code_offset(p, fp32)
     G = p.H // p.gs
     bound = np.zeros((len(rows), p.I))
     for e in np.unique(ids):
@@ -171,7 +177,7 @@ def h_model_bound(p, rows):
 Y_MODEL_REL = 2.0 ** -14
 
 
-def check_y_model(oracle_lib, p, rows, h_gpu, y_gpu, what="y"):
+def check_y_model(oracle_lib, p, rows, h_gpu, y_gpu, fp32, what="y"):
     """Per-element check of the weighted down output of the given flat rows
     against the oracle's down projection of the kernel's own h (bf16, or
     bf16 hi + lo in fp32 mode): |y_gpu - w y_model| <= 2^-14 w (sum_n |W h| +
@@ -180,7 +186,7 @@ def check_y_model(oracle_lib, p, rows, h_gpu, y_gpu, what="y"):
     valid = (ids >= 0) & (ids < p.E)
     w = p.topk_weights.ravel()[rows].astype(np.float64)[:, None]
     ym, ya = oracle_lib.down_rows(p, np.where(valid, ids, p.E), h_gpu)
-    bound = Y_MODEL_REL * w * (ya + bias_magnitude(p, ids, h_gpu))
+    bound = Y_MODEL_REL * w * (ya + bias_magnitude(p, ids, h_gpu, fp32))
     model = w * ym
     err = np.abs(y_gpu - model)[valid]
     worst = float(np.max(err / np.maximum(bound[valid], 1e-300))) if err.size else 0.0

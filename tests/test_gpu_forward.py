@@ -67,7 +67,7 @@ def compare(oracle_lib, p, fp32, tokens=None, swiglu=False, run=None):
     h = np.where(valid[:, None], h, 0.0)
     # y: weighted, flat order
     y = ws_y_rows(ws, lay, p, rows)
-    ymodel, ybound = check_y_model(oracle_lib, p, rows, h, y)
+    ymodel, ybound = check_y_model(oracle_lib, p, rows, h, y, fp32)
     yref = (ref["y"] * p.topk_weights.ravel()[rows][:, None])[valid]
     o = out[toks]
     if fp32:
@@ -85,7 +85,7 @@ def compare(oracle_lib, p, fp32, tokens=None, swiglu=False, run=None):
             rms = float(np.sqrt(np.mean(ref["h"][valid] ** 2)))
             over = valid & (np.max(np.abs(h - ref["h"]) - half_ulp_bf16(np.maximum(np.abs(h), np.abs(ref["h"]))),
                                    axis=1) > 1e-3 * rms)
-            hb = h_model_bound(p, rows[over])
+            hb = h_model_bound(p, rows[over], fp32)
             err = np.abs(h[over] - ref["h"][over]) - half_ulp_bf16(np.maximum(np.abs(h[over]), np.abs(ref["h"][over])))
             worst = float(np.max(err / np.maximum(hb, 1e-300)))
             log(f"  h: {int(over.sum())} rows over 1e-3 rms; per element excess / model bound max = {worst:.3g}")

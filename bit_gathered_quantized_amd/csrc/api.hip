@@ -98,7 +98,8 @@ moe_ws_layout make_layout(const moe_problem* p) {
     l.h = take(hbytes * A * p->I);
     l.h_sums = take(sizeof(float) * A * (p->I / 16));
     l.y = take(sizeof(float) * A * p->H);
-    l.route_hist = take(sizeof(int32_t) * moe::route_count_wgs(A) * (static_cast<size_t>(p->E) + 1));
+    // per-segment key counts, then one order check per segment (pre-sorted entry)
+    l.route_hist = take(sizeof(int32_t) * moe::route_count_wgs(A) * (static_cast<size_t>(p->E) + 2));
     l.total = off;
     return l;
 }
@@ -157,7 +158,7 @@ moe_status forward_impl(const moe_problem* p, const void* x, const int32_t* ids,
     r.tiles_skinny = reinterpret_cast<int32_t*>(base + l.tiles_skinny);
     r.num_tiles = reinterpret_cast<int32_t*>(base + l.num_tiles);
     r.presorted = presorted;
-    r.count_wgs = presorted != nullptr ? 0 : moe::route_count_wgs(r.A);
+    r.count_wgs = moe::route_count_wgs(r.A);
     r.hist = reinterpret_cast<int32_t*>(base + l.route_hist);
     r.x = static_cast<const uint16_t*>(x);
     r.T = p->T;

@@ -199,9 +199,10 @@ struct RouteArgs {
     // of range, 2 if not a permutation; in both failure cases the kernel sorts
     // by itself.
     const int32_t* presorted;
-    // count_wgs > 0: the sort spreads over that many workgroups of
-    // kRouteSegment assignments, counts in hist [count_wgs][E + 1] (forward
-    // only, no caller's order); 0: one workgroup sorts
+    // count_wgs > 0: the sort (or the check of a caller's order) spreads over
+    // that many workgroups of kRouteSegment assignments, counts in hist
+    // [count_wgs][E + 1], then one order status per segment (forward only);
+    // 0: one workgroup sorts
     int32_t count_wgs;
     int32_t* hist;
     // activation preparation (forward only; x == nullptr skips it)

@@ -409,6 +409,19 @@ __global__ __launch_bounds__(kRouteThreads) void moe_route_sort_tiles(RouteArgs 
 // and its own base per key from hist (sums in workgroup order, so the sort is
 // the same stable sort), ranks its rows with a wave match-any and scatters;
 // one more workgroup writes counts, offsets and the tile lists meanwhile.
+//
+// With a caller's order (the pre-sorted entry) the same segments, of slots,
+// check it in three steps, one per launch (each needs the last one's writes
+// from every workgroup): moe_route_count also checks its slots' range and
+// order and writes inv_perm from the order; moe_route_verify checks that
+// inv_perm maps every slot back to itself (a permutation); moe_route_scatter
+// then uses the order if every segment passed, else sorts as without one.
+// Segment status (after hist): 0 ok, 1 not sorted or out of range, 2 not a
+// permutation.
+__device__ __forceinline__ int32_t* seg_status(const RouteArgs& a) {
+    return a.hist + static_cast<size_t>(a.count_wgs) * (a.E + 1);
+}
+
 __global__ __launch_bounds__(kRouteThreads) void moe_route_count(RouteArgs a) {
     if (static_cast<int>(blockIdx.x) >= a.count_wgs) {
         prepare_x(a, blockIdx.x - a.count_wgs);
@@ -421,9 +434,41 @@ __global__ __launch_bounds__(kRouteThreads) void moe_route_count(RouteArgs a) {
     __syncthreads();
     const int ai = blockIdx.x * kRouteSegment + tid;
     if (ai < a.A) atomicAdd(&s_cnt[load_key(a, ai, a.A, E)], 1);
+    if (a.presorted != nullptr) {
+        // slot ai of the caller's order (the adjacent-pair check of
+        // presorted_order_ok, spread over the segments)
+        bool bad = false;
+        if (ai < a.A) {
+            const int32_t a0 = a.presorted[ai];
+            if (a0 < 0 || a0 >= a.A) {
+                bad = true;
+            } else {
+                a.inv_perm[a0] = ai;
+                if (ai + 1 < a.A) {
+                    const int32_t a1 = a.presorted[ai + 1];
+                    bad = a1 < 0 || a1 >= a.A || key_of(a, a0) > key_of(a, a1);
+                }
+            }
+        }
+        bad = __syncthreads_or(bad);
+        if (tid == 0) seg_status(a)[blockIdx.x] = bad ? 1 : 0;
+    }
     __syncthreads();
     int32_t* const h = a.hist + static_cast<size_t>(blockIdx.x) * nkeys;
     for (int i = tid; i < nkeys; i += kRouteThreads) h[i] = s_cnt[i];
+}
+
+// Pre-sorted entry, second step: every slot of the segment maps back to
+// itself through inv_perm (two slots naming one assignment cannot both).
+__global__ __launch_bounds__(kRouteThreads) void moe_route_verify(RouteArgs a) {
+    const int s = blockIdx.x * kRouteSegment + threadIdx.x;
+    bool bad = false;
+    if (s < a.A) {
+        const int32_t a0 = a.presorted[s];
+        bad = a0 >= 0 && a0 < a.A && a.inv_perm[a0] != s;
+    }
+    bad = __syncthreads_or(bad);
+    if (threadIdx.x == 0 && bad && seg_status(a)[blockIdx.x] == 0) seg_status(a)[blockIdx.x] = 2;
 }
 
 __global__ __launch_bounds__(kRouteThreads) void moe_route_scatter(RouteArgs a) {
@@ -436,6 +481,14 @@ __global__ __launch_bounds__(kRouteThreads) void moe_route_scatter(RouteArgs a) 
     int32_t* const s_toff = s_off + nkeys + 1;              // [nkeys + 1]
     int32_t* const s_soff = s_toff + nkeys + 1;             // [nkeys + 1]
     int32_t* const s_wsum = s_soff + nkeys + 1;             // [waves + 1]
+    // a caller's order: used if every segment passed (1 before 2 if not)
+    int32_t order_status = 0;
+    if (a.presorted != nullptr) {
+        int32_t st = 0;
+        for (int w = tid; w < a.count_wgs; w += kRouteThreads) st |= 1 << seg_status(a)[w];
+        st = __syncthreads_or(st & 2) ? 1 : (__syncthreads_or(st & 4) ? 2 : 0);
+        order_status = st;
+    }
     if (wg == a.count_wgs) {
         // the last workgroup writes counts, offsets and the tile lists (from
         // the same totals), while the others scatter
@@ -447,7 +500,13 @@ __global__ __launch_bounds__(kRouteThreads) void moe_route_scatter(RouteArgs a) 
         }
         __syncthreads();
         block_exclusive_scan(s_cnt, s_off, nkeys, s_wsum);
-        emit_tiles<kRouteThreads>(a, s_tab, s_cnt, s_off, s_toff, s_soff, s_wsum, 0);
+        emit_tiles<kRouteThreads>(a, s_tab, s_cnt, s_off, s_toff, s_soff, s_wsum, order_status);
+        return;
+    }
+    if (a.presorted != nullptr && order_status == 0) {
+        // the order as given (inv_perm came with the first step)
+        const int s = wg * kRouteSegment + tid;
+        if (s < a.A) a.perm[s] = a.presorted[s];
         return;
     }
     const int nbits = 32 - __clz(E);
@@ -509,8 +568,7 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t stream, const KTiming& t
     }
     const size_t lds = route_lds_bytes(a.E);
     if (a.count_wgs > 0) {
-        if (a.presorted != nullptr || a.hist == nullptr || a.count_wgs != route_count_wgs(a.A))
-            return hipErrorInvalidValue;
+        if (a.hist == nullptr || a.count_wgs != route_count_wgs(a.A)) return hipErrorInvalidValue;
         if (lds > 64 * 1024) {
             const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(moe_route_scatter),
                                                      hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -522,6 +580,11 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t stream, const KTiming& t
         hipLaunchKernelGGL(moe_route_count, dim3(a.count_wgs + prep), dim3(kRouteThreads), lds1, stream, a);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
+        if (a.presorted != nullptr) {
+            hipLaunchKernelGGL(moe_route_verify, dim3(a.count_wgs), dim3(kRouteThreads), 0, stream, a);
+            e = hipGetLastError();
+            if (e != hipSuccess) return e;
+        }
         hipLaunchKernelGGL(moe_route_scatter, dim3(a.count_wgs + 1), dim3(kRouteThreads), lds, stream, a);
         e = hipGetLastError();
         if (e != hipSuccess) return e;

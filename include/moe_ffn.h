@@ -216,7 +216,9 @@ typedef struct {
                             one shorter, and `tiles` stays empty         */
     size_t route_hist;   /* int32 [ceil(A/1024), E+1] when A > 2048 (else
                             empty): per-key counts of each 1024-assignment
-                            segment, for the route launches              */
+                            segment, for the route launches; then int32
+                            [ceil(A/1024)]: each segment's check of a
+                            caller's order (pre-sorted entry)            */
 } moe_ws_layout;
 
 moe_status moe_ffn_workspace_layout(const moe_problem* p, moe_ws_layout* layout);
@@ -261,12 +263,14 @@ moe_status moe_expert_ffn_forward(const moe_problem* p, const void* x,
  *                              non-decreasing in s (ids outside [0, E) last);
  *                              any order within an expert; 4-byte aligned
  *
- * The route launch checks the order on the device, as the page's fail-safe
+ * The route launches check the order on the device, as the page's fail-safe
  * does ("Deep-review round": a strided adjacent-pair scan, which holds exactly
  * when the order is globally non-decreasing), and also that it is a
- * permutation.  If a check fails it records why in the workspace's
- * num_tiles[4] and sorts by itself, so the result is always correct and the
- * host never waits.  Results are bit-identical to moe_expert_ffn_forward's
+ * permutation (above 2048 assignments in three launches over 1024-slot
+ * segments, else in one workgroup).  If a check fails they record why in
+ * the workspace's num_tiles[4] (1 not sorted or out of range, 2 not a
+ * permutation) and sort by themselves, so the result is always correct and
+ * the host never waits.  Results are bit-identical to moe_expert_ffn_forward's
  * (they do not depend on the order of rows within an expert).
  */
 moe_status moe_expert_ffn_forward_presorted(const moe_problem* p, const void* x,

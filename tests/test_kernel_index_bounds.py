@@ -117,7 +117,8 @@ class Setup:
             w_d=p.E * p.H * p.I * p.bits // 32, s_d=p.E * p.H * self.Gi,
             tiles=4 * self.max_tiles, tiles_skinny=4 * self.max_skinny,
             h_u16=(2 if fp32 else 1) * self.A * p.I, hs=self.A * p.I // 16,
-            y=self.A * p.H, out=p.T * p.H)
+            y=self.A * p.H, out=p.T * p.H,
+            hist=(-(-self.A // K_ROUTE_SEGMENT) if self.A > K_ROUTE_MULTI_MIN else 0) * (p.E + 2))
 
     def maxg_wide(self, K, kind="gateup"):
         big = max_groups(self.gs)
@@ -412,7 +413,13 @@ def check_route_and_combine(c, s):
         c.within("route: assignment read", ai[ai < s.A], s.A)
         # the extra scatter workgroup sums hist [count_wgs][nkeys] for the tile lists
         w, kk = np.meshgrid(np.arange(count_wgs), np.arange(nkeys), indexing="ij")
-        c.within("route: emitter hist read", w * nkeys + kk, count_wgs * nkeys)
+        c.within("route: emitter hist read", w * nkeys + kk, s.size["hist"])
+        # pre-sorted entry: slot s reads order[s] and order[s + 1] (s + 1 < A),
+        # writes inv_perm only for an assignment in range, and one status per
+        # segment after hist
+        sl = ai[ai < s.A]
+        c.within("route: order read", np.minimum(sl + 1, s.A - 1), s.A)
+        c.within("route: segment status", count_wgs * nkeys + np.arange(count_wgs), s.size["hist"])
     if s.A <= 64:
         # one row of keys: wave 1's counts, offsets and emit scratch inside s_tab
         used = nkeys + (nkeys + 1) + 2 * nkeys + 2 * (nkeys + 1)

@@ -18,7 +18,7 @@ from test_gpu_presorted import _run, _sorted_orders
 
 pytestmark = pytest.mark.gpu
 
-N_CASES = 32
+N_CASES = 96
 
 
 def fuzz_case(i: int):

@@ -56,7 +56,8 @@ class MoeWsLayout(ctypes.Structure):
                 ("counts", "offsets", "perm", "inv_perm", "tiles", "num_tiles", "x_perm", "x_sums",
                  "h", "h_sums", "y", "total")] + \
                [(n, ctypes.c_int32) for n in ("max_tiles", "bm_big", "bm_small", "max_skinny")] + \
-               [("tiles_skinny", ctypes.c_size_t), ("route_hist", ctypes.c_size_t)]
+               [("tiles_skinny", ctypes.c_size_t), ("route_hist", ctypes.c_size_t),
+                ("x8_hi", ctypes.c_size_t), ("x8_lo", ctypes.c_size_t), ("x8_scales", ctypes.c_size_t)]
 
 
 _lib = None

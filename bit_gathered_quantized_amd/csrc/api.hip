@@ -100,6 +100,11 @@ moe_ws_layout make_layout(const moe_problem* p) {
     l.y = take(sizeof(float) * A * p->H);
     // per-segment key counts, then one order check per segment (pre-sorted entry)
     l.route_hist = take(sizeof(int32_t) * moe::route_count_wgs(A) * (static_cast<size_t>(p->E) + 2));
+    // x as e4m3 hi + lo with block scales, for the wide gate|up kernel's fp8 operands
+    const bool fp8 = moe::fp8_wide_gateup(p->T, p->group_size, p->bits, p->flags);
+    l.x8_hi = take(fp8 ? static_cast<size_t>(p->T) * p->H : 0);
+    l.x8_lo = take(fp8 ? static_cast<size_t>(p->T) * p->H : 0);
+    l.x8_scales = take(fp8 ? static_cast<size_t>(p->T) * moe::x8_stride(p->H) : 0);
     l.total = off;
     return l;
 }
@@ -166,6 +171,10 @@ moe_status forward_impl(const moe_problem* p, const void* x, const int32_t* ids,
     r.gs = p->group_size;
     r.xp = reinterpret_cast<uint16_t*>(base + l.x_perm);
     r.xs = reinterpret_cast<float*>(base + l.x_sums);
+    const bool fp8 = moe::fp8_wide_gateup(p->T, p->group_size, p->bits, p->flags);
+    r.x8hi = fp8 ? reinterpret_cast<uint8_t*>(base + l.x8_hi) : nullptr;
+    r.x8lo = fp8 ? reinterpret_cast<uint8_t*>(base + l.x8_lo) : nullptr;
+    r.x8s = fp8 ? reinterpret_cast<uint8_t*>(base + l.x8_scales) : nullptr;
 
     moe::FfnArgs f;
     f.T = p->T;
@@ -183,6 +192,9 @@ moe_status forward_impl(const moe_problem* p, const void* x, const int32_t* ids,
     f.x = static_cast<const uint16_t*>(x);
     f.xp = r.xp;
     f.xs = r.xs;
+    f.x8hi = r.x8hi;
+    f.x8lo = r.x8lo;
+    f.x8s = r.x8s;
     f.hs = reinterpret_cast<float*>(base + l.h_sums);
     f.ids = ids;
     f.topk_w = topk_w;
@@ -262,6 +274,9 @@ moe_status moe_sort_build_tiles(const int32_t* topk_ids, int32_t T, int32_t k, i
     r.H = 0;
     r.xp = nullptr;
     r.xs = nullptr;
+    r.x8hi = nullptr;
+    r.x8lo = nullptr;
+    r.x8s = nullptr;
     return moe::launch_route(r, static_cast<hipStream_t>(stream)) == hipSuccess ? MOE_OK
                                                                                : MOE_ERR_HIP;
 }

@@ -1255,6 +1255,321 @@ __device__ __forceinline__ void gateup_wide(const FfnArgs& a, WideSmem<RB, 1, 2,
         epilogue(std::false_type{});
 }
 
+// ================================================= wide gate|up, fp8 operands
+// bf16 mode with 4-bit codes in 64-column chains (fp8_wide_gateup): the same
+// product on the scaled 32x32x64 fp8 MFMA.  A code q as the e4m3 byte q reads
+// exactly as q * 2^-9, so two masks of a code word give its eight codes as
+// fp8 operands (even nibbles, then odd); the route left x as e4m3 hi + lo
+// with one power-of-two scale per 32 columns (x 2^-e = hi + lo), which the
+// MFMA applies per lane (its row and 32-column half), and the codes take the
+// fixed scale 2^9 (the K order this needs: put_fp8).  Per chain of 64
+// columns and 32x32 block:
+//   P = x_hi . q + x_lo . q,   acc += s P
+// and after the K loop the bias term sum_g b X_g (offset 0: q itself is the
+// operand).  A wave owns 32 h columns: 32-row weight block 0 = the gate rows,
+// block 1 = the matching up rows, so the GeGLU pairs stay in one lane; the
+// 64 rows of a tile are two 32-row blocks.  Output element j of lane l (32x32
+// layout): row 8 (j / 4) + 4 (l / 32) + j % 4, column l % 32.
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ f32x16 mfma_fp8(i32x8 a, i32x8 b, f32x16 c, int sa) {
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, sa, 0, 127 + 9);
+}
+
+// The lane's 32 codes (four words, see put_fp8) as an e4m3 operand: per
+// word the even nibbles (columns 0, 2, 4, 6), then the odd ones.
+__device__ __forceinline__ i32x8 codes_as_fp8(u32x4 w) {
+    i32x8 r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        r[2 * i] = static_cast<int>(w[i] & 0x0F0F0F0Fu);
+        r[2 * i + 1] = static_cast<int>((w[i] >> 4) & 0x0F0F0F0Fu);
+    }
+    return r;
+}
+
+// The wave's weight chunk in LDS.  The MFMA's K order: byte i of a lane in
+// half kh (lane / 32) is K = 32 (i / 16) + 16 kh + i % 16, and the lane's
+// A scale covers K block kh ([32 kh, 32 kh + 32)).  So for chain j (64
+// columns, words 8 j .. 8 j + 7) the lane in half kh takes the words of
+// columns 16 kh + [0, 16) and 32 + 16 kh + [0, 16): words 8 j + 2 kh, +1,
+// 8 j + 4 + 2 kh, +1, kept together as slot 2 j + kh of the row (four
+// 16-byte slots per row, slot s at s ^ ((r >> 1) & 3) so that the 32 rows an
+// operand read touches fall on distinct banks).  A lane loaded words
+// 4 pc .. 4 pc + 3 of its row: the pairs go to slots 2 (pc / 2) and
+// 2 (pc / 2) + 1, at word 2 (pc % 2).
+__device__ __forceinline__ void put_fp8(uint32_t* lds, const u32x4 (&v)[4][1]) {
+    const int lane = threadIdx.x & 63, rr = lane >> 2, pc = lane & 3;
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) {
+        const int r = 16 * cb + rr, sw = (r >> 1) & 3, s0 = 2 * (pc >> 1);
+        uint32_t* const row = lds + 16 * r + 2 * (pc & 1);
+        *reinterpret_cast<u32x2*>(row + 4 * (s0 ^ sw)) = u32x2{v[cb][0][0], v[cb][0][1]};
+        *reinterpret_cast<u32x2*>(row + 4 * ((s0 + 1) ^ sw)) = u32x2{v[cb][0][2], v[cb][0][3]};
+    }
+}
+__device__ __forceinline__ u32x4 get_fp8(const uint32_t* lds, int r, int p) {
+    return *reinterpret_cast<const u32x4*>(lds + 16 * r + 4 * (p ^ ((r >> 1) & 3)));
+}
+
+// The wide gate|up LDS of the fp8 path: the bf16 layout plus the staged rows'
+// block scales (one word per row: the chunk's four 32-column blocks), per
+// activation buffer.
+template <int MAXG>
+struct alignas(16) GateupFp8Smem : WideSmem<4, 1, 2, MAXG, 4> {
+    uint32_t sw8[2][64];
+};
+
+// Activation chunk c of the fp8 path: thread t copies piece t % 16 of rows
+// t / 16 + 16 i -- pieces 0..7 the hi bytes of columns 128 c + 16 p .. + 15,
+// pieces 8..15 the lo bytes -- into the same LDS rows as the bf16 staging
+// (a half chunk past H reads the last half again, never used), and the
+// rows' scale words.
+template <int RB>
+struct Stager8 {
+    u32x4 v[RB];
+    uint32_t w[RB];
+    __device__ __forceinline__ void load(const uint8_t* const (&hi)[RB], const uint8_t* const (&lo)[RB],
+                                         const uint32_t* const (&sc)[RB], int c, int nh) {
+        const int pc = threadIdx.x & 15, q8 = pc & 7;
+        const int col = 64 * min(2 * c + (q8 >> 2), nh - 1) + 16 * (q8 & 3);
+#pragma unroll
+        for (int i = 0; i < RB; ++i) {
+            v[i] = *reinterpret_cast<const u32x4*>((pc < 8 ? hi[i] : lo[i]) + col);
+            w[i] = sc[i][c];  // the row's 16 threads read the same word: no branch in the loop
+        }
+    }
+    template <int MAXG>
+    __device__ __forceinline__ void store(GateupFp8Smem<MAXG>& sm, int buf) const {
+        const int pc = threadIdx.x & 15, r0 = threadIdx.x >> 4;
+#pragma unroll
+        for (int i = 0; i < RB; ++i) {
+            *reinterpret_cast<u32x4*>(&sm.a[buf][0][(r0 + 16 * i) * kAStride + 4 * pc]) = v[i];
+            sm.sw8[buf][r0 + 16 * i] = w[i];  // the same value from the row's 16 threads
+        }
+    }
+};
+
+// sum_g b[n, g] X[m, g] for the wave's four 32x32 blocks, accumulated onto
+// acc by the MFMA: the bias rows of all four weight blocks go to the wave's
+// scale table (free after the K loop: with offset 0 the bias term needs no
+// scale), the group sums are in LDS (stage_group_sums); X enters as bf16
+// hi + lo, b is bf16 already.  Entries past G are zero on the X side and
+// replaced by zero on the b side (they read the next row or stale LDS).
+template <int GS, int MAXG, int NP>
+__device__ __forceinline__ void wide_bias_fp8(GateupFp8Smem<MAXG>& sm, const BiasRows<4, NP>& br, int G,
+                                              int rows, f32x16 (&acc)[2][2]) {
+    constexpr int NS = (Geo<GS>::kMaxG + 15) / 16, XS = kXStride<GS>;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, n = lane & 31, kh = lane >> 5;
+    const float* xl = reinterpret_cast<const float*>(&sm.a[0][0][0]);
+    uint16_t* const tb = sm.ts[wave];
+    __builtin_amdgcn_wave_barrier();  // the wave's scale reads are done
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) br.store(tb + 16 * cb * G, cb, G);
+    __syncthreads();  // the group sums and the bias rows are in place
+    const int steps = (G + 15) / 16;
+#pragma unroll
+    for (int st = 0; st < NS; ++st) {
+        if (st < steps) {
+            const int g0 = 16 * st + 8 * kh;
+            u32x4 b[2];
+#pragma unroll
+            for (int c2 = 0; c2 < 2; ++c2) {
+                const uint16_t* const br16 = tb + (32 * c2 + n) * G + g0;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const uint32_t lo = g0 + 2 * i < G ? br16[2 * i] : 0u;
+                    const uint32_t hi = g0 + 2 * i + 1 < G ? br16[2 * i + 1] : 0u;
+                    b[c2][i] = lo | (hi << 16);
+                }
+            }
+#pragma unroll
+            for (int r2 = 0; r2 < 2; ++r2) {
+                if (32 * r2 < rows) {
+                    const float* const xr = xl + (32 * r2 + n) * XS + g0;
+                    const f32x4 x0 = *reinterpret_cast<const f32x4*>(xr);
+                    const f32x4 x1 = *reinterpret_cast<const f32x4*>(xr + 4);
+                    float v[8];
+#pragma unroll
+                    for (int k = 0; k < 8; ++k) v[k] = g0 + k < G ? (k < 4 ? x0[k] : x1[k - 4]) : 0.f;
+                    u32x4 xh, xo;
+                    pack_split(v, xh, xo);
+#pragma unroll
+                    for (int c2 = 0; c2 < 2; ++c2) {
+                        acc[r2][c2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(xh), as_bf16x8(b[c2]),
+                                                                              acc[r2][c2], 0, 0, 0);
+                        acc[r2][c2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(xo), as_bf16x8(b[c2]),
+                                                                              acc[r2][c2], 0, 0, 0);
+                    }
+                }
+            }
+        }
+    }
+}
+
+template <int GS, int MAXG>
+__device__ __forceinline__ void gateup_wide_fp8(const FfnArgs& a, GateupFp8Smem<MAXG>& sm, int e, int row_begin,
+                                                int rows, int by) {
+    constexpr int RB = 4, CB = 4, SH = Geo<GS>::kShift;
+    const int tid = threadIdx.x, lane = tid & 63, n = lane & 31, kh = lane >> 5;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: weight rows are per wave
+    const int H = a.H, I = a.I, G = H / GS, S8 = x8_stride(H);
+    const size_t A = static_cast<size_t>(a.T) * a.k;
+    const int n0 = by * 128;
+    const bool active = n0 + 32 * wave < I;
+    const int hbase = active ? n0 + 32 * wave : 0;
+
+    // weight blocks: 0/1 the gate rows hbase + [0, 32), 2/3 the up rows
+    size_t row0[CB];
+    const uint32_t* blk[CB];
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+        row0[cb] = static_cast<size_t>(e) * 2 * I + hbase + 16 * (cb & 1) + (cb >> 1) * I;
+        blk[cb] = a.w_gu + row0[cb] * (H / 8);
+    }
+    Tables<CB, false, (MAXG + 31) / 32> tab;
+    tab.load(a.s_gu, a.b_gu, row0, G);
+
+    int tok[RB];
+    const uint8_t* shi[RB];
+    const uint8_t* slo[RB];
+    const uint32_t* ssc[RB];
+#pragma unroll
+    for (int i = 0; i < RB; ++i) {
+        const int r = (tid >> 4) + 16 * i;
+        tok[i] = a.perm[row_begin + min(r, rows - 1)] / a.k;
+        shi[i] = a.x8hi + static_cast<size_t>(tok[i]) * H;
+        slo[i] = a.x8lo + static_cast<size_t>(tok[i]) * H;
+        ssc[i] = reinterpret_cast<const uint32_t*>(a.x8s + static_cast<size_t>(tok[i]) * S8);
+    }
+    const int nh = H / 64, nch = (H + 127) / 128;
+    Stager8<RB> st;
+    st.load(shi, slo, ssc, 0, nh);
+    tab.store(sm.ts[wave], nullptr, G);
+    st.store(sm, 0);
+
+    f32x16 acc[2][2];
+#pragma unroll
+    for (int r2 = 0; r2 < 2; ++r2)
+#pragma unroll
+        for (int c2 = 0; c2 < 2; ++c2) acc[r2][c2] = f32x16{};
+
+    const uint16_t* bblk[CB];
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) bblk[cb] = a.b_gu + row0[cb] * G;
+    BiasRows<CB, Geo<GS>::kMaxG / 32> br;
+    constexpr int XJ = (MAXG + 15) / 16;
+    float xv[RB][XJ];
+    auto last = [&] {
+        br.load(bblk, G);
+        const int pc = tid & 15;
+#pragma unroll
+        for (int i = 0; i < RB; ++i) {
+            const float* xrow = a.xs + static_cast<size_t>(tok[i]) * G;
+#pragma unroll
+            for (int j = 0; j < XJ; ++j) xv[i][j] = pc + 16 * j < G ? xrow[pc + 16 * j] : 0.f;
+        }
+    };
+
+    uint32_t* const wl = sm.w[wave];
+    WaveW<CB, GS, 4> ww;
+    ww.init(wl, blk, H / 8);
+    u32x4 wn[CB][1];
+    ww.load(0, wn);
+    put_fp8(wl, wn);
+    __syncthreads();  // chunk 0 and the scale tables are in place
+
+    auto chunk = [&](int c, auto last_tag) {
+        constexpr bool kLast = decltype(last_tag)::value;
+        const int buf = c & 1;
+        u32x4 wq[2][2];
+#pragma unroll
+        for (int c2 = 0; c2 < 2; ++c2)
+#pragma unroll
+            for (int j = 0; j < 2; ++j) wq[c2][j] = get_fp8(wl, 32 * c2 + n, 2 * j + kh);
+        // the block scales of the lane's two rows (the chunk's four blocks)
+        const uint32_t cur[2] = {sm.sw8[buf][n], sm.sw8[buf][32 + n]};
+        if constexpr (!kLast) {
+            st.load(shi, slo, ssc, c + 1, nh);
+            ww.load(c + 1, wn);
+        } else {
+            last();
+        }
+        if (active) {
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const int ch = 2 * c + j;  // chain of 64 columns; its group is ch >> SH
+                if (ch < nh) {
+                    const int g = ch >> SH;
+                    i32x8 b[2];
+                    float s16[2];
+#pragma unroll
+                    for (int c2 = 0; c2 < 2; ++c2) {
+                        b[c2] = codes_as_fp8(wq[c2][j]);
+                        s16[c2] = scale16(sm.ts[wave][(32 * c2 + n) * G + g]);
+                    }
+#pragma unroll
+                    for (int r2 = 0; r2 < 2; ++r2) {
+                        if (32 * r2 < rows) {
+                            // columns 16 kh + [0, 16) and 32 + 16 kh + [0, 16) of the chain
+                            const int row = 32 * r2 + n, p0 = 4 * j + kh;
+                            const u32x4 h0 = lds_frag(sm, buf, 0, row, p0), h1 = lds_frag(sm, buf, 0, row, p0 + 2);
+                            const u32x4 l0 = lds_frag(sm, buf, 0, row, 8 + p0), l1 = lds_frag(sm, buf, 0, row, 10 + p0);
+                            const i32x8 xh = {static_cast<int>(h0[0]), static_cast<int>(h0[1]), static_cast<int>(h0[2]),
+                                              static_cast<int>(h0[3]), static_cast<int>(h1[0]), static_cast<int>(h1[1]),
+                                              static_cast<int>(h1[2]), static_cast<int>(h1[3])};
+                            const i32x8 xo = {static_cast<int>(l0[0]), static_cast<int>(l0[1]), static_cast<int>(l0[2]),
+                                              static_cast<int>(l0[3]), static_cast<int>(l1[0]), static_cast<int>(l1[1]),
+                                              static_cast<int>(l1[2]), static_cast<int>(l1[3])};
+                            const int sa = static_cast<int>((cur[r2] >> (8 * (2 * j + kh))) & 0xFFu);
+#pragma unroll
+                            for (int c2 = 0; c2 < 2; ++c2) {
+                                f32x16 pz = {};
+                                pz = mfma_fp8(xh, b[c2], pz, sa);
+                                pz = mfma_fp8(xo, b[c2], pz, sa);
+#pragma unroll
+                                for (int v = 0; v < 16; ++v) acc[r2][c2][v] = fmaf(s16[c2], pz[v], acc[r2][c2][v]);
+                            }
+                        }
+                    }
+                }
+            }
+        }
+        __builtin_amdgcn_wave_barrier();
+        if constexpr (!kLast) {
+            put_fp8(wl, wn);
+            st.store(sm, buf ^ 1);
+        }
+        __syncthreads();
+    };
+    for (int c = 0; c + 1 < nch; ++c) chunk(c, std::false_type{});
+    chunk(nch - 1, std::true_type{});
+
+    stage_group_sums<GS>(sm, G, [&](int i, int j, int) { return xv[i][j]; });
+    wide_bias_fp8<GS>(sm, br, G, rows, acc);
+
+    // GeGLU epilogue and the 16-column block sums of h
+    HOut<false> ho;
+    ho.init(a, A, row_begin, rows, active);
+    auto epilogue = [&](auto silu_tag) {
+#pragma unroll
+        for (int r2 = 0; r2 < 2; ++r2) {
+            if (32 * r2 >= rows) break;  // rows past the tile
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int r = 32 * r2 + 8 * (v >> 2) + 4 * kh + (v & 3);
+                const float seen = ho.template put<decltype(silu_tag)::value>(r, hbase + n, acc[r2][0][v],
+                                                                              acc[r2][1][v]);
+                ho.put_sum(r, hbase / 16 + (n >> 4), seen, lane & 15);
+            }
+        }
+    };
+    if (a.flags & MOE_F_SWIGLU)
+        epilogue(std::true_type{});
+    else
+        epilogue(std::false_type{});
+}
+
 // down wide, column block `by` of 256 output columns (ceil(H / 256) blocks).  Wave w owns output columns
 // n0 + 64 w + [0, 64): four 16-row weight blocks.
 template <int GS, int RB, int MAXG, bool kF32H, int BITS>
@@ -1402,15 +1717,27 @@ template <bool kF32H, int MAXG, int BITS>
 using GateupWideSmem = WideSmem<kWideRB<kF32H, BITS>, 1, 2, MAXG, BITS>;
 template <bool kF32H, int MAXG, int BITS>
 using DownWideSmem = DownSmem<kWideRB<kF32H, BITS>, kF32H, MAXG, BITS>;
+// The wide gate|up takes fp8 operands in bf16 mode with 4-bit codes in
+// 64-column chains (the host prepares x for it under the same condition).
+template <bool kF32H, int GS, int BITS>
+constexpr bool kFp8Gateup = !kF32H && BITS == 4 && Geo<GS>::kChain == 64;
+template <bool kF32H, int MAXG, int GS, int BITS>
+using GateupSmem = std::conditional_t<kFp8Gateup<kF32H, GS, BITS>, GateupFp8Smem<MAXG>,
+                                      GateupWideSmem<kF32H, MAXG, BITS>>;
 
 template <bool kF32H, int MAXG, int GS, int BITS>
-__global__ __launch_bounds__(kThreads, (kWideWgsPerCu<GateupWideSmem<kF32H, MAXG, BITS>>)) void moe_gateup_wide(
+__global__ __launch_bounds__(kThreads, (kWideWgsPerCu<GateupSmem<kF32H, MAXG, GS, BITS>>)) void moe_gateup_wide(
     FfnArgs a) {
-    __shared__ GateupWideSmem<kF32H, MAXG, BITS> sm;
     int ti, by;
     if (!wide_work(a, (a.I + 127) / 128, ti, by)) return;
     const int4 tile = reinterpret_cast<const int4*>(a.tiles)[ti];
-    gateup_wide<GS, kWideRB<kF32H, BITS>, MAXG, kF32H, BITS>(a, sm, tile.x, tile.y, tile.z, by);
+    if constexpr (kFp8Gateup<kF32H, GS, BITS>) {
+        __shared__ GateupFp8Smem<MAXG> sm;
+        gateup_wide_fp8<GS, MAXG>(a, sm, tile.x, tile.y, tile.z, by);
+    } else {
+        __shared__ GateupWideSmem<kF32H, MAXG, BITS> sm;
+        gateup_wide<GS, kWideRB<kF32H, BITS>, MAXG, kF32H, BITS>(a, sm, tile.x, tile.y, tile.z, by);
+    }
 }
 
 template <bool kF32H, int MAXG, int GS, int BITS>

@@ -30,6 +30,18 @@ constexpr int kRouteWaves = kRouteThreads / 64;
 constexpr int kBmBig = 64;
 constexpr int kBmBigF32 = 32;  // with MOE_F_FP32_INTERMEDIATE or 8-bit codes
 constexpr int kBmSmall = 16;
+// The fp8 operand path of the wide gate|up kernel: bf16 mode, 4-bit codes in
+// groups of 64 or 128 columns, batches that can have wide tiles.  The code q
+// as an e4m3 byte reads exactly as q * 2^-9 (subnormal below 8, and the
+// normal binade from 8 on continues the same step), and x splits exactly into
+// e4m3 hi + lo under a power-of-two scale per 32 columns.
+inline bool fp8_wide_gateup(int64_t T, int gs, int bits, uint32_t flags) {
+    return T > kBmSmall && bits == 4 && (gs == 64 || gs == 128) && !(flags & MOE_F_FP32_INTERMEDIATE);
+}
+// Bytes per row of the block scales: H / 32, rounded up to 4 (a chunk of 128
+// columns reads its four scales as one word; a final half chunk reads two
+// padding bytes, unused).
+__host__ __device__ inline int x8_stride(int H) { return (H / 32 + 3) / 4 * 4; }
 // Largest H and I the kernels take (the scale and bias tables in LDS and the
 // bias contraction are sized for it).
 constexpr int kMaxDim = 4096;
@@ -211,6 +223,11 @@ struct RouteArgs {
     int32_t gs;         // quantisation group size: 32, 64 or 128
     uint16_t* xp;       // [T, H] bf16, pieces reordered by permute8
     float* xs;          // [T, H/gs] group sums
+    // x as e4m3 hi + lo under a power-of-two scale per 32 columns (nullptr:
+    // not written; see x8_stride)
+    uint8_t* x8hi;      // [T, H] e4m3, each 8-column piece in the order 0,2,4,6,1,3,5,7
+    uint8_t* x8lo;      // [T, H] e4m3, the remainder x * 2^-e - hi, same order
+    uint8_t* x8s;       // [T, x8_stride(H)] e8m0 block scales (127 + e)
 };
 hipError_t launch_route(const RouteArgs& a, hipStream_t stream, const KTiming& t = {});
 constexpr int kRouteSegment = kRouteThreads;  // assignments per counting workgroup
@@ -229,6 +246,9 @@ struct FfnArgs {
     const uint16_t* x;
     const uint16_t* xp;  // [T, H] x with pieces reordered by permute8
     const float* xs;     // [T, H/gs] group sums of x
+    const uint8_t* x8hi;  // x split into e4m3 hi + lo with block scales (RouteArgs)
+    const uint8_t* x8lo;
+    const uint8_t* x8s;
     float* hs;           // [A, I/16] sums of h over 16-column blocks (as the down matmul sees it)
     const int32_t* ids;
     const float* topk_w;

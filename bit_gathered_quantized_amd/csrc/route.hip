@@ -115,6 +115,18 @@ __device__ void wave_exclusive_scan(const int32_t* in, int32_t* out, int n) {
 // term.  Thread p handles piece p of the [T, H/8] piece grid; the gs/8 pieces
 // of a group are that many consecutive lanes (gs divides H, so a group never
 // straddles two rows).
+// Four values (already scaled) as e4m3 hi bytes (.x) and the e4m3 bytes of
+// their remainders v - hi (.y), value i in byte i, rounded to nearest even.
+__device__ __forceinline__ uint2 fp8_quad(float v0, float v1, float v2, float v3) {
+    int h = __builtin_amdgcn_cvt_pk_fp8_f32(v0, v1, 0, false);
+    h = __builtin_amdgcn_cvt_pk_fp8_f32(v2, v3, h, true);
+    int l = __builtin_amdgcn_cvt_pk_fp8_f32(v0 - __builtin_amdgcn_cvt_f32_fp8(h, 0),
+                                            v1 - __builtin_amdgcn_cvt_f32_fp8(h, 1), 0, false);
+    l = __builtin_amdgcn_cvt_pk_fp8_f32(v2 - __builtin_amdgcn_cvt_f32_fp8(h, 2),
+                                        v3 - __builtin_amdgcn_cvt_f32_fp8(h, 3), l, true);
+    return make_uint2(static_cast<uint32_t>(h), static_cast<uint32_t>(l));
+}
+
 __device__ void prepare_x(const RouteArgs& a, int block) {
     const int pieces_per_row = a.H / 8;
     const int lanes = a.gs / 8;  // 4, 8 or 16
@@ -128,9 +140,42 @@ __device__ void prepare_x(const RouteArgs& a, int block) {
     s += __shfl_xor(s, 2);
     if (lanes >= 8) s += __shfl_xor(s, 4);
     if (lanes >= 16) s += __shfl_xor(s, 8);
+    // x as e4m3 hi + lo (fp8 wide path): the block of 32 columns (4 lanes)
+    // takes the scale 2^e with max |x| * 2^-e in [128, 256) (e4m3 holds up to
+    // 448); hi = e4m3(x 2^-e) to nearest even, lo = e4m3(x 2^-e - hi), exact
+    // down to |x 2^-e| = 1/4 (the remainder has at most 4 significant bits)
+    float m = 0.f;
+    float f[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        f[2 * i] = bf16_to_f32(static_cast<uint16_t>(v[i] & 0xFFFFu));
+        f[2 * i + 1] = bf16_to_f32(static_cast<uint16_t>(v[i] >> 16));
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(f[i]));
+    m = fmaxf(m, __shfl_xor(m, 1));
+    m = fmaxf(m, __shfl_xor(m, 2));
     if (!ok) return;
     reinterpret_cast<u32x4*>(a.xp)[p] = permute8(v);
     if ((p & (lanes - 1)) == 0) a.xs[p / lanes] = s;
+    if (a.x8hi != nullptr) {
+        int ex = 0;
+        if (m > 0.f) {
+            (void)frexpf(m, &ex);
+            ex -= 8;
+        }
+        ex = min(max(ex, -127), 127);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) f[i] = ldexpf(f[i], -ex);
+        // piece order 0,2,4,6 | 1,3,5,7: the even and odd nibbles of a code word
+        const uint2 ev = fp8_quad(f[0], f[2], f[4], f[6]), od = fp8_quad(f[1], f[3], f[5], f[7]);
+        reinterpret_cast<u32x2*>(a.x8hi)[p] = u32x2{ev.x, od.x};
+        reinterpret_cast<u32x2*>(a.x8lo)[p] = u32x2{ev.y, od.y};
+        if ((p & 3) == 0) {
+            const int64_t t = p / pieces_per_row, blk = (p - t * pieces_per_row) / 4;
+            a.x8s[t * x8_stride(a.H) + blk] = static_cast<uint8_t>(127 + ex);
+        }
+    }
 }
 
 // Key of flat assignment a (its expert id, or E for an out-of-range id).

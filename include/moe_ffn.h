@@ -219,6 +219,15 @@ typedef struct {
                             segment, for the route launches; then int32
                             [ceil(A/1024)]: each segment's check of a
                             caller's order (pre-sorted entry)            */
+    size_t x8_hi;        /* e4m3 [T, H] and                                 */
+    size_t x8_lo;        /* e4m3 [T, H]: x * 2^-e = hi + lo, each 8-column
+                            piece in the order 0,2,4,6,1,3,5,7, with one e
+                            per 32 columns                                 */
+    size_t x8_scales;    /* uint8 [T, H/32 rounded up to 4]: 127 + e.
+                            These three are empty unless the wide gate|up
+                            matmul takes fp8 operands: more than bm_small
+                            tokens, 4-bit codes in groups of 64 or 128,
+                            without MOE_F_FP32_INTERMEDIATE                */
 } moe_ws_layout;
 
 moe_status moe_ffn_workspace_layout(const moe_problem* p, moe_ws_layout* layout);

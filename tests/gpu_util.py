@@ -195,6 +195,27 @@ def check_y_model(oracle_lib, p, rows, h_gpu, y_gpu, fp32, what="y"):
     return model, bound
 
 
+def fp8_wide_gateup(p, fp32: bool) -> bool:
+    """Whether the forward's wide gate|up matmul takes fp8 operands (x as
+    e4m3 hi + lo, the codes as e4m3 bytes): bf16 mode, 4-bit codes in groups
+    of 64 or 128, more than 16 tokens.  Its sums then differ in the last
+    bits from the skinny path's exact bf16 operand."""
+    return (not fp32) and p.bits == 4 and p.gs in (64, 128) and p.T > 16
+
+
+def assert_same_or_within(a, b, same_path: bool, bound, what=""):
+    """Outputs of the same tokens from two forwards: the same bits when both
+    took paths of one arithmetic; otherwise within the sum of the two runs'
+    per-element model bounds (each already checked against the oracle)."""
+    if same_path:
+        np.testing.assert_array_equal(a, b)
+        return
+    d = np.abs(a - b)
+    log(f"  {what}: paths differ; {int(np.count_nonzero(d))} of {d.size} elements differ, "
+        f"max |a - b| / bound = {float(np.max(d / np.maximum(bound, 1e-300))):.3g}")
+    assert np.all(d <= bound), f"{what}: apart by more than the two model bounds"
+
+
 def half_ulp_bf16(v: np.ndarray) -> np.ndarray:
     v = np.abs(v)
     e = np.floor(np.log2(np.maximum(v, 1e-38)))

@@ -49,7 +49,11 @@ def test_workspace_layout_and_sizes():
     # per-key counts of each 1024-assignment segment for the route launches
     assert lay.total - lay.route_hist >= (A // 1024) * 129 * 4
     small = bgq.workspace_layout(bgq.problem(256, 8, 128, 2816, 704))
-    assert small.total == small.route_hist  # 2048 assignments: one workgroup sorts
+    assert small.x8_hi == small.route_hist  # 2048 assignments: one workgroup sorts
+    # x as e4m3 hi + lo with a scale byte per 32 columns (rows padded to 4 bytes)
+    assert lay.x8_lo - lay.x8_hi >= 2048 * 2816 and lay.x8_scales - lay.x8_lo >= 2048 * 2816
+    assert lay.total - lay.x8_scales >= 2048 * 88
+    assert lay.x8_hi >= lay.route_hist
     assert lay.y - lay.h_sums >= A * (704 // 16) * 4  # 16-column block sums of h
     assert lay.bm_big == 64 and lay.bm_small == 16
     assert lay.max_tiles == A // 64 + 128
@@ -60,6 +64,21 @@ def test_workspace_layout_and_sizes():
     p32 = bgq.problem(2048, 8, 128, 2816, 704, bgq.MOE_F_FP32_INTERMEDIATE)
     l32 = bgq.workspace_layout(p32)
     assert l32.h_sums - l32.h >= A * 704 * 4
+
+
+@pytest.mark.parametrize("T,flags,gs,bits,fp8", [
+    (17, 0, 64, 4, True), (2048, 0, 128, 4, True), (16, 0, 64, 4, False),
+    (2048, 2, 64, 4, False), (2048, 0, 32, 4, False), (2048, 0, 64, 8, False)])
+def test_fp8_activation_layout(T, flags, gs, bits, fp8):
+    """The fp8 copies of x exist exactly when the wide gate|up matmul takes
+    fp8 operands: more than 16 tokens, bf16 mode, 4-bit codes in groups of
+    64 or 128."""
+    I = 768 if gs == 128 else 704
+    lay = bgq.workspace_layout(bgq.problem(T, 8, 128, 2816, I, flags, group_size=gs, bits=bits))
+    size = lay.total - lay.x8_hi
+    assert (size > 0) == fp8
+    if fp8:
+        assert size >= T * 2816 * 2 + T * 88
 
 
 @pytest.mark.parametrize("kw,status", [

@@ -119,6 +119,10 @@ class Setup:
             h_u16=(2 if fp32 else 1) * self.A * p.I, hs=self.A * p.I // 16,
             y=self.A * p.H, out=p.T * p.H,
             hist=(-(-self.A // K_ROUTE_SEGMENT) if self.A > K_ROUTE_MULTI_MIN else 0) * (p.E + 2))
+        # fp8_wide_gateup: x as e4m3 hi + lo and a scale byte per 32 columns
+        self.fp8 = (p.T > K_BM_SMALL and p.bits == 4 and p.gs in (64, 128) and not fp32)
+        self.S8 = (p.H // 32 + 3) // 4 * 4
+        self.size.update(x8=p.T * p.H if self.fp8 else 0, x8s=p.T * self.S8 if self.fp8 else 0)
 
     def maxg_wide(self, K, kind="gateup"):
         big = max_groups(self.gs)
@@ -438,6 +442,55 @@ def check_route_and_combine(c, s):
     c.within("combine: out store", (s.T - 1) * s.H + s.H - 1, s.size["out"])
 
 
+K_FP8_SMEM_SW = 2 * 64                  # GateupFp8Smem::sw8, u32
+
+
+def check_fp8_gateup(c, s):
+    """prepare_x's fp8 split (route.hip) and gateup_wide_fp8 with Stager8,
+    put_fp8 / get_fp8, wide_bias_fp8 (csrc/gemm_kernels.h)."""
+    if not s.fp8:
+        return
+    T, H = s.T, s.H
+    # prepare_x: piece p (8 columns) writes bytes 8p .. 8p + 7 of hi and lo,
+    # and the first of every 4 pieces one scale byte t * S8 + block
+    pieces = np.arange(T * H // 8)
+    c.within("x8: hi/lo piece store", 8 * pieces + 7, s.size["x8"])
+    t = pieces // (H // 8)
+    blk = (pieces - t * (H // 8)) // 4
+    c.within("x8: scale store", t * s.S8 + blk, s.size["x8s"])
+    c.true("x8: the scale row holds every block", H // 32 <= s.S8 and s.S8 % 4 == 0)
+    ti, by, _ = wide_items(s, -(-s.I // 128))
+    if ti.size == 0:
+        return
+    nh, nch = H // 64, -(-H // 128)
+    # Stager8: row token tok, chunk c: hi/lo bytes at 64 min(2c + h, nh - 1) + 16 q .. + 15
+    cc = np.arange(nch)
+    col_last = 64 * np.minimum(2 * cc + 1, nh - 1) + 16 * 3 + 15
+    c.within("fp8 gate|up: x8 row read", int(col_last.max()), H)
+    c.within("fp8 gate|up: scale word read (bytes)", 4 * (nch - 1) + 3, s.S8)
+    tok = s.perm[s.wide[ti, 1].astype(np.int64) + np.minimum(63, s.wide[ti, 2].astype(np.int64) - 1)] // s.k
+    c.within("fp8 gate|up: token", tok, T)
+    # LDS: staged rows 0..63, pieces 0..15 (hi 0..7, lo 8..15); the MFMA reads
+    # pieces 4 j + kh, + 2 and 8 + those; scale words sw8[buf][0..63]
+    j, kh = np.meshgrid(np.arange(2), np.arange(2), indexing="ij")
+    c.within("fp8 gate|up: activation piece read", 10 + 4 * j + kh, 16)
+    c.within("fp8 gate|up: staged row read", 32 + 31, 64)
+    c.true("fp8 gate|up: scale words fit", 64 <= K_FP8_SMEM_SW // 2)
+    # weights: row 16 cb + lane / 4 (< 64), slot (2 (pc / 2) + {0, 1}) ^ ((r >> 1) & 3) < 4,
+    # 16 u32 per row: the wave's 64 x 16 u32 buffer
+    r = np.arange(64)[:, None]
+    pc = np.arange(4)[None, :]
+    for s0 in (2 * (pc >> 1), 2 * (pc >> 1) + 1):
+        c.within("fp8 gate|up: weight slot store", 16 * r + 4 * (s0 ^ ((r >> 1) & 3)) + 2 * (pc & 1) + 1, 64 * 16)
+    c.within("fp8 gate|up: weight slot read", 16 * 63 + 4 * 3 + 3, 64 * 16)
+    # bias rows of the four blocks in the scale table: 64 rows of G (G <= MAXG)
+    maxg = s.maxg_wide(H, "gateup")
+    c.true("fp8 gate|up: bias rows fit the scale table", 64 * s.Gh <= 64 * maxg)
+    ns = -(-max_groups(s.gs) // 16)
+    xs_stride = max_groups(s.gs) + 4
+    c.within("fp8 gate|up: group sum read", 63 * xs_stride + 16 * ns - 1, 64 * xs_stride)
+
+
 def check_problem(oracle, p, fp32):
     s = Setup(oracle, p, fp32)
     c = Checker(f"{p.name} fp32={fp32} gs={p.gs} bits={p.bits}")
@@ -445,6 +498,7 @@ def check_problem(oracle, p, fp32):
     for kind in ("gateup", "down"):
         check_skinny(c, s, kind)
         check_wide(c, s, kind)
+    check_fp8_gateup(c, s)
     check_route_and_combine(c, s)
     c.done()
     return s

@@ -1721,6 +1721,12 @@ using DownWideSmem = DownSmem<kWideRB<kF32H, BITS>, kF32H, MAXG, BITS>;
 // 64-column chains (the host prepares x for it under the same condition).
 template <bool kF32H, int GS, int BITS>
 constexpr bool kFp8Gateup = !kF32H && BITS == 4 && Geo<GS>::kChain == 64;
+// Tiles of at least kFp8MinRows rows take the fp8 operands.  An expert of
+// more than kBmBig rows is cut into tiles of at least (kBmBig + 1) / 2 rows,
+// so all tiles of one expert take the same path and a row's bits do not
+// depend on its place among its expert's rows.
+constexpr int kFp8MinRows = 32;
+static_assert((kBmBig + 1) / 2 >= kFp8MinRows, "an expert's tiles must share one operand path");
 template <bool kF32H, int MAXG, int GS, int BITS>
 using GateupSmem = std::conditional_t<kFp8Gateup<kF32H, GS, BITS>, GateupFp8Smem<MAXG>,
                                       GateupWideSmem<kF32H, MAXG, BITS>>;
@@ -1732,8 +1738,13 @@ __global__ __launch_bounds__(kThreads, (kWideWgsPerCu<GateupSmem<kF32H, MAXG, GS
     if (!wide_work(a, (a.I + 127) / 128, ti, by)) return;
     const int4 tile = reinterpret_cast<const int4*>(a.tiles)[ti];
     if constexpr (kFp8Gateup<kF32H, GS, BITS>) {
+        // tiles of fewer than 32 rows (one 32-row block) on the exact bf16
+        // operand, which is faster there
         __shared__ GateupFp8Smem<MAXG> sm;
-        gateup_wide_fp8<GS, MAXG>(a, sm, tile.x, tile.y, tile.z, by);
+        if (tile.z >= kFp8MinRows)
+            gateup_wide_fp8<GS, MAXG>(a, sm, tile.x, tile.y, tile.z, by);
+        else
+            gateup_wide<GS, kWideRowBlocks, MAXG, false, BITS>(a, sm, tile.x, tile.y, tile.z, by);
     } else {
         __shared__ GateupWideSmem<kF32H, MAXG, BITS> sm;
         gateup_wide<GS, kWideRB<kF32H, BITS>, MAXG, kF32H, BITS>(a, sm, tile.x, tile.y, tile.z, by);

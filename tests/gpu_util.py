@@ -196,11 +196,17 @@ def check_y_model(oracle_lib, p, rows, h_gpu, y_gpu, fp32, what="y"):
 
 
 def fp8_wide_gateup(p, fp32: bool) -> bool:
-    """Whether the forward's wide gate|up matmul takes fp8 operands (x as
+    """Whether some wide gate|up tile of the forward takes fp8 operands (x as
     e4m3 hi + lo, the codes as e4m3 bytes): bf16 mode, 4-bit codes in groups
-    of 64 or 128, more than 16 tokens.  Its sums then differ in the last
-    bits from the skinny path's exact bf16 operand."""
-    return (not fp32) and p.bits == 4 and p.gs in (64, 128) and p.T > 16
+    of 64 or 128, more than 16 tokens, and a tile of at least 32 rows (the
+    forward cuts an expert of c > 16 rows into ceil(c / 64) near-equal
+    tiles, so that is an expert of at least 32 rows).  Such rows differ in
+    the last bits from the exact bf16 operand."""
+    if fp32 or p.bits != 4 or p.gs not in (64, 128) or p.T <= 16:
+        return False
+    ids = p.topk_ids.ravel()
+    counts = np.bincount(ids[(ids >= 0) & (ids < p.E)], minlength=p.E)
+    return bool((counts >= 32).any())
 
 
 def assert_same_or_within(a, b, same_path: bool, bound, what=""):

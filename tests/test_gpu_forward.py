@@ -365,6 +365,7 @@ def test_rows_bitwise_independent_of_tile_path(oracle_lib, fp32, gs, bits):
     oa, ba = compare(oracle_lib, a, fp32, with_bound=True)
     ob, bb = compare(oracle_lib, b, fp32, with_bound=True)
     assert_same_or_within(ob[:20], oa, not fp8_wide_gateup(b, fp32), ba + bb[:20], "skinny vs wide tile")
+    assert fp8_wide_gateup(b, fp32) == ((not fp32) and bits == 4 and gs in (64, 128))
     # and a token permutation only permutes the output
     perm = np.random.default_rng(5).permutation(b.T)
     q = dataclasses.replace(b)

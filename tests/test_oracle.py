@@ -461,6 +461,19 @@ def test_forward_tiles_invariants(oracle_lib, seed):
             assert w[:, 2].sum() == c
 
 
+def test_forward_tiles_one_operand_path_per_expert(oracle_lib):
+    """The bf16 gate|up launch picks its operand format per tile (fp8 from
+    32 rows up).  With 64-row tiles every tile of an expert falls on the same
+    side of 32 rows, and the side is that of the expert's own count, so a
+    row's bits never depend on where it sits among its expert's rows."""
+    counts = np.arange(17, 1025, dtype=np.int32)
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    wide, _ = oracle_lib.forward_tiles(counts, offsets, 64, 16)
+    for e, c in enumerate(counts):
+        rows = wide[wide[:, 0] == e, 2]
+        assert np.all((rows >= 32) == (c >= 32)), (c, rows)
+
+
 # ------------------------------------------------- whole-batch entry point
 @pytest.mark.parametrize("case", ["tiny", "invalid", "silu", "gs32-8bit", "gs128-indep"])
 def test_ffn_all_same_bits_as_per_token_path(oracle_lib, case):

@@ -351,8 +351,15 @@ def _skinny_batch(c, s, kind, GS, BITS, NB, ncb, K, N, G, ti, cb):
         c.resource(f"{kind} skinny: weight block", row0[b] * row_words * 4, 64 * row_words,
                    s.size[wbuf] * 4)
         c.within(f"{kind} skinny: weight row", row0[b] + 15, N * s.E)
-    # SkinnySmem: w [NB * 16 * 4 * BITS] u32, ts/tb [NB * 16 * MAXG]
+    # SkinnySmem: w [NB * 16 * 4 * BITS] u32, ts/tb [NB * 16 * MAXG] u16, dst/wt [16]
     c.true("skinny: table store fits", (NB - 1) * 16 * G + 8 * (2 * G - 1) + 7 < NB * 16 * MAXG)
+    # bias_from_table: lane q reads entries 8 q + 32 st + [0, 8) of every row
+    # of both tables for st < ceil(G / 32), masked at or past G: the reads of
+    # tb's last row go up to 62 bytes past its G entries and must stay inside
+    # the struct (tb's spare entries, then dst/wt)
+    steps = -(-G // 32)
+    last_read = NB * 16 * MAXG + (NB * 16 - 1) * G + 8 * 3 + 32 * (steps - 1) + 7  # u16 past ts
+    c.within("skinny: bias table read (u16 past ts)", last_read, 2 * NB * 16 * MAXG + 2 * 16 * 2)
     arow = rbeg + np.minimum(lr[None, :], rows - 1)  # the lane's activation row
     c.within(f"{kind} skinny: sorted row", arow, s.A)
     kc64 = kchain(GS) == 64

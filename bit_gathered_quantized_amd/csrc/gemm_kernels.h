@@ -1508,9 +1508,13 @@ __device__ __forceinline__ void gateup_wide_fp8(const FfnArgs& a, GateupFp8Smem<
                         b[c2] = codes_as_fp8(wq[c2][j]);
                         s16[c2] = scale16(sm.ts[wave][(32 * c2 + n) * G + g]);
                     }
+                    // both 32-row halves, also in a tile of exactly 32 rows (its
+                    // staged rows 32..63 repeat its last row and are never
+                    // stored): with no branch between them the scheduler runs
+                    // one half's scale FMAs beside the other half's MFMAs
 #pragma unroll
                     for (int r2 = 0; r2 < 2; ++r2) {
-                        if (32 * r2 < rows) {
+                        {
                             // columns 16 kh + [0, 16) and 32 + 16 kh + [0, 16) of the chain
                             const int row = 32 * r2 + n, p0 = 4 * j + kh;
                             const u32x4 h0 = lds_frag(sm, buf, 0, row, p0), h1 = lds_frag(sm, buf, 0, row, p0 + 2);
